@@ -1,0 +1,238 @@
+"""Seeded synthetic inputs for the attention forward and the paged decode.
+
+This module only draws and encodes data: it holds none of the attention
+arithmetic.  Both the HIP path (through the binding) and the CPU oracle take
+their inputs from here, and from nowhere else.
+
+Every array is drawn in float32 from NumPy's PCG64 generator seeded with
+``[seed, stream_id]`` and rounded to bfloat16 (round to nearest, ties to even)
+by bit arithmetic.  bf16 tensors are returned as ``uint16`` arrays of their bit
+patterns, in the memory layout the library consumes:
+
+* BSHD: ``[B, S, H, D]``; BHSD: ``[B, H, S, D]`` (D innermost in both).
+* Paged KV pool: ``[num_pages, 16, Hkv, D]`` with an int32 block table
+  ``[B, max_blocks]`` (unused entries are -1) and int32 ``seq_lens``.
+
+The five named workloads below are synthetic stand-ins for the workloads the
+pages measure on (Llama-style GQA prefill, video-diffusion self and cross
+attention, vLLM-style paged decode): same shapes, value distributions and
+structure, random data.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+D = 128
+PAGE = 16
+BF16_QNAN = np.uint16(0x7FC0)
+
+# stream ids for default_rng([seed, stream])
+_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX = range(8)
+
+BSHD = 0
+BHSD = 1
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def _rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(stream)])
+
+
+def _normal(seed, stream, shape):
+    return _rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
+
+
+def _uniform(seed, stream, shape, lo=-1.0, hi=1.0):
+    return _rng(seed, stream).uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def _draw(dist, seed, stream, shape):
+    if dist == "normal":
+        return _normal(seed, stream, shape)
+    if dist == "uniform":
+        return _uniform(seed, stream, shape)
+    if dist == "zeros":
+        return np.zeros(shape, np.float32)
+    raise ValueError(dist)
+
+
+def layout_shape(layout: int, B: int, H: int, S: int, d: int = D):
+    return (B, S, H, d) if layout == BSHD else (B, H, S, d)
+
+
+@dataclass
+class Prefill:
+    """One prefill problem; q/k/v are bf16 bit arrays in `layout`."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    layout: int
+    causal: bool
+    scale: float
+    name: str = ""
+    hot_rows: list = field(default_factory=list)  # (b, s, h) query vectors scaled x8
+
+    @property
+    def flops(self) -> float:
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * D
+        return f / 2 if self.causal else f
+
+
+def prefill_inputs(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0,
+                   scale=None, q_dist="normal", k_dist="normal", v_dist="normal",
+                   n_hot=0, name="") -> Prefill:
+    """Draw a prefill problem.  `n_hot` query vectors Q[b, s, h, :] (drawn by
+    the seed) are multiplied by 8 before rounding; x8 is a power of two, so it
+    commutes with the bf16 rounding."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qf = _draw(q_dist, seed, _S_Q, layout_shape(layout, B, Hq, Sq))
+    hot = []
+    if n_hot:
+        r = _rng(seed, _S_HOT)
+        flat = r.choice(B * Sq * Hq, size=n_hot, replace=False)
+        for f in sorted(int(x) for x in flat):
+            b, rem = divmod(f, Sq * Hq)
+            s, h = divmod(rem, Hq)
+            hot.append((b, s, h))
+            if layout == BSHD:
+                qf[b, s, h, :] *= 8.0
+            else:
+                qf[b, h, s, :] *= 8.0
+    q = f32_to_bf16_bits(qf)
+    del qf
+    k = f32_to_bf16_bits(_draw(k_dist, seed, _S_K, layout_shape(layout, B, Hkv, Sk)))
+    v = f32_to_bf16_bits(_draw(v_dist, seed, _S_V, layout_shape(layout, B, Hkv, Sk)))
+    return Prefill(q, k, v, B, Hq, Hkv, Sq, Sk, layout, bool(causal), float(scale),
+                   name=name, hot_rows=hot)
+
+
+@dataclass
+class Decode:
+    q: np.ndarray            # bf16 bits [B, Hq, D]
+    k_pool: np.ndarray       # bf16 bits [P, 16, Hkv, D]
+    v_pool: np.ndarray
+    block_table: np.ndarray  # int32 [B, max_blocks], -1 beyond each sequence
+    seq_lens: np.ndarray     # int32 [B]
+    B: int
+    Hq: int
+    Hkv: int
+    scale: float
+    name: str = ""
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def tokens(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum())
+
+    @property
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: K and V of every valid token of every KV
+        head, plus Q, O, LSE, the block-table entries read and seq_lens."""
+        n_pages_read = int(sum((int(x) + PAGE - 1) // PAGE for x in self.seq_lens))
+        return (2 * D * 2 * self.Hkv * self.tokens + self.B * self.Hq * D * 2 * 2
+                + self.B * self.Hq * 4 + n_pages_read * 4 + self.B * 4)
+
+    @property
+    def flops(self) -> float:
+        return 4.0 * self.Hq * D * self.tokens
+
+
+def decode_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, scale=None, lens=None,
+                  permute=True, poison_tail=True, name="") -> Decode:
+    """Paged decode problem: lens ~ U{1..max_len} (unless given), 16-token
+    pages dealt out in sequence order from one random permutation of the pool;
+    slots past each sequence's end hold bf16 NaN."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if lens is None:
+        lens = _rng(seed, _S_LENS).integers(1, max_len + 1, size=B)
+    lens = np.asarray(lens, dtype=np.int32)
+    assert lens.shape == (B,) and lens.min() >= 1
+    max_blocks = (max_len + PAGE - 1) // PAGE
+    nb = (lens.astype(np.int64) + PAGE - 1) // PAGE
+    assert nb.max() <= max_blocks
+    P = int(nb.sum())
+    ids = _rng(seed, _S_PERM).permutation(P) if permute else np.arange(P)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nb[b]] = ids[off:off + nb[b]]
+        off += int(nb[b])
+    kp = f32_to_bf16_bits(_normal(seed, _S_K, (P, PAGE, Hkv, D)))
+    vp = f32_to_bf16_bits(_normal(seed, _S_V, (P, PAGE, Hkv, D)))
+    if poison_tail:
+        for b in range(B):
+            t = int(lens[b]) % PAGE
+            if t:
+                last = table[b, nb[b] - 1]
+                kp[last, t:] = BF16_QNAN
+                vp[last, t:] = BF16_QNAN
+    q = f32_to_bf16_bits(_normal(seed, _S_Q, (B, Hq, D)))
+    return Decode(q, kp, vp, table, lens, B, Hq, Hkv, float(scale), name=name)
+
+
+# --------------------------------------------------------------------------
+# The named workloads (d = 128, bf16, scale = 1/sqrt(128) throughout).
+
+def config1(seed=1):
+    """Tiny MHA forward, BSHD, non-causal; 8 query vectors scaled x8."""
+    return prefill_inputs(1, 4, 4, 256, 256, layout=BSHD, seed=seed, n_hot=8,
+                          name="mha_tiny_b1_h4_s256_bshd")
+
+
+def config2(seed=2):
+    """MHA prefill B=4, H=32, S=4096, BHSD, non-causal."""
+    return prefill_inputs(4, 32, 32, 4096, 4096, layout=BHSD, seed=seed,
+                          name="mha_prefill_b4_h32_s4096_bhsd")
+
+
+def config3(seed=3):
+    """Causal GQA prefill B=8, Hq=32, Hkv=8, S=8192, BSHD; V ~ U(-1, 1)."""
+    return prefill_inputs(8, 32, 8, 8192, 8192, layout=BSHD, causal=True,
+                          seed=seed, v_dist="uniform",
+                          name="gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd")
+
+
+def config4_self(seed=4):
+    """Diffusion-style self attention B=2, H=12, S=32760, BSHD."""
+    return prefill_inputs(2, 12, 12, 32760, 32760, layout=BSHD, seed=seed,
+                          name="diffusion_self_b2_h12_s32760_bshd")
+
+
+def config4_cross(seed=4, self_problem: Prefill | None = None):
+    """Cross attention reusing the self-attention Q against 512 fresh keys."""
+    if self_problem is None:
+        self_problem = config4_self(seed)
+    k = f32_to_bf16_bits(_normal(seed, _S_KX, layout_shape(BSHD, 2, 12, 512)))
+    v = f32_to_bf16_bits(_normal(seed, _S_VX, layout_shape(BSHD, 2, 12, 512)))
+    return Prefill(self_problem.q, k, v, 2, 12, 12, 32760, 512, BSHD, False,
+                   self_problem.scale, name="diffusion_cross_b2_h12_sq32760_sk512_bshd")
+
+
+def config5(seed=5):
+    """Paged split-KV decode B=32, Hq=32, Hkv=8, lens ~ U{1..4096}."""
+    return decode_inputs(32, 32, 8, max_len=4096, seed=seed,
+                         name="paged_decode_b32_hq32_hkv8_len4096_page16")

@@ -1,0 +1,14 @@
+"""CPU fp64 oracle for exact attention (TEST INFRASTRUCTURE).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The library path never calls it, and it shares no code with the
+HIP kernels: the two meet only in the seeded input generator (``attn_inputs``).
+
+* ``oracle.attention``: the materialised definition, softmax(scale*Q*K^T)*V,
+  in float64 on the exact bf16 inputs, for prefill (MHA/GQA/MQA, causal,
+  cross-attention, BSHD/BHSD) and for the paged decode (gather, then the same
+  definition).
+* ``oracle.online``: a float64 model of the blockwise online softmax and of the
+  split-KV merge, used only to pin the oracle to the pages' merge rule.
+"""
+from . import attention, online  # noqa: F401

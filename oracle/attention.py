@@ -1,0 +1,237 @@
+"""Materialised fp64 attention: the oracle (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg may use this
+module; the library never does.
+
+What it computes, and where the pages define it:
+
+* Attention is the fused operation softmax(Q K^T / sqrt(d)) V ("MoonMath AI
+  open-sources a HIP attention kernel for AMD MI300X that beats AITER v3",
+  definition paragraph), here with a caller-given scale (the default
+  1/sqrt(d) is the one in "IO-aware tiling strategy in FlashAttention-4",
+  checklist item 2).  The plain, materialised form builds the full score matrix
+  S = scale*Q*K^T, takes a row softmax and multiplies by V ("IO-aware tiling
+  strategy in FlashAttention-4", body, second paragraph).
+* Several query heads share one K/V head (MQA/GQA: "Engineering the
+  FlashAttention-4 kernel port to ROCm", section on vendor-agnostic multi-query
+  inference).  Reading taken: contiguous groups, kv = h // (Hq / Hkv).
+* Causal masking keeps the lower triangle ("Reverse engineering Flash Attention
+  4's proprietary fused attention kernel", point 1, the upper_triangular mask).
+  Reading taken when Sq != Sk: bottom-right alignment, key j is visible from
+  query i iff j <= i + (Sk - Sq).  A row with no visible key returns O = 0 and
+  LSE = -inf.
+* LSE is the natural log of the softmax denominator over visible keys,
+  m + ln(l), the statistics the pages say are kept ("Reverse engineering ...",
+  point 2; "IO-aware tiling ...", backward-pass paragraph).
+* Paged decode: K/V of sequence b live in 16-token pages listed by an int32
+  block table ("Engineering the FlashAttention-4 kernel port to ROCm",
+  multi-query section, paged KV cache); the oracle gathers them into a dense
+  [len_b, Hkv, d] tensor and applies the same definition with one query row.
+
+Inputs are the bf16 bit patterns the GPU sees, upcast exactly to float64; the
+scale is rounded to float32 first, as the library receives it.  Everything else
+is float64.  Rows are independent, so computing them in chunks changes nothing.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+from threadpoolctl import threadpool_limits
+
+BSHD = 0
+BHSD = 1
+PAGE = 16
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns (uint16) to float64."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def scale_as_f32(scale: float) -> float:
+    """The library takes the scale as a float32; the oracle uses that value."""
+    return float(np.float32(scale))
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """Query head h reads K/V head h // (Hq/Hkv) (contiguous GQA groups)."""
+    return h // (Hq // Hkv)
+
+
+def visible_keys(i: int, Sq: int, Sk: int, causal: bool) -> int:
+    """Number of keys (a prefix 0..n-1) that query row i attends to."""
+    if not causal:
+        return Sk
+    return max(0, min(Sk, i + (Sk - Sq) + 1))
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * Q K^T for q [n, d], k [Sk, d] -> [n, Sk]."""
+    return scale * (q @ k.T)
+
+
+def row_softmax(s: np.ndarray):
+    """Row softmax of s (entries -inf are masked).  Returns (P, m, l) with
+    m the row max and l = sum_j exp(s_ij - m); an all-masked row has P = 0,
+    m = -inf, l = 0."""
+    m = s.max(axis=1)
+    empty = m == -np.inf
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    p = e / np.where(empty, 1.0, l)[:, None]
+    return p, m, l
+
+
+def attend_rows(q, k, v, scale, n_visible=None):
+    """Materialised attention for query rows q [n, d] against k, v [Sk, d]
+    (float64).  n_visible[i] limits row i to keys 0..n_visible[i]-1.
+    Returns (o [n, d], lse [n])."""
+    if k.shape[0] == 0:  # no key at all: every row is empty
+        return np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf)
+    s = scores(q, k, scale)
+    if n_visible is not None:
+        j = np.arange(k.shape[0])
+        s = np.where(j[None, :] >= np.asarray(n_visible)[:, None], -np.inf, s)
+    p, m, l = row_softmax(s)
+    o = p @ v
+    with np.errstate(divide="ignore"):
+        lse = np.where(m == -np.inf, -np.inf, m + np.log(np.where(l > 0, l, 1.0)))
+    return o, lse
+
+
+def _logical(x, layout):
+    """View a [B,S,H,D] (BSHD) or [B,H,S,D] (BHSD) array as [B,H,S,D]."""
+    return x.transpose(0, 2, 1, 3) if layout == BSHD else x
+
+
+def _workers():
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def attention(q_bits, k_bits, v_bits, B, Hq, Hkv, Sq, Sk, scale, causal, layout,
+              chunk=256, workers=None):
+    """Full prefill oracle.  Returns (o [B, Hq, Sq, D] float64 in logical
+    head-major order, lse [B, Hq, Sq] float64)."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    qv = _logical(q_bits, layout)
+    kv = _logical(k_bits, layout)
+    vv = _logical(v_bits, layout)
+    d = q_bits.shape[-1]
+    sc = scale_as_f32(scale)
+    o = np.zeros((B, Hq, Sq, d), np.float64)
+    lse = np.zeros((B, Hq, Sq), np.float64)
+    nvis = np.array([visible_keys(i, Sq, Sk, causal) for i in range(Sq)], np.int64)
+
+    def job(b, h, i0):
+        g = kv_head_of(h, Hq, Hkv)
+        i1 = min(Sq, i0 + chunk)
+        kmax = int(nvis[i0:i1].max()) if causal else Sk
+        qq = bf16_to_f64(qv[b, h, i0:i1])
+        kk = bf16_to_f64(kv[b, g, :kmax])
+        vv_ = bf16_to_f64(vv[b, g, :kmax])
+        oo, ll = attend_rows(qq, kk, vv_, sc, np.minimum(nvis[i0:i1], kmax))
+        o[b, h, i0:i1] = oo
+        lse[b, h, i0:i1] = ll
+
+    jobs = [(b, h, i0) for b in range(B) for h in range(Hq) for i0 in range(0, Sq, chunk)]
+    _run(job, jobs, workers)
+    return o, lse
+
+
+def attention_sampled(q_bits, k_bits, v_bits, B, Hq, Hkv, Sq, Sk, scale, causal,
+                      layout, samples, workers=None):
+    """Oracle outputs for selected query rows only.  samples: list of
+    (b, h, i).  Returns (o [n, D], lse [n]) in the order given."""
+    qv = _logical(q_bits, layout)
+    kv = _logical(k_bits, layout)
+    vv = _logical(v_bits, layout)
+    sc = scale_as_f32(scale)
+    d = q_bits.shape[-1]
+    o = np.zeros((len(samples), d), np.float64)
+    lse = np.zeros(len(samples), np.float64)
+    # group rows by (b, h) so each K/V head is upcast once per group
+    groups = {}
+    for n, (b, h, i) in enumerate(samples):
+        groups.setdefault((b, h), []).append((n, i))
+
+    def job(b, h):
+        g = kv_head_of(h, Hq, Hkv)
+        items = groups[(b, h)]
+        rows = np.array([i for _, i in items])
+        nv = np.array([visible_keys(int(i), Sq, Sk, causal) for i in rows])
+        kmax = int(nv.max())
+        qq = bf16_to_f64(qv[b, h, rows])
+        kk = bf16_to_f64(kv[b, g, :kmax])
+        vv_ = bf16_to_f64(vv[b, g, :kmax])
+        oo, ll = attend_rows(qq, kk, vv_, sc, nv)
+        for r, (n, _) in enumerate(items):
+            o[n] = oo[r]
+            lse[n] = ll[r]
+
+    _run(job, list(groups.keys()), workers)
+    return o, lse
+
+
+def gather_pages(pool_bits, block_table, seq_len, b, g):
+    """Dense [len, D] view of KV head g of sequence b from a paged pool
+    [num_pages, 16, Hkv, D]: token t lives in page block_table[b, t // 16],
+    slot t % 16."""
+    t = np.arange(int(seq_len))
+    pages = block_table[b, t // PAGE]
+    return pool_bits[pages, t % PAGE, g]
+
+
+def decode_paged(q_bits, k_pool, v_pool, block_table, seq_lens, Hkv, scale,
+                 workers=None):
+    """Paged decode oracle: one query row per (b, h) against all seq_lens[b]
+    cached tokens.  Returns (o [B, Hq, D], lse [B, Hq]) float64."""
+    B, Hq, d = q_bits.shape
+    sc = scale_as_f32(scale)
+    o = np.zeros((B, Hq, d), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+
+    def job(b):
+        n = int(seq_lens[b])
+        for g in range(Hkv):
+            kk = bf16_to_f64(gather_pages(k_pool, block_table, n, b, g))
+            vv = bf16_to_f64(gather_pages(v_pool, block_table, n, b, g))
+            heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
+            oo, ll = attend_rows(bf16_to_f64(q_bits[b, heads]), kk, vv, sc)
+            o[b, heads] = oo
+            lse[b, heads] = ll
+
+    _run(job, list(range(B)), workers)
+    return o, lse
+
+
+def _run(fn, jobs, workers):
+    workers = workers or _workers()
+    if workers == 1 or len(jobs) == 1:
+        for j in jobs:
+            fn(*j) if isinstance(j, tuple) else fn(j)
+        return
+    # one BLAS thread per worker: the parallelism is over independent rows
+    with threadpool_limits(limits=1, user_api="blas"), \
+            ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(fn, *j) if isinstance(j, tuple) else ex.submit(fn, j) for j in jobs]
+        for f in futs:
+            f.result()
+
+
+def flops_prefill(B, Hq, Sq, Sk, d, causal):
+    """Algorithmic FLOP of the forward: 4*B*Hq*Sq*Sk*d, halved when causal."""
+    f = 4.0 * B * Hq * Sq * Sk * d
+    return f / 2 if causal else f
+
+
+__all__ = ["bf16_to_f64", "scale_as_f32", "kv_head_of", "visible_keys", "scores",
+           "row_softmax", "attend_rows", "attention", "attention_sampled",
+           "gather_pages", "decode_paged", "flops_prefill"]
