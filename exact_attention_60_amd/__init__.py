@@ -1,0 +1,172 @@
+"""Exact attention on MI355X (gfx950): Python binding of libattn.so.
+
+The binding only marshals arguments: it checks tensor dtypes, devices and
+shapes, allocates outputs (and the decode workspace) with torch, and calls the
+C ABI declared in include/attn.h with raw pointers and the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; if the
+library is not built the binding raises instead of computing anything itself.
+
+    o, lse = attn_fwd(q, k, v, causal=False, scale=None, layout="bshd")
+    o, lse = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_BSHD = 0
+ATTN_BHSD = 1
+HEAD_DIM = 128
+PAGE_SIZE = 16
+
+STATUS = {
+    0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
+    -4: "ATTN_ERR_ALIGN", -5: "ATTN_ERR_WORKSPACE", -6: "ATTN_ERR_LAUNCH",
+    -7: "ATTN_ERR_DEVICE",
+}
+
+# every symbol include/attn.h declares
+EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_paged",
+           "attn_status_string", "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = library().attn_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def library() -> ctypes.CDLL:
+    """Load libattn.so (built in-tree by exact_attention_60_amd._build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m exact_attention_60_amd._build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        lib.attn_fwd.restype = i
+        lib.attn_decode_workspace_bytes.argtypes = [i, i, i]
+        lib.attn_decode_workspace_bytes.restype = sz
+        lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
+                                          sz, vp]
+        lib.attn_decode_paged.restype = i
+        lib.attn_status_string.argtypes = [i]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_version.argtypes = []
+        lib.attn_version.restype = i
+        _lib = lib
+    return _lib
+
+
+def attn_version() -> int:
+    return library().attn_version()
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(status).decode()
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, max_blocks_per_seq: int) -> int:
+    return int(library().attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_bf16(name, t):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
+             layout: str = "bshd", out=None, lse=None, stream=None):
+    """Fused exact attention forward.  q: [B, Sq, Hq, 128] (bshd) or
+    [B, Hq, Sq, 128] (bhsd); k, v likewise with Hkv heads and Sk keys.
+    Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(n, t)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q, k, v must be 4-D and k, v of equal shape")
+    lay = {"bshd": ATTN_BSHD, "bhsd": ATTN_BHSD}[layout.lower()]
+    if lay == ATTN_BSHD:
+        B, Sq, Hq, d = q.shape
+        _, Sk, Hkv, _ = k.shape
+    else:
+        B, Hq, Sq, d = q.shape
+        _, Hkv, Sk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q and k disagree on batch or head dim")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)),
+                            lay, _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: float | None = None,
+                      out=None, lse=None, workspace=None, stream=None):
+    """One paged decode step.  q: [B, Hq, 128]; k_cache, v_cache:
+    [num_pages, 16, Hkv, 128]; block_table: int32 [B, max_blocks];
+    seq_lens: int32 [B].  Returns (o bf16 [B, Hq, 128], lse fp32 [B, Hq])."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_bf16(n, t)
+    for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    B, Hq, d = q.shape
+    num_pages, page, Hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d or block_table.shape[0] != B:
+        raise ValueError("inconsistent decode shapes")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_decode_workspace_bytes(B, Hq, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = library().attn_decode_paged(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page, max_blocks,
+        num_pages, float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged")
+    return out, lse
+
+
+__all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_string",
+           "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "EXPORTS", "LIB_PATH"]

@@ -1,0 +1,151 @@
+// C ABI of the gfx950 attention library: argument checks, launch geometry and
+// launches on the caller's stream.  Every check runs before the first HIP
+// call, so invalid arguments are reported without touching a device, and the
+// library never allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, -1 unusable
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Checks once per device that it is a gfx950 and caches its CU count.
+int current_device_cus(int* cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    st = ok ? 1 : -1;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return ATTN_ERR_DEVICE;
+  *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return ATTN_VERSION; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (sizes must be >= 1, Hq a multiple of Hkv, within limits)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (d must be 128, page_size 16, layout BSHD/BHSD, scale finite and > 0, causal 0/1)";
+    case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int d, float scale, int causal, int layout,
+             void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
+      (causal != 0 && causal != 1) || !scale_ok(scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  const int64_t D = attn::kHeadDim;
+  attn::PrefillArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  if (layout == ATTN_BSHD) {
+    a.q_sb = (int64_t)Sq * Hq * D; a.q_sh = D; a.q_ss = (int64_t)Hq * D;
+    a.k_sb = (int64_t)Sk * Hkv * D; a.k_sh = D; a.k_ss = (int64_t)Hkv * D;
+  } else {
+    a.q_sb = (int64_t)Hq * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
+    a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
+  }
+  // K/V of one (batch, kv head) are addressed with 32-bit byte offsets
+  if ((int64_t)(Sk - 1) * a.k_ss * 2 + 256 > INT32_MAX) return ATTN_ERR_SHAPE;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
+  a.group = Hq / Hkv;
+  a.n_qt = (Sq + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
+  a.c = scale * 1.4426950408889634f;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+  const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
+  if (B < 1 || Hq < 1 || max_blocks_per_seq < 1) return 0;
+  const size_t splits = (size_t)attn::decode_max_splits(max_blocks_per_seq);
+  return (size_t)B * Hq * splits * (attn::kHeadDim + 1) * sizeof(float);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      int B, int Hq, int Hkv, int d, int page_size, int max_blocks_per_seq,
+                      int num_pages, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_pages < 1)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * attn::kPage > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (d != attn::kHeadDim || page_size != attn::kPage || !scale_ok(scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) ||
+      !aligned16(seq_lens) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+
+  attn::DecodeArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.kc = static_cast<const __bf16*>(k_cache);
+  a.vc = static_cast<const __bf16*>(v_cache);
+  a.table = block_table;
+  a.lens = seq_lens;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.n_hb = (a.G + attn::kDecodeHeadsPerBlock - 1) / attn::kDecodeHeadsPerBlock;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_splits = attn::decode_max_splits(max_blocks_per_seq);
+  a.pps = attn::decode_pages_per_split(B, Hkv, a.n_hb, max_blocks_per_seq, cus);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + (size_t)B * Hq * a.max_splits * attn::kHeadDim;
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  a.token_stride = (int64_t)Hkv * attn::kHeadDim;
+  a.page_stride = (int64_t)attn::kPage * a.token_stride;
+  a.c = scale * 1.4426950408889634f;
+  const hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

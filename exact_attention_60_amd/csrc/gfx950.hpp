@@ -1,0 +1,99 @@
+// gfx950 (CDNA4) building blocks shared by the attention kernels.
+//
+// Lane layouts relied on (wave64; verified on the device by a layout probe):
+//  * v_mfma_f32_32x32x16_bf16: A operand lane l holds A[l%32][k-slots of half
+//    l/32], B operand lane l holds B[k-slots of half l/32][l%32], the k-slots
+//    being the same for A and B; accumulator register r of lane l holds
+//    C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//  * ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
+//    j%4 of the 4-element (64-bit) row addressed by lane 4*e + j/4, for
+//    e = 0..3.
+//  * v_permlane32_swap with both operands equal returns the lower half of the
+//    wave broadcast to both halves (first result) and the upper half (second).
+//  * the float -> bf16 conversion (v_cvt_pk_bf16_f32) rounds to nearest even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Value of lane (l ^ 32), for a wave64.
+__device__ __forceinline__ float xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const bool upper = (threadIdx.x & 32) != 0;
+  return __uint_as_float(upper ? r[0] : r[1]);
+}
+__device__ __forceinline__ float max_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+// two floats -> packed fp16 (v_cvt_pk_f16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+// sum of the two fp16 halves of u added to acc in fp32 (v_dot2c_f32_f16)
+__device__ __forceinline__ float sum2_f16(uint32_t u, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u), one, acc, false);
+}
+// sum of the two bf16 halves of u added to acc in fp32 (v_dot2c_f32_bf16)
+__device__ __forceinline__ float sum2_bf16(uint32_t u, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), one, acc, false);
+}
+// two bf16 (packed in u) -> two fp16 (packed); exact for |x| in the fp16
+// normal range, |x| >= 65520 becomes +-inf
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
+  return pack_f16(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+
+// p must point into __shared__ memory (8-byte aligned).
+__device__ __forceinline__ bf16x4 lds_read_tr(const void* p) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, t);
+}
+
+// True if any lane of the wave has `pred` set (wave-uniform result).
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+}  // namespace attn

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI host code (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// ---- prefill -------------------------------------------------------------
+constexpr int kHeadDim = 128;
+constexpr int kPrefillWaves = 4;                      // waves per workgroup
+constexpr int kPrefillRowsPerWave = 64;               // two 32-row MFMA blocks
+constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // 256 query rows
+constexpr int kPrefillBN = 64;                        // keys per K/V tile
+
+struct PrefillArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_ss;  // element strides of batch, head, sequence (q and o)
+  int64_t k_sb, k_sh, k_ss;  // same for k and v
+  int B, Hq, Hkv, Sq, Sk;
+  int group;                 // Hq / Hkv
+  int n_qt;                  // ceil(Sq / kPrefillBM)
+  float c;                   // scale * log2(e)
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
+
+// ---- paged decode ----------------------------------------------------------
+constexpr int kPage = 16;
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeMinPagesPerSplit = 8;   // bounds the workspace
+constexpr int kDecodeHeadsPerBlock = 16;     // query heads per MFMA column block
+
+struct DecodeArgs {
+  const __bf16* q;
+  const __bf16* kc;
+  const __bf16* vc;
+  const int32_t* table;
+  const int32_t* lens;
+  float* ws_o;     // [B, Hq, max_splits, 128] fp32 normalised partial outputs
+  float* ws_lse;   // [B, Hq, max_splits]      fp32 partial LSE (natural log)
+  __bf16* o;
+  float* lse;
+  int B, Hq, Hkv, G, n_hb;   // G = Hq / Hkv, n_hb = ceil(G / 16)
+  int max_blocks, max_splits, pps;
+  int64_t page_stride;       // elements per page: 16 * Hkv * 128
+  int64_t token_stride;      // elements per token slot: Hkv * 128
+  float c;                   // scale * log2(e)
+};
+
+int decode_max_splits(int max_blocks);
+int decode_pages_per_split(int B, int Hkv, int n_hb, int max_blocks, int num_cus);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

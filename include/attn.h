@@ -1,0 +1,143 @@
+/*
+ * attn.h - C ABI of the gfx950 (MI355X) exact-attention library (libattn.so).
+ *
+ * Two operations:
+ *
+ *   attn_fwd           O = softmax(scale * Q K^T) V, computed tile by tile with
+ *                      an online softmax so the score matrix never reaches HBM;
+ *                      also returns LSE, the natural-log softmax denominator.
+ *   attn_decode_paged  the same definition for one query row per sequence
+ *                      against a paged KV cache, split over the keys, with the
+ *                      partial results merged by their log-sum-exps.
+ *
+ * Definitions followed (page titles and sections):
+ *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
+ *    or BHSD without transposes, arbitrary lengths including cross-attention:
+ *    "MoonMath AI open-sources a HIP attention kernel for AMD MI300X that beats
+ *    AITER v3", definition and scope paragraphs;
+ *  - tiling with a running row max m and denominator l, merged per block as
+ *    m' = max(m, m_new), l' = l*exp(m - m') + l_new: "IO-aware tiling strategy
+ *    in FlashAttention-4", body;
+ *  - shared K/V heads for several query heads (MQA/GQA), paged KV cache with
+ *    16-token pages and an int32 block table: "Engineering the FlashAttention-4
+ *    kernel port to ROCm: HIP migration and multi-query inference
+ *    optimisation", multi-query section;
+ *  - causal (upper-triangular) masking: "Reverse engineering Flash Attention
+ *    4's proprietary fused attention kernel", point 1;
+ *  - the key split with a merge of partials for the tail: MoonMath page,
+ *    third-Q-tile paragraph;
+ *  - launching on the caller's stream so the call overlaps a larger
+ *    pipeline: MoonMath page, use-case paragraph.
+ *
+ * Conventions common to every entry point
+ *  - bf16 tensors are passed as raw device pointers to IEEE bfloat16 data;
+ *    d (head dim) must be 128 and is innermost and contiguous.
+ *  - Pointers are device pointers, 16-byte aligned.  The caller allocates and
+ *    owns every buffer (inputs, outputs, tables, workspace); the library never
+ *    allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it and the call returns; buffers must stay alive until
+ *    the stream has passed the launch.  Results are bitwise deterministic for
+ *    identical inputs and shapes (no atomics in the arithmetic, fixed order).
+ *  - Outputs must not alias inputs.
+ *  - Every argument check runs before any HIP call; a failed check returns its
+ *    status and enqueues nothing.  A launch the runtime rejects returns
+ *    ATTN_ERR_LAUNCH.  Faults inside kernels surface at the caller's next
+ *    synchronisation, as HIP defines.
+ *  - Reading taken for GQA: query head h uses K/V head h / (Hq / Hkv).
+ *  - Reading taken for causal with Sq != Sk: bottom-right alignment, key j is
+ *    visible from query i iff j <= i + (Sk - Sq).  A query row that sees no key
+ *    gets O = 0 and LSE = -inf.
+ *  - The scale is applied in fp32 to fp32 scores (never folded into bf16 Q).
+ *  - O is rounded to bf16 with round-to-nearest-even.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  ATTN_ERR_SHAPE = -2,       /* a size is < 1, Hq % Hkv != 0, size overflow    */
+  ATTN_ERR_UNSUPPORTED = -3, /* d != 128, page_size != 16, bad layout, scale   */
+  ATTN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned               */
+  ATTN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required     */
+  ATTN_ERR_LAUNCH = -6,      /* the HIP runtime rejected a launch              */
+  ATTN_ERR_DEVICE = -7       /* no usable gfx950 device / device query failed  */
+} attn_status;
+
+enum { ATTN_BSHD = 0, ATTN_BHSD = 1 };
+
+/*
+ * attn_fwd - fused exact attention forward (prefill, self- or cross-attention).
+ *
+ *   q    bf16, layout `layout`: BSHD [B, Sq, Hq, d] or BHSD [B, Hq, Sq, d]
+ *   k, v bf16, same layout:     BSHD [B, Sk, Hkv, d] or BHSD [B, Hkv, Sk, d]
+ *   o    bf16 output, same layout and shape as q
+ *   lse  fp32 output [B, Hq, Sq] (contiguous, for both layouts); natural log of
+ *        sum_j exp(scale * q_i . k_j) over the visible keys j
+ *   B, Hq, Hkv, Sq, Sk >= 1, Hq % Hkv == 0, d == 128
+ *   scale  finite float32 (1/sqrt(d) is the usual value)
+ *   causal 0 or 1
+ *
+ * Returns ATTN_OK or an attn_status error.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             int layout, void* stream);
+
+/*
+ * attn_decode_workspace_bytes - device workspace that attn_decode_paged needs
+ * for its split partials (fp32 partial outputs and their LSEs), for a batch of
+ * B sequences, Hq query heads and block tables of max_blocks_per_seq entries.
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq);
+
+/*
+ * attn_decode_paged - one decode step: attention of one query row per
+ * (sequence, query head) against every cached token, over a paged KV cache.
+ *
+ *   q            bf16 [B, Hq, d]
+ *   k_cache,     bf16 [num_pages, page_size, Hkv, d]: token t of sequence b
+ *   v_cache      is slot t % 16 of page block_table[b, t / 16]
+ *   block_table  int32 [B, max_blocks_per_seq]; entries p < ceil(seq_lens[b]/16)
+ *                must lie in [0, num_pages); entries beyond are never read
+ *   seq_lens     int32 [B], 1 <= seq_lens[b] <= max_blocks_per_seq * 16,
+ *                counting every cached token (the current one included)
+ *   o            bf16 output [B, Hq, d]
+ *   lse          fp32 output [B, Hq]
+ *   page_size == 16, d == 128, Hq % Hkv == 0
+ *   workspace    device memory of at least
+ *                attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq) bytes;
+ *                its contents on entry do not matter
+ *
+ * The table and seq_lens live on the device and are not read by the host, so
+ * their preconditions are documented, not checked.  Cache slots past a
+ * sequence's end may hold any bits (NaN included): they are never used.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o,
+                      float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                      int max_blocks_per_seq, int num_pages, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(int status);
+
+/* ATTN_VERSION of the built library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

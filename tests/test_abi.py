@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports what include/attn.h declares, and rejects
+invalid arguments before any HIP call (CPU only: no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_60_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ea.library()
+    declared = header_functions()
+    assert set(declared) == set(ea.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # and they are real dynamic symbols of the .so
+    out = os.popen(f"nm -D --defined-only {ea.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_status_strings():
+    assert ea.attn_version() == 1
+    for code in ea.STATUS:
+        assert ea.attn_status_string(code)
+    assert ea.attn_status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes():
+    # partials: B * Hq * ceil(max_blocks / 8) splits of (128 + 1) floats
+    assert ea.attn_decode_workspace_bytes(32, 32, 256) == 32 * 32 * 32 * 129 * 4
+    assert ea.attn_decode_workspace_bytes(1, 1, 1) == 129 * 4
+    assert ea.attn_decode_workspace_bytes(0, 1, 1) == 0
+    assert ea.attn_decode_workspace_bytes(1, 1, 0) == 0
+
+
+P = 0x10000  # a fake, 16-byte aligned "device" pointer: never dereferenced
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.1,
+             causal=0, layout=0, stream=None)
+    a.update(kw)
+    return ea.library().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                 a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"],
+                                 a["layout"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(v=None), -1),
+    (dict(B=0), -2), (dict(Sq=0), -2), (dict(Sk=-1), -2), (dict(Hq=3, Hkv=2), -2),
+    (dict(d=64), -3), (dict(layout=2), -3), (dict(causal=2), -3), (dict(scale=0.0), -3),
+    (dict(scale=float("nan")), -3), (dict(scale=float("inf")), -3), (dict(scale=-1.0), -3),
+    (dict(q=P + 8), -4), (dict(o=P + 2), -4), (dict(lse=P + 4), -4),
+    (dict(Sk=(1 << 22) + 1, Hkv=2, Hq=2, layout=0), -2),   # K/V of one head exceed 32-bit offsets
+])
+def test_fwd_argument_errors(kw, code):
+    assert fwd(**kw) == code
+
+
+def dec(**kw):
+    a = dict(q=P, k=P, v=P, tab=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, page=16,
+             mb=4, npages=8, scale=0.1, ws=P, wsb=10 ** 6, stream=None)
+    a.update(kw)
+    return ea.library().attn_decode_paged(a["q"], a["k"], a["v"], a["tab"], a["lens"], a["o"],
+                                          a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], a["page"],
+                                          a["mb"], a["npages"], a["scale"], a["ws"], a["wsb"],
+                                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tab=None), -1), (dict(lens=None), -1), (dict(q=None), -1),
+    (dict(B=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(mb=0), -2), (dict(npages=0), -2),
+    (dict(d=256), -3), (dict(page=32), -3), (dict(scale=0.0), -3),
+    (dict(k=P + 8), -4), (dict(tab=P + 4), -4),
+    (dict(ws=None), -5), (dict(wsb=100), -5),
+])
+def test_decode_argument_errors(kw, code):
+    assert dec(**kw) == code
+
+
+def test_valid_arguments_need_a_gfx950_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    # all checks pass, so the library asks HIP for the device and finds none
+    assert fwd() == -7
+    assert dec() == -7

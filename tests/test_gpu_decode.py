@@ -1,0 +1,121 @@
+"""Parity of the HIP paged split-KV decode with the fp64 oracle (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as gen
+import exact_attention_60_amd as ea
+import oracle.attention as att
+from gpu_util import dev_bf16, dev_i32, host_f64, need_gpu
+from tolerance import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def run_decode(d: gen.Decode, workspace=None):
+    o, lse = ea.attn_decode_paged(dev_bf16(d.q), dev_bf16(d.k_pool), dev_bf16(d.v_pool),
+                                  dev_i32(d.block_table), dev_i32(d.seq_lens), scale=d.scale,
+                                  workspace=workspace)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_decode(d: gen.Decode, o, lse, what=""):
+    o_ref, l_ref = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
+                                    d.scale)
+    check_o(host_f64(o), o_ref, what)
+    check_lse(host_f64(lse), l_ref, what)
+
+
+CASES = [
+    # B, Hq, Hkv, max_len, lens
+    (1, 1, 1, 16, [1]),
+    (3, 4, 1, 64, [1, 16, 17]),
+    (4, 8, 8, 300, [300, 1, 129, 32]),
+    (5, 32, 8, 1000, None),
+    (2, 32, 1, 700, [700, 513]),          # MQA: 32 query heads on one K/V head
+    (6, 24, 2, 2000, None),               # group of 12 heads
+    (2, 40, 2, 500, [499, 100]),          # group of 20 heads: two head blocks
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_Hq{c[1]}_Hkv{c[2]}_L{c[3]}")
+def test_decode_small(case):
+    B, Hq, Hkv, L, lens = case
+    d = gen.decode_inputs(B, Hq, Hkv, max_len=L, seed=B * 7 + L, lens=lens)
+    o, lse = run_decode(d)
+    check_decode(d, o, lse, str(case))
+
+
+def test_config5_full():
+    d = gen.config5()
+    o, lse = run_decode(d)
+    check_decode(d, o, lse, "config5")
+
+
+def test_permuted_pages_equal_identity_bitwise():
+    d = gen.decode_inputs(8, 32, 8, max_len=1500, seed=91, permute=False)
+    o1, l1 = run_decode(d)
+    perm = np.random.default_rng(92).permutation(d.num_pages)
+    inv = np.argsort(perm)
+    tab = d.block_table.copy()
+    tab[tab >= 0] = perm[tab[tab >= 0]]
+    d2 = gen.Decode(d.q, d.k_pool[inv], d.v_pool[inv], tab, d.seq_lens, d.B, d.Hq, d.Hkv, d.scale)
+    o2, l2 = run_decode(d2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_poisoned_tail_slots_and_garbage_workspace():
+    """Cache slots past each sequence hold NaN (from the generator) and the
+    workspace starts as NaN: neither may leak into the result."""
+    d = gen.decode_inputs(4, 8, 2, max_len=200, seed=93, lens=[5, 33, 200, 17])
+    ws = torch.full((ea.attn_decode_workspace_bytes(4, 8, d.max_blocks) // 4,), float("nan"),
+                    device="cuda")
+    o, lse = run_decode(d, workspace=ws)
+    check_decode(d, o, lse, "poison")
+
+
+def test_decode_v_beyond_fp16_range():
+    d = gen.decode_inputs(4, 8, 2, max_len=600, seed=96, lens=[600, 31, 257, 100])
+    v = (d.v_pool.astype(np.uint32) << 16).view(np.float32).copy()
+    v[::3, :, :, 7] = 4.0e5     # every third page holds a huge V column
+    d.v_pool = gen.f32_to_bf16_bits(v)
+    # keep the NaN poison past each sequence end
+    for b in range(d.B):
+        t = int(d.seq_lens[b]) % 16
+        if t:
+            d.v_pool[d.block_table[b, (int(d.seq_lens[b]) - 1) // 16], t:] = 0x7FC0
+    o, lse = run_decode(d)
+    check_decode(d, o, lse, "huge V decode")
+
+
+def test_decode_deterministic():
+    d = gen.decode_inputs(16, 32, 8, max_len=4096, seed=94)
+    o1, l1 = run_decode(d)
+    o2, l2 = run_decode(d)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_equals_prefill_single_row():
+    """A decode step and the forward with one causal query row against the
+    same (gathered, dense) keys both match the oracle."""
+    d = gen.decode_inputs(3, 8, 2, max_len=400, seed=95, lens=[400, 77, 16])
+    o, lse = run_decode(d)
+    o_ref, l_ref = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
+                                    d.scale)
+    for b, n in enumerate(d.seq_lens):
+        n = int(n)
+        pages = d.block_table[b, np.arange(n) // 16]
+        kd = d.k_pool[pages, np.arange(n) % 16][None]
+        vd = d.v_pool[pages, np.arange(n) % 16][None]
+        o2, l2 = ea.attn_fwd(dev_bf16(d.q[b][None, None]), dev_bf16(kd), dev_bf16(vd),
+                             causal=True, scale=d.scale)
+        torch.cuda.synchronize()
+        check_o(host_f64(o2[0, 0]), o_ref[b], "fwd row")
+        check_lse(host_f64(l2[0, :, 0]), l_ref[b], "fwd row lse")
+        check_o(host_f64(o[b]), o_ref[b], "decode row")

@@ -1,0 +1,183 @@
+"""Parity of the HIP attention forward with the fp64 oracle (GPU)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as gen
+import exact_attention_60_amd as ea
+import oracle.attention as att
+from gpu_util import (bits_of, check_full, check_sampled, dev_bf16, host_f64, logical_o,
+                      need_gpu, run_fwd)
+from tolerance import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def test_config1_tiny_mha_all_elements():
+    p = gen.config1()
+    o, lse = run_fwd(p)
+    check_full(p, o, lse, "config1")
+
+
+def test_golden_fixture_cases():
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "oracle_small.json")))
+    for c in fx["cases"]:
+        p = gen.prefill_inputs(c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sk"], layout=c["layout"],
+                               causal=c["causal"], seed=c["seed"])
+        o, lse = run_fwd(p)
+        o_ref = np.array(c["o"]).reshape(p.B, p.Hq, p.Sq, 128)
+        l_ref = np.array([(-np.inf if x is None else x) for x in c["lse"]]).reshape(p.B, p.Hq, p.Sq)
+        check_o(logical_o(o, p.layout), o_ref, "golden")
+        check_lse(host_f64(lse), l_ref, "golden")
+
+
+SHAPES = [
+    # B, Hq, Hkv, Sq, Sk, layout, causal
+    (1, 2, 2, 1, 1, gen.BSHD, False),
+    (1, 2, 1, 17, 15, gen.BSHD, False),
+    (2, 4, 2, 63, 65, gen.BHSD, False),
+    (1, 3, 3, 129, 127, gen.BSHD, True),
+    (1, 8, 2, 300, 300, gen.BSHD, True),
+    (2, 4, 1, 257, 257, gen.BHSD, True),
+    (1, 4, 4, 513, 200, gen.BSHD, False),
+    (1, 2, 2, 100, 700, gen.BHSD, True),    # Sq < Sk: bottom-right causal
+    (1, 2, 1, 400, 150, gen.BSHD, True),    # Sq > Sk: first rows see no key
+    (1, 16, 2, 64, 1000, gen.BSHD, False),
+    (3, 2, 2, 1, 333, gen.BHSD, True),      # one query row sees every key
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s" % (
+    s[0], s[1], s[2], s[3], s[4], "bshd" if s[5] == 0 else "bhsd", "causal" if s[6] else "full"))
+def test_ragged_shapes_all_elements(shape):
+    B, Hq, Hkv, Sq, Sk, lay, causal = shape
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=lay, causal=causal, seed=B * 1000 + Sq + Sk,
+                           n_hot=min(4, Sq * Hq))
+    o, lse = run_fwd(p)
+    check_full(p, o, lse, str(shape))
+
+
+def test_scaled_rows_and_other_scales():
+    for scale in (0.02, 0.5):
+        p = gen.prefill_inputs(1, 2, 2, 200, 333, layout=gen.BSHD, seed=7, scale=scale, n_hot=16)
+        o, lse = run_fwd(p)
+        check_full(p, o, lse, f"scale={scale}")
+
+
+def test_causal_row0_is_v0_bitwise():
+    p = gen.prefill_inputs(2, 4, 2, 300, 300, layout=gen.BSHD, causal=True, seed=77)
+    o, _ = run_fwd(p)
+    ob = bits_of(o)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(ob[b, 0, h], p.v[b, 0, h // 2])
+
+
+def test_layouts_agree_bitwise():
+    p = gen.prefill_inputs(2, 4, 2, 270, 190, layout=gen.BSHD, causal=True, seed=78)
+    o1, l1 = run_fwd(p)
+    q2 = dev_bf16(p.q.transpose(0, 2, 1, 3))
+    k2 = dev_bf16(p.k.transpose(0, 2, 1, 3))
+    v2 = dev_bf16(p.v.transpose(0, 2, 1, 3))
+    o2, l2 = ea.attn_fwd(q2, k2, v2, causal=True, scale=p.scale, layout="bhsd")
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(o1).transpose(0, 2, 1, 3), bits_of(o2))
+    assert torch.equal(l1, l2)
+
+
+def test_gqa_equals_repeated_mha_bitwise():
+    for Hkv in (1, 2, 4):
+        p = gen.prefill_inputs(1, 8, Hkv, 150, 260, layout=gen.BSHD, causal=False, seed=79 + Hkv)
+        o1, l1 = run_fwd(p)
+        G = 8 // Hkv
+        kr = dev_bf16(np.repeat(p.k, G, axis=2))
+        vr = dev_bf16(np.repeat(p.v, G, axis=2))
+        o2, l2 = ea.attn_fwd(dev_bf16(p.q), kr, vr, causal=False, scale=p.scale, layout="bshd")
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), Hkv
+
+
+def test_deterministic_repeat():
+    p = gen.prefill_inputs(1, 8, 2, 700, 700, layout=gen.BSHD, causal=True, seed=80)
+    o1, l1 = run_fwd(p)
+    o2, l2 = run_fwd(p)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Guard zones around O and LSE keep their sentinel values."""
+    p = gen.prefill_inputs(1, 4, 2, 333, 222, layout=gen.BHSD, causal=True, seed=81)
+    q, k, v = dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v)
+    n_o = q.numel()
+    G = 4096  # guard elements (8 KB, keeps 16-byte alignment)
+    ob = torch.full((n_o + 2 * G,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((4 * 333 + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    o = ob[G:G + n_o].view(q.shape)
+    lse = lb[G:G + 4 * 333].view(1, 4, 333)
+    ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bhsd", out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(ob[:G] == 7.0) and torch.all(ob[G + n_o:] == 7.0)
+    assert torch.all(lb[:G] == 7.0) and torch.all(lb[G + 4 * 333:] == 7.0)
+    check_full(p, o, lse, "guarded")
+
+
+def test_nonfinite_stays_in_its_rows():
+    """A NaN in one query row only spoils that row (non-finite inputs are
+    outside the parity contract; this checks containment only)."""
+    p = gen.prefill_inputs(1, 2, 2, 130, 140, layout=gen.BSHD, seed=82)
+    q = p.q.copy()
+    q[0, 5, 1, 3] = 0x7FC0
+    o, lse = ea.attn_fwd(dev_bf16(q), dev_bf16(p.k), dev_bf16(p.v), scale=p.scale)
+    torch.cuda.synchronize()
+    of = host_f64(o)
+    bad = ~np.isfinite(of)
+    assert bad[0, 5, 1].all()
+    bad[0, 5, 1] = False
+    assert not bad.any()
+
+
+def test_v_beyond_fp16_range():
+    """V entries far beyond the fp16 range (3e5 and -2e6) take the bf16 path
+    and still meet the bound; a constant V column gives that constant."""
+    p = gen.prefill_inputs(1, 4, 2, 300, 1500, layout=gen.BSHD, causal=True, seed=83)
+    v = (p.v.astype(np.uint32) << 16).view(np.float32).copy()
+    v[:, :, :, 5] = 3.0e5
+    v[0, 700, 1, 9] = -2.0e6
+    p.v = gen.f32_to_bf16_bits(v)
+    o, lse = run_fwd(p)
+    check_full(p, o, lse, "huge V")
+    # 3e5 rounds to the bf16 value 299008 (spacing 2048 there)
+    assert np.all(host_f64(o)[..., 5] == 299008.0)
+
+
+# ---- the full-size workloads (launch configuration of the benchmark), sampled rows
+
+def _full_size(p, seed):
+    o, lse = run_fwd(p)
+    assert bool(torch.isfinite(o.float()).all()), "non-finite output"
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE"
+    return check_sampled(p, o, lse, n=300, seed=seed, what=p.name)
+
+
+def test_config2_mha_prefill_sampled():
+    _full_size(gen.config2(), 2)
+
+
+def test_config3_causal_gqa_sampled():
+    _full_size(gen.config3(), 3)
+
+
+def test_config4_self_and_cross_sampled():
+    ps = gen.config4_self()
+    _full_size(ps, 4)
+    pc = gen.config4_cross(self_problem=ps)
+    del ps
+    _full_size(pc, 5)
