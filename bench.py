@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 exact-attention library on one MI355X.
+
+One step is one pass of the hot path over one batch of synthetic inputs that
+are already resident in HBM:
+
+* prefill: attn_fwd on the MHA workload B=4, Hq=Hkv=32, Sq=Sk=4096, d=128,
+  bf16, BHSD, non-causal (the headline TFLOP/s, FLOP = 4*B*Hq*Sq*Sk*d);
+* decode: attn_decode_paged on B=32, Hq=32, Hkv=8, 16-token pages, context
+  lengths U{1..4096}, reported as algorithmic HBM GB/s; four independent
+  copies of the KV pool (more than 1 GB in all) are rotated so that the
+  256 MB last-level cache cannot serve a call from the previous one.
+
+Times come from HIP events on the stream the kernels are launched on.  The
+fp64 CPU oracle is timed on the host cores on a bounded sample of the same
+workload as a reported baseline.  Prints one JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --counters      # short run for rocprofv3 counter passes
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (d=128); paged decode HBM GB/s"
+
+
+def sha256_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profiles(kernel_key, source, launches_per_call=1):
+    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy kernel of known size), or None if absent or taken on a
+    different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data[kernel_key]
+        if ent.get("source_sha256") != sha256_of(source):
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except (KeyError, ValueError, TypeError):
+        return None
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def cpu_baseline(p, budget_s, torch):
+    """Time the oracle (as it is) on whole (b, h) heads of the prefill
+    workload until about budget_s seconds of host work are done."""
+    import oracle.attention as att
+    from threadpoolctl import threadpool_info
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    order = [(b, h) for b in range(p.B) for h in range(p.Hq)]
+    for (b, h) in order:
+        qs = p.q[b:b + 1, h:h + 1]
+        ks = p.k[b:b + 1, h:h + 1]
+        vs = p.v[b:b + 1, h:h + 1]
+        att.attention(qs, ks, vs, 1, 1, 1, p.Sq, p.Sk, p.scale, False, 1, workers=workers)
+        flops += 4.0 * p.Sq * p.Sk * 128
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    blas = sorted({i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"})
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{heads} of {p.B * p.Hq} (b,h) heads of the same workload, all "
+                      f"{p.Sq} query rows x {p.Sk} keys, fp64 NumPy, {workers} worker threads "
+                      f"x 1 BLAS thread (BLAS pool size {blas}); {dt:.1f} s",
+            "seconds": dt}
+
+
+def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
+    """Turn rocprofv3 output (a --kernel-trace --stats run and two --pmc runs
+    of `bench.py --counters`, FETCH_SIZE then WRITE_SIZE) into the summaries
+    kept under profiles/: kernel_stats.md and traffic.json."""
+    import csv
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    stats = list(csv.DictReader(open(os.path.join(ktrace_dir, "run_kernel_stats.csv"))))
+    lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "",
+             "Command (from the repository root on the GPU box):", "", "```", command["ktrace"],
+             "```", "", "| kernel | calls | average us | min us | max us | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        if "attn::" not in name and "copyBuffer" not in name:
+            continue
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    fetch = list(csv.DictReader(open(os.path.join(fetch_dir, "run_counter_collection.csv"))))
+    write = list(csv.DictReader(open(os.path.join(write_dir, "run_counter_collection.csv"))))
+    wmap = {r["Dispatch_Id"]: r for r in write}
+    copy_bytes = float(1 << 30)
+    # the reference copy is the largest copyBuffer dispatch (1 GiB read + 1 GiB written)
+    copies = [r for r in fetch if "copyBuffer" in r["Kernel_Name"]]
+    cref = max(copies, key=lambda r: float(r["Counter_Value"]))
+    f_fetch = copy_bytes / (float(cref["Counter_Value"]) * 1024)
+    f_write = copy_bytes / (float(wmap[cref["Dispatch_Id"]]["Counter_Value"]) * 1024)
+    per = {}
+    for r in fetch:
+        key = ("prefill_kernel" if "prefill_kernel" in r["Kernel_Name"] else
+               "decode_split_kernel" if "decode_split" in r["Kernel_Name"] else
+               "decode_merge_kernel" if "decode_merge" in r["Kernel_Name"] else None)
+        if key is None:
+            continue
+        fb = float(r["Counter_Value"]) * 1024 * f_fetch
+        wb = float(wmap[r["Dispatch_Id"]]["Counter_Value"]) * 1024 * f_write
+        per.setdefault(key, []).append((fb, wb))
+    srcs = {"prefill_kernel": "prefill.hip", "decode_split_kernel": "decode.hip",
+            "decode_merge_kernel": "decode.hip"}
+    traffic = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                        "dispatch), each scaled by the reading of a 1 GiB device copy",
+               "fetch_scale": f_fetch, "write_scale": f_write,
+               "commands": [command["fetch"], command["write"]]}
+    lines += ["", "# HBM traffic per launch (rocprofv3 --pmc)", "",
+              "Commands:", "", "```", command["fetch"], command["write"], "```", "",
+              f"Scale factors from a 1 GiB copy: FETCH_SIZE x {f_fetch:.4f}, "
+              f"WRITE_SIZE x {f_write:.4f}.", "",
+              "| kernel | launches | read MB | written MB | total MB |", "|---|---|---|---|---|"]
+    for key, vals in per.items():
+        fb = sum(v[0] for v in vals) / len(vals)
+        wb = sum(v[1] for v in vals) / len(vals)
+        traffic[key] = {"source_sha256": sha256_of(os.path.join(ROOT, "exact_attention_60_amd",
+                                                                 "csrc", srcs[key])),
+                        "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                        "hbm_bytes_per_launch": fb + wb, "launches": len(vals)}
+        lines.append(f"| {key} | {len(vals)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                     f"{(fb + wb) / 1e6:.1f} |")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    with open(os.path.join(out_dir, "kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="host seconds spent timing the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="no timing: one device copy of 1 GiB, then 3 prefill and 3 decode "
+                         "calls, for rocprofv3 counter passes")
+    ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/kernel_stats.md and profiles/traffic.json from rocprofv3 "
+                         "output directories (no GPU needed)")
+    args = ap.parse_args()
+    if args.summarize:
+        cmd = {"ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d <out>/ktrace "
+                         "-o run -- python3 bench.py --steps 30 --warmup 5 --no-cpu-baseline",
+               "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o run "
+                        "-- python3 bench.py --counters",
+               "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write -o run "
+                        "-- python3 bench.py --counters"}
+        summarize_profiles(*args.summarize, cmd)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus}: this library and benchmark run on one GPU only; "
+              "there is no multi-GPU path to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attn_inputs as gen
+    import exact_attention_60_amd as ea
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ea.library()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- prefill inputs (resident in HBM before timing)
+    p = gen.config2()
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+    def prefill(_i):
+        ea.attn_fwd(q, k, v, causal=False, scale=p.scale, layout="bhsd", out=o, lse=lse)
+
+    # ---- decode inputs: four copies of the pool, rotated
+    d = gen.config5()
+    qd = to_dev(d.q)
+    kp0, vp0 = to_dev(d.k_pool), to_dev(d.v_pool)
+    pools = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(3)]
+    tab = torch.from_numpy(d.block_table).to(dev)
+    lens = torch.from_numpy(d.seq_lens).to(dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((d.B, d.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(ea.attn_decode_workspace_bytes(d.B, d.Hq, d.max_blocks), dtype=torch.uint8,
+                     device=dev)
+
+    def decode(i):
+        kp, vp = pools[i % len(pools)]
+        ea.attn_decode_paged(qd, kp, vp, tab, lens, scale=d.scale, out=od, lse=lsed, workspace=ws)
+
+    if args.counters:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)          # reference: reads and writes exactly 1 GiB
+        for i in range(3):
+            prefill(i)
+        for i in range(3):
+            decode(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "copy_bytes": n}))
+        return
+
+    def log(msg):
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    log("inputs resident; timing prefill")
+    ms_p = time_calls(prefill, args.steps, args.warmup, torch)
+    log(f"prefill {ms_p:.3f} ms/call; timing decode")
+    ms_d = time_calls(decode, max(args.steps, 20), args.warmup, torch)
+    log(f"decode {ms_d * 1e3:.1f} us/call; sampled parity")
+
+    tflops = p.flops / (ms_p * 1e-3) / 1e12
+    gbs = d.bytes / (ms_d * 1e-3) / 1e9
+
+    # ---- quick sampled parity of what was timed
+    import oracle.attention as att
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tolerance import o_tolerance
+    r = np.random.default_rng(0)
+    rows = [(int(r.integers(p.B)), int(r.integers(p.Hq)), int(r.integers(p.Sq))) for _ in range(64)]
+    o_ref, l_ref = att.attention_sampled(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
+                                         False, p.layout, rows)
+    og = torch.stack([o[b, h, i] for (b, h, i) in rows]).float().cpu().numpy()
+    lg = torch.stack([lse[b, h, i] for (b, h, i) in rows]).cpu().numpy()
+    par_p = float((np.abs(og - o_ref) / o_tolerance(o_ref)).max())
+    par_pl = float(np.abs(lg - l_ref).max())
+    od_ref, ld_ref = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
+                                      d.scale)
+    par_d = float((np.abs(od.float().cpu().numpy() - od_ref) / o_tolerance(od_ref)).max())
+
+    src_p = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill.hip")
+    src_d = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "decode.hip")
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_p, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq,
+                   "Sk": p.Sk, "d": 128, "layout": "bhsd", "causal": False,
+                   "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profiles("prefill_kernel", src_p),
+                     "kernel": "prefill_kernel<false>",
+                     "per_launch": {"flop": p.flops, "ms": round(ms_p, 4)}},
+        "decode": {"workload": d.name, "value": round(gbs, 1), "unit": "GB/s",
+                   "us_per_call": round(ms_d * 1e3, 2), "tokens": d.tokens,
+                   "algorithmic_bytes": d.bytes,
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": traffic_from_profiles("decode_split_kernel", src_d),
+                                "kernel": "decode_split_kernel + decode_merge_kernel"}},
+        "parity": {"prefill_sampled_rows": len(rows), "prefill_max_err_over_tol": round(par_p, 4),
+                   "prefill_max_lse_err": par_pl, "decode_max_err_over_tol": round(par_d, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        cb = cpu_baseline(p, args.cpu_seconds, torch)
+        cb["value"] = round(cb["value"], 6)
+        cb["seconds"] = round(cb["seconds"], 2)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,8 +7,8 @@ namespace attn {
 
 // ---- prefill -------------------------------------------------------------
 constexpr int kHeadDim = 128;
-constexpr int kPrefillWaves = 4;                      // waves per workgroup
-constexpr int kPrefillRowsPerWave = 64;               // two 32-row MFMA blocks
+constexpr int kPrefillWaves = 8;                      // waves per workgroup (2 per SIMD)
+constexpr int kPrefillRowsPerWave = 32;               // one 32-row MFMA block per wave
 constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // 256 query rows
 constexpr int kPrefillBN = 64;                        // keys per K/V tile
 

@@ -8,36 +8,44 @@
 // m'); the output accumulator is multiplied by the same per-row factor and
 // divided by l once, at the end.
 //
-// Design (MI355X-first, not the pages' NVIDIA or gfx942 kernels):
-//  * one workgroup = 4 waves = 256 query rows of one (batch, query head);
-//    each wave owns 64 rows as two 32-row MFMA blocks, with its Q fragments
-//    and fp32 output accumulators in registers (the data placement of the
-//    MoonMath page's kernel keeps Q and the accumulators in registers too);
-//  * K and V tiles of 64 keys are copied HBM -> LDS directly by the buffer
-//    unit (buffer_load ... lds, 16 B per lane, 256 B contiguous per row),
-//    double buffered: tile t+1 is in flight while tile t is computed, one
-//    barrier per tile.  Both K and V sit in LDS (160 KB per CU on gfx950); rows are 256 B
-//    with an XOR swizzle of their 16-byte chunks so that the MFMA operand reads
-//    are free of bank conflicts;
-//  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
-//    the accumulator then holds one query row per lane (half of the keys in
-//    each lane half), so the row max and row sum are in-lane plus one
-//    v_permlane32_swap, and the bf16-packed probabilities are already the
-//    B operand of O^T = V^T P^T without any data movement;
-//  * the V^T operand comes straight from the row-major V tile through the
-//    gfx950 LDS transpose read (ds_read_b64_tr_b16);
+// Design (MI355X-first; the pages' NVIDIA and gfx942 kernels are prior art):
+//  * one workgroup = 8 waves = 256 query rows of one (batch, query head),
+//    two waves per SIMD.  Each wave owns 32 rows with its Q fragments and
+//    fp32 output accumulators in registers (the MoonMath page's kernel keeps
+//    Q and the accumulators in registers too).
+//  * The waves form two groups (one wave of each per SIMD) that run the same
+//    per-tile sequence half a tile apart, in phases separated by workgroup
+//    barriers: while one group issues MFMAs (P.V of the previous tile, then
+//    Q.K of this tile) the other runs the softmax of its current tile on the
+//    VALU.  On gfx950 a wave's VALU work does not overlap its own MFMAs, so
+//    this pairing is what keeps the matrix cores fed (the MoonMath page's
+//    two-group, phase-shifted eight-wave design, re-derived here with both K
+//    and V in LDS).
+//  * K and V tiles of 64 keys are copied HBM -> LDS by the buffer unit
+//    (buffer_load ... lds, 16 B per lane, 256 B per row), double buffered, one
+//    tile ahead; keys past Sk fall outside the buffer range and read as zero.
+//    Rows are 256 B with an XOR swizzle of their 16-byte chunks so the MFMA
+//    operand reads are free of bank conflicts.
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
+//    the accumulator holds one query row per lane (half of the keys in each
+//    lane half), so the row max and sum are in-lane plus one
+//    v_permlane32_swap, and the packed probabilities are already the B operand
+//    of O^T = V^T P^T.  The V^T operand comes straight from the row-major V
+//    tile through the gfx950 LDS transpose read (ds_read_b64_tr_b16).
 //  * P.V runs in fp16 (11 significant bits; bf16 keeps 8, too few for the
 //    parity bound when a few large V entries nearly cancel): each V tile is
-//    converted to fp16 once in LDS, and the denominator sums the same rounded
-//    probabilities that multiply V.  A V value outside the fp16 range (or a
-//    non-finite input) makes the accumulator non-finite; the workgroup then
-//    redoes its tile loop with bf16 P and V, which covers the bf16 range;
-//  * the rescale of the output accumulator is skipped while no row max in the
-//    wave has grown by more than 2^8 (probabilities stay <= 256, far from fp32
-//    or bf16 limits); the result is the same quotient, so it stays exact;
-//  * causal: tiles above the diagonal are never loaded, waves whose rows see
-//    none of a tile skip its arithmetic, only boundary tiles are masked, and
-//    the heaviest query tiles are dispatched first;
+//    converted to fp16 once in LDS by the lanes that copied it, and the
+//    denominator sums the same rounded probabilities that multiply V.  A V
+//    value outside the fp16 range (or a non-finite input) leaves a non-finite
+//    accumulator; the workgroup then redoes its tiles with bf16 P and V,
+//    which covers the whole bf16 range.
+//  * The rescale of the output accumulator is skipped while no row max in the
+//    wave has grown by more than 2^8 (probabilities stay <= 256, far from
+//    fp16 or fp32 limits); the quotient is the same, so the result stays exact.
+//  * Causal: tiles above the diagonal are never loaded, waves whose rows see
+//    none of a tile skip its arithmetic, only boundary tiles are masked, the
+//    two groups hold interleaved 32-row blocks so they stay balanced on the
+//    diagonal, and the heaviest query tiles are dispatched first.
 //  * blockIdx is remapped so that workgroups sharing K/V land on one XCD
 //    (workgroups are dealt to the 8 XCDs round robin), keeping K/V re-reads in
 //    that XCD's L2.
@@ -50,10 +58,13 @@ namespace {
 constexpr int D = kHeadDim;
 constexpr int BN = kPrefillBN;
 constexpr int BM = kPrefillBM;
-constexpr int NT = kPrefillWaves * 64;
-constexpr int QB = kPrefillRowsPerWave / 32;
+constexpr int NW = kPrefillWaves;           // 8
+constexpr int NT = NW * 64;                 // 512 threads
 constexpr int TILE_BYTES = BN * D * 2;      // 16 KB for one K or V tile
+constexpr int ROWS_PER_WAVE_DMA = BN / 4;   // 16 rows of each tile copied per group-0 wave
 constexpr float TAU = 8.0f;                 // log2 headroom before a rescale
+
+static_assert(kPrefillRowsPerWave == 32 && NW == 8 && BM == 256, "layout assumed below");
 
 // 4-bit swizzle of a row index: a bijection on 0..15 that sends rows r and
 // r+4k to different 4-chunk groups.
@@ -68,264 +79,324 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
 }
 
-// Asynchronous copy of one K or V tile (64 keys x 256 B) from HBM straight
-// into LDS (buffer_load_dwordx4 ... lds): each wave moves 16 rows with four
-// instructions of 1 KB; lane i of an instruction lands at byte 16*i of that
-// 1 KB, i.e. row +i/16, physical chunk i%16, so it fetches the logical chunk
-// that the swizzle places there.  Keys >= Sk are outside the buffer's range
-// and read as zeros.
+// Asynchronous copy of a wave's 16 rows of one K or V tile from HBM into LDS
+// (buffer_load_dwordx4 ... lds).  Each instruction moves 1 KB: lane i lands
+// at byte 16*i, i.e. row +i/16, physical chunk i%16, so it fetches the
+// logical chunk that the swizzle puts there.
 struct TileLoader {
   __amdgpu_buffer_rsrc_t rk, rv;
-  uint32_t voff[4];       // per-lane byte offset of this lane's chunk, row j*4 + lane/16
+  uint32_t voff[4];       // per-lane byte offset, rows 4*j + lane/16 of the wave's 16
   uint32_t tile_bytes;    // BN * row stride in bytes
-  int lds_row0;           // first tile row this wave fills (16 * wave)
+  int row0;               // first tile row this wave copies
 
   __device__ void init(const __bf16* kp, const __bf16* vp, int64_t k_ss, int Sk, int wave,
                        int lane) {
+    wave &= 3;
     const uint32_t ss = (uint32_t)(k_ss * 2);
     const uint32_t nrec = (uint32_t)((int64_t)(Sk - 1) * ss + 256);
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)nrec, 0x00020000);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)nrec, 0x00020000);
     tile_bytes = ss * BN;
-    lds_row0 = 16 * wave;
+    row0 = ROWS_PER_WAVE_DMA * wave;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = lds_row0 + 4 * j + (lane >> 4);
+      const int row = row0 + 4 * j + (lane >> 4);
       const int c = (lane & 15) ^ swz(row & 15);
       voff[j] = (uint32_t)row * ss + (uint32_t)c * 16;
     }
   }
-  __device__ __forceinline__ void issue(int tile, char* kt, char* vt) const {
+  __device__ __forceinline__ void issue_k(int tile, char* kt) const {
     const uint32_t base = (uint32_t)tile * tile_bytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int lds_off = (lds_row0 + 4 * j) * 256;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ATTN_LDS void*)(kt + lds_off), 16,
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ATTN_LDS void*)(kt + (row0 + 4 * j) * 256), 16,
                                                voff[j] + base, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vt + lds_off), 16,
+  }
+  __device__ __forceinline__ void issue_v(int tile, char* vt) const {
+    const uint32_t base = (uint32_t)tile * tile_bytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vt + (row0 + 4 * j) * 256), 16,
                                                voff[j] + base, 0, 0, 0);
-    }
   }
 };
 
-__device__ __forceinline__ void wait_tile_loads() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// s_waitcnt through the intrinsic, so the compiler's own wait tracking knows
+// about it: vmcnt(0) (this wave's LDS copies have landed), and
+// vmcnt(0) lgkmcnt(0) (also its LDS writes are done).
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_copies_and_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// Workgroup barrier without a hardware memory fence: every cross-wave LDS
+// dependency in the loop is ordered by an explicit wait before it.  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// Converts, in place, the 4 x 16 B of a V tile that this lane's own copy
-// instructions brought into LDS from bf16 to fp16 (the lane waited for its
-// copies, so the bytes are there; the following barrier publishes them).
-__device__ __forceinline__ void convert_v_share(char* vt, int wave, int lane) {
+// In-place bf16 -> fp16 conversion of 4 x 16 B of a V tile: rows
+// 16*(wave%4) .. +15, the rows whose copy the same-numbered wave of the other
+// group issued and waited for before the last barrier.  The reads are issued
+// first and the conversion done later, so the LDS latency hides behind the
+// softmax; the barrier that follows the store publishes the result.
+struct VShare {
+  u32x4 x[4];
+};
+__device__ __forceinline__ char* v_share_addr(char* vt, int wave, int lane, int j) {
+  return vt + (ROWS_PER_WAVE_DMA * (wave & 3) + 4 * j) * 256 + lane * 16;
+}
+__device__ __forceinline__ void v_share_load(VShare& v, char* vt, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v.x[j] = *(const u32x4*)v_share_addr(vt, wave, lane, j);
+}
+__device__ __forceinline__ void v_share_store_f16(const VShare& v, char* vt, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    u32x4* p = (u32x4*)(vt + (16 * wave + 4 * j) * 256 + lane * 16);
-    u32x4 x = *p;
     u32x4 y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = bf16x2_to_f16x2(x[i]);
-    *p = y;
+    for (int i = 0; i < 4; ++i) y[i] = bf16x2_to_f16x2(v.x[j][i]);
+    *(u32x4*)v_share_addr(vt, wave, lane, j) = y;
   }
 }
 
-// Per-wave state of the forward: Q fragments, output accumulators, running
-// row max (log2 units) and the lane's partial row sum.
-struct WaveState {
-  bf16x8 qf[QB][8];
-  f32x16 oacc[QB][4];
-  float m_use[QB];
-  float lsum[QB];
+// Everything one wave carries through the tile loop.
+struct Wave {
+  bf16x8 qf[8];        // Q fragments: B operand of S^T = K Q^T (query = lane%32)
+  f32x16 oacc[4];      // O^T accumulators, d blocks of 32
+  f32x16 s[2];         // S^T of the current tile, two 32-key blocks
+  u32x4 pf[2][2];      // packed probabilities of the current tile (B operand of P.V)
+  float m_use;         // running max in log2 units (scale*log2e folded in)
+  float lsum;          // this lane's part of the row sum
+  int koff[8];         // LDS offsets of the K operand per 16-wide d step
+  int voff[2][4];      // LDS offsets of the V^T transpose reads
+  int first, last;     // the wave's query rows
+  int l32, hi;
 };
 
-// One K/V tile of the online softmax for one wave.  F16: the probabilities
-// and the V tile are fp16 for O^T += V^T P^T (V was converted in LDS);
-// otherwise both are bf16.
-template <bool CAUSAL, bool F16>
-__device__ __forceinline__ void tile_step(WaveState& st, const char* kt, const char* vt,
-                                          const int (&koff)[8], const int (&voff)[2][4],
-                                          int kbase, int w_first, int Sk, int off, float c,
-                                          int l32, int hi) {
-  // ---- S^T = K Q^T for 64 keys x 64 rows
-  f32x16 s[2][QB];
+// MFMA phase of a wave: O^T += V^T P^T for the previous tile (16 MFMAs,
+// k-step major so consecutive MFMAs feed different accumulators), then
+// S^T = K Q^T for this tile (16 MFMAs).  The LDS operand reads run DEPTH
+// MFMAs ahead of their use (sched_barrier pins that order), so the matrix
+// core does not wait on LDS latency.
+template <bool F16, bool PV, bool QK>
+__device__ __forceinline__ void mfma_seq(Wave& w, const char* kt, const char* vt_prev) {
+  constexpr int NPV = PV ? 16 : 0;
+  constexpr int N = NPV + (QK ? 16 : 0);
+  constexpr int DEPTH = 4;
+  auto load = [&](int i) -> bf16x8 {
+    if (i < NPV) {
+      const int kk = i >> 2, db = i & 3;                 // k-step (kb, e) and d block
+      const char* base = vt_prev + ((kk >> 1) * 32 + 16 * (kk & 1)) * 256;
+      const bf16x4 lo = lds_read_tr(base + w.voff[0][db]);
+      const bf16x4 up = lds_read_tr(base + w.voff[1][db]);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    }
+    const int j = i - NPV, ks = j >> 1, kb = j & 1;
+    return *(const bf16x8*)(kt + kb * 32 * 256 + w.koff[ks]);
+  };
+  auto mma = [&](int i, const bf16x8& f) {
+    if (i < NPV) {
+      const int kk = i >> 2, db = i & 3;
+      if (F16)
+        w.oacc[db] = mfma32(__builtin_bit_cast(f16x8, f),
+                            __builtin_bit_cast(f16x8, w.pf[kk >> 1][kk & 1]), w.oacc[db]);
+      else
+        w.oacc[db] = mfma32(f, __builtin_bit_cast(bf16x8, w.pf[kk >> 1][kk & 1]), w.oacc[db]);
+    } else {
+      const int j = i - NPV, ks = j >> 1, kb = j & 1;
+      w.s[kb] = mfma32(f, w.qf[ks], w.s[kb]);
+    }
+  };
+  if (QK) {
+    w.s[0] = f32x16{};
+    w.s[1] = f32x16{};
+  }
+  bf16x8 fr[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) fr[i] = load(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma(i, fr[i % DEPTH]);
+    if (i + DEPTH < N) fr[i % DEPTH] = load(i + DEPTH);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool F16>
+__device__ __forceinline__ void mfma_phase(Wave& w, const char* kt, const char* vt_prev,
+                                           bool do_pv, bool do_qk) {
+  if (do_pv && do_qk)
+    mfma_seq<F16, true, true>(w, kt, vt_prev);
+  else if (do_qk)
+    mfma_seq<F16, false, true>(w, kt, vt_prev);
+  else if (do_pv)
+    mfma_seq<F16, true, false>(w, kt, vt_prev);
+}
+
+// Softmax phase of a wave for the tile whose scores are in w.s.  Fast path:
+// probabilities against the current running max, packed for the next MFMA
+// phase and summed (rounded values, four independent chains).  Every
+// probability is <= this lane's partial tile sum, so if that sum stays below
+// 2^12 none of them is near the fp16 limit and the running max may stay as it
+// is (the quotient O = sum p v / sum p does not depend on it).  Otherwise (and
+// for the first tile of a row) the slow path takes the row max, rescales the
+// accumulators and recomputes the tile.
+template <bool F16>
+__device__ __forceinline__ float probs(Wave& w, float c, float msub) {
+  // staged so that each stage is 16-32 independent instructions: the wave
+  // runs beside another wave's MFMAs and cannot afford dependency stalls
+  float x[32];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+    for (int r = 0; r < 16; ++r) x[16 * kb + r] = __builtin_fmaf(w.s[kb][r], c, -msub);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int i = 0; i < 32; ++i) x[i] = fast_exp2(x[i]);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t u[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 kf = *(const bf16x8*)(kt + kb * 32 * 256 + koff[ks]);
+  for (int i = 0; i < 16; ++i) u[i] = F16 ? pack_f16(x[2 * i], x[2 * i + 1]) : pack_bf16(x[2 * i], x[2 * i + 1]);
+  __builtin_amdgcn_sched_barrier(0);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(kf, st.qf[qb][ks], s[kb][qb]);
-    }
-  }
-  // ---- mask key tails and the causal diagonal (boundary tiles only)
-  const bool need_mask = (kbase + BN > Sk) || (CAUSAL && kbase + BN - 1 > w_first + off);
-  if (need_mask) {
+  for (int i = 0; i < 16; ++i) acc[i & 3] = F16 ? sum2_f16(u[i], acc[i & 3]) : sum2_bf16(u[i], acc[i & 3]);
+  // u[4*j .. 4*j+3] hold keys 8*(j) .. of s[kb][8e..8e+7] with j = 2*kb + e
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = w_first + qb * 32 + l32;
-      const int lim = (CAUSAL ? min(Sk - 1, row + off) : Sk - 1) - kbase - 4 * hi;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + (r & 3);
-          if (key > lim) s[kb][qb][r] = -INFINITY;
-        }
-    }
-  }
-  // ---- online softmax; P packed as the B operand of O^T += V^T P^T.  The
-  // denominator sums the rounded probabilities, the same weights that
-  // multiply V.
-  u32x4 pf[QB][2][2];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float mx = s[0][qb][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-    mx = max_halves(mx);
-    const float m_tile = mx * c;
-    if (wave_any(m_tile > st.m_use[qb] + TAU)) {
-      const float m_new = fmaxf(st.m_use[qb], m_tile);
-      const float alpha = (m_new == st.m_use[qb]) ? 1.f : fast_exp2(st.m_use[qb] - m_new);
-      st.lsum[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) st.oacc[qb][db] *= alpha;
-      st.m_use[qb] = m_new;
-    }
-    const float msub = (st.m_use[qb] == -INFINITY) ? 0.f : st.m_use[qb];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[kb][qb][8 * e + i], c, -msub));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u = F16 ? pack_f16(p[2 * i], p[2 * i + 1])
-                                 : pack_bf16(p[2 * i], p[2 * i + 1]);
-          pf[qb][kb][e][i] = u;
-          st.lsum[qb] = F16 ? sum2_f16(u, st.lsum[qb]) : sum2_bf16(u, st.lsum[qb]);
-        }
-      }
-  }
-  // ---- O^T += V^T P^T
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const char* base = vt + (kb * 32 + 16 * e) * 256;
-        const bf16x4 lo = lds_read_tr(base + voff[0][db]);
-        const bf16x4 up = lds_read_tr(base + voff[1][db]);
-        const bf16x8 vb = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (F16)
-            st.oacc[qb][db] = mfma32(__builtin_bit_cast(f16x8, vb),
-                                     __builtin_bit_cast(f16x8, pf[qb][kb][e]), st.oacc[qb][db]);
-          else
-            st.oacc[qb][db] = mfma32(vb, __builtin_bit_cast(bf16x8, pf[qb][kb][e]),
-                                     st.oacc[qb][db]);
-        }
-      }
-  }
+      for (int i = 0; i < 4; ++i) w.pf[kb][e][i] = u[4 * (2 * kb + e) + i];
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-struct LoopCtx {
+template <bool CAUSAL, bool F16>
+__device__ __forceinline__ void softmax_phase(Wave& w, int kbase, int Sk, int off, float c) {
+  const bool need_mask = (kbase + BN > Sk) || (CAUSAL && kbase + BN - 1 > w.first + off);
+  if (need_mask) {
+    const int row = w.first + w.l32;
+    const int lim = (CAUSAL ? min(Sk - 1, row + off) : Sk - 1) - kbase - 4 * w.hi;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + (r & 3);
+        if (key > lim) w.s[kb][r] = -INFINITY;
+      }
+  }
+  float tsum = probs<F16>(w, c, w.m_use);
+  const bool ok = (w.m_use != -INFINITY) && (tsum <= 4096.f);
+  if (wave_any(!ok)) {
+    float mx = w.s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, w.s[kb][r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(w.m_use, mx * c);
+    const float alpha = (m_new == w.m_use) ? 1.f : fast_exp2(w.m_use - m_new);
+    w.lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) w.oacc[db] *= alpha;
+    w.m_use = m_new;
+    tsum = probs<F16>(w, c, (m_new == -INFINITY) ? 0.f : m_new);
+  }
+  w.lsum += tsum;
+}
+
+struct Ctx {
   TileLoader ld;
-  int koff[8];
-  int voff[2][4];
-  int n_tiles, w_first, w_last, Sk, off, wave, lane, l32, hi;
-  bool w_any;
+  int n_tiles, Sk, off, wave, lane, group;
   float c;
 };
 
-// The tile loop of one workgroup: K/V tiles double buffered in kv0/kv1, tile
-// t+1 copied while tile t is computed; with F16 each lane converts the V
-// bytes it copied to fp16 before the barrier that publishes the tile.
+// The phased tile loop.  Phase 2t: group 0 runs the MFMA phase of tile t
+// (P.V of t-1, Q.K of t), group 1 the softmax of tile t-1; phase 2t+1:
+// group 0 the softmax of t, group 1 the MFMA phase of t.  K(t) and V(t-1)
+// are read during phases 2t and 2t+1.
+//  * group 0 copies K(t+1) into the other K buffer right after its reads of
+//    phase 2t and waits for it at the end of phase 2t+1;
+//  * group 1 copies V(t) into the other V buffer at the start of phase 2t (a
+//    softmax phase, no LDS reads) and waits for it before the mid barrier;
+//  * in phase 2t+1 group 0, after its softmax, converts all of V(t) to fp16.
+// The barrier that ends phase 2t+1 publishes K(t+1) and V(t) for phase 2t+2.
 template <bool CAUSAL, bool F16>
-__device__ __forceinline__ void tile_loop(WaveState& st, const LoopCtx& x, char* kv0, char* kv1) {
+__device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, char* vbuf) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.oacc[qb][db] = f32x16{};
-    st.m_use[qb] = -INFINITY;
-    st.lsum[qb] = 0.f;
-  }
-  if (x.n_tiles > 0) {
-    x.ld.issue(0, kv0, kv0 + TILE_BYTES);
-    wait_tile_loads();
-    if (F16) convert_v_share(kv0 + TILE_BYTES, x.wave, x.lane);
-  }
-  __syncthreads();
-  auto visible = [&](int kbase) {
-    return x.w_any && (!CAUSAL || kbase <= x.w_last + x.off);
+  for (int db = 0; db < 4; ++db) w.oacc[db] = f32x16{};
+  w.m_use = -INFINITY;
+  w.lsum = 0.f;
+  const int T = x.n_tiles;
+  auto visible = [&](int t) {
+    return t >= 0 && t < T && w.first <= w.last && (!CAUSAL || t * BN <= w.last + x.off);
   };
-  // two tiles per trip so that each buffer index is a compile-time constant
-  for (int t = 0; t < x.n_tiles; t += 2) {
-    const bool more1 = t + 1 < x.n_tiles;
-    if (more1) x.ld.issue(t + 1, kv1, kv1 + TILE_BYTES);
-    if (visible(t * BN))
-      tile_step<CAUSAL, F16>(st, kv0, kv0 + TILE_BYTES, x.koff, x.voff, t * BN, x.w_first, x.Sk,
-                             x.off, x.c, x.l32, x.hi);
-    if (more1) {
-      wait_tile_loads();
-      if (F16) convert_v_share(kv1 + TILE_BYTES, x.wave, x.lane);
+  const bool g0 = x.group == 0;
+  if (T > 0 && g0) x.ld.issue_k(0, kbuf);
+  wait_copies_and_lds();
+  barrier();
+  for (int t = 0; t <= T; ++t) {
+    char* kt = kbuf + (t & 1) * TILE_BYTES;            // K(t)
+    char* vprev = vbuf + ((t + 1) & 1) * TILE_BYTES;   // V(t-1)
+    char* vcur = vbuf + (t & 1) * TILE_BYTES;          // V(t)
+    // ---- phase 2t
+    if (g0) {
+      mfma_phase<F16>(w, kt, vprev, visible(t - 1), visible(t));
+      if (t + 1 < T) x.ld.issue_k(t + 1, kbuf + ((t + 1) & 1) * TILE_BYTES);
+    } else {
+      if (t < T) x.ld.issue_v(t, vcur);
+      if (visible(t - 1)) softmax_phase<CAUSAL, F16>(w, (t - 1) * BN, x.Sk, x.off, x.c);
+      wait_copies();
     }
-    __syncthreads();
-    if (!more1) break;
-    const bool more2 = t + 2 < x.n_tiles;
-    if (more2) x.ld.issue(t + 2, kv0, kv0 + TILE_BYTES);
-    if (visible((t + 1) * BN))
-      tile_step<CAUSAL, F16>(st, kv1, kv1 + TILE_BYTES, x.koff, x.voff, (t + 1) * BN, x.w_first,
-                             x.Sk, x.off, x.c, x.l32, x.hi);
-    if (more2) {
-      wait_tile_loads();
-      if (F16) convert_v_share(kv0 + TILE_BYTES, x.wave, x.lane);
+    barrier();
+    // ---- phase 2t+1
+    if (g0) {
+      VShare vs;
+      const bool conv = F16 && t < T;
+      if (conv) v_share_load(vs, vcur, x.wave, x.lane);
+      if (visible(t)) softmax_phase<CAUSAL, F16>(w, t * BN, x.Sk, x.off, x.c);
+      if (conv) v_share_store_f16(vs, vcur, x.wave, x.lane);
+      wait_copies();
+    } else {
+      mfma_phase<F16>(w, kt, vprev, visible(t - 1), visible(t));
     }
-    __syncthreads();
+    wait_copies_and_lds();
+    barrier();
   }
 }
 
-__device__ __forceinline__ bool state_finite(const WaveState& st) {
-  bool ok = true;
+__device__ __forceinline__ bool state_finite(const Wave& w) {
+  bool ok = __builtin_isfinite(w.lsum);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    ok = ok && __builtin_isfinite(st.lsum[qb]);
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ok = ok && __builtin_isfinite(st.oacc[qb][db][r]);
-  }
+    for (int r = 0; r < 16; ++r) ok = ok && __builtin_isfinite(w.oacc[db][r]);
   return ok;
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(NT, 1) void prefill_kernel(PrefillArgs a) {
-  // two K/V buffers as separate arrays so that the copy into one provably
-  // does not alias the reads of the other
-  __shared__ __attribute__((aligned(1024))) char kv0[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kv1[2 * TILE_BYTES];
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];
 
-  LoopCtx x;
+  Ctx x;
   const int tid = threadIdx.x;
   x.lane = tid & 63;
   x.wave = tid >> 6;
-  x.l32 = x.lane & 31;
-  x.hi = x.lane >> 5;
-  const int lane = x.lane, hi = x.hi, l32 = x.l32;
+  x.group = x.wave >> 2;                 // waves 0-3 and 4-7: one of each per SIMD
+  Wave w;
+  w.l32 = x.lane & 31;
+  w.hi = x.lane >> 5;
+  const int lane = x.lane;
 
   // ---- which (batch, head, query tile) this workgroup computes
   const int BH = a.B * a.Hq;
   int bh, qt;
   if (CAUSAL) {
-    const int row = blockIdx.x / BH;            // heaviest query tiles first
+    const int row = blockIdx.x / BH;     // heaviest query tiles first
     qt = a.n_qt - 1 - row;
     bh = xcd_remap(blockIdx.x - row * BH, BH);
   } else {
@@ -341,79 +412,75 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(PrefillArgs a) {
   const __bf16* vp = a.v + b * a.k_sb + hk * a.k_sh;
 
   const int q0 = qt * BM;
-  x.off = a.Sk - a.Sq;                          // causal: key j visible iff j <= i + off
+  x.off = a.Sk - a.Sq;                   // causal: key j visible iff j <= i + off
   x.Sk = a.Sk;
   x.c = a.c;
   const int last_row = min(q0 + BM, a.Sq) - 1;
   int n_keys = a.Sk;
   if (CAUSAL) n_keys = min(a.Sk, max(0, last_row + x.off + 1));
   x.n_tiles = (n_keys + BN - 1) / BN;
-  x.w_first = q0 + x.wave * kPrefillRowsPerWave;                  // wave's rows
-  x.w_last = min(x.w_first + kPrefillRowsPerWave, a.Sq) - 1;
-  x.w_any = x.w_first < a.Sq;
+  // 32-row blocks interleaved between the groups: SIMD s holds blocks 2s, 2s+1
+  const int rb = 2 * (x.wave & 3) + x.group;
+  w.first = q0 + 32 * rb;
+  w.last = min(w.first + 31, a.Sq - 1);
   x.ld.init(kp, vp, a.k_ss, a.Sk, x.wave, lane);
 
   // ---- per-lane LDS offsets
   // K operand (A of S^T): row kb*32 + l32, chunk 2*ks + hi
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) x.koff[ks] = tile_off(l32, 2 * ks + hi);
+  for (int ks = 0; ks < 8; ++ks) w.koff[ks] = tile_off(w.l32, 2 * ks + w.hi);
   // V^T operand via transpose reads: lane (block beta = lane/16, j = lane%16)
   // addresses row base + 4*hi + j/4, columns db*32 + 16*(beta&1) + 4*(j%4)
   {
     const int j = lane & 15;
     const int chalf = (lane >> 4) & 1;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int r = 8 * w + 4 * hi + (j >> 2);
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + 4 * w.hi + (j >> 2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int col = db * 32 + 16 * chalf + 4 * (j & 3);
-        x.voff[w][db] = tile_off(r, col >> 3) + (col & 7) * 2;
+        w.voff[h][db] = tile_off(r, col >> 3) + (col & 7) * 2;
       }
     }
   }
 
-  WaveState st;
-  // ---- Q fragments (B operand of S^T = K Q^T): row = query, k-slots = d
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = x.w_first + qb * 32 + l32;
+  // ---- Q fragments: row = query, k-slots = d
+  {
+    const int row = w.first + w.l32;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       if (row < a.Sq)
-        st.qf[qb][ks] = *(const bf16x8*)(qp + (int64_t)row * a.q_ss + 16 * ks + 8 * hi);
+        w.qf[ks] = *(const bf16x8*)(qp + (int64_t)row * a.q_ss + 16 * ks + 8 * w.hi);
       else
-        st.qf[qb][ks] = bf16x8{};
+        w.qf[ks] = bf16x8{};
     }
   }
 
-  tile_loop<CAUSAL, true>(st, x, kv0, kv1);
+  tile_loop<CAUSAL, true>(w, x, kbuf, vbuf);
   // A V value beyond the fp16 range (|v| >= 65520) or a non-finite input
   // shows up as a non-finite accumulator: redo this workgroup with bf16
   // probabilities and bf16 V, which covers the whole bf16 range.
-  if (__syncthreads_or(!state_finite(st))) tile_loop<CAUSAL, false>(st, x, kv0, kv1);
+  if (__syncthreads_or(!state_finite(w))) tile_loop<CAUSAL, false>(w, x, kbuf, vbuf);
 
   // ---- epilogue: O = acc / l (bf16, RTNE) in q's layout; LSE = ln(sum exp)
+  const float l = sum_halves(w.lsum);
+  const int row = w.first + w.l32;
+  if (row < a.Sq) {
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    __bf16* op = a.o + b * a.q_sb + hq * a.q_sh + (int64_t)row * a.q_ss;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = sum_halves(st.lsum[qb]);
-    const int row = x.w_first + qb * 32 + l32;
-    if (row < a.Sq) {
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      __bf16* op = a.o + b * a.q_sb + hq * a.q_sh + (int64_t)row * a.q_ss;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x2 u;
-          u[0] = pack_bf16(st.oacc[qb][db][4 * j + 0] * inv, st.oacc[qb][db][4 * j + 1] * inv);
-          u[1] = pack_bf16(st.oacc[qb][db][4 * j + 2] * inv, st.oacc[qb][db][4 * j + 3] * inv);
-          *(u32x2*)(op + db * 32 + 8 * j + 4 * hi) = u;
-        }
-      if (hi == 0) {
-        const float lse = (l > 0.f) ? (st.m_use[qb] + __log2f(l)) * kLn2 : -INFINITY;
-        a.lse[((int64_t)(b * a.Hq + hq)) * a.Sq + row] = lse;
+      for (int j = 0; j < 4; ++j) {
+        u32x2 u;
+        u[0] = pack_bf16(w.oacc[db][4 * j + 0] * inv, w.oacc[db][4 * j + 1] * inv);
+        u[1] = pack_bf16(w.oacc[db][4 * j + 2] * inv, w.oacc[db][4 * j + 3] * inv);
+        *(u32x2*)(op + db * 32 + 8 * j + 4 * w.hi) = u;
       }
+    if (w.hi == 0) {
+      const float lse = (l > 0.f) ? (w.m_use + __log2f(l)) * kLn2 : -INFINITY;
+      a.lse[((int64_t)(b * a.Hq + hq)) * a.Sq + row] = lse;
     }
   }
 }
