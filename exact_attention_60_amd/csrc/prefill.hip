@@ -126,6 +126,8 @@ struct TileLoader {
 // vmcnt(0) lgkmcnt(0) (also its LDS writes are done).
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_copies_and_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// lgkmcnt(0) only: this wave's LDS writes are done
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without a hardware memory fence: every cross-wave LDS
 // dependency in the loop is ordered by an explicit wait before it.  The empty
 // asm statements keep the compiler from moving memory accesses across it.
@@ -135,31 +137,22 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-// In-place bf16 -> fp16 conversion of 4 x 16 B of a V tile: rows
-// 16*(wave%4) .. +15, the rows whose copy the same-numbered wave of the other
-// group issued and waited for before the last barrier.  The reads are issued
-// first and the conversion done later, so the LDS latency hides behind the
-// softmax; the barrier that follows the store publishes the result.
-struct VShare {
-  u32x4 x[4];
-};
-__device__ __forceinline__ char* v_share_addr(char* vt, int wave, int lane, int j) {
-  return vt + (ROWS_PER_WAVE_DMA * (wave & 3) + 4 * j) * 256 + lane * 16;
-}
-__device__ __forceinline__ void v_share_load(VShare& v, char* vt, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v.x[j] = *(const u32x4*)v_share_addr(vt, wave, lane, j);
-}
-__device__ __forceinline__ void v_share_store_f16(const VShare& v, char* vt, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4 y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = bf16x2_to_f16x2(v.x[j][i]);
-    *(u32x4*)v_share_addr(vt, wave, lane, j) = y;
-  }
+// V^T tile: the P.V operand of lane (d = 32*db + lane%32, hi = lane/32) for
+// k-step kk is the 8 keys 16*kk + {4hi..4hi+3, 8+4hi..8+4hi+3} of row d.
+// V^T rows are 128 B (64 keys); the 16-byte chunk 2*kk + hi of row d holds
+// exactly those 8 keys in k-slot order, at physical chunk
+// (2*kk + hi) ^ ((d >> 1) & 7) so that 16 lanes reading one chunk hit 16
+// different banks.
+__device__ __forceinline__ int vt_off(int d, int chunk) {
+  return d * 128 + ((chunk ^ ((d >> 1) & 7)) << 4);
 }
 
+// One wave's share of turning the bf16 V tile (row-major, as copied) into the
+// V^T tile: k-step kk = wave%4, i.e. keys 16*kk .. 16*kk+15 -- exactly the 16
+// rows this wave copied, so it only has to wait for its own copies -- for all
+// four d blocks.
+// Everything one wave carries through the tile loop.
+struct Wave;
 // Everything one wave carries through the tile loop.
 struct Wave {
   bf16x8 qf[8];        // Q fragments: B operand of S^T = K Q^T (query = lane%32)
@@ -169,70 +162,115 @@ struct Wave {
   float m_use;         // running max in log2 units (scale*log2e folded in)
   float lsum;          // this lane's part of the row sum
   int koff[8];         // LDS offsets of the K operand per 16-wide d step
-  int voff[2][4];      // LDS offsets of the V^T transpose reads
+  int vtoff[4];        // LDS offsets of the V^T operand per k-step (d block 0)
+  int cvoff[2][4];     // transpose-read offsets into the bf16 V tile per d block
   int first, last;     // the wave's query rows
   int l32, hi;
 };
 
-// MFMA phase of a wave: O^T += V^T P^T for the previous tile (16 MFMAs,
-// k-step major so consecutive MFMAs feed different accumulators), then
-// S^T = K Q^T for this tile (16 MFMAs).  The LDS operand reads run DEPTH
-// MFMAs ahead of their use (sched_barrier pins that order), so the matrix
-// core does not wait on LDS latency.
-template <bool F16, bool PV, bool QK>
-__device__ __forceinline__ void mfma_seq(Wave& w, const char* kt, const char* vt_prev) {
-  constexpr int NPV = PV ? 16 : 0;
-  constexpr int N = NPV + (QK ? 16 : 0);
-  constexpr int DEPTH = 4;
-  auto load = [&](int i) -> bf16x8 {
-    if (i < NPV) {
-      const int kk = i >> 2, db = i & 3;                 // k-step (kb, e) and d block
-      const char* base = vt_prev + ((kk >> 1) * 32 + 16 * (kk & 1)) * 256;
-      const bf16x4 lo = lds_read_tr(base + w.voff[0][db]);
-      const bf16x4 up = lds_read_tr(base + w.voff[1][db]);
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+template <bool F16>
+__device__ __forceinline__ void v_transpose_share(const Wave& w, const char* vb, char* vtb, int wave) {
+  const int kk = wave & 3;                          // not a compile-time index:
+  const int woff = vt_off(w.l32, 2 * kk + w.hi);    // no indexing of w.vtoff
+  const char* base = vb + 16 * kk * 256;
+  bf16x8 x[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const bf16x4 lo = lds_read_tr(base + w.cvoff[0][db]);
+    const bf16x4 up = lds_read_tr(base + w.cvoff[1][db]);
+    x[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    u32x4 y = __builtin_bit_cast(u32x4, x[db]);
+    if (F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = bf16x2_to_f16x2(y[i]);
     }
-    const int j = i - NPV, ks = j >> 1, kb = j & 1;
-    return *(const bf16x8*)(kt + kb * 32 * 256 + w.koff[ks]);
+    *(u32x4*)(vtb + db * 32 * 128 + woff) = y;
+  }
+}
+
+// MFMA phase of a wave: S^T = K Q^T for this tile (16 MFMAs), then
+// O^T += V^T P^T for the previous tile (16 MFMAs, k-step major so
+// consecutive MFMAs feed different accumulators).  The LDS operand reads run
+// DEPTH MFMAs ahead of their use (sched_barrier pins that order); the first
+// DEPTH reads (K fragments) are issued by the caller before the barrier that
+// opens the phase, so the matrix core starts as soon as the phase does.
+constexpr int DEPTH = 4;
+struct Prefetch {
+  bf16x8 fr[DEPTH];
+};
+
+__device__ __forceinline__ bf16x8 k_operand(const Wave& w, const char* kt, int j) {
+  const int ks = j >> 1, kb = j & 1;
+  return *(const bf16x8*)(kt + kb * 32 * 256 + w.koff[ks]);
+}
+__device__ __forceinline__ bf16x8 vt_operand(const Wave& w, const char* vt, int j) {
+  const int kk = j >> 2, db = j & 3;                 // k-step (kb, e) and d block
+  return *(const bf16x8*)(vt + db * 32 * 128 + w.vtoff[kk]);
+}
+// the first DEPTH operands of an MFMA phase that starts with Q.K
+__device__ __forceinline__ void prefetch_k(Prefetch& pf, const Wave& w, const char* kt) {
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) pf.fr[i] = k_operand(w, kt, i);
+}
+
+template <bool F16, bool QK, bool PV, bool PREFETCHED>
+__device__ __forceinline__ void mfma_seq(Wave& w, Prefetch& pf, const char* kt,
+                                         const char* vt_prev) {
+  constexpr int NQK = QK ? 16 : 0;
+  constexpr int N = NQK + (PV ? 16 : 0);
+  auto load = [&](int i) -> bf16x8 {
+    return (i < NQK) ? k_operand(w, kt, i) : vt_operand(w, vt_prev, i - NQK);
   };
   auto mma = [&](int i, const bf16x8& f) {
-    if (i < NPV) {
-      const int kk = i >> 2, db = i & 3;
+    if (i < NQK) {
+      const int ks = i >> 1, kb = i & 1;
+      w.s[kb] = mfma32(f, w.qf[ks], w.s[kb]);
+    } else {
+      const int j = i - NQK, kk = j >> 2, db = j & 3;
       if (F16)
         w.oacc[db] = mfma32(__builtin_bit_cast(f16x8, f),
                             __builtin_bit_cast(f16x8, w.pf[kk >> 1][kk & 1]), w.oacc[db]);
       else
         w.oacc[db] = mfma32(f, __builtin_bit_cast(bf16x8, w.pf[kk >> 1][kk & 1]), w.oacc[db]);
-    } else {
-      const int j = i - NPV, ks = j >> 1, kb = j & 1;
-      w.s[kb] = mfma32(f, w.qf[ks], w.s[kb]);
     }
   };
   if (QK) {
     w.s[0] = f32x16{};
     w.s[1] = f32x16{};
   }
-  bf16x8 fr[DEPTH];
+  if (!PREFETCHED) {
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i) fr[i] = load(i);
+    for (int i = 0; i < DEPTH; ++i) pf.fr[i] = load(i);
+  }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    mma(i, fr[i % DEPTH]);
-    if (i + DEPTH < N) fr[i % DEPTH] = load(i + DEPTH);
+    mma(i, pf.fr[i % DEPTH]);
+    if (i + DEPTH < N) pf.fr[i % DEPTH] = load(i + DEPTH);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool F16>
-__device__ __forceinline__ void mfma_phase(Wave& w, const char* kt, const char* vt_prev,
-                                           bool do_pv, bool do_qk) {
-  if (do_pv && do_qk)
-    mfma_seq<F16, true, true>(w, kt, vt_prev);
-  else if (do_qk)
-    mfma_seq<F16, false, true>(w, kt, vt_prev);
-  else if (do_pv)
-    mfma_seq<F16, true, false>(w, kt, vt_prev);
+__device__ __forceinline__ void mfma_phase(Wave& w, Prefetch& pf, const char* kt,
+                                           const char* vt_prev, bool do_qk, bool do_pv,
+                                           bool prefetched) {
+  if (do_qk && do_pv) {
+    if (prefetched)
+      mfma_seq<F16, true, true, true>(w, pf, kt, vt_prev);
+    else
+      mfma_seq<F16, true, true, false>(w, pf, kt, vt_prev);
+  } else if (do_qk) {
+    if (prefetched)
+      mfma_seq<F16, true, false, true>(w, pf, kt, vt_prev);
+    else
+      mfma_seq<F16, true, false, false>(w, pf, kt, vt_prev);
+  } else if (do_pv) {
+    mfma_seq<F16, false, true, false>(w, pf, kt, vt_prev);
+  }
 }
 
 // Softmax phase of a wave for the tile whose scores are in w.s.  Fast path:
@@ -314,17 +352,21 @@ struct Ctx {
 };
 
 // The phased tile loop.  Phase 2t: group 0 runs the MFMA phase of tile t
-// (P.V of t-1, Q.K of t), group 1 the softmax of tile t-1; phase 2t+1:
-// group 0 the softmax of t, group 1 the MFMA phase of t.  K(t) and V(t-1)
-// are read during phases 2t and 2t+1.
-//  * group 0 copies K(t+1) into the other K buffer right after its reads of
-//    phase 2t and waits for it at the end of phase 2t+1;
-//  * group 1 copies V(t) into the other V buffer at the start of phase 2t (a
-//    softmax phase, no LDS reads) and waits for it before the mid barrier;
-//  * in phase 2t+1 group 0, after its softmax, converts all of V(t) to fp16.
-// The barrier that ends phase 2t+1 publishes K(t+1) and V(t) for phase 2t+2.
+// (Q.K of t, P.V of t-1), group 1 the softmax of tile t-1; phase 2t+1:
+// group 0 the softmax of t, group 1 the MFMA phase of t.
+//  * Group 1 copies K(t+1) and V(t) (bf16) at the start of phase 2t (a
+//    softmax phase, no LDS reads) and waits for both before the mid barrier,
+//    so from phase 2t+1 on they are visible to every wave.  K(t+1) goes to
+//    the K buffer last read in phase 2t-1; the single V staging buffer was
+//    last read in phase 2t-1.
+//  * At the end of phase 2t each group-1 wave transposes the 16 rows of V(t)
+//    it copied into the V^T buffer last read in phase 2t-1 (V^T(t-2)'s),
+//    converting to fp16; V^T(t) is first read in phase 2t+2.
+//  * Each group issues the first K-operand reads of its next MFMA phase at
+//    the end of its softmax phase, when that K tile is already visible.
 template <bool CAUSAL, bool F16>
-__device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, char* vbuf) {
+__device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, char* vbuf,
+                                          char* vtbuf) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.oacc[db] = f32x16{};
   w.m_use = -INFINITY;
@@ -334,35 +376,40 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
     return t >= 0 && t < T && w.first <= w.last && (!CAUSAL || t * BN <= w.last + x.off);
   };
   const bool g0 = x.group == 0;
-  if (T > 0 && g0) x.ld.issue_k(0, kbuf);
+  Prefetch pf;
+  if (T > 0 && !g0) x.ld.issue_k(0, kbuf);
   wait_copies_and_lds();
   barrier();
+  bool pre = false;   // this wave holds the first operands of its next MFMA phase
   for (int t = 0; t <= T; ++t) {
-    char* kt = kbuf + (t & 1) * TILE_BYTES;            // K(t)
-    char* vprev = vbuf + ((t + 1) & 1) * TILE_BYTES;   // V(t-1)
-    char* vcur = vbuf + (t & 1) * TILE_BYTES;          // V(t)
+    char* kt = kbuf + (t & 1) * TILE_BYTES;             // K(t)
+    char* knext = kbuf + ((t + 1) & 1) * TILE_BYTES;    // K(t+1)
+    char* vtprev = vtbuf + ((t + 1) & 1) * TILE_BYTES;  // V^T(t-1)
+    char* vtcur = vtbuf + (t & 1) * TILE_BYTES;         // V^T(t), written in phase 2t+1
     // ---- phase 2t
     if (g0) {
-      mfma_phase<F16>(w, kt, vprev, visible(t - 1), visible(t));
-      if (t + 1 < T) x.ld.issue_k(t + 1, kbuf + ((t + 1) & 1) * TILE_BYTES);
+      mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre);
+      pre = false;
     } else {
-      if (t < T) x.ld.issue_v(t, vcur);
+      if (t + 1 < T) x.ld.issue_k(t + 1, knext);
+      if (t < T) x.ld.issue_v(t, vbuf);
       if (visible(t - 1)) softmax_phase<CAUSAL, F16>(w, (t - 1) * BN, x.Sk, x.off, x.c);
       wait_copies();
+      if (t < T) v_transpose_share<F16>(w, vbuf, vtcur, x.wave);
+      pre = visible(t);
+      if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
     }
-    barrier();
+    barrier();   // K(t+1), V(t) copies have landed (group 1 waited for them)
     // ---- phase 2t+1
     if (g0) {
-      VShare vs;
-      const bool conv = F16 && t < T;
-      if (conv) v_share_load(vs, vcur, x.wave, x.lane);
       if (visible(t)) softmax_phase<CAUSAL, F16>(w, t * BN, x.Sk, x.off, x.c);
-      if (conv) v_share_store_f16(vs, vcur, x.wave, x.lane);
-      wait_copies();
+      pre = visible(t + 1);
+      if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
     } else {
-      mfma_phase<F16>(w, kt, vprev, visible(t - 1), visible(t));
+      mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre);
+      pre = false;
+      wait_lds();  // the V^T(t) writes of phase 2t are done before they are published
     }
-    wait_copies_and_lds();
     barrier();
   }
 }
@@ -379,8 +426,9 @@ __device__ __forceinline__ bool state_finite(const Wave& w) {
 template <bool CAUSAL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];   // K, double buffered
+  __shared__ __attribute__((aligned(1024))) char vbuf[TILE_BYTES];       // V as copied (bf16)
+  __shared__ __attribute__((aligned(1024))) char vtbuf[2 * TILE_BYTES];  // V^T (fp16), double buffered
 
   Ctx x;
   const int tid = threadIdx.x;
@@ -429,8 +477,15 @@ void prefill_kernel(PrefillArgs a) {
   // K operand (A of S^T): row kb*32 + l32, chunk 2*ks + hi
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) w.koff[ks] = tile_off(w.l32, 2 * ks + w.hi);
-  // V^T operand via transpose reads: lane (block beta = lane/16, j = lane%16)
-  // addresses row base + 4*hi + j/4, columns db*32 + 16*(beta&1) + 4*(j%4)
+  // V^T operand: row d = l32 (+ 32*db as an immediate), chunk 2*kk + hi
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) w.vtoff[kk] = vt_off(w.l32, 2 * kk + w.hi);
+  // transpose reads of the bf16 V tile: lane (block beta = lane/16,
+  // j = lane%16) addresses row 8*h + 4*hi + j/4 of a 16-key step, columns
+  // 32*db + 16*(beta&1) + 4*(j%4); lane j of each 16-lane block receives 4
+  // keys of column 32*db + 16*(beta&1) + j.  The swizzle only permutes
+  // 16-byte chunks and d block db is chunks 4*db .. 4*db+3, so the offsets of
+  // block db differ from block 0's by a lane-dependent XOR: kept per block.
   {
     const int j = lane & 15;
     const int chalf = (lane >> 4) & 1;
@@ -440,7 +495,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int col = db * 32 + 16 * chalf + 4 * (j & 3);
-        w.voff[h][db] = tile_off(r, col >> 3) + (col & 7) * 2;
+        w.cvoff[h][db] = tile_off(r, col >> 3) + (col & 7) * 2;
       }
     }
   }
@@ -457,11 +512,11 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  tile_loop<CAUSAL, true>(w, x, kbuf, vbuf);
+  tile_loop<CAUSAL, true>(w, x, kbuf, vbuf, vtbuf);
   // A V value beyond the fp16 range (|v| >= 65520) or a non-finite input
   // shows up as a non-finite accumulator: redo this workgroup with bf16
   // probabilities and bf16 V, which covers the whole bf16 range.
-  if (__syncthreads_or(!state_finite(w))) tile_loop<CAUSAL, false>(w, x, kbuf, vbuf);
+  if (__syncthreads_or(!state_finite(w))) tile_loop<CAUSAL, false>(w, x, kbuf, vbuf, vtbuf);
 
   // ---- epilogue: O = acc / l (bf16, RTNE) in q's layout; LSE = ln(sum exp)
   const float l = sum_halves(w.lsum);
