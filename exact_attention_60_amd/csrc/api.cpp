@@ -112,7 +112,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_pages < 1)
     return ATTN_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * attn::kPage > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (B > 65535 || attn::decode_max_splits(max_blocks_per_seq) > 65535) return ATTN_ERR_SHAPE;
   if (d != attn::kHeadDim || page_size != attn::kPage || !scale_ok(scale))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) ||
@@ -135,6 +135,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.G = Hq / Hkv;
   a.n_hb = (a.G + attn::kDecodeHeadsPerBlock - 1) / attn::kDecodeHeadsPerBlock;
   a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
   a.max_splits = attn::decode_max_splits(max_blocks_per_seq);
   a.pps = attn::decode_pages_per_split(B, Hkv, a.n_hb, max_blocks_per_seq, cus);
   a.ws_o = static_cast<float*>(workspace);

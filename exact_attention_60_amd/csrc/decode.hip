@@ -38,13 +38,10 @@ namespace {
 constexpr int D = kHeadDim;
 constexpr int NT = kDecodeWaves * 64;
 constexpr float TAU = 8.0f;
+constexpr int kDecodePrefetch = 1;   // pages in flight beyond the one computed
 
 typedef short i16x4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int row_off(int row, int c) {
-  return row * 256 + ((c ^ swz(row & 15)) << 4);
-}
 
 __device__ __forceinline__ f32x4 mfma16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -56,6 +53,12 @@ __device__ __forceinline__ f32x4 mfma16x16_bf16(const u32x2& a, const u32x2& b, 
 __device__ __forceinline__ f32x4 mfma16x16_f16(const u32x2& a, const u32x2& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Sequence length as used: clamped to [0, 16 * max_blocks] so that no block
+// table entry past the row is ever read.
+__device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int b) {
+  return min(max(a.lens[b], 0), a.max_blocks * kPage);
 }
 
 // sum / max over the four 16-lane groups (lanes l, l^16, l^32, l^48)
@@ -71,24 +74,67 @@ __device__ __forceinline__ float sum_groups(float v) {
   return sum_halves(v);
 }
 
-__global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kDecodeWaves * 16 * D * 4];  // 32 KB
-  __shared__ float mbuf[kDecodeWaves][16];
-  __shared__ float lbuf[kDecodeWaves][16];
+// s_waitcnt vmcnt(n) (other counters left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / a.n_hb;
-  const int hb = blockIdx.y - g * a.n_hb;
-  const int b = blockIdx.z;
-  const int len = a.lens[b];
-  const int np = (len + kPage - 1) / kPage;
-  const int p0 = s * a.pps;
-  if (p0 >= np) return;  // whole workgroup: uniform exit before any barrier
-  const int p1 = min(np, p0 + a.pps);
+// The four K fragments of a page (d = 32*ks + 8*grp .. +8 of one token row).
+// The loads are issued as plain instructions that the compiler does not
+// track: its own wait counts ignore the LDS copies issued in between, so it
+// would wait for later pages' loads too.  wait_page<N> is the matching wait
+// (vmcnt(N)); it names the fragments as operands so that no use of them is
+// scheduled before it.
+__device__ __forceinline__ void load_k(bf16x8 (&kf)[4], const __bf16* row) {
+  asm volatile(
+      "global_load_dwordx4 %0, %4, off\n\t"
+      "global_load_dwordx4 %1, %4, off offset:64\n\t"
+      "global_load_dwordx4 %2, %4, off offset:128\n\t"
+      "global_load_dwordx4 %3, %4, off offset:192"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3])
+      : "v"(row)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_page(bf16x8 (&kf)[4]) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%4)"
+               : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3])
+               : "n"(N)
+               : "memory");
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_split_kernel(DecodeArgs a) {
+  // V page slots per wave, as separate arrays so that reads of one slot do
+  // not wait for copies into another
+  __shared__ __attribute__((aligned(1024))) char vslot0[kDecodeWaves][16 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vslot1[kDecodeWaves][16 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vslot2[kDecodePrefetch > 1 ? kDecodeWaves : 1][16 * D * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  // work unit of this wave: K/V head g, query-head block hb.  The waves of a
+  // workgroup take consecutive units, so together they read the same pages
+  // of neighbouring heads (contiguous bytes of the page) at the same time.
+  const int unit = blockIdx.x * kDecodeWaves + wave;
+  if (unit >= a.Hkv * a.n_hb) return;   // no barrier below: waves are independent
+  const int g = unit / a.n_hb;
+  const int hb = unit - g * a.n_hb;
+  // Workgroup i runs on XCD i % 8.  The sequence index is rotated by the
+  // split index so that one sequence's splits land on different XCDs (each
+  // XCD has its own L2 and its own share of the memory bandwidth); without
+  // it every split of a sequence would go to the same XCDs.
+  const int s = blockIdx.z;
+  const int b = (int)((blockIdx.y + (unsigned)s) % (unsigned)a.B);
+  const int len = seq_len_of(a, b);
+  const int np = (len + kPage - 1) / kPage;
+  const int p0 = s * a.pps;
+  if (p0 >= np) return;
+  const int p1 = min(np, p0 + a.pps);
+
   const int col = lane & 15;   // MFMA column: query head (scores) / token row (K loads)
   const int grp = lane >> 4;   // lane group 0..3
 
@@ -111,41 +157,81 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{};
 
-  char* vst = smem + wave * (16 * 256);    // this wave's V page (4 KB)
-  // V staging: lane -> token row lane/4, chunks 4*(lane%4) + jj
-  const int st_tok = lane >> 2;
-  // transpose-read offsets for the A operand of O^T = V^T P^T (16x16x16):
-  // lane (block grp, j = col) addresses token 4*grp + j/4, d 16*blk + 4*(j%4)
-  int troff[8];
+  // LDS layout of a V page slot (4 KB): eight 512-byte d-blocks, block blk
+  // holding d = 16*blk .. 16*blk+15 of the 16 tokens as [token][16 d].  A
+  // transposed read of one block by the 64 lanes covers its 512 bytes
+  // exactly once (no bank conflicts), and the eight blocks differ only by a
+  // constant offset.
+  // Copy: instruction j moves 1 KB, lane i landing at byte 1024*j + 16*i,
+  // i.e. block 2*j + i/32, token (i%32)/2, half i%2 of the block's 32 bytes.
+  const uint32_t tsb = (uint32_t)(a.token_stride * 2);   // token stride in bytes
+  uint32_t voff[4];
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-    const int d0 = 16 * blk + 4 * (col & 3);
-    troff[blk] = row_off(4 * grp + (col >> 2), d0 >> 3) + (d0 & 7) * 2;
-  }
+  for (int j = 0; j < 4; ++j)
+    voff[j] = (uint32_t)((lane & 31) >> 1) * tsb + (uint32_t)(2 * j + (lane >> 5)) * 32 +
+              (uint32_t)(lane & 1) * 16;
+  // transposed read for the A operand of O^T = V^T P^T (16x16x16): lane
+  // (group grp, j = col) addresses token 4*grp + j/4, d 16*blk + 4*(j%4)
+  const uint32_t tr_lane = (uint32_t)(4 * grp + (col >> 2)) * 32 + (uint32_t)(col & 3) * 8;
 
-  const int32_t* tab = a.table + (int64_t)b * a.max_blocks;
+  // the split's block-table entries, one per lane (a split has at most 64
+  // pages), so that no page waits on a table lookup
+  const int32_t tab_lane = (p0 + lane < p1) ? a.table[(int64_t)b * a.max_blocks + p0 + lane] : 0;
   const float c = a.c;
-  for (int p = p0 + wave; p < p1; p += kDecodeWaves) {
-    const int64_t phys = tab[p];
+  auto page_of = [&](int p) { return __builtin_amdgcn_readlane(tab_lane, p - p0); };
+  // tokens of page p that take part: those before the sequence end, none if
+  // the table entry is outside [0, num_pages) (then page 0 is addressed and
+  // nothing of it is used)
+  auto tokens_in = [&](int p) {
+    const bool ok = (uint32_t)page_of(p) < (uint32_t)a.num_pages;
+    return ok ? min(len - p * kPage, kPage) : 0;
+  };
+
+  // Issue page p: K rows into registers as the A operand (token = col,
+  // d = 32*ks + 8*grp), V rows into LDS slot `vs`.  V rows past the valid
+  // tokens are outside the buffer range of the copy, which stores zeros for
+  // them, so poisoned cache slots never reach the arithmetic.
+  auto issue_page = [&](bf16x8 (&kf)[4], char* vs, int p) {
+    const int e = page_of(p);
+    const int64_t phys = ((uint32_t)e < (uint32_t)a.num_pages) ? e : 0;
     const __bf16* kpg = a.kc + phys * a.page_stride + (int64_t)g * D;
     const __bf16* vpg = a.vc + phys * a.page_stride + (int64_t)g * D;
-    const int tok0 = p * kPage;
-    // ---- loads: K rows as the A operand (token = col, d = 32ks + 8grp), V rows
-    bf16x8 kf[4];
+    load_k(kf, kpg + (int64_t)col * a.token_stride + 8 * grp);
+    const int nt = tokens_in(p);
+    const uint32_t nrec = nt > 0 ? (uint32_t)(nt - 1) * tsb + 256u : 0u;
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vpg, (short)0, (int)nrec, 0x00020000);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = *(const bf16x8*)(kpg + (int64_t)col * a.token_stride + 32 * ks + 8 * grp);
-    u32x4 vr[4];
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vs + j * 1024), 16, voff[j], 0,
+                                               0, 0);
+  };
+
+  // V^T operands of a page from its LDS slot (ds_read_b64_tr_b16), as
+  // untracked instructions too: the compiler would otherwise wait for every
+  // LDS copy in flight, the later pages' included.  The page's copies have
+  // landed (wait_page) before this runs.
+  auto read_v_page = [&](u32x2 (&vf)[8], const char* vs) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(const ATTN_LDS char*)vs + tr_lane;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      vr[jj] = *(const u32x4*)(vpg + (int64_t)st_tok * a.token_stride + 8 * (4 * (lane & 3) + jj));
+    for (int blk = 0; blk < 8; ++blk)
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vf[blk]) : "v"(addr), "n"(512 * blk) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vf[0]), "+v"(vf[1]), "+v"(vf[2]), "+v"(vf[3]), "+v"(vf[4]), "+v"(vf[5]),
+                   "+v"(vf[6]), "+v"(vf[7])
+                 :
+                 : "memory");
+  };
+
+  auto compute_page = [&](const bf16x8 (&kf)[4], const char* vs, int p) {
+    const int nt = tokens_in(p);
     // ---- scores: lane holds head `col`, tokens 4*grp + i
     f32x4 sacc = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) sacc = mfma16x32(kf[ks], qf[ks], sacc);
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = (tok0 + 4 * grp + i < len) ? sacc[i] : -INFINITY;
+    for (int i = 0; i < 4; ++i) sv[i] = (4 * grp + i < nt) ? sacc[i] : -INFINITY;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = max_groups(mx);
     const float m_tile = mx * c;
@@ -161,121 +247,179 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a) {
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(__builtin_fmaf(sv[i], c, -msub));
-    // ---- V page to LDS, rows past the sequence end zeroed.  P.V runs in
-    // fp16 (V converted here) unless a V value of this page is beyond the
-    // fp16 range, in which case the page uses bf16 P and V.
-    const bool tok_ok = tok0 + st_tok < len;
+    // ---- V^T operands from the LDS slot.  P.V runs in fp16 (V converted
+    // here) unless a V value of this page is beyond the fp16 range, in which
+    // case the page uses bf16 P and V.
+    u32x2 vf[8];
+    read_v_page(vf, vs);
     uint32_t big = 0;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      if (!tok_ok) vr[jj] = u32x4{0, 0, 0, 0};
+    for (int blk = 0; blk < 8; ++blk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t m = vr[jj][i] & 0x7fff7fffu;
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t m = vf[blk][i] & 0x7fff7fffu;
         big |= ((m & 0xffffu) > 0x477fu) | ((m >> 16) > 0x477fu);
       }
-    }
-    const bool f16_page = !wave_any(big != 0);
-    u32x2 pu;
-    if (f16_page) {
+    if (!wave_any(big != 0)) {
+      u32x2 pu;
       pu[0] = pack_f16(pv[0], pv[1]);
       pu[1] = pack_f16(pv[2], pv[3]);
       lsum = sum2_f16(pu[1], sum2_f16(pu[0], lsum));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[jj][i] = bf16x2_to_f16x2(vr[jj][i]);
+      for (int blk = 0; blk < 8; ++blk) {
+        vf[blk][0] = bf16x2_to_f16x2(vf[blk][0]);
+        vf[blk][1] = bf16x2_to_f16x2(vf[blk][1]);
+        oacc[blk] = mfma16x16_f16(vf[blk], pu, oacc[blk]);
+      }
     } else {
+      // rare: products into a fresh accumulator, added to the running one
+      u32x2 pu;
       pu[0] = pack_bf16(pv[0], pv[1]);
       pu[1] = pack_bf16(pv[2], pv[3]);
       lsum = sum2_bf16(pu[1], sum2_bf16(pu[0], lsum));
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) oacc[blk] += mfma16x16_bf16(vf[blk], pu, f32x4{});
     }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      *(u32x4*)(vst + row_off(st_tok, 4 * (lane & 3) + jj)) = vr[jj];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      const u32x2 vf = __builtin_bit_cast(u32x2, lds_read_tr(vst + troff[blk]));
-      oacc[blk] = f16_page ? mfma16x16_f16(vf, pu, oacc[blk]) : mfma16x16_bf16(vf, pu, oacc[blk]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+  };
 
-  // ---- merge the four waves' (m, l, O) in LDS
-  const float l_tot = sum_groups(lsum);
-  __syncthreads();  // every wave is done with its V page
-  float* obuf = (float*)smem;  // [wave][head col][d]
-  if (grp == 0) {
-    mbuf[wave][col] = m_use;
-    lbuf[wave][col] = l_tot;
-  }
-#pragma unroll
-  for (int blk = 0; blk < 8; ++blk)
-    *(f32x4*)(obuf + (wave * 16 + col) * D + 16 * blk + 4 * grp) = oacc[blk];
-  __syncthreads();
-
+  // The wave walks the split's pages in order with the loads of the next
+  // kDecodePrefetch pages in flight while the current page is computed (one
+  // register / LDS slot per page, rotated).  The prefetches are issued
+  // unconditionally (past the split's end they re-read the split's last
+  // page) so that each wait is a fixed count: after issuing page
+  // p + kDecodePrefetch, the 8 * kDecodePrefetch memory operations of the
+  // pages after p may still be outstanding.
   {
-    const int hc = tid >> 4;          // head column 0..15
-    const int d0 = (tid & 15) * 8;    // 8 d values
-    const int hl = hb * 16 + hc;
-    if (hl < a.G) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mbuf[w][hc]);
-      float wt[kDecodeWaves];
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float mw = mbuf[w][hc];
-        wt[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        L += wt[w] * lbuf[w][hc];
+    const int plast = p1 - 1;
+    int p = p0;
+    if constexpr (kDecodePrefetch == 1) {
+      char* const va = vslot0[wave];
+      char* const vb = vslot1[wave];
+      bf16x8 ka[4], kb[4];
+      issue_page(ka, va, p);
+      for (;;) {
+        issue_page(kb, vb, min(p + 1, plast));
+        wait_page<8>(ka);
+        compute_page(ka, va, p);
+        if (++p >= p1) break;
+        issue_page(ka, va, min(p + 1, plast));
+        wait_page<8>(kb);
+        compute_page(kb, vb, p);
+        if (++p >= p1) break;
       }
-      const float inv = (L > 0.f) ? 1.f / L : 0.f;
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float* src = obuf + (w * 16 + hc) * D + d0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += wt[w] * src[i];
+    } else {
+      char* const va = vslot0[wave];
+      char* const vb = vslot1[wave];
+      char* const vc = vslot2[wave];
+      bf16x8 ka[4], kb[4], kc[4];
+      issue_page(ka, va, p);
+      issue_page(kb, vb, min(p + 1, plast));
+      for (;;) {
+        issue_page(kc, vc, min(p + 2, plast));
+        wait_page<16>(ka);
+        compute_page(ka, va, p);
+        if (++p >= p1) break;
+        issue_page(ka, va, min(p + 2, plast));
+        wait_page<16>(kb);
+        compute_page(kb, vb, p);
+        if (++p >= p1) break;
+        issue_page(kb, vb, min(p + 2, plast));
+        wait_page<16>(kc);
+        compute_page(kc, vc, p);
+        if (++p >= p1) break;
       }
-      const int hqo = g * a.G + hl;
-      const int64_t slot = ((int64_t)b * a.Hq + hqo) * a.max_splits + s;
-      float* dst = a.ws_o + slot * D + d0;
-      *(f32x4*)dst = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-      *(f32x4*)(dst + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-      if ((tid & 15) == 0)
-        a.ws_lse[slot] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
+    wait_vm<0>();   // no copy into LDS may outlive the wave
+  }
+
+  // ---- this split's normalised output and natural-log LSE per head.
+  // C layout of the 16x16 accumulator: lane column = head, rows 4*grp + i
+  // of block blk = d 16*blk + 4*grp + i.
+  const float l_tot = sum_groups(lsum);
+  if (hvalid) {
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int64_t slot = ((int64_t)b * a.Hq + hq) * a.max_splits + s;
+    float* dst = a.ws_o + slot * D + 4 * grp;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) *(f32x4*)(dst + 16 * blk) = oacc[blk] * inv;
+    if (grp == 0)
+      a.ws_lse[slot] = (l_tot > 0.f) ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-// One wave per (b, query head); lane owns d = 2*lane, 2*lane+1.
+// One wave per (b, query head); lane owns d = 2*lane, 2*lane+1.  The split
+// LSEs are read by the lanes in parallel and reduced across the wave; the
+// weighted sum over splits runs in split order (deterministic).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return max_halves(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return sum_halves(v);
+}
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int C = 16;   // partial outputs loaded per batch
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wid >= a.B * a.Hq) return;
   const int lane = threadIdx.x & 63;
   const int b = wid / a.Hq;
-  const int len = a.lens[b];
-  const int np = (len + kPage - 1) / kPage;
-  const int ns = (np + a.pps - 1) / a.pps;
   const int64_t slot0 = (int64_t)wid * a.max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_lse[slot0 + s]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ls = a.ws_lse[slot0 + s];
-    const float w = (ls == -INFINITY) ? 0.f : fast_exp2((ls - M) * kLog2e);
-    const float2 ov = *(const float2*)(a.ws_o + (slot0 + s) * D + 2 * lane);
-    L += w;
-    o0 += w * ov.x;
-    o1 += w * ov.y;
+  const float* lse_p = a.ws_lse + slot0;
+  const float* o_p = a.ws_o + slot0 * D + 2 * lane;
+  // The first 64 split LSEs and the first C partial outputs are loaded
+  // before the split count is known (it needs the sequence length), so that
+  // the common case costs one memory round trip; slots past the count are
+  // never used.
+  const float lse_first = (lane < a.max_splits) ? lse_p[lane] : -INFINITY;
+  float2 ov[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i)
+    ov[i] = (i < a.max_splits) ? *(const float2*)(o_p + (int64_t)i * D) : float2{0.f, 0.f};
+  const int np = (seq_len_of(a, b) + kPage - 1) / kPage;
+  const int ns = (np + a.pps - 1) / a.pps;
+
+  auto lse_at = [&](int s0) {   // this lane's split of the batch s0 .. s0+63
+    return (s0 + lane < ns) ? (s0 == 0 ? lse_first : lse_p[s0 + lane]) : -INFINITY;
+  };
+  float M = lse_at(0);
+  for (int s0 = 64; s0 < ns; s0 += 64) M = fmaxf(M, lse_at(s0));
+  M = wave_max(M);
+  auto weight = [&](float ls) { return (ls == -INFINITY) ? 0.f : fast_exp2((ls - M) * kLog2e); };
+  float wl = weight(lse_at(0));   // weight of split `lane`
+  float Lp = wl;
+  for (int s0 = 64; s0 < ns; s0 += 64) Lp += weight(lse_at(s0));
+  const float L = wave_sum(Lp);
+
+  // O = sum_s w_s O_s in split order
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    if (i < ns) {
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
+      o0 += w * ov[i].x;
+      o1 += w * ov[i].y;
+    }
+  }
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    if (s0 > 0) wl = weight(lse_at(s0));
+    for (int i0 = (s0 == 0 ? C : 0); i0 < 64 && s0 + i0 < ns; i0 += C) {
+#pragma unroll
+      for (int i = 0; i < C; ++i)
+        if (s0 + i0 + i < ns) ov[i] = *(const float2*)(o_p + (int64_t)(s0 + i0 + i) * D);
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        if (s0 + i0 + i < ns) {
+          const float w =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i0 + i));
+          o0 += w * ov[i].x;
+          o1 += w * ov[i].y;
+        }
+      }
+    }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
   *(uint32_t*)(a.o + (int64_t)wid * D + 2 * lane) = pack_bf16(o0 * inv, o1 * inv);
@@ -288,20 +432,26 @@ int decode_max_splits(int max_blocks) {
   return (max_blocks + kDecodeMinPagesPerSplit - 1) / kDecodeMinPagesPerSplit;
 }
 
-// Pages per split: a power of two >= 8 chosen so that, with sequences about
-// half full on average, the grid holds about eight workgroups per CU.
+// Pages per split: a power of two >= kDecodeMinPagesPerSplit chosen so that,
+// with sequences about half full on average, the grid holds about
+// kDecodeWavesPerCu busy waves per CU (each wave walks one split of one head).
 int decode_pages_per_split(int B, int Hkv, int n_hb, int max_blocks, int num_cus) {
-  const double est_pages = (double)B * Hkv * n_hb * max_blocks * 0.5;
-  const double target_wgs = 8.0 * (num_cus > 0 ? num_cus : 256);
+  const double est_page_heads = (double)B * Hkv * n_hb * max_blocks * 0.5;
+  const double target_waves = (double)kDecodeWavesPerCu * (num_cus > 0 ? num_cus : 256);
   int pps = kDecodeMinPagesPerSplit;
-  while (pps < max_blocks && est_pages / pps > target_wgs) pps *= 2;
+  while (pps < max_blocks && pps < kDecodeMaxPagesPerSplit && est_page_heads / pps > target_waves)
+    pps *= 2;
   return pps;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int splits = (a.max_blocks + a.pps - 1) / a.pps;
-  if (splits > a.max_splits) return hipErrorInvalidValue;
-  dim3 grid1(splits, a.Hkv * a.n_hb, a.B);
+  if (splits > a.max_splits || splits > 65535 || a.B > 65535 || a.pps > kDecodeMaxPagesPerSplit)
+    return hipErrorInvalidValue;
+  // splits outermost: every sequence's first splits (full ones) start
+  // first, the short last splits and the empty ones (past a sequence's end)
+  // come last
+  dim3 grid1((a.Hkv * a.n_hb + kDecodeWaves - 1) / kDecodeWaves, a.B, splits);
   hipLaunchKernelGGL(decode_split_kernel, grid1, dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -31,7 +31,9 @@ hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream)
 // ---- paged decode ----------------------------------------------------------
 constexpr int kPage = 16;
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeMinPagesPerSplit = 8;   // bounds the workspace
+constexpr int kDecodeMinPagesPerSplit = 4;   // bounds the workspace
+constexpr int kDecodeMaxPagesPerSplit = 64;  // one block-table entry per lane
+constexpr int kDecodeWavesPerCu = 8;         // split-size target
 constexpr int kDecodeHeadsPerBlock = 16;     // query heads per MFMA column block
 
 struct DecodeArgs {
@@ -46,6 +48,7 @@ struct DecodeArgs {
   float* lse;
   int B, Hq, Hkv, G, n_hb;   // G = Hq / Hkv, n_hb = ceil(G / 16)
   int max_blocks, max_splits, pps;
+  int num_pages;
   int64_t page_stride;       // elements per page: 16 * Hkv * 128
   int64_t token_stride;      // elements per token slot: Hkv * 128
   float c;                   // scale * log2(e)

@@ -97,8 +97,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * attn_decode_workspace_bytes - device workspace that attn_decode_paged needs
  * for its split partials (fp32 partial outputs and their LSEs), for a batch of
- * B sequences, Hq query heads and block tables of max_blocks_per_seq entries.
- * Returns 0 for invalid sizes.
+ * B sequences, Hq query heads and block tables of max_blocks_per_seq entries:
+ * B * Hq * ceil(max_blocks_per_seq / 4) * 129 * 4 bytes.  Returns 0 for
+ * invalid sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq);
 
@@ -112,7 +113,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq);
  *   block_table  int32 [B, max_blocks_per_seq]; entries p < ceil(seq_lens[b]/16)
  *                must lie in [0, num_pages); entries beyond are never read
  *   seq_lens     int32 [B], 1 <= seq_lens[b] <= max_blocks_per_seq * 16,
- *                counting every cached token (the current one included)
+ *                counting every cached token (the current one included);
+ *                B <= 65535 and max_blocks_per_seq <= 262140
  *   o            bf16 output [B, Hq, d]
  *   lse          fp32 output [B, Hq]
  *   page_size == 16, d == 128, Hq % Hkv == 0
@@ -121,8 +123,12 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq);
  *                its contents on entry do not matter
  *
  * The table and seq_lens live on the device and are not read by the host, so
- * their preconditions are documented, not checked.  Cache slots past a
- * sequence's end may hold any bits (NaN included): they are never used.
+ * their preconditions are documented, not checked; out-of-contract values stay
+ * memory-safe: a length is clamped to [0, 16 * max_blocks_per_seq], a table
+ * entry outside [0, num_pages) is not dereferenced and its 16 tokens are left
+ * out, and a sequence left with no tokens gets O = 0 and LSE = -inf.  Cache
+ * slots past a sequence's end may hold any bits (NaN included): they are
+ * never used.
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* seq_lens, void* o,

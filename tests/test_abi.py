@@ -37,8 +37,9 @@ def test_version_and_status_strings():
 
 
 def test_workspace_bytes():
-    # partials: B * Hq * ceil(max_blocks / 8) splits of (128 + 1) floats
-    assert ea.attn_decode_workspace_bytes(32, 32, 256) == 32 * 32 * 32 * 129 * 4
+    # partials: B * Hq * ceil(max_blocks / 4) splits of (128 + 1) floats
+    assert ea.attn_decode_workspace_bytes(32, 32, 256) == 32 * 32 * 64 * 129 * 4
+    assert ea.attn_decode_workspace_bytes(2, 3, 9) == 2 * 3 * 3 * 129 * 4
     assert ea.attn_decode_workspace_bytes(1, 1, 1) == 129 * 4
     assert ea.attn_decode_workspace_bytes(0, 1, 1) == 0
     assert ea.attn_decode_workspace_bytes(1, 1, 0) == 0
@@ -84,6 +85,7 @@ def dec(**kw):
     (dict(d=256), -3), (dict(page=32), -3), (dict(scale=0.0), -3),
     (dict(k=P + 8), -4), (dict(tab=P + 4), -4),
     (dict(ws=None), -5), (dict(wsb=100), -5),
+    (dict(B=65536, wsb=1 << 62), -2), (dict(mb=262141, wsb=1 << 62), -2),   # grid limits
 ])
 def test_decode_argument_errors(kw, code):
     assert dec(**kw) == code

@@ -52,6 +52,52 @@ def test_decode_small(case):
     check_decode(d, o, lse, str(case))
 
 
+@pytest.mark.parametrize("case", [(1, 8, 1, 40000, [40000]), (2, 16, 2, 20000, [20000, 3001])],
+                         ids=["B1_L40000", "B2_L20000"])
+def test_decode_many_splits(case):
+    """Long sequences in a small batch: hundreds of splits per sequence, so
+    the merge runs over several batches of split results."""
+    B, Hq, Hkv, L, lens = case
+    d = gen.decode_inputs(B, Hq, Hkv, max_len=L, seed=L + B, lens=lens)
+    o, lse = run_decode(d)
+    check_decode(d, o, lse, str(case))
+
+
+def test_out_of_contract_lengths_and_table_entries():
+    """Values the contract excludes stay memory-safe and defined: a length
+    past the table is clamped to 16 * max_blocks, a table entry outside
+    [0, num_pages) drops its 16 tokens, and a length <= 0 gives O = 0 and
+    LSE = -inf."""
+    d = gen.decode_inputs(5, 8, 2, max_len=320, seed=97, lens=[320, 100, 64, 50, 200])
+    lens = d.seq_lens.copy()
+    tab = d.block_table.copy()
+    lens[0] = 10 ** 6                 # clamped to 320
+    tab[1, 2] = d.num_pages + 5       # tokens 32..47 of sequence 1 dropped
+    tab[4, 0] = -7                    # tokens 0..15 of sequence 4 dropped
+    lens[2] = 0
+    lens[3] = -5
+    o, lse = ea.attn_decode_paged(dev_bf16(d.q), dev_bf16(d.k_pool), dev_bf16(d.v_pool),
+                                  dev_i32(tab), dev_i32(lens), scale=d.scale)
+    torch.cuda.synchronize()
+    # the same attention written within the contract: dropped pages removed
+    # from the table (the tokens keep their order; attention has no positions)
+    ref_tab = np.full_like(d.block_table, -1)
+    ref_lens = d.seq_lens.copy()
+    for b in range(d.B):
+        row = [int(x) for x in d.block_table[b] if x >= 0]
+        if b == 1:
+            row.pop(2)
+            ref_lens[b] -= 16
+        if b == 4:
+            row.pop(0)
+            ref_lens[b] -= 16
+        ref_tab[b, :len(row)] = row
+    ref_lens[2] = 0
+    ref_lens[3] = 0
+    ref = gen.Decode(d.q, d.k_pool, d.v_pool, ref_tab, ref_lens, d.B, d.Hq, d.Hkv, d.scale)
+    check_decode(ref, o, lse, "out of contract")
+
+
 def test_config5_full():
     d = gen.config5()
     o, lse = run_decode(d)
