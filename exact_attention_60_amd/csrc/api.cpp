@@ -101,7 +101,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
   if (B < 1 || Hq < 1 || max_blocks_per_seq < 1) return 0;
   const size_t splits = (size_t)attn::decode_max_splits(max_blocks_per_seq);
-  return (size_t)B * Hq * splits * (attn::kHeadDim + 1) * sizeof(float);
+  // partial outputs and LSEs, then one count per (sequence, unit group) (at
+  // most Hq unit groups)
+  return (size_t)B * Hq * (splits * (attn::kHeadDim + 1) + 1) * sizeof(float);
 }
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -112,7 +114,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_pages < 1)
     return ATTN_ERR_SHAPE;
-  if (B > 65535 || attn::decode_max_splits(max_blocks_per_seq) > 65535) return ATTN_ERR_SHAPE;
+  if (B > 65535 || max_blocks_per_seq > 262140) return ATTN_ERR_SHAPE;
   if (d != attn::kHeadDim || page_size != attn::kPage || !scale_ok(scale))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) ||
@@ -136,16 +138,18 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.n_hb = (a.G + attn::kDecodeHeadsPerBlock - 1) / attn::kDecodeHeadsPerBlock;
   a.max_blocks = max_blocks_per_seq;
   a.num_pages = num_pages;
+  a.X = (Hkv * a.n_hb + attn::kDecodeWaves - 1) / attn::kDecodeWaves;
   a.max_splits = attn::decode_max_splits(max_blocks_per_seq);
-  a.pps = attn::decode_pages_per_split(B, Hkv, a.n_hb, max_blocks_per_seq, cus);
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = a.ws_o + (size_t)B * Hq * a.max_splits * attn::kHeadDim;
+  a.ws_cnt = reinterpret_cast<int*>(a.ws_lse + (size_t)B * Hq * a.max_splits);
+  a.nwg = 0;
   a.o = static_cast<__bf16*>(o);
   a.lse = lse;
   a.token_stride = (int64_t)Hkv * attn::kHeadDim;
   a.page_stride = (int64_t)attn::kPage * a.token_stride;
   a.c = scale * 1.4426950408889634f;
-  const hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = attn::launch_decode(a, cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -1,34 +1,43 @@
-// Split-KV paged decode for gfx950: one query row per (sequence, query head)
-// against every cached token of a paged KV cache, in two kernels.
+// Paged decode for gfx950: one query row per (sequence, query head) against
+// every cached token of a paged KV cache, in two kernels.
 //
 // The cache layout follows "Engineering the FlashAttention-4 kernel port to
 // ROCm: HIP migration and multi-query inference optimisation" (multi-query
 // section): 16-token pages listed by an int32 block table, several query heads
 // sharing one K/V head (Q:32 / KV:8 there), tokens contiguous along the
-// sequence with a stride of head_dim * kv_heads.  The split of the keys with a
-// log-sum-exp merge of partial results is the Flash-Decoding style tail split
-// of "MoonMath AI open-sources a HIP attention kernel for AMD MI300X that beats
-// AITER v3" (third-Q-tile paragraph), generalised from two partial softmaxes to
-// any number; within a split the online softmax is the block merge of
-// "IO-aware tiling strategy in FlashAttention-4" (body).
+// sequence with a stride of head_dim * kv_heads.  Splitting the keys and
+// merging the partial softmaxes through their log-sum-exp is the
+// Flash-Decoding style split of "MoonMath AI open-sources a HIP attention
+// kernel for AMD MI300X that beats AITER v3" (third-Q-tile paragraph),
+// generalised from two partial results to any number; within a part the
+// online softmax is the block merge of "IO-aware tiling strategy in
+// FlashAttention-4" (body).
 //
-// decode_split_kernel, grid (splits, Hkv * head_blocks, B), 4 waves:
-//   the workgroup covers pages [s*pps, min((s+1)*pps, ceil(len/16))) of one
-//   sequence for up to 16 query heads of one K/V head; wave w takes every 4th
-//   page.  Per page (16 tokens x 256 B of K and of V for this head):
+// decode_partial_kernel: a persistent grid of exactly as many 8-wave
+//   workgroups as the GPU holds at once.  Work is laid out as page slots
+//   (unit group x, concatenated pages of all sequences), a unit group being
+//   eight (K/V head, 16-query-head block) units; the slots are cut into equal
+//   chunks of at most 64 pages and workgroup j takes chunks j, j + grid, ...
+//   so every CU streams the same number of bytes whatever the lengths.  A
+//   chunk is cut further at sequence ends into segments; wave w of the
+//   workgroup runs unit 8x + w over the segment's pages (the waves read the
+//   same pages of neighbouring heads: whole 16-token pages when Hkv = 8).
+//   Per page (16 tokens x 256 B of K and of V for one head):
 //     S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows straight from global,
 //     Q^T in registers, columns = query heads), tokens past the end masked;
 //     running max / sum per head (log2 units, rescale skipped while the max
 //     grows by less than 2^8);
-//     V page converted to fp16 and staged in LDS (rows past the end zeroed,
-//     so poisoned cache slots never reach the arithmetic), read back
-//     transposed with ds_read_b64_tr_b16, O^T += V^T P^T on
-//     v_mfma_f32_16x16x16_f16 with fp16 probabilities (a page holding a V
-//     value beyond the fp16 range keeps bf16 for both operands instead).
-//   The four waves' states are merged exactly in LDS and the split's
-//   normalised fp32 output and natural-log LSE go to the workspace.
+//     the V page copied into LDS by buffer_load ... lds (rows past the end
+//     stored as zeros, so poisoned cache slots never reach the arithmetic),
+//     read back transposed with ds_read_b64_tr_b16, converted to fp16, and
+//     O^T += V^T P^T on v_mfma_f32_16x16x16_f16 with fp16 probabilities (a
+//     page holding a V value beyond the fp16 range keeps bf16 for both).
+//   Each segment writes its normalised fp32 output and natural-log LSE per
+//   head to the workspace, in the slot of its chunk counted from the first
+//   chunk of that (sequence, unit group); the workgroup that holds a
+//   sequence's first page also writes how many chunks the sequence spans.
 // decode_merge_kernel, one wave per (b, query head): LSE = M + ln sum e^(LSE_s-M),
-//   O = sum e^(LSE_s - LSE) O_s in split order (deterministic), O to bf16 RTNE.
+//   O = sum e^(LSE_s - LSE) O_s in chunk order (deterministic), O to bf16 RTNE.
 #include "gfx950.hpp"
 #include "kernels.h"
 
@@ -38,6 +47,7 @@ namespace {
 constexpr int D = kHeadDim;
 constexpr int NT = kDecodeWaves * 64;
 constexpr float TAU = 8.0f;
+constexpr int kMaxSeqChunks = 1024;   // ceil(65535 / 64) sequence chunks
 constexpr int kDecodePrefetch = 1;   // pages in flight beyond the one computed
 
 typedef short i16x4v __attribute__((ext_vector_type(4)));
@@ -106,35 +116,56 @@ __device__ __forceinline__ void wait_page(bf16x8 (&kf)[4]) {
                : "memory");
 }
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_split_kernel(DecodeArgs a) {
-  // V page slots per wave, as separate arrays so that reads of one slot do
-  // not wait for copies into another
-  __shared__ __attribute__((aligned(1024))) char vslot0[kDecodeWaves][16 * D * 2];
-  __shared__ __attribute__((aligned(1024))) char vslot1[kDecodeWaves][16 * D * 2];
-  __shared__ __attribute__((aligned(1024))) char vslot2[kDecodePrefetch > 1 ? kDecodeWaves : 1][16 * D * 2];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  // work unit of this wave: K/V head g, query-head block hb.  The waves of a
-  // workgroup take consecutive units, so together they read the same pages
-  // of neighbouring heads (contiguous bytes of the page) at the same time.
-  const int unit = blockIdx.x * kDecodeWaves + wave;
-  if (unit >= a.Hkv * a.n_hb) return;   // no barrier below: waves are independent
+// Number of pages of sequence b as used.
+__device__ __forceinline__ int seq_pages(const DecodeArgs& a, int b) {
+  return (seq_len_of(a, b) + kPage - 1) / kPage;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// Cut of the page slots into chunks: W = X * T slots, NC chunks, chunk c
+// holding q + 1 slots if c < rem, else q (at most 64, at least 4 unless
+// there is a single chunk).  Identical on every workgroup and in the merge.
+struct Chunks {
+  int64_t T, W, NC, q, rem;
+  __device__ Chunks(int64_t T_, int X, int nwg) : T(T_), W((int64_t)X * T_) {
+    if (W == 0) { NC = 0; q = 0; rem = 0; return; }
+    const int64_t rounds = (W + (int64_t)kDecodeMaxChunkPages * nwg - 1) / ((int64_t)kDecodeMaxChunkPages * nwg);
+    NC = min((int64_t)nwg * rounds, W / kDecodeMinChunkPages);
+    if (NC < 1) NC = 1;
+    q = W / NC;
+    rem = W - q * NC;
+  }
+  __device__ int64_t begin(int64_t c) const { return c * q + min(c, rem); }
+  __device__ int64_t chunk_of(int64_t L) const {
+    const int64_t big = rem * (q + 1);
+    return L < big ? L / (q + 1) : rem + (L - big) / q;
+  }
+};
+
+// One wave: unit (K/V head, query-head block) over pages [p0, p1) of
+// sequence b; writes the normalised partial output and its LSE to `slot`.
+__device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char* vb, char* vc, int b,
+                                            int unit, int p0, int p1, int slot) {
+  const int lane = threadIdx.x & 63;
   const int g = unit / a.n_hb;
   const int hb = unit - g * a.n_hb;
-  // Workgroup i runs on XCD i % 8.  The sequence index is rotated by the
-  // split index so that one sequence's splits land on different XCDs (each
-  // XCD has its own L2 and its own share of the memory bandwidth); without
-  // it every split of a sequence would go to the same XCDs.
-  const int s = blockIdx.z;
-  const int b = (int)((blockIdx.y + (unsigned)s) % (unsigned)a.B);
   const int len = seq_len_of(a, b);
-  const int np = (len + kPage - 1) / kPage;
-  const int p0 = s * a.pps;
-  if (p0 >= np) return;
-  const int p1 = min(np, p0 + a.pps);
-
   const int col = lane & 15;   // MFMA column: query head (scores) / token row (K loads)
   const int grp = lane >> 4;   // lane group 0..3
 
@@ -174,8 +205,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
   // (group grp, j = col) addresses token 4*grp + j/4, d 16*blk + 4*(j%4)
   const uint32_t tr_lane = (uint32_t)(4 * grp + (col >> 2)) * 32 + (uint32_t)(col & 3) * 8;
 
-  // the split's block-table entries, one per lane (a split has at most 64
-  // pages), so that no page waits on a table lookup
+  // the segment's block-table entries, one per lane (a segment has at most
+  // 64 pages), so that no page waits on a table lookup
   const int32_t tab_lane = (p0 + lane < p1) ? a.table[(int64_t)b * a.max_blocks + p0 + lane] : 0;
   const float c = a.c;
   auto page_of = [&](int p) { return __builtin_amdgcn_readlane(tab_lane, p - p0); };
@@ -282,19 +313,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     }
   };
 
-  // The wave walks the split's pages in order with the loads of the next
+  // The wave walks the segment's pages in order with the loads of the next
   // kDecodePrefetch pages in flight while the current page is computed (one
   // register / LDS slot per page, rotated).  The prefetches are issued
-  // unconditionally (past the split's end they re-read the split's last
-  // page) so that each wait is a fixed count: after issuing page
-  // p + kDecodePrefetch, the 8 * kDecodePrefetch memory operations of the
-  // pages after p may still be outstanding.
+  // unconditionally (past the segment's end they re-read its last page) so
+  // that each wait is a fixed count: after issuing page p + kDecodePrefetch,
+  // the 8 * kDecodePrefetch memory operations of the pages after p may still
+  // be outstanding.
   {
     const int plast = p1 - 1;
     int p = p0;
     if constexpr (kDecodePrefetch == 1) {
-      char* const va = vslot0[wave];
-      char* const vb = vslot1[wave];
       bf16x8 ka[4], kb[4];
       issue_page(ka, va, p);
       for (;;) {
@@ -308,9 +337,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
         if (++p >= p1) break;
       }
     } else {
-      char* const va = vslot0[wave];
-      char* const vb = vslot1[wave];
-      char* const vc = vslot2[wave];
       bf16x8 ka[4], kb[4], kc[4];
       issue_page(ka, va, p);
       issue_page(kb, vb, min(p + 1, plast));
@@ -332,24 +358,111 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     wait_vm<0>();   // no copy into LDS may outlive the wave
   }
 
-  // ---- this split's normalised output and natural-log LSE per head.
+  // ---- the segment's normalised output and natural-log LSE per head.
   // C layout of the 16x16 accumulator: lane column = head, rows 4*grp + i
   // of block blk = d 16*blk + 4*grp + i.
   const float l_tot = sum_groups(lsum);
   if (hvalid) {
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int64_t slot = ((int64_t)b * a.Hq + hq) * a.max_splits + s;
-    float* dst = a.ws_o + slot * D + 4 * grp;
+    const int64_t ws = ((int64_t)b * a.Hq + hq) * a.max_splits + slot;
+    float* dst = a.ws_o + ws * D + 4 * grp;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) *(f32x4*)(dst + 16 * blk) = oacc[blk] * inv;
     if (grp == 0)
-      a.ws_lse[slot] = (l_tot > 0.f) ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
+      a.ws_lse[ws] = (l_tot > 0.f) ? (m_use + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-// One wave per (b, query head); lane owns d = 2*lane, 2*lane+1.  The split
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_partial_kernel(DecodeArgs a) {
+  // V page slots per wave, as separate arrays so that reads of one slot do
+  // not wait for copies into another
+  __shared__ __attribute__((aligned(1024))) char vslot0[kDecodeWaves][16 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vslot1[kDecodeWaves][16 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vslot2[kDecodePrefetch > 1 ? kDecodeWaves : 1][16 * D * 2];
+  // pages per chunk of 64 sequences, then their exclusive prefix sums
+  __shared__ int ck_tot[kMaxSeqChunks];
+  __shared__ int64_t ck_pre[kMaxSeqChunks + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int nck = (a.B + 63) / 64;
+
+  // ---- page counts of all sequences (every workgroup computes the same)
+  for (int k = wave; k < nck; k += kDecodeWaves) {
+    const int bb = 64 * k + lane;
+    const int t = wave_sum_i(bb < a.B ? seq_pages(a, bb) : 0);
+    if (lane == 0) ck_tot[k] = t;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int64_t carry = 0;
+    for (int k0 = 0; k0 < nck; k0 += 64) {
+      const int t = (k0 + lane < nck) ? ck_tot[k0 + lane] : 0;
+      const int incl = wave_incl_scan(t);
+      if (k0 + lane < nck) ck_pre[k0 + lane] = carry + incl - t;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) ck_pre[nck] = carry;
+  }
+  __syncthreads();
+
+  const int U = a.Hkv * a.n_hb;
+  const Chunks ch(ck_pre[nck], a.X, gridDim.x);
+
+  // sequence holding page position r (0 <= r < T) of the concatenated list:
+  // binary search over the chunk prefixes, then a scan of that chunk's 64
+  // lengths (kept while the search stays in the same chunk)
+  int cached_k = -1, np_lane = 0, incl_lane = 0;
+  auto find_seq = [&](int64_t r, int& b, int64_t& pre_b, int& np_b) {
+    int lo = 0, hi = nck - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ck_pre[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    if (lo != cached_k) {
+      const int bb = 64 * lo + lane;
+      np_lane = bb < a.B ? seq_pages(a, bb) : 0;
+      incl_lane = wave_incl_scan(np_lane);
+      cached_k = lo;
+    }
+    const int64_t base = ck_pre[lo];
+    const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl_lane > r);
+    const int l0 = __builtin_ctzll(m);
+    np_b = __builtin_amdgcn_readlane(np_lane, l0);
+    pre_b = base + __builtin_amdgcn_readlane(incl_lane, l0) - np_b;
+    b = 64 * lo + l0;
+  };
+
+  for (int64_t c = blockIdx.x; c < ch.NC; c += gridDim.x) {
+    int64_t L = ch.begin(c);
+    const int64_t Lend = ch.begin(c + 1);
+    while (L < Lend) {
+      const int x = (int)(L / ch.T);
+      const int64_t r = L - (int64_t)x * ch.T;
+      int b, np_b;
+      int64_t pre_b;
+      find_seq(r, b, pre_b, np_b);
+      const int64_t seg_end = min(Lend, (int64_t)x * ch.T + pre_b + np_b);
+      const int p0 = (int)(r - pre_b);
+      const int p1 = p0 + (int)(seg_end - L);
+      const int64_t c_first = ch.chunk_of((int64_t)x * ch.T + pre_b);
+      if (p0 == 0 && wave == 0 && lane == 0)
+        a.ws_cnt[(int64_t)b * a.X + x] =
+            (int)(ch.chunk_of((int64_t)x * ch.T + pre_b + np_b - 1) - c_first + 1);
+      const int unit = kDecodeWaves * x + wave;
+      const int slot = (int)(c - c_first);
+      if (unit < U && slot < a.max_splits) run_segment(a, vslot0[wave], vslot1[wave],
+                                                       vslot2[kDecodePrefetch > 1 ? wave : 0],
+                                                       b, unit, p0, p1, slot);
+      L = seg_end;
+    }
+  }
+}
+
+// One wave per (b, query head); lane owns d = 2*lane, 2*lane+1.  The part
 // LSEs are read by the lanes in parallel and reduced across the wave; the
-// weighted sum over splits runs in split order (deterministic).
+// weighted sum over parts runs in chunk order (deterministic).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -370,17 +483,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int64_t slot0 = (int64_t)wid * a.max_splits;
   const float* lse_p = a.ws_lse + slot0;
   const float* o_p = a.ws_o + slot0 * D + 2 * lane;
-  // The first 64 split LSEs and the first C partial outputs are loaded
-  // before the split count is known (it needs the sequence length), so that
-  // the common case costs one memory round trip; slots past the count are
-  // never used.
+  // The first 64 part LSEs and the first C partial outputs are loaded
+  // before the part count is known, so that the common case costs one
+  // memory round trip; slots past the count are never used.
   const float lse_first = (lane < a.max_splits) ? lse_p[lane] : -INFINITY;
   float2 ov[C];
 #pragma unroll
   for (int i = 0; i < C; ++i)
     ov[i] = (i < a.max_splits) ? *(const float2*)(o_p + (int64_t)i * D) : float2{0.f, 0.f};
-  const int np = (seq_len_of(a, b) + kPage - 1) / kPage;
-  const int ns = (np + a.pps - 1) / a.pps;
+  const int hq = wid - b * a.Hq;
+  const int G = a.G;
+  const int x = ((hq / G) * a.n_hb + (hq % G) / 16) / kDecodeWaves;
+  const int cnt = a.ws_cnt[(int64_t)b * a.X + x];
+  // a sequence without pages has no parts (and no count written)
+  const int ns = seq_pages(a, b) == 0 ? 0 : min(max(cnt, 1), a.max_splits);
 
   auto lse_at = [&](int s0) {   // this lane's split of the batch s0 .. s0+63
     return (s0 + lane < ns) ? (s0 == 0 ? lse_first : lse_p[s0 + lane]) : -INFINITY;
@@ -426,34 +542,35 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[wid] = (L > 0.f) ? M + __logf(L) : -INFINITY;
 }
 
+
 }  // namespace
 
 int decode_max_splits(int max_blocks) {
-  return (max_blocks + kDecodeMinPagesPerSplit - 1) / kDecodeMinPagesPerSplit;
+  return (max_blocks + kDecodeMinChunkPages - 1) / kDecodeMinChunkPages + 1;
 }
 
-// Pages per split: a power of two >= kDecodeMinPagesPerSplit chosen so that,
-// with sequences about half full on average, the grid holds about
-// kDecodeWavesPerCu busy waves per CU (each wave walks one split of one head).
-int decode_pages_per_split(int B, int Hkv, int n_hb, int max_blocks, int num_cus) {
-  const double est_page_heads = (double)B * Hkv * n_hb * max_blocks * 0.5;
-  const double target_waves = (double)kDecodeWavesPerCu * (num_cus > 0 ? num_cus : 256);
-  int pps = kDecodeMinPagesPerSplit;
-  while (pps < max_blocks && pps < kDecodeMaxPagesPerSplit && est_page_heads / pps > target_waves)
-    pps *= 2;
-  return pps;
+namespace {
+constexpr int kMaxDevices = 64;
+int g_wgs_per_cu[kMaxDevices];   // 0 = not yet queried
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const int splits = (a.max_blocks + a.pps - 1) / a.pps;
-  if (splits > a.max_splits || splits > 65535 || a.B > 65535 || a.pps > kDecodeMaxPagesPerSplit)
-    return hipErrorInvalidValue;
-  // splits outermost: every sequence's first splits (full ones) start
-  // first, the short last splits and the empty ones (past a sequence's end)
-  // come last
-  dim3 grid1((a.Hkv * a.n_hb + kDecodeWaves - 1) / kDecodeWaves, a.B, splits);
-  hipLaunchKernelGGL(decode_split_kernel, grid1, dim3(NT), 0, stream, a);
-  hipError_t e = hipGetLastError();
+hipError_t launch_decode(DecodeArgs a, int num_cus, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int per_cu = __atomic_load_n(&g_wgs_per_cu[dev], __ATOMIC_ACQUIRE);
+  if (per_cu == 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_kernel, NT, 0);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    __atomic_store_n(&g_wgs_per_cu[dev], per_cu, __ATOMIC_RELEASE);
+  }
+  if (a.B > 64 * kMaxSeqChunks) return hipErrorInvalidValue;
+  // exactly one resident workgroup per slot: every CU gets the same share
+  a.nwg = per_cu * (num_cus > 0 ? num_cus : 256);
+  hipLaunchKernelGGL(decode_partial_kernel, dim3(a.nwg), dim3(NT), 0, stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int waves = a.B * a.Hq;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream, a);

@@ -30,11 +30,10 @@ hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream)
 
 // ---- paged decode ----------------------------------------------------------
 constexpr int kPage = 16;
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeMinPagesPerSplit = 4;   // bounds the workspace
-constexpr int kDecodeMaxPagesPerSplit = 64;  // one block-table entry per lane
-constexpr int kDecodeWavesPerCu = 8;         // split-size target
-constexpr int kDecodeHeadsPerBlock = 16;     // query heads per MFMA column block
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeMaxChunkPages = 64;   // one block-table entry per lane
+constexpr int kDecodeMinChunkPages = 4;    // bounds the partial results per sequence
+constexpr int kDecodeHeadsPerBlock = 16;   // query heads per MFMA column block
 
 struct DecodeArgs {
   const __bf16* q;
@@ -44,18 +43,21 @@ struct DecodeArgs {
   const int32_t* lens;
   float* ws_o;     // [B, Hq, max_splits, 128] fp32 normalised partial outputs
   float* ws_lse;   // [B, Hq, max_splits]      fp32 partial LSE (natural log)
+  int* ws_cnt;     // [B, X] number of partial results of (sequence, unit group)
   __bf16* o;
   float* lse;
   int B, Hq, Hkv, G, n_hb;   // G = Hq / Hkv, n_hb = ceil(G / 16)
-  int max_blocks, max_splits, pps;
+  int X;                     // unit groups: ceil(Hkv * n_hb / 4)
+  int max_blocks, max_splits;
   int num_pages;
+  int nwg;                   // workgroups of the partial kernel (set at launch)
   int64_t page_stride;       // elements per page: 16 * Hkv * 128
   int64_t token_stride;      // elements per token slot: Hkv * 128
   float c;                   // scale * log2(e)
 };
 
+// partial results a (sequence, unit group) can need: ceil(max_blocks / 4) + 1
 int decode_max_splits(int max_blocks);
-int decode_pages_per_split(int B, int Hkv, int n_hb, int max_blocks, int num_cus);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(DecodeArgs a, int num_cus, hipStream_t stream);
 
 }  // namespace attn

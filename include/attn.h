@@ -98,8 +98,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * attn_decode_workspace_bytes - device workspace that attn_decode_paged needs
  * for its split partials (fp32 partial outputs and their LSEs), for a batch of
  * B sequences, Hq query heads and block tables of max_blocks_per_seq entries:
- * B * Hq * ceil(max_blocks_per_seq / 4) * 129 * 4 bytes.  Returns 0 for
- * invalid sizes.
+ * B * Hq * (S * 129 + 1) * 4 bytes with S = ceil(max_blocks_per_seq / 4) + 1
+ * partial results per (sequence, head).  Returns 0 for invalid sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq);
 

@@ -37,10 +37,11 @@ def test_version_and_status_strings():
 
 
 def test_workspace_bytes():
-    # partials: B * Hq * ceil(max_blocks / 4) splits of (128 + 1) floats
-    assert ea.attn_decode_workspace_bytes(32, 32, 256) == 32 * 32 * 64 * 129 * 4
-    assert ea.attn_decode_workspace_bytes(2, 3, 9) == 2 * 3 * 3 * 129 * 4
-    assert ea.attn_decode_workspace_bytes(1, 1, 1) == 129 * 4
+    # B * Hq * (S * (128 + 1) + 1) floats with S = ceil(max_blocks / 4) + 1
+    # partial results per (sequence, head), plus one count per (sequence, head)
+    assert ea.attn_decode_workspace_bytes(32, 32, 256) == 32 * 32 * (65 * 129 + 1) * 4
+    assert ea.attn_decode_workspace_bytes(2, 3, 9) == 2 * 3 * (4 * 129 + 1) * 4
+    assert ea.attn_decode_workspace_bytes(1, 1, 1) == (2 * 129 + 1) * 4
     assert ea.attn_decode_workspace_bytes(0, 1, 1) == 0
     assert ea.attn_decode_workspace_bytes(1, 1, 0) == 0
 

@@ -41,6 +41,8 @@ CASES = [
     (2, 32, 1, 700, [700, 513]),          # MQA: 32 query heads on one K/V head
     (6, 24, 2, 2000, None),               # group of 12 heads
     (2, 40, 2, 500, [499, 100]),          # group of 20 heads: two head blocks
+    (130, 4, 1, 100, None),               # sequences in three chunks of 64
+    (700, 8, 2, 48, None),                # many short sequences
 ]
 
 
