@@ -9,7 +9,10 @@ are already resident in HBM:
 * decode: attn_decode_paged on B=32, Hq=32, Hkv=8, 16-token pages, context
   lengths U{1..4096}, reported as algorithmic HBM GB/s; four independent
   copies of the KV pool (more than 1 GB in all) are rotated so that the
-  256 MB last-level cache cannot serve a call from the previous one.
+  256 MB last-level cache cannot serve a call from the previous one;
+* the other prefill workloads (causal GQA B=8 S=8192, diffusion-style self
+  attention S=32760 and its cross attention against 512 keys), timed the
+  same way and reported beside the headline (skip with --no-extra).
 
 Times come from HIP events on the stream the kernels are launched on.  The
 fp64 CPU oracle is timed on the host cores on a bounded sample of the same
@@ -47,7 +50,7 @@ def traffic_from_profiles(kernel_key, source, launches_per_call=1):
     """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
     scaled by a copy kernel of known size), or None if absent or taken on a
     different version of the kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
     try:
@@ -102,25 +105,38 @@ def cpu_baseline(p, budget_s, torch):
             "seconds": dt}
 
 
+TRAFFIC_FILE = "hbm_traffic__prefill_mha_b4_h32_s4096__decode_b32_hq32_hkv8.json"
+
+
 def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
-    """Turn rocprofv3 output (a --kernel-trace --stats run and two --pmc runs
-    of `bench.py --counters`, FETCH_SIZE then WRITE_SIZE) into the summaries
-    kept under profiles/: kernel_stats.md and traffic.json."""
+    """Turn rocprofv3 output (a --kernel-trace --stats run of bench.py and two
+    --pmc runs of `bench.py --counters`, FETCH_SIZE then WRITE_SIZE) into the
+    short summaries kept under profiles/, one per kernel and workload, and the
+    per-launch HBM traffic that bench.py reports."""
     import csv
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    stats = list(csv.DictReader(open(os.path.join(ktrace_dir, "run_kernel_stats.csv"))))
-    lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-             "Command (from the repository root on the GPU box):", "", "```", command["ktrace"],
-             "```", "", "| kernel | calls | average us | min us | max us | share % |",
-             "|---|---|---|---|---|---|"]
-    for r in stats:
-        name = r["Name"]
-        if "attn::" not in name and "copyBuffer" not in name:
-            continue
-        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                     f"{float(r['Percentage']):.1f} |")
+    stats = {r["Name"]: r for r in csv.DictReader(open(os.path.join(ktrace_dir,
+                                                                    "run_kernel_stats.csv")))}
+    # the bench launches each workload's calls back to back in a fixed order,
+    # so the n-th dispatch of a kernel belongs to a known workload
+    trace = list(csv.DictReader(open(os.path.join(ktrace_dir, "run_kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by_kernel = {}
+    for r in trace:
+        by_kernel.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    per_wl = {}   # (workload, kernel part) -> durations
+    for kpart, plan in command["plan"].items():
+        names = [n for n in by_kernel if kpart in n]
+        if len(names) != 1 or len(by_kernel[names[0]]) != sum(c for _, c in plan):
+            raise SystemExit(f"summarize: dispatches of {kpart} do not match the bench's plan")
+        durs, i = by_kernel[names[0]], 0
+        for wl, cnt in plan:
+            per_wl[(wl, kpart)] = durs[i:i + cnt]
+            i += cnt
+
+    # ---- HBM traffic per launch
     fetch = list(csv.DictReader(open(os.path.join(fetch_dir, "run_counter_collection.csv"))))
     write = list(csv.DictReader(open(os.path.join(write_dir, "run_counter_collection.csv"))))
     wmap = {r["Dispatch_Id"]: r for r in write}
@@ -133,24 +149,22 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
     per = {}
     for r in fetch:
         key = ("prefill_kernel" if "prefill_kernel" in r["Kernel_Name"] else
-               "decode_split_kernel" if "decode_split" in r["Kernel_Name"] else
+               "decode_partial_kernel" if "decode_partial" in r["Kernel_Name"] else
                "decode_merge_kernel" if "decode_merge" in r["Kernel_Name"] else None)
         if key is None:
             continue
         fb = float(r["Counter_Value"]) * 1024 * f_fetch
         wb = float(wmap[r["Dispatch_Id"]]["Counter_Value"]) * 1024 * f_write
         per.setdefault(key, []).append((fb, wb))
-    srcs = {"prefill_kernel": "prefill.hip", "decode_split_kernel": "decode.hip",
+    srcs = {"prefill_kernel": "prefill.hip", "decode_partial_kernel": "decode.hip",
             "decode_merge_kernel": "decode.hip"}
     traffic = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
-                        "dispatch), each scaled by the reading of a 1 GiB device copy",
+                        "dispatch), each scaled by the reading of a 1 GiB device copy; prefill "
+                        "on mha_prefill_b4_h32_s4096_bhsd, decode on "
+                        "paged_decode_b32_hq32_hkv8_len4096_page16",
                "fetch_scale": f_fetch, "write_scale": f_write,
                "commands": [command["fetch"], command["write"]]}
-    lines += ["", "# HBM traffic per launch (rocprofv3 --pmc)", "",
-              "Commands:", "", "```", command["fetch"], command["write"], "```", "",
-              f"Scale factors from a 1 GiB copy: FETCH_SIZE x {f_fetch:.4f}, "
-              f"WRITE_SIZE x {f_write:.4f}.", "",
-              "| kernel | launches | read MB | written MB | total MB |", "|---|---|---|---|---|"]
+    trows = {}
     for key, vals in per.items():
         fb = sum(v[0] for v in vals) / len(vals)
         wb = sum(v[1] for v in vals) / len(vals)
@@ -158,12 +172,85 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
                                                                  "csrc", srcs[key])),
                         "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                         "hbm_bytes_per_launch": fb + wb, "launches": len(vals)}
-        lines.append(f"| {key} | {len(vals)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
-                     f"{(fb + wb) / 1e6:.1f} |")
-    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        trows[key] = (f"| {key} | {len(vals)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                      f"{(fb + wb) / 1e6:.1f} |")
+    with open(os.path.join(out_dir, TRAFFIC_FILE), "w") as f:
         json.dump(traffic, f, indent=1)
-    with open(os.path.join(out_dir, "kernel_stats.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
+
+    def kstats_row(kpart):
+        for name, r in stats.items():
+            if kpart in name:
+                return (f"| `{kpart}` (all workloads of the run) | {r['Calls']} | "
+                        f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                        f"{float(r['MaxNs']) / 1e3:.1f} |")
+        return f"| `{kpart}` | - | - | - | - |"
+
+    def wl_row(wl, kpart):
+        d = per_wl[(wl, kpart)]
+        return (f"| `{kpart}` on {wl} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | "
+                f"{max(d):.1f} |")
+
+    head = ["Command (from the repository root on the GPU box):", "", "```", command["ktrace"],
+            "```", "", "| kernel / workload | dispatches | average us | min us | max us |",
+            "|---|---|---|---|---|"]
+    thead = ["", "HBM traffic per launch (rocprofv3 --pmc), commands:", "", "```",
+             command["fetch"], command["write"], "```", "",
+             f"Scale factors from a 1 GiB device copy: FETCH_SIZE x {f_fetch:.4f}, "
+             f"WRITE_SIZE x {f_write:.4f}.", "",
+             "| kernel | launches | read MB | written MB | total MB |", "|---|---|---|---|---|"]
+    files = {
+        "prefill_kernel__mha_prefill_b4_h32_s4096_bhsd.md": (
+            "# prefill_kernel on mha_prefill_b4_h32_s4096_bhsd (B=4, H=32, S=4096, BHSD)",
+            [wl_row("mha_prefill_b4_h32_s4096_bhsd", "prefill_kernel<false>"),
+             kstats_row("prefill_kernel<false>")], ["prefill_kernel"]),
+        "decode_partial_and_merge_kernels__paged_decode_b32_hq32_hkv8_len4096.md": (
+            "# decode_partial_kernel + decode_merge_kernel on paged_decode_b32_hq32_hkv8_"
+            "len4096_page16",
+            [wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_partial_kernel"),
+             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_merge_kernel")],
+            ["decode_partial_kernel", "decode_merge_kernel"]),
+        "prefill_kernel__causal_gqa_s8192_and_diffusion_s32760.md": (
+            "# prefill_kernel on the causal GQA and diffusion-style workloads",
+            [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true>"),
+             wl_row("diffusion_self_b2_h12_s32760_bshd", "prefill_kernel<false>"),
+             wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false>")], []),
+    }
+    for fname, (title, rows, tkeys) in files.items():
+        body = [title, ""] + head + rows
+        if tkeys:
+            body += thead + [trows[k] for k in tkeys if k in trows]
+        with open(os.path.join(out_dir, fname), "w") as f:
+            f.write("\n".join(body) + "\n")
+
+
+def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
+    """Time attn_fwd on the other prefill workloads (same method as the
+    headline: inputs resident, HIP events on the launch stream)."""
+    res = []
+    steps = max(3, min(args.steps, 10))
+    p4 = None
+    for make in (gen.config3, gen.config4_self, lambda: gen.config4_cross(self_problem=p4)):
+        p = make()
+        if p.Sk == p.Sq == 32760:
+            p4 = p
+        log(f"timing {p.name}")
+        q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+        lay = "bshd" if p.layout == gen.BSHD else "bhsd"
+        o = torch.empty_like(q)
+        lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+        def run(_i):
+            ea.attn_fwd(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
+
+        ms = time_calls(run, steps, 2, torch)
+        tf = p.flops / (ms * 1e-3) / 1e12
+        res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq,
+                    "Sk": p.Sk, "causal": p.causal, "layout": lay, "ms_per_call": round(ms, 4),
+                    "flop": p.flops, "TFLOP/s": round(tf, 2),
+                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -174,6 +261,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="host seconds spent timing the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other prefill workloads (causal GQA, diffusion self/cross)")
     ap.add_argument("--counters", action="store_true",
                     help="no timing: one device copy of 1 GiB, then 3 prefill and 3 decode "
                          "calls, for rocprofv3 counter passes")
@@ -182,12 +271,21 @@ def main():
                          "output directories (no GPU needed)")
     args = ap.parse_args()
     if args.summarize:
-        cmd = {"ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d <out>/ktrace "
-                         "-o run -- python3 bench.py --steps 30 --warmup 5 --no-cpu-baseline",
-               "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o run "
-                        "-- python3 bench.py --counters",
-               "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write -o run "
-                        "-- python3 bench.py --counters"}
+        st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
+        cmd = {"plan": {"prefill_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu),
+                                                  ("diffusion_self_b2_h12_s32760_bshd", xs),
+                                                  ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs)],
+                        "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs)],
+                        "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
+                                                   st + wu)],
+                        "decode_merge_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
+                                                 st + wu)]},
+               "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace "
+                         "-o run -- python3 -u bench.py --no-cpu-baseline",
+               "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
+                        "-o run -- python3 -u bench.py --counters",
+               "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
+                        "-o run -- python3 -u bench.py --counters"}
         summarize_profiles(*args.summarize, cmd)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -305,11 +403,13 @@ def main():
                    "algorithmic_bytes": d.bytes,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": traffic_from_profiles("decode_split_kernel", src_d),
-                                "kernel": "decode_split_kernel + decode_merge_kernel"}},
+                                "traffic": traffic_from_profiles("decode_partial_kernel", src_d),
+                                "kernel": "decode_partial_kernel + decode_merge_kernel"}},
         "parity": {"prefill_sampled_rows": len(rows), "prefill_max_err_over_tol": round(par_p, 4),
                    "prefill_max_lse_err": par_pl, "decode_max_err_over_tol": round(par_d, 4)},
     }
+    if not args.no_extra:
+        out["other_workloads"] = extra_workloads(args, gen, ea, torch, dev, to_dev, log)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         cb = cpu_baseline(p, args.cpu_seconds, torch)
