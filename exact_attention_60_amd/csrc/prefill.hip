@@ -258,6 +258,10 @@ template <bool F16>
 __device__ __forceinline__ void mfma_phase(Wave& w, Prefetch& pf, const char* kt,
                                            const char* vt_prev, bool do_qk, bool do_pv,
                                            bool prefetched) {
+  // The other wave on this SIMD runs its softmax meanwhile; raised priority
+  // keeps its VALU stream from delaying this wave's operand reads and MFMA
+  // issue (the arbiter otherwise favours the older wave).
+  __builtin_amdgcn_s_setprio(3);
   if (do_qk && do_pv) {
     if (prefetched)
       mfma_seq<F16, true, true, true>(w, pf, kt, vt_prev);
@@ -271,6 +275,7 @@ __device__ __forceinline__ void mfma_phase(Wave& w, Prefetch& pf, const char* kt
   } else if (do_pv) {
     mfma_seq<F16, false, true, false>(w, pf, kt, vt_prev);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Softmax phase of a wave for the tile whose scores are in w.s.  Fast path:
