@@ -61,7 +61,7 @@ constexpr int BM = kPrefillBM;
 constexpr int NW = kPrefillWaves;           // 8
 constexpr int NT = NW * 64;                 // 512 threads
 constexpr int TILE_BYTES = BN * D * 2;      // 16 KB for one K or V tile
-constexpr int ROWS_PER_WAVE_DMA = BN / 4;   // 16 rows of each tile copied per group-0 wave
+constexpr int ROWS_PER_WAVE_DMA = BN / 4;   // 16 rows of each tile copied per group-1 wave
 constexpr float TAU = 8.0f;                 // log2 headroom before a rescale
 
 static_assert(kPrefillRowsPerWave == 32 && NW == 8 && BM == 256, "layout assumed below");
