@@ -167,3 +167,23 @@ def test_decode_equals_prefill_single_row():
         check_o(host_f64(o2[0, 0]), o_ref[b], "fwd row")
         check_lse(host_f64(l2[0, :, 0]), l_ref[b], "fwd row lse")
         check_o(host_f64(o[b]), o_ref[b], "decode row")
+
+
+def _random_decode_cases(n, seed):
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(r.choice([1, 2, 4, 8]))
+        G = int(r.choice([1, 2, 4, 7, 16, 24]))
+        B = int(r.integers(1, 40))
+        out.append((B, Hkv * G, Hkv, int(r.integers(1, 2500))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_decode_cases(16, 77),
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_L%d" % c)
+def test_decode_random_shapes(case):
+    B, Hq, Hkv, L = case
+    d = gen.decode_inputs(B, Hq, Hkv, max_len=L, seed=B * 31 + L)
+    o, lse = run_decode(d)
+    check_decode(d, o, lse, str(case))

@@ -181,3 +181,27 @@ def test_config4_self_and_cross_sampled():
     pc = gen.config4_cross(self_problem=ps)
     del ps
     _full_size(pc, 5)
+
+
+def _random_shapes(n, seed):
+    """Seeded random small shapes: any group size, both layouts, causal or
+    not, lengths not multiples of the 256-row / 64-key tiles."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(r.choice([1, 2, 3, 4]))
+        G = int(r.choice([1, 2, 3, 5, 8]))
+        out.append((int(r.integers(1, 3)), Hkv * G, Hkv, int(r.integers(1, 600)),
+                    int(r.integers(1, 700)), int(r.integers(0, 2)), bool(r.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(24, 2024),
+                         ids=lambda s: "B%d_Hq%d_Hkv%d_Sq%d_Sk%d_L%d_C%d" % (
+                             s[0], s[1], s[2], s[3], s[4], s[5], int(s[6])))
+def test_random_shapes_all_elements(shape):
+    B, Hq, Hkv, Sq, Sk, lay, causal = shape
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=lay, causal=causal,
+                           seed=7 * Sq + 13 * Sk + Hq, n_hot=min(3, Sq * Hq))
+    o, lse = run_fwd(p)
+    check_full(p, o, lse, str(shape))
