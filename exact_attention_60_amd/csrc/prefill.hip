@@ -17,10 +17,12 @@
 //    per-tile sequence half a tile apart, in phases separated by workgroup
 //    barriers: while one group issues MFMAs (P.V of the previous tile, then
 //    Q.K of this tile) the other runs the softmax of its current tile on the
-//    VALU.  On gfx950 a wave's VALU work does not overlap its own MFMAs, so
-//    this pairing is what keeps the matrix cores fed (the MoonMath page's
-//    two-group, phase-shifted eight-wave design, re-derived here with both K
-//    and V in LDS).
+//    VALU (the MoonMath page's two-group, phase-shifted eight-wave design,
+//    re-derived here with both K and V in LDS).  A wave's own independent
+//    VALU instructions also issue while its MFMAs execute, which the MFMA
+//    phase uses for the V transpose; giving every wave both jobs instead
+//    (softmax of tile t between its own Q.K MFMAs of tile t+1) measured
+//    slower on this chip, its MFMAs then waiting on their LDS operand reads.
 //  * K and V tiles of 64 keys are copied HBM -> LDS by the buffer unit
 //    (buffer_load ... lds, 16 B per lane, 256 B per row), double buffered, one
 //    tile ahead; keys past Sk fall outside the buffer range and read as zero.
@@ -168,28 +170,52 @@ struct Wave {
   int l32, hi;
 };
 
-template <bool F16>
-__device__ __forceinline__ void v_transpose_share(const Wave& w, const char* vb, char* vtb, int wave) {
-  const int kk = wave & 3;                          // not a compile-time index:
-  const int woff = vt_off(w.l32, 2 * kk + w.hi);    // no indexing of w.vtoff
-  const char* base = vb + 16 * kk * 256;
-  bf16x8 x[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const bf16x4 lo = lds_read_tr(base + w.cvoff[0][db]);
-    const bf16x4 up = lds_read_tr(base + w.cvoff[1][db]);
-    x[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+// In two halves (d blocks 2h, 2h+1), each a read step and a write step, so
+// that the MFMA wave can spread them between its MFMAs.
+struct VTranspose {
+  const char* base;    // this wave's 16 rows of the bf16 V tile
+  char* vtb;           // the V^T tile
+  int woff;
+  bf16x8 x[2];
+  __device__ __forceinline__ VTranspose(const Wave& w, const char* vb, char* vt, int wave) {
+    const int kk = wave & 3;                        // not a compile-time index:
+    woff = vt_off(w.l32, 2 * kk + w.hi);            // no indexing of w.vtoff
+    base = vb + 16 * kk * 256;
+    vtb = vt;
   }
+  __device__ __forceinline__ void read(const Wave& w, int h) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    u32x4 y = __builtin_bit_cast(u32x4, x[db]);
-    if (F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = bf16x2_to_f16x2(y[i]);
+    for (int j = 0; j < 2; ++j) {
+      const bf16x4 lo = lds_read_tr(base + w.cvoff[0][2 * h + j]);
+      const bf16x4 up = lds_read_tr(base + w.cvoff[1][2 * h + j]);
+      x[j] = bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
     }
-    *(u32x4*)(vtb + db * 32 * 128 + woff) = y;
   }
-}
+  template <bool F16>
+  __device__ __forceinline__ void write(int h) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 y = __builtin_bit_cast(u32x4, x[j]);
+      if (F16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = bf16x2_to_f16x2(y[i]);
+      }
+      *(u32x4*)(vtb + (2 * h + j) * 32 * 128 + woff) = y;
+    }
+  }
+  template <bool F16>
+  __device__ __forceinline__ void all(const Wave& w) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      read(w, h);
+      write<F16>(h);
+    }
+  }
+};
+
+struct NoExtra {
+  __device__ __forceinline__ void operator()(int, int) const {}
+};
 
 // MFMA phase of a wave: S^T = K Q^T for this tile (16 MFMAs), then
 // O^T += V^T P^T for the previous tile (16 MFMAs, k-step major so
@@ -216,9 +242,9 @@ __device__ __forceinline__ void prefetch_k(Prefetch& pf, const Wave& w, const ch
   for (int i = 0; i < DEPTH; ++i) pf.fr[i] = k_operand(w, kt, i);
 }
 
-template <bool F16, bool QK, bool PV, bool PREFETCHED>
+template <bool F16, bool QK, bool PV, bool PREFETCHED, class Extra>
 __device__ __forceinline__ void mfma_seq(Wave& w, Prefetch& pf, const char* kt,
-                                         const char* vt_prev) {
+                                         const char* vt_prev, Extra&& extra) {
   constexpr int NQK = QK ? 16 : 0;
   constexpr int N = NQK + (PV ? 16 : 0);
   auto load = [&](int i) -> bf16x8 {
@@ -250,30 +276,36 @@ __device__ __forceinline__ void mfma_seq(Wave& w, Prefetch& pf, const char* kt,
     __builtin_amdgcn_sched_barrier(0);
     mma(i, pf.fr[i % DEPTH]);
     if (i + DEPTH < N) pf.fr[i % DEPTH] = load(i + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+    extra(i, N);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool F16>
+// `extra(i, n)` runs after MFMA i of the n; if the wave has no MFMAs in the
+// phase, `alone()` runs instead.
+template <bool F16, class Extra, class Alone>
 __device__ __forceinline__ void mfma_phase(Wave& w, Prefetch& pf, const char* kt,
                                            const char* vt_prev, bool do_qk, bool do_pv,
-                                           bool prefetched) {
+                                           bool prefetched, Extra&& extra, Alone&& alone) {
   // The other wave on this SIMD runs its softmax meanwhile; raised priority
   // keeps its VALU stream from delaying this wave's operand reads and MFMA
   // issue (the arbiter otherwise favours the older wave).
   __builtin_amdgcn_s_setprio(3);
   if (do_qk && do_pv) {
     if (prefetched)
-      mfma_seq<F16, true, true, true>(w, pf, kt, vt_prev);
+      mfma_seq<F16, true, true, true>(w, pf, kt, vt_prev, extra);
     else
-      mfma_seq<F16, true, true, false>(w, pf, kt, vt_prev);
+      mfma_seq<F16, true, true, false>(w, pf, kt, vt_prev, extra);
   } else if (do_qk) {
     if (prefetched)
-      mfma_seq<F16, true, false, true>(w, pf, kt, vt_prev);
+      mfma_seq<F16, true, false, true>(w, pf, kt, vt_prev, extra);
     else
-      mfma_seq<F16, true, false, false>(w, pf, kt, vt_prev);
+      mfma_seq<F16, true, false, false>(w, pf, kt, vt_prev, extra);
   } else if (do_pv) {
-    mfma_seq<F16, false, true, false>(w, pf, kt, vt_prev);
+    mfma_seq<F16, false, true, false>(w, pf, kt, vt_prev, extra);
+  } else {
+    alone();
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -364,9 +396,12 @@ struct Ctx {
 //    so from phase 2t+1 on they are visible to every wave.  K(t+1) goes to
 //    the K buffer last read in phase 2t-1; the single V staging buffer was
 //    last read in phase 2t-1.
-//  * At the end of phase 2t each group-1 wave transposes the 16 rows of V(t)
-//    it copied into the V^T buffer last read in phase 2t-1 (V^T(t-2)'s),
-//    converting to fp16; V^T(t) is first read in phase 2t+2.
+//  * In phase 2t+1 each group-1 wave transposes the 16 rows of V(t) it
+//    copied into the V^T buffer last read in phase 2t-1 (V^T(t-2)'s),
+//    converting to fp16, with the instructions spread between the MFMAs of
+//    its MFMA phase (a wave's independent VALU instructions issue while its
+//    own MFMAs execute, so this takes them off the softmax side of phase 2t);
+//    V^T(t) is first read in phase 2t+2.
 //  * Each group issues the first K-operand reads of its next MFMA phase at
 //    the end of its softmax phase, when that K tile is already visible.
 template <bool CAUSAL, bool F16>
@@ -393,14 +428,13 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
     char* vtcur = vtbuf + (t & 1) * TILE_BYTES;         // V^T(t), written in phase 2t+1
     // ---- phase 2t
     if (g0) {
-      mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre);
+      mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre, NoExtra{}, [] {});
       pre = false;
     } else {
       if (t + 1 < T) x.ld.issue_k(t + 1, knext);
       if (t < T) x.ld.issue_v(t, vbuf);
       if (visible(t - 1)) softmax_phase<CAUSAL, F16>(w, (t - 1) * BN, x.Sk, x.off, x.c);
       wait_copies();
-      if (t < T) v_transpose_share<F16>(w, vbuf, vtcur, x.wave);
       pre = visible(t);
       if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
     }
@@ -411,9 +445,23 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
       pre = visible(t + 1);
       if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
     } else {
-      mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre);
+      // V(t) -> V^T(t) between the MFMAs (V(t) landed before the mid barrier)
+      VTranspose tr(w, vbuf, vtcur, x.wave);
+      const bool tr_now = t < T;
+      mfma_phase<F16>(
+          w, pf, kt, vtprev, visible(t), visible(t - 1), pre,
+          [&](int i, int n) {
+            if (!tr_now) return;
+            if (i == 1) tr.read(w, 0);
+            if (i == n / 4 + 1) tr.write<F16>(0);
+            if (i == n / 2) tr.read(w, 1);
+            if (i == (3 * n) / 4) tr.write<F16>(1);
+          },
+          [&] {
+            if (tr_now) tr.all<F16>(w);
+          });
       pre = false;
-      wait_lds();  // the V^T(t) writes of phase 2t are done before they are published
+      wait_lds();  // the V^T(t) writes are done before they are published
     }
     barrier();
   }
