@@ -88,6 +88,11 @@ enum { ATTN_BSHD = 0, ATTN_BHSD = 1 };
  *   scale  finite float32 (1/sqrt(d) is the usual value)
  *   causal 0 or 1
  *
+ * Size limits (ATTN_ERR_SHAPE): the K/V rows of one (batch, kv head) are
+ * addressed with 32-bit byte offsets, so (Sk - 1) * row stride * 2 + 256 must
+ * stay below 2^31 (row stride = Hkv * 128 elements in BSHD, 128 in BHSD), and
+ * B * Hq * ceil(Sq / 256) must stay below 2^31.
+ *
  * Returns ATTN_OK or an attn_status error.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
