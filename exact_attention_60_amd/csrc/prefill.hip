@@ -574,22 +574,34 @@ void prefill_kernel(PrefillArgs a) {
   // ---- epilogue: O = acc / l (bf16, RTNE) in q's layout; LSE = ln(sum exp)
   const float l = sum_halves(w.lsum);
   const int row = w.first + w.l32;
-  if (row < a.Sq) {
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    __bf16* op = a.o + b * a.q_sb + hq * a.q_sh + (int64_t)row * a.q_ss;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  // O goes through LDS (the tile buffers are free: every wave is past the
+  // last barrier of the tile loop) so that the global stores write whole
+  // 256-byte rows, 16 bytes per lane.  Lane (row l32, half hi) holds
+  // d = 32 db + 8 j + 4 hi + e, i.e. 8 bytes of 16-byte chunk 4 db + j of its
+  // row; each wave stages its 32 rows (8 KB) with the tile swizzle and reads
+  // back only its own rows.
+  char* st = (x.wave < 4 ? kbuf : vtbuf) + (x.wave & 3) * 8192;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 u;
-        u[0] = pack_bf16(w.oacc[db][4 * j + 0] * inv, w.oacc[db][4 * j + 1] * inv);
-        u[1] = pack_bf16(w.oacc[db][4 * j + 2] * inv, w.oacc[db][4 * j + 3] * inv);
-        *(u32x2*)(op + db * 32 + 8 * j + 4 * w.hi) = u;
-      }
-    if (w.hi == 0) {
-      const float lse = (l > 0.f) ? (w.m_use + __log2f(l)) * kLn2 : -INFINITY;
-      a.lse[((int64_t)(b * a.Hq + hq)) * a.Sq + row] = lse;
+    for (int j = 0; j < 4; ++j) {
+      u32x2 u;
+      u[0] = pack_bf16(w.oacc[db][4 * j + 0] * inv, w.oacc[db][4 * j + 1] * inv);
+      u[1] = pack_bf16(w.oacc[db][4 * j + 2] * inv, w.oacc[db][4 * j + 3] * inv);
+      *(u32x2*)(st + tile_off(w.l32, 4 * db + j) + 8 * w.hi) = u;
     }
+  wait_lds();
+  __bf16* ob = a.o + b * a.q_sb + hq * a.q_sh;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int rr = 4 * k + (lane >> 4), cc = lane & 15;
+    const u32x4 v = *(const u32x4*)(st + tile_off(rr, cc));
+    if (w.first + rr < a.Sq) *(u32x4*)(ob + (int64_t)(w.first + rr) * a.q_ss + 8 * cc) = v;
+  }
+  if (row < a.Sq && w.hi == 0) {
+    const float lse = (l > 0.f) ? (w.m_use + __log2f(l)) * kLn2 : -INFINITY;
+    a.lse[((int64_t)(b * a.Hq + hq)) * a.Sq + row] = lse;
   }
 }
 
