@@ -41,9 +41,12 @@
 //    value outside the fp16 range (or a non-finite input) leaves a non-finite
 //    accumulator; the workgroup then redoes its tiles with bf16 P and V,
 //    which covers the whole bf16 range.
-//  * The rescale of the output accumulator is skipped while no row max in the
-//    wave has grown by more than 2^8 (probabilities stay <= 256, far from
-//    fp16 or fp32 limits); the quotient is the same, so the result stays exact.
+//  * The rescale of the output accumulator is skipped while the probabilities
+//    of a tile, taken against the running max as it stands, sum to at most
+//    2^12 per lane: each is then <= 4096, far from the fp16 and fp32 limits,
+//    and the quotient O = sum p v / sum p is the same, so the result stays
+//    exact.  A row's first tile, or a larger sum, takes the row max and
+//    rescales.
 //  * Causal: tiles above the diagonal are never loaded, waves whose rows see
 //    none of a tile skip its arithmetic, only boundary tiles are masked, the
 //    two groups hold interleaved 32-row blocks so they stay balanced on the
@@ -64,7 +67,6 @@ constexpr int NW = kPrefillWaves;           // 8
 constexpr int NT = NW * 64;                 // 512 threads
 constexpr int TILE_BYTES = BN * D * 2;      // 16 KB for one K or V tile
 constexpr int ROWS_PER_WAVE_DMA = BN / 4;   // 16 rows of each tile copied per group-1 wave
-constexpr float TAU = 8.0f;                 // log2 headroom before a rescale
 
 static_assert(kPrefillRowsPerWave == 32 && NW == 8 && BM == 256, "layout assumed below");
 
