@@ -30,7 +30,7 @@ PAGE = 16
 BF16_QNAN = np.uint16(0x7FC0)
 
 # stream ids for default_rng([seed, stream])
-_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX = range(8)
+_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX, _S_EQK, _S_EQV = range(10)
 
 BSHD = 0
 BHSD = 1
@@ -192,6 +192,58 @@ def decode_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, scale=None, lens=None,
                 vp[last, t:] = BF16_QNAN
     q = f32_to_bf16_bits(_normal(seed, _S_Q, (B, Hq, D)))
     return Decode(q, kp, vp, table, lens, B, Hq, Hkv, float(scale), name=name)
+
+
+# --------------------------------------------------------------------------
+# Structured inputs for exactness checks: every key of a (sequence, K/V head)
+# is one random vector, so all visible scores of a query row are equal, and V
+# holds values with few significant bits, so that sums of a few of them are
+# exact in float32.
+
+def short_values(seed, stream, shape, binades=0) -> np.ndarray:
+    """bf16 bits of s * (1 + m/128) * 2^e with a random sign s, m ~ U{0..127}
+    and e ~ U{-binades..binades}: every bf16 significand in 2*binades + 1
+    binades."""
+    r = _rng(seed, stream)
+    m = r.integers(0, 128, size=shape).astype(np.uint32)
+    e = r.integers(-binades, binades + 1, size=shape).astype(np.int64)
+    sign = r.integers(0, 2, size=shape).astype(np.uint32)
+    bits = (sign << 15) | ((127 + e).astype(np.uint32) << 7) | m
+    return bits.astype(np.uint16)
+
+
+def equal_keys_prefill(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0,
+                       binades=0, name="") -> Prefill:
+    """Q ~ N(0, 1); K[b, :, g] is one N(0, 1) vector repeated over the keys;
+    V from short_values."""
+    q = f32_to_bf16_bits(_normal(seed, _S_Q, layout_shape(layout, B, Hq, Sq)))
+    row = f32_to_bf16_bits(_normal(seed, _S_EQK, (B, 1, Hkv, D)))
+    k = np.ascontiguousarray(np.broadcast_to(row, (B, Sk, Hkv, D)))
+    v = short_values(seed, _S_EQV, (B, Sk, Hkv, D), binades)
+    if layout == BHSD:
+        k = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+        v = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    return Prefill(q, k, v, B, Hq, Hkv, Sq, Sk, layout, bool(causal), 1.0 / math.sqrt(D),
+                   name=name)
+
+
+def equal_keys_decode(lens, Hq, Hkv, *, seed=0, binades=0, name="") -> Decode:
+    """A paged problem (decode_inputs, random table) whose K rows are one
+    N(0, 1) vector per (sequence, K/V head) and whose V values come from
+    short_values; slots past each sequence's end keep the NaN poison."""
+    lens = np.asarray(lens, dtype=np.int32)
+    B = lens.shape[0]
+    max_len = int(-(-int(lens.max()) // PAGE) * PAGE)
+    p = decode_inputs(B, Hq, Hkv, max_len=max_len, seed=seed, lens=lens, name=name)
+    rows = f32_to_bf16_bits(_normal(seed, _S_EQK, (B, Hkv, D)))
+    vals = short_values(seed, _S_EQV, p.v_pool.shape, binades)
+    for b in range(B):
+        n = int(lens[b])
+        for t in range(n):
+            pg = p.block_table[b, t // PAGE]
+            p.k_pool[pg, t % PAGE] = rows[b]
+            p.v_pool[pg, t % PAGE] = vals[pg, t % PAGE]
+    return p
 
 
 # --------------------------------------------------------------------------

@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (d=128); paged decode HBM GB/s"
+ROUNDING_MODES = ("rtne", "rtna", "rtz")   # rules of the bf16 output, timed on the headline
 
 
 def sha256_of(path):
@@ -201,8 +202,10 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
     files = {
         "prefill_kernel__mha_prefill_b4_h32_s4096_bhsd.md": (
             "# prefill_kernel on mha_prefill_b4_h32_s4096_bhsd (B=4, H=32, S=4096, BHSD)",
-            [wl_row("mha_prefill_b4_h32_s4096_bhsd", "prefill_kernel<false>"),
-             kstats_row("prefill_kernel<false>")], ["prefill_kernel"]),
+            [wl_row("mha_prefill_b4_h32_s4096_bhsd", "prefill_kernel<false>")] +
+            [wl_row(f"mha_prefill_b4_h32_s4096_bhsd_{m}", "prefill_kernel<false>")
+             for m in ROUNDING_MODES] +
+            [kstats_row("prefill_kernel<false>")], ["prefill_kernel"]),
         "decode_partial_and_merge_kernels__paged_decode_b32_hq32_hkv8_len4096.md": (
             "# decode_partial_kernel + decode_merge_kernel on paged_decode_b32_hq32_hkv8_"
             "len4096_page16",
@@ -253,6 +256,24 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     return res
 
 
+def rounding_modes(args, p, ea, torch, q, k, v, o, lse, log):
+    """The headline prefill under each rounding rule of the bf16 output (every
+    shape is measured under RTNE, RTNA and RTZ on the pages)."""
+    res = {}
+    steps = max(3, min(args.steps, 10))
+    for mode in ROUNDING_MODES:
+        log(f"timing {p.name} with rounding {mode}")
+
+        def run(_i):
+            ea.attn_fwd(q, k, v, causal=False, scale=p.scale, layout="bhsd", rounding=mode,
+                        out=o, lse=lse)
+
+        ms = time_calls(run, steps, 2, torch)
+        res[mode] = {"ms_per_call": round(ms, 4),
+                     "TFLOP/s": round(p.flops / (ms * 1e-3) / 1e12, 2)}
+    return {"workload": p.name, **res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,8 +293,10 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
-        cmd = {"plan": {"prefill_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu),
-                                                  ("diffusion_self_b2_h12_s32760_bshd", xs),
+        cmd = {"plan": {"prefill_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu)] +
+                                                 [(f"mha_prefill_b4_h32_s4096_bhsd_{m}", xs)
+                                                  for m in ROUNDING_MODES] +
+                                                 [("diffusion_self_b2_h12_s32760_bshd", xs),
                                                   ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs)],
                         "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
@@ -409,6 +432,7 @@ def main():
                    "prefill_max_lse_err": par_pl, "decode_max_err_over_tol": round(par_d, 4)},
     }
     if not args.no_extra:
+        out["rounding_modes"] = rounding_modes(args, p, ea, torch, q, k, v, o, lse, log)
         out["other_workloads"] = extra_workloads(args, gen, ea, torch, dev, to_dev, log)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")

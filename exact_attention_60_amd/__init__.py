@@ -6,8 +6,13 @@ C ABI declared in include/attn.h with raw pointers and the current HIP stream.
 Every step of the computation runs in the library's HIP kernels; if the
 library is not built the binding raises instead of computing anything itself.
 
-    o, lse = attn_fwd(q, k, v, causal=False, scale=None, layout="bshd")
-    o, lse = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens)
+    o, lse = attn_fwd(q, k, v, causal=False, scale=None, layout="bshd", rounding="rtne")
+    o, lse = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, rounding="rtne")
+
+``rounding`` is the rule of the final fp32 -> bf16 conversion of O: "rtne"
+(nearest, ties to even; the plain entry points), "rtna" (nearest, ties away
+from zero) or "rtz" (toward zero); the other two call the *_rounded entry
+points.
 """
 from __future__ import annotations
 
@@ -22,6 +27,7 @@ ATTN_BSHD = 0
 ATTN_BHSD = 1
 HEAD_DIM = 128
 PAGE_SIZE = 16
+ROUNDING = {"rtne": 0, "rtna": 1, "rtz": 2}
 
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
@@ -30,8 +36,8 @@ STATUS = {
 }
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_decode_workspace_bytes", "attn_decode_paged",
-           "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_decode_workspace_bytes", "attn_decode_paged",
+           "attn_decode_paged_rounded", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -53,11 +59,16 @@ def library() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
         lib.attn_fwd.restype = i
+        lib.attn_fwd_rounded.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+        lib.attn_fwd_rounded.restype = i
         lib.attn_decode_workspace_bytes.argtypes = [i, i, i]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
                                           sz, vp]
         lib.attn_decode_paged.restype = i
+        lib.attn_decode_paged_rounded.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                                  f, i, vp, sz, vp]
+        lib.attn_decode_paged_rounded.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -100,8 +111,15 @@ def _check_bf16(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _rounding_code(rounding: str) -> int:
+    try:
+        return ROUNDING[rounding.lower()]
+    except KeyError:
+        raise ValueError(f"rounding must be one of {sorted(ROUNDING)}, got {rounding!r}") from None
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
-             layout: str = "bshd", out=None, lse=None, stream=None):
+             layout: str = "bshd", rounding: str = "rtne", out=None, lse=None, stream=None):
     """Fused exact attention forward.  q: [B, Sq, Hq, 128] (bshd) or
     [B, Hq, Sq, 128] (bhsd); k, v likewise with Hkv heads and Sk keys.
     Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
@@ -111,6 +129,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
         raise ValueError("q, k, v must be 4-D and k, v of equal shape")
     lay = {"bshd": ATTN_BSHD, "bhsd": ATTN_BHSD}[layout.lower()]
+    rnd = _rounding_code(rounding)
     if lay == ATTN_BSHD:
         B, Sq, Hq, d = q.shape
         _, Sk, Hkv, _ = k.shape
@@ -125,16 +144,19 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    st = library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)),
-                            lay, _stream_ptr(stream))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+            Sq, Sk, d, float(scale), int(bool(causal)), lay)
+    if rnd == ROUNDING["rtne"]:
+        st, where = library().attn_fwd(*args, _stream_ptr(stream)), "attn_fwd"
+    else:
+        st, where = library().attn_fwd_rounded(*args, rnd, _stream_ptr(stream)), "attn_fwd_rounded"
     if st != 0:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, where)
     return out, lse
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: float | None = None,
-                      out=None, lse=None, workspace=None, stream=None):
+                      rounding: str = "rtne", out=None, lse=None, workspace=None, stream=None):
     """One paged decode step.  q: [B, Hq, 128]; k_cache, v_cache:
     [num_pages, 16, Hkv, 128]; block_table: int32 [B, max_blocks];
     seq_lens: int32 [B].  Returns (o bf16 [B, Hq, 128], lse fp32 [B, Hq])."""
@@ -149,6 +171,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     if v_cache.shape != k_cache.shape or d2 != d or block_table.shape[0] != B:
         raise ValueError("inconsistent decode shapes")
     max_blocks = block_table.shape[1]
+    rnd = _rounding_code(rounding)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = attn_decode_workspace_bytes(B, Hq, max_blocks)
@@ -158,15 +181,19 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    st = library().attn_decode_paged(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page, max_blocks,
-        num_pages, float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream_ptr(stream))
+    head = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+            seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page, max_blocks,
+            num_pages, float(scale))
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if rnd == ROUNDING["rtne"]:
+        st, where = library().attn_decode_paged(*head, *tail), "attn_decode_paged"
+    else:
+        st, where = library().attn_decode_paged_rounded(*head, rnd, *tail), "attn_decode_paged_rounded"
     if st != 0:
-        raise AttnError(st, "attn_decode_paged")
+        raise AttnError(st, where)
     return out, lse
 
 
 __all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_string",
-           "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "EXPORTS", "LIB_PATH"]
+           "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
+           "LIB_PATH"]

@@ -12,6 +12,10 @@
 #include "attn.h"
 #include "kernels.h"
 
+static_assert(attn::kRoundRTNE == ATTN_ROUND_RTNE && attn::kRoundRTNA == ATTN_ROUND_RTNA &&
+                  attn::kRoundRTZ == ATTN_ROUND_RTZ,
+              "kernel rounding codes follow the ABI's");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -40,6 +44,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
+bool rounding_ok(int r) { return r == ATTN_ROUND_RTNE || r == ATTN_ROUND_RTNA || r == ATTN_ROUND_RTZ; }
+
 }  // namespace
 
 extern "C" {
@@ -51,7 +57,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape (sizes must be >= 1, Hq a multiple of Hkv, within limits)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (d must be 128, page_size 16, layout BSHD/BHSD, scale finite and > 0, causal 0/1)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (d must be 128, page_size 16, layout BSHD/BHSD, scale finite and > 0, causal 0/1, rounding RTNE/RTNA/RTZ)";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
@@ -60,13 +66,13 @@ const char* attn_status_string(int status) {
   }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-             int Hkv, int Sq, int Sk, int d, float scale, int causal, int layout,
-             void* stream) {
+int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal, int layout,
+                     int rounding, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
-      (causal != 0 && causal != 1) || !scale_ok(scale))
+      (causal != 0 && causal != 1) || !scale_ok(scale) || !rounding_ok(rounding))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_ALIGN;
@@ -91,11 +97,19 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.n_qt = (Sq + attn::kPrefillBM - 1) / attn::kPrefillBM;
   if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
   a.c = scale * 1.4426950408889634f;
+  a.rounding = rounding;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
   const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int d, float scale, int causal, int layout,
+             void* stream) {
+  return attn_fwd_rounded(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, layout,
+                          ATTN_ROUND_RTNE, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
@@ -106,16 +120,17 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
   return (size_t)B * Hq * (splits * (attn::kHeadDim + 1) + 1) * sizeof(float);
 }
 
-int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
-                      int B, int Hq, int Hkv, int d, int page_size, int max_blocks_per_seq,
-                      int num_pages, float scale, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                              int max_blocks_per_seq, int num_pages, float scale, int rounding,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_pages < 1)
     return ATTN_ERR_SHAPE;
   if (B > 65535 || max_blocks_per_seq > 262140) return ATTN_ERR_SHAPE;
-  if (d != attn::kHeadDim || page_size != attn::kPage || !scale_ok(scale))
+  if (d != attn::kHeadDim || page_size != attn::kPage || !scale_ok(scale) ||
+      !rounding_ok(rounding))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) ||
       !aligned16(seq_lens) || !aligned16(o) || !aligned16(lse))
@@ -149,8 +164,19 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.token_stride = (int64_t)Hkv * attn::kHeadDim;
   a.page_stride = (int64_t)attn::kPage * a.token_stride;
   a.c = scale * 1.4426950408889634f;
+  a.rounding = rounding;
   const hipError_t e = attn::launch_decode(a, cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      int B, int Hq, int Hkv, int d, int page_size, int max_blocks_per_seq,
+                      int num_pages, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return attn_decode_paged_rounded(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
+                                   d, page_size, max_blocks_per_seq, num_pages, scale,
+                                   ATTN_ROUND_RTNE, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

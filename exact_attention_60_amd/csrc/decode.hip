@@ -37,7 +37,8 @@
 //   chunk of that (sequence, unit group); the workgroup that holds a
 //   sequence's first page also writes how many chunks the sequence spans.
 // decode_merge_kernel, one wave per (b, query head): LSE = M + ln sum e^(LSE_s-M),
-//   O = sum e^(LSE_s - LSE) O_s in chunk order (deterministic), O to bf16 RTNE.
+//   O = sum e^(LSE_s - LSE) O_s in chunk order (deterministic), O to bf16
+//   under the caller's rounding rule.
 #include "gfx950.hpp"
 #include "kernels.h"
 
@@ -538,7 +539,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  *(uint32_t*)(a.o + (int64_t)wid * D + 2 * lane) = pack_bf16(o0 * inv, o1 * inv);
+  uint32_t packed;
+  with_rounding(a.rounding, [&](auto mode) { packed = pack_bf16_as<mode()>(o0 * inv, o1 * inv); });
+  *(uint32_t*)(a.o + (int64_t)wid * D + 2 * lane) = packed;
   if (lane == 0) a.lse[wid] = (L > 0.f) ? M + __logf(L) : -INFINITY;
 }
 

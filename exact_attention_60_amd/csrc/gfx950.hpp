@@ -15,6 +15,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "kernels.h"
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -64,6 +68,37 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   p[0] = (__bf16)lo;
   p[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, p);
+}
+// bf16 bits of x (in the upper half of the result) by integer arithmetic on
+// the sign-magnitude encoding: adding HALF (0x8000, half a bf16 spacing, for
+// RTNA; 0 for RTZ) to the magnitude and dropping the low 16 bits.  With
+// 0x8000 a tie carries into the kept bits, i.e. away from zero, and values from
+// half a spacing past the largest finite bf16 carry into the exponent and give
+// inf; with 0 it is truncation.  NaN becomes the quiet NaN 0x7FC0 with x's
+// sign.
+template <uint32_t HALF>
+__device__ __forceinline__ uint32_t bf16_bits_hi(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t nan = (u & 0x80000000u) | 0x7fc00000u;
+  return ((u & 0x7fffffffu) > 0x7f800000u ? nan : u + HALF) & 0xffff0000u;
+}
+// two floats -> packed bf16 under the rounding rule MODE (kRound*)
+template <int MODE>
+__device__ __forceinline__ uint32_t pack_bf16_as(float lo, float hi) {
+  if constexpr (MODE == kRoundRTNE) {
+    return pack_bf16(lo, hi);
+  } else {
+    constexpr uint32_t half = MODE == kRoundRTNA ? 0x8000u : 0u;
+    return (bf16_bits_hi<half>(lo) >> 16) | bf16_bits_hi<half>(hi);
+  }
+}
+// Calls f(std::integral_constant<int, MODE>) for the run-time rule `mode`, so
+// that the conversion code is chosen once, outside the caller's loops.
+template <class F>
+__device__ __forceinline__ void with_rounding(int mode, F&& f) {
+  if (mode == kRoundRTNA) f(std::integral_constant<int, kRoundRTNA>{});
+  else if (mode == kRoundRTZ) f(std::integral_constant<int, kRoundRTZ>{});
+  else f(std::integral_constant<int, kRoundRTNE>{});
 }
 // two floats -> packed fp16 (v_cvt_pk_f16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {

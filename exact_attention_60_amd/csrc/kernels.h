@@ -12,6 +12,11 @@ constexpr int kPrefillRowsPerWave = 32;               // one 32-row MFMA block p
 constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // 256 query rows
 constexpr int kPrefillBN = 64;                        // keys per K/V tile
 
+// Rounding rules of the final fp32 -> bf16 output conversion (the values of
+// ATTN_ROUND_* in attn.h): to nearest with ties to even (the hardware
+// conversion), to nearest with ties away from zero, toward zero.
+enum : int { kRoundRTNE = 0, kRoundRTNA = 1, kRoundRTZ = 2 };
+
 struct PrefillArgs {
   const __bf16* q;
   const __bf16* k;
@@ -24,6 +29,7 @@ struct PrefillArgs {
   int group;                 // Hq / Hkv
   int n_qt;                  // ceil(Sq / kPrefillBM)
   float c;                   // scale * log2(e)
+  int rounding;              // kRoundRTNE / kRoundRTNA / kRoundRTZ for O
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
@@ -54,6 +60,7 @@ struct DecodeArgs {
   int64_t page_stride;       // elements per page: 16 * Hkv * 128
   int64_t token_stride;      // elements per token slot: Hkv * 128
   float c;                   // scale * log2(e)
+  int rounding;              // kRoundRTNE / kRoundRTNA / kRoundRTZ for O
 };
 
 // partial results a (sequence, unit group) can need: ceil(max_blocks / 4) + 1

@@ -573,7 +573,8 @@ void prefill_kernel(PrefillArgs a) {
   // probabilities and bf16 V, which covers the whole bf16 range.
   if (__syncthreads_or(!state_finite(w))) tile_loop<CAUSAL, false>(w, x, kbuf, vbuf, vtbuf);
 
-  // ---- epilogue: O = acc / l (bf16, RTNE) in q's layout; LSE = ln(sum exp)
+  // ---- epilogue: O = acc / l (bf16 under the caller's rounding rule) in q's
+  // layout; LSE = ln(sum exp)
   const float l = sum_halves(w.lsum);
   const int row = w.first + w.l32;
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
@@ -584,15 +585,17 @@ void prefill_kernel(PrefillArgs a) {
   // row; each wave stages its 32 rows (8 KB) with the tile swizzle and reads
   // back only its own rows.
   char* st = (x.wave < 4 ? kbuf : vtbuf) + (x.wave & 3) * 8192;
+  with_rounding(a.rounding, [&](auto mode) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x2 u;
-      u[0] = pack_bf16(w.oacc[db][4 * j + 0] * inv, w.oacc[db][4 * j + 1] * inv);
-      u[1] = pack_bf16(w.oacc[db][4 * j + 2] * inv, w.oacc[db][4 * j + 3] * inv);
-      *(u32x2*)(st + tile_off(w.l32, 4 * db + j) + 8 * w.hi) = u;
-    }
+      for (int j = 0; j < 4; ++j) {
+        u32x2 u;
+        u[0] = pack_bf16_as<mode()>(w.oacc[db][4 * j + 0] * inv, w.oacc[db][4 * j + 1] * inv);
+        u[1] = pack_bf16_as<mode()>(w.oacc[db][4 * j + 2] * inv, w.oacc[db][4 * j + 3] * inv);
+        *(u32x2*)(st + tile_off(w.l32, 4 * db + j) + 8 * w.hi) = u;
+      }
+  });
   wait_lds();
   __bf16* ob = a.o + b * a.q_sb + hq * a.q_sh;
 #pragma unroll

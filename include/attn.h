@@ -27,7 +27,10 @@
  *  - the key split with a merge of partials for the tail: MoonMath page,
  *    third-Q-tile paragraph;
  *  - launching on the caller's stream so the call overlaps a larger
- *    pipeline: MoonMath page, use-case paragraph.
+ *    pipeline: MoonMath page, use-case paragraph;
+ *  - three rounding rules for the bf16 output (to nearest with ties to even,
+ *    to nearest with ties away from zero, toward zero): MoonMath page,
+ *    numerics and benchmark paragraphs.
  *
  * Conventions common to every entry point
  *  - bf16 tensors are passed as raw device pointers to IEEE bfloat16 data;
@@ -49,7 +52,11 @@
  *    visible from query i iff j <= i + (Sk - Sq).  A query row that sees no key
  *    gets O = 0 and LSE = -inf.
  *  - The scale is applied in fp32 to fp32 scores (never folded into bf16 Q).
- *  - O is rounded to bf16 with round-to-nearest-even.
+ *  - O is rounded to bf16 with round-to-nearest-even by attn_fwd and
+ *    attn_decode_paged; their *_rounded variants take the rule as an argument.
+ *    The rule applies to the final fp32 -> bf16 conversion of O only; the
+ *    probabilities inside the kernels are rounded to nearest even as always,
+ *    and LSE does not depend on it.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -61,7 +68,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 1
+#define ATTN_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
@@ -75,6 +82,16 @@ typedef enum {
 } attn_status;
 
 enum { ATTN_BSHD = 0, ATTN_BHSD = 1 };
+
+/*
+ * Rounding rule of the final fp32 -> bf16 conversion of O:
+ *   ATTN_ROUND_RTNE  to nearest, ties to the value with an even last bit
+ *   ATTN_ROUND_RTNA  to nearest, ties away from zero; from half a spacing past
+ *                    the largest finite bf16 the result is +-inf
+ *   ATTN_ROUND_RTZ   toward zero (truncation); finite values never become inf
+ * In every rule NaN stays NaN and +-0, +-inf keep their sign.
+ */
+enum { ATTN_ROUND_RTNE = 0, ATTN_ROUND_RTNA = 1, ATTN_ROUND_RTZ = 2 };
 
 /*
  * attn_fwd - fused exact attention forward (prefill, self- or cross-attention).
@@ -98,6 +115,20 @@ enum { ATTN_BSHD = 0, ATTN_BHSD = 1 };
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
              int layout, void* stream);
+
+/*
+ * attn_fwd_rounded - attn_fwd with the rounding rule of O as an argument
+ * ("MoonMath AI open-sources a HIP attention kernel for AMD MI300X that beats
+ * AITER v3", benchmark paragraph: every shape is measured under RTNE, RTNA and
+ * RTZ).  `rounding` is one of ATTN_ROUND_*; any other value returns
+ * ATTN_ERR_UNSUPPORTED.  Every other argument, limit and status is as for
+ * attn_fwd, which is attn_fwd_rounded with ATTN_ROUND_RTNE.  O under the three
+ * rules comes from the same fp32 values, so the results differ by at most one
+ * bf16 spacing per element; LSE is identical.
+ */
+int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     int layout, int rounding, void* stream);
 
 /*
  * attn_decode_workspace_bytes - device workspace that attn_decode_paged needs
@@ -140,6 +171,19 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       float* lse, int B, int Hq, int Hkv, int d, int page_size,
                       int max_blocks_per_seq, int num_pages, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_rounded - attn_decode_paged with the rounding rule of O
+ * (one of ATTN_ROUND_*, else ATTN_ERR_UNSUPPORTED) as an argument; the same
+ * rules as attn_fwd_rounded, applied when the merged fp32 output is written.
+ * Everything else is as for attn_decode_paged, which is this call with
+ * ATTN_ROUND_RTNE.
+ */
+int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                              int max_blocks_per_seq, int num_pages, float scale, int rounding,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 1
+    assert ea.attn_version() == 2
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -49,13 +49,16 @@ def test_workspace_bytes():
 P = 0x10000  # a fake, 16-byte aligned "device" pointer: never dereferenced
 
 
-def fwd(**kw):
+def fwd(rounding=None, **kw):
+    """attn_fwd, or attn_fwd_rounded when a rounding code is given."""
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.1,
              causal=0, layout=0, stream=None)
     a.update(kw)
-    return ea.library().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
-                                 a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"],
-                                 a["layout"], a["stream"])
+    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+            a["d"], a["scale"], a["causal"], a["layout"])
+    if rounding is None:
+        return ea.library().attn_fwd(*args, a["stream"])
+    return ea.library().attn_fwd_rounded(*args, rounding, a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,16 +71,28 @@ def fwd(**kw):
 ])
 def test_fwd_argument_errors(kw, code):
     assert fwd(**kw) == code
+    for r in (0, 1, 2):                      # the rounded variant checks the same
+        assert fwd(rounding=r, **kw) == code
 
 
-def dec(**kw):
+@pytest.mark.parametrize("r", [-1, 3, 100])
+def test_unknown_rounding_rule_is_unsupported(r):
+    assert fwd(rounding=r) == -3
+    assert dec(rounding=r) == -3
+
+
+def dec(rounding=None, **kw):
+    """attn_decode_paged, or attn_decode_paged_rounded when a rounding code is
+    given."""
     a = dict(q=P, k=P, v=P, tab=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, page=16,
              mb=4, npages=8, scale=0.1, ws=P, wsb=10 ** 6, stream=None)
     a.update(kw)
-    return ea.library().attn_decode_paged(a["q"], a["k"], a["v"], a["tab"], a["lens"], a["o"],
-                                          a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], a["page"],
-                                          a["mb"], a["npages"], a["scale"], a["ws"], a["wsb"],
-                                          a["stream"])
+    head = (a["q"], a["k"], a["v"], a["tab"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"],
+            a["Hkv"], a["d"], a["page"], a["mb"], a["npages"], a["scale"])
+    tail = (a["ws"], a["wsb"], a["stream"])
+    if rounding is None:
+        return ea.library().attn_decode_paged(*head, *tail)
+    return ea.library().attn_decode_paged_rounded(*head, rounding, *tail)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -90,6 +105,8 @@ def dec(**kw):
 ])
 def test_decode_argument_errors(kw, code):
     assert dec(**kw) == code
+    for r in (0, 1, 2):
+        assert dec(rounding=r, **kw) == code
 
 
 def test_valid_arguments_need_a_gfx950_device():
@@ -99,3 +116,12 @@ def test_valid_arguments_need_a_gfx950_device():
     # all checks pass, so the library asks HIP for the device and finds none
     assert fwd() == -7
     assert dec() == -7
+    for r in (0, 1, 2):
+        assert fwd(rounding=r) == -7
+        assert dec(rounding=r) == -7
+
+
+def test_binding_rejects_unknown_rounding_name():
+    with pytest.raises(ValueError):
+        ea._rounding_code("nearest")
+    assert [ea._rounding_code(n) for n in ("RTNE", "rtna", "rtz")] == [0, 1, 2]
