@@ -30,7 +30,8 @@ PAGE = 16
 BF16_QNAN = np.uint16(0x7FC0)
 
 # stream ids for default_rng([seed, stream])
-_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX, _S_EQK, _S_EQV = range(10)
+(_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX, _S_EQK, _S_EQV, _S_KNEW,
+ _S_VNEW) = range(12)
 
 BSHD = 0
 BHSD = 1
@@ -192,6 +193,29 @@ def decode_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, scale=None, lens=None,
                 vp[last, t:] = BF16_QNAN
     q = f32_to_bf16_bits(_normal(seed, _S_Q, (B, Hq, D)))
     return Decode(q, kp, vp, table, lens, B, Hq, Hkv, float(scale), name=name)
+
+
+@dataclass
+class DecodeAppend:
+    """A decode step that first appends the current token: `base` is the
+    paged problem (lengths count the current token), k_new / v_new its K and V
+    rows (bf16 bits [B, Hkv, D]).  The pool slots of the current tokens hold
+    bf16 NaN, standing for cache memory not yet written."""
+    base: Decode
+    k_new: np.ndarray
+    v_new: np.ndarray
+
+
+def decode_append_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, lens=None, name="") -> DecodeAppend:
+    d = decode_inputs(B, Hq, Hkv, max_len=max_len, seed=seed, lens=lens, name=name)
+    for b in range(B):
+        t = int(d.seq_lens[b]) - 1
+        page = d.block_table[b, t // PAGE]
+        d.k_pool[page, t % PAGE] = BF16_QNAN
+        d.v_pool[page, t % PAGE] = BF16_QNAN
+    k_new = f32_to_bf16_bits(_normal(seed, _S_KNEW, (B, Hkv, D)))
+    v_new = f32_to_bf16_bits(_normal(seed, _S_VNEW, (B, Hkv, D)))
+    return DecodeAppend(d, k_new, v_new)
 
 
 # --------------------------------------------------------------------------

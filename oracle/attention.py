@@ -212,6 +212,34 @@ def decode_paged(q_bits, k_pool, v_pool, block_table, seq_lens, Hkv, scale,
     return o, lse
 
 
+def append_token(k_pool, v_pool, block_table, seq_lens, k_new, v_new):
+    """KV-cache append: the current token of sequence b is token seq_lens[b]-1
+    (the lengths count it), and its K and V rows k_new[b], v_new[b] ([Hkv, D]
+    bf16 bits) go to slot (len-1) % 16 of page block_table[b, (len-1) // 16]
+    of the paged pools ("Engineering the FlashAttention-4 kernel port to
+    ROCm", multi-query section, for the paged format; "Reverse engineering
+    Flash Attention 4's proprietary fused attention kernel", first point, for
+    updating the shared KV cache together with the attention).  Returns
+    updated copies of the pools."""
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    for b in range(len(seq_lens)):
+        t = int(seq_lens[b]) - 1
+        page = block_table[b, t // PAGE]
+        kp[page, t % PAGE] = k_new[b]
+        vp[page, t % PAGE] = v_new[b]
+    return kp, vp
+
+
+def decode_paged_append(q_bits, k_new, v_new, k_pool, v_pool, block_table, seq_lens, Hkv,
+                        scale, workers=None):
+    """Append the current token's K/V to the cache, then the paged decode over
+    every token including it.  Returns (o, lse, k_pool', v_pool')."""
+    kp, vp = append_token(k_pool, v_pool, block_table, seq_lens, k_new, v_new)
+    o, lse = decode_paged(q_bits, kp, vp, block_table, seq_lens, Hkv, scale, workers)
+    return o, lse, kp, vp
+
+
 def _run(fn, jobs, workers):
     workers = workers or _workers()
     if workers == 1 or len(jobs) == 1:
@@ -234,4 +262,5 @@ def flops_prefill(B, Hq, Sq, Sk, d, causal):
 
 __all__ = ["bf16_to_f64", "scale_as_f32", "kv_head_of", "visible_keys", "scores",
            "row_softmax", "attend_rows", "attention", "attention_sampled",
-           "gather_pages", "decode_paged", "flops_prefill"]
+           "gather_pages", "decode_paged", "append_token", "decode_paged_append",
+           "flops_prefill"]

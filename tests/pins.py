@@ -20,6 +20,9 @@ Facts used (none of them is the oracle's own formula retyped):
   P12 torch CPU float64 scaled_dot_product_attention / logsumexp agree
   P13 a single key gives O = V[0], LSE = s_00
   P14 all-zero keys give O = mean(V), LSE = ln(Sk)
+  P15 decode with a cache append equals torch float64 attention over the
+      cached tokens before the current one followed by the new K/V row, and
+      the pools change only in the current tokens' slots
 """
 from __future__ import annotations
 
@@ -300,6 +303,42 @@ def pin_p12_torch_sdpa(att, onl):
                 _close(l, lt[b, h], rtol=1e-12, atol=1e-12, what="P12 LSE")
 
 
+def pin_p15_append(att, onl):
+    import torch
+    import torch.nn.functional as F
+    lens = [1, 16, 17, 33, 2]
+    p = gen.decode_append_inputs(5, 6, 2, max_len=48, seed=90, lens=lens)
+    d = p.base
+    o, l, kp, vp = att.decode_paged_append(d.q, p.k_new, p.v_new, d.k_pool, d.v_pool,
+                                           d.block_table, d.seq_lens, 2, SC)
+    sc = float(np.float32(SC))
+    for b, n in enumerate(lens):
+        # the tokens cached before the current one, read through the table of
+        # the pools as they were, then the current token's rows
+        old_k = [d.k_pool[d.block_table[b, t // 16], t % 16] for t in range(n - 1)]
+        old_v = [d.v_pool[d.block_table[b, t // 16], t % 16] for t in range(n - 1)]
+        kd = _f64(np.stack(old_k + [p.k_new[b]]))          # [n, Hkv, D]
+        vd = _f64(np.stack(old_v + [p.v_new[b]]))
+        for h in range(6):
+            g = h // 3
+            qt = torch.from_numpy(_f64(d.q[b, h]))[None, None, None]
+            kt = torch.from_numpy(kd[:, g])[None, None]
+            vt = torch.from_numpy(vd[:, g])[None, None]
+            ot = F.scaled_dot_product_attention(qt, kt, vt, scale=sc)[0, 0, 0].numpy()
+            lt = torch.logsumexp(torch.matmul(qt, kt.transpose(-1, -2)) * sc, dim=-1).item()
+            _close(o[b, h], ot, rtol=1e-10, atol=1e-12, what="P15 O")
+            _close(l[b, h], lt, rtol=1e-12, atol=1e-12, what="P15 LSE")
+    # the pools: only the current tokens' slots change, to the new rows
+    for pool, new, upd in ((d.k_pool, p.k_new, kp), (d.v_pool, p.v_new, vp)):
+        changed = np.zeros(pool.shape[:2], bool)
+        for b, n in enumerate(lens):
+            pg, sl = d.block_table[b, (n - 1) // 16], (n - 1) % 16
+            changed[pg, sl] = True
+            assert np.array_equal(upd[pg, sl], new[b]), "P15 new row"
+        assert np.array_equal(upd[~changed], pool[~changed]), "P15 other slots"
+    assert np.all(np.isfinite(o)), "P15 the stale slot leaked"
+
+
 def pin_p13_single_key(att, onl):
     q = _rand((1, 3, 1, D), 70)
     k = _rand((1, 3, 1, D), 71)
@@ -328,5 +367,6 @@ def pin_p14_zero_keys(att, onl):
 ALL_PINS = [pin_p1_rows_sum_to_one, pin_p2_identical_keys, pin_p3_dominant_logit,
             pin_p4_causal, pin_p5_online_blockwise, pin_p6_split_merge,
             pin_p7_key_shift, pin_p8_permutation, pin_p9_gqa_is_repeated_mha,
-            pin_p10_layouts, pin_p11_paged, pin_p12_torch_sdpa, pin_p13_single_key,
+            pin_p10_layouts, pin_p11_paged, pin_p12_torch_sdpa, pin_p15_append,
+            pin_p13_single_key,
             pin_p14_zero_keys]

@@ -106,10 +106,39 @@ def _mut_scale_not_f32(m):
     m.scale_as_f32 = lambda s: float(s) * (1 + 1e-6)
 
 
+def _mut_append_past_end(m):
+    def append_token(k_pool, v_pool, table, lens, k_new, v_new):
+        kp, vp = k_pool.copy(), v_pool.copy()
+        for b in range(len(lens)):
+            t = int(lens[b])          # one slot too far
+            kp[table[b, t // m.PAGE], t % m.PAGE] = k_new[b]
+            vp[table[b, t // m.PAGE], t % m.PAGE] = v_new[b]
+        return kp, vp
+    m.append_token = append_token
+
+
+def _mut_append_k_only(m):
+    orig = m.append_token
+
+    def append_token(k_pool, v_pool, table, lens, k_new, v_new):
+        kp, _ = orig(k_pool, v_pool, table, lens, k_new, v_new)
+        return kp, v_pool.copy()
+    m.append_token = append_token
+
+
+def _mut_append_heads_reversed(m):
+    orig = m.append_token
+
+    def append_token(k_pool, v_pool, table, lens, k_new, v_new):
+        return orig(k_pool, v_pool, table, lens, k_new[:, ::-1], v_new[:, ::-1])
+    m.append_token = append_token
+
+
 MUTANTS = [_mut_no_scale, _mut_exp_sign, _mut_gqa_modulo, _mut_causal_off_by_one,
            _mut_causal_top_left, _mut_pv_transposed, _mut_lse_log2, _mut_lse_no_max,
            _mut_layout_swapped, _mut_page_slot_swapped, _mut_no_normalisation,
-           _mut_scale_not_f32]
+           _mut_scale_not_f32, _mut_append_past_end, _mut_append_k_only,
+           _mut_append_heads_reversed]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
