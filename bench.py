@@ -210,7 +210,9 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
             "# decode_partial_kernel + decode_merge_kernel on paged_decode_b32_hq32_hkv8_"
             "len4096_page16",
             [wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_partial_kernel"),
-             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_merge_kernel")],
+             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_merge_kernel"),
+             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_partial_kernel"),
+             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_merge_kernel")],
             ["decode_partial_kernel", "decode_merge_kernel"]),
         "prefill_kernel__causal_gqa_s8192_and_diffusion_s32760.md": (
             "# prefill_kernel on the causal GQA and diffusion-style workloads",
@@ -254,6 +256,29 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
         del q, k, v, o, lse
     torch.cuda.empty_cache()
     return res
+
+
+def decode_append(args, d, ea, torch, qd, pools, tab, lens, od, lsed, ws, to_dev, log):
+    """The decode workload with the current token appended to the cache in the
+    same call (attn_decode_paged_append): new K/V rows drawn for every
+    sequence; each call writes them into the rotated pools and attends."""
+    import attn_inputs as gen
+    r = np.random.default_rng(7)
+    kn = to_dev(gen.f32_to_bf16_bits(r.standard_normal((d.B, d.Hkv, 128)).astype(np.float32)))
+    vn = to_dev(gen.f32_to_bf16_bits(r.standard_normal((d.B, d.Hkv, 128)).astype(np.float32)))
+    log(f"timing {d.name} with the cache append")
+
+    def run(i):
+        kp, vp = pools[i % len(pools)]
+        ea.attn_decode_paged_append(qd, kn, vn, kp, vp, tab, lens, scale=d.scale, out=od,
+                                    lse=lsed, workspace=ws)
+
+    ms = time_calls(run, max(args.steps, 20), 3, torch)
+    # the plain decode's bytes plus the new rows read and written once
+    nbytes = d.bytes + 2 * 2 * d.B * d.Hkv * 128 * 2
+    return {"workload": d.name + "_append", "us_per_call": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def rounding_modes(args, p, ea, torch, q, k, v, o, lse, log):
@@ -300,9 +325,13 @@ def main():
                                                   ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs)],
                         "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
-                                                   st + wu)],
+                                                   st + wu),
+                                                  ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
+                                                   max(st, 20) + 3)],
                         "decode_merge_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
-                                                 st + wu)]},
+                                                 st + wu),
+                                                ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
+                                                 max(st, 20) + 3)]},
                "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace "
                          "-o run -- python3 -u bench.py --no-cpu-baseline",
                "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
@@ -432,6 +461,8 @@ def main():
                    "prefill_max_lse_err": par_pl, "decode_max_err_over_tol": round(par_d, 4)},
     }
     if not args.no_extra:
+        out["decode_append"] = decode_append(args, d, ea, torch, qd, pools, tab, lens, od, lsed,
+                                             ws, to_dev, log)
         out["rounding_modes"] = rounding_modes(args, p, ea, torch, q, k, v, o, lse, log)
         out["other_workloads"] = extra_workloads(args, gen, ea, torch, dev, to_dev, log)
     if not args.no_cpu_baseline:

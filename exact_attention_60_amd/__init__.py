@@ -8,6 +8,8 @@ library is not built the binding raises instead of computing anything itself.
 
     o, lse = attn_fwd(q, k, v, causal=False, scale=None, layout="bshd", rounding="rtne")
     o, lse = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, rounding="rtne")
+    o, lse = attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table,
+                                      seq_lens)   # writes the new rows into the caches
 
 ``rounding`` is the rule of the final fp32 -> bf16 conversion of O: "rtne"
 (nearest, ties to even; the plain entry points), "rtna" (nearest, ties away
@@ -37,7 +39,8 @@ STATUS = {
 
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_decode_workspace_bytes", "attn_decode_paged",
-           "attn_decode_paged_rounded", "attn_status_string", "attn_version")
+           "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_status_string",
+           "attn_version")
 
 _lib = None
 
@@ -69,6 +72,9 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_paged_rounded.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                                   f, i, vp, sz, vp]
         lib.attn_decode_paged_rounded.restype = i
+        lib.attn_decode_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                                 i, i, i, f, i, vp, sz, vp]
+        lib.attn_decode_paged_append.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -156,13 +162,20 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
 
 
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: float | None = None,
-                      rounding: str = "rtne", out=None, lse=None, workspace=None, stream=None):
+                      rounding: str = "rtne", out=None, lse=None, workspace=None, stream=None,
+                      k_new=None, v_new=None):
     """One paged decode step.  q: [B, Hq, 128]; k_cache, v_cache:
     [num_pages, 16, Hkv, 128]; block_table: int32 [B, max_blocks];
     seq_lens: int32 [B].  Returns (o bf16 [B, Hq, 128], lse fp32 [B, Hq])."""
     torch = _torch()
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_bf16(n, t)
+    append = k_new is not None or v_new is not None
+    if append:
+        if k_new is None or v_new is None:
+            raise ValueError("k_new and v_new go together")
+        _check_bf16("k_new", k_new)
+        _check_bf16("v_new", v_new)
     for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
@@ -170,6 +183,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     num_pages, page, Hkv, d2 = k_cache.shape
     if v_cache.shape != k_cache.shape or d2 != d or block_table.shape[0] != B:
         raise ValueError("inconsistent decode shapes")
+    if append and (tuple(k_new.shape) != (B, Hkv, d) or tuple(v_new.shape) != (B, Hkv, d)):
+        raise ValueError("k_new and v_new must be [B, Hkv, 128]")
     max_blocks = block_table.shape[1]
     rnd = _rounding_code(rounding)
     if scale is None:
@@ -185,7 +200,11 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
             seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page, max_blocks,
             num_pages, float(scale))
     tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(stream))
-    if rnd == ROUNDING["rtne"]:
+    if append:
+        st = library().attn_decode_paged_append(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), *head[1:], rnd, *tail)
+        where = "attn_decode_paged_append"
+    elif rnd == ROUNDING["rtne"]:
         st, where = library().attn_decode_paged(*head, *tail), "attn_decode_paged"
     else:
         st, where = library().attn_decode_paged_rounded(*head, rnd, *tail), "attn_decode_paged_rounded"
@@ -194,6 +213,15 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     return out, lse
 
 
-__all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_string",
+def attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, **kw):
+    """Append the current token (K/V rows k_new, v_new: [B, Hkv, 128]) to the
+    paged caches at position seq_lens[b] - 1, then decode over every token;
+    the caches are written in place.  Returns (o, lse)."""
+    return attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, k_new=k_new,
+                             v_new=v_new, **kw)
+
+
+__all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_paged_append",
+           "attn_decode_workspace_bytes", "attn_status_string",
            "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

@@ -120,11 +120,17 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
   return (size_t)B * Hq * (splits * (attn::kHeadDim + 1) + 1) * sizeof(float);
 }
 
-int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_table, const int32_t* seq_lens, void* o,
-                              float* lse, int B, int Hq, int Hkv, int d, int page_size,
-                              int max_blocks_per_seq, int num_pages, float scale, int rounding,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The three decode entry points share this: argument checks, then the launch.
+// knew / vnew are null unless the call appends the current token.
+int decode_call(const void* q, const void* knew, const void* vnew, const void* k_cache,
+                const void* v_cache, void* kc_out, void* vc_out, const int32_t* block_table,
+                const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d,
+                int page_size, int max_blocks_per_seq, int num_pages, float scale, int rounding,
+                void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_pages < 1)
     return ATTN_ERR_SHAPE;
@@ -133,7 +139,8 @@ int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_
       !rounding_ok(rounding))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_table) ||
-      !aligned16(seq_lens) || !aligned16(o) || !aligned16(lse))
+      !aligned16(seq_lens) || !aligned16(o) || !aligned16(lse) || !aligned16(knew) ||
+      !aligned16(vnew))
     return ATTN_ERR_ALIGN;
   const size_t need = attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -165,8 +172,37 @@ int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_
   a.page_stride = (int64_t)attn::kPage * a.token_stride;
   a.c = scale * 1.4426950408889634f;
   a.rounding = rounding;
+  a.knew = static_cast<const __bf16*>(knew);
+  a.vnew = static_cast<const __bf16*>(vnew);
+  a.kc_out = static_cast<__bf16*>(kc_out);
+  a.vc_out = static_cast<__bf16*>(vc_out);
   const hipError_t e = attn::launch_decode(a, cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                              int max_blocks_per_seq, int num_pages, float scale, int rounding,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_table,
+                     seq_lens, o, lse, B, Hq, Hkv, d, page_size, max_blocks_per_seq, num_pages,
+                     scale, rounding, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                             void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                             int max_blocks_per_seq, int num_pages, float scale, int rounding,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) return ATTN_ERR_NULL;
+  return decode_call(q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_table, seq_lens,
+                     o, lse, B, Hq, Hkv, d, page_size, max_blocks_per_seq, num_pages, scale,
+                     rounding, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,

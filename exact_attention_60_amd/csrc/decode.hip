@@ -32,6 +32,12 @@
 //     read back transposed with ds_read_b64_tr_b16, converted to fp16, and
 //     O^T += V^T P^T on v_mfma_f32_16x16x16_f16 with fp16 probabilities (a
 //     page holding a V value beyond the fp16 range keeps bf16 for both).
+//   With a cache append, the current token (position len - 1) takes its K row
+//   from the new rows instead of the cache (a per-lane load address) and its
+//   V row is written over the stale copy in the LDS slot before the page is
+//   read back; at the end of that segment the wave of head block 0 stores
+//   both rows into the cache slot.  Nothing else in the launch reads that
+//   head's bytes of the slot, so no ordering between workgroups is needed.
 //   Each segment writes its normalised fp32 output and natural-log LSE per
 //   head to the workspace, in the slot of its chunk counted from the first
 //   chunk of that (sequence, unit group); the workgroup that holds a
@@ -211,6 +217,29 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
   const int32_t tab_lane = (p0 + lane < p1) ? a.table[(int64_t)b * a.max_blocks + p0 + lane] : 0;
   const float c = a.c;
   auto page_of = [&](int p) { return __builtin_amdgcn_readlane(tab_lane, p - p0); };
+  // cache append: page pn (-1 if not in this segment), slot sn of the current
+  // token; lanes 0..15 hold d = 8*lane .. 8*lane+7 of its K and V rows.  The
+  // two loads are issued right after the segment's first page, untracked like
+  // the page loads: every later wait_page (vmcnt(8), only the newest page's
+  // eight operations allowed in flight) has completed them, so they cost no
+  // wait of their own.  A table entry outside [0, num_pages) for that page
+  // makes the page contribute nothing and suppresses the cache write.
+  const int t_new = len - 1;
+  const int pn = (a.knew != nullptr && t_new >= 0 && t_new / kPage >= p0 && t_new / kPage < p1)
+                     ? t_new / kPage : -1;
+  const int sn = t_new & (kPage - 1);
+  const int64_t new_row = ((int64_t)b * a.Hkv + g) * D;
+  u32x4 kn = u32x4{}, vn = u32x4{};
+  auto load_new_rows = [&]() {
+    if (pn >= 0 && lane < 16) {
+      asm volatile(
+          "global_load_dwordx4 %0, %2, off\n\t"
+          "global_load_dwordx4 %1, %3, off"
+          : "=&v"(kn), "=&v"(vn)
+          : "v"(a.knew + new_row + 8 * lane), "v"(a.vnew + new_row + 8 * lane)
+          : "memory");
+    }
+  };
   // tokens of page p that take part: those before the sequence end, none if
   // the table entry is outside [0, num_pages) (then page 0 is addressed and
   // nothing of it is used)
@@ -228,7 +257,9 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
     const int64_t phys = ((uint32_t)e < (uint32_t)a.num_pages) ? e : 0;
     const __bf16* kpg = a.kc + phys * a.page_stride + (int64_t)g * D;
     const __bf16* vpg = a.vc + phys * a.page_stride + (int64_t)g * D;
-    load_k(kf, kpg + (int64_t)col * a.token_stride + 8 * grp);
+    const __bf16* krow = kpg + (int64_t)col * a.token_stride;
+    if (p == pn && col == sn) krow = a.knew + new_row;   // the appended token
+    load_k(kf, krow + 8 * grp);
     const int nt = tokens_in(p);
     const uint32_t nrec = nt > 0 ? (uint32_t)(nt - 1) * tsb + 256u : 0u;
     const __amdgpu_buffer_rsrc_t rv =
@@ -255,7 +286,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
                  : "memory");
   };
 
-  auto compute_page = [&](const bf16x8 (&kf)[4], const char* vs, int p) {
+  auto compute_page = [&](const bf16x8 (&kf)[4], char* vs, int p) {
     const int nt = tokens_in(p);
     // ---- scores: lane holds head `col`, tokens 4*grp + i
     f32x4 sacc = f32x4{};
@@ -279,6 +310,16 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(__builtin_fmaf(sv[i], c, -msub));
+    // the appended token's V row replaces the stale copy of its slot: the
+    // page's copies have landed (wait_page), and a wave's LDS accesses stay in
+    // order, so the transposed reads below see it.  Written as an untracked
+    // instruction: the compiler would otherwise wait for the next page's LDS
+    // copies before it.
+    if (p == pn && lane < 16) {
+      const uint32_t at = (uint32_t)(uintptr_t)(ATTN_LDS char*)vs + 512 * (lane >> 1) + 32 * sn +
+                          16 * (lane & 1);
+      asm volatile("ds_write_b128 %0, %1" : : "v"(at), "v"(vn) : "memory");
+    }
     // ---- V^T operands from the LDS slot.  P.V runs in fp16 (V converted
     // here) unless a V value of this page is beyond the fp16 range, in which
     // case the page uses bf16 P and V.
@@ -327,6 +368,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
     if constexpr (kDecodePrefetch == 1) {
       bf16x8 ka[4], kb[4];
       issue_page(ka, va, p);
+      load_new_rows();
       for (;;) {
         issue_page(kb, vb, min(p + 1, plast));
         wait_page<8>(ka);
@@ -340,6 +382,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
     } else {
       bf16x8 ka[4], kb[4], kc[4];
       issue_page(ka, va, p);
+      load_new_rows();
       issue_page(kb, vb, min(p + 1, plast));
       for (;;) {
         issue_page(kc, vc, min(p + 2, plast));
@@ -358,6 +401,14 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
     }
     wait_vm<0>();   // no copy into LDS may outlive the wave
   }
+  // the appended token's rows into the cache (one writer per (b, K/V head))
+  if (pn >= 0 && hb == 0 && lane < 16 && (uint32_t)page_of(pn) < (uint32_t)a.num_pages) {
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(kn), "+v"(vn) : : "memory");
+    const int64_t at = (int64_t)page_of(pn) * a.page_stride + (int64_t)sn * a.token_stride +
+                       (int64_t)g * D + 8 * lane;
+    *(u32x4*)(a.kc_out + at) = kn;
+    *(u32x4*)(a.vc_out + at) = vn;
+  }
 
   // ---- the segment's normalised output and natural-log LSE per head.
   // C layout of the 16x16 accumulator: lane column = head, rows 4*grp + i
@@ -374,7 +425,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
   }
 }
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_partial_kernel(DecodeArgs a) {
   // V page slots per wave, as separate arrays so that reads of one slot do
   // not wait for copies into another
   __shared__ __attribute__((aligned(1024))) char vslot0[kDecodeWaves][16 * D * 2];

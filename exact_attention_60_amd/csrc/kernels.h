@@ -61,6 +61,13 @@ struct DecodeArgs {
   int64_t token_stride;      // elements per token slot: Hkv * 128
   float c;                   // scale * log2(e)
   int rounding;              // kRoundRTNE / kRoundRTNA / kRoundRTZ for O
+  // cache append (null when the call does not append): the current token's
+  // K and V rows [B, Hkv, 128], and the caches as writable pointers (the
+  // same memory as kc / vc)
+  const __bf16* knew;
+  const __bf16* vnew;
+  __bf16* kc_out;
+  __bf16* vc_out;
 };
 
 // partial results a (sequence, unit group) can need: ceil(max_blocks / 4) + 1

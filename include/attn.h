@@ -28,6 +28,9 @@
  *    third-Q-tile paragraph;
  *  - launching on the caller's stream so the call overlaps a larger
  *    pipeline: MoonMath page, use-case paragraph;
+ *  - updating the shared KV cache inside the attention call (the current
+ *    token's K/V appended, then attended): "Reverse engineering Flash
+ *    Attention 4's proprietary fused attention kernel", first point;
  *  - three rounding rules for the bf16 output (to nearest with ties to even,
  *    to nearest with ties away from zero, toward zero): MoonMath page,
  *    numerics and benchmark paragraphs.
@@ -68,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 2
+#define ATTN_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -184,6 +187,36 @@ int attn_decode_paged_rounded(const void* q, const void* k_cache, const void* v_
                               float* lse, int B, int Hq, int Hkv, int d, int page_size,
                               int max_blocks_per_seq, int num_pages, float scale, int rounding,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_append - one decode step that first appends the current
+ * token to the paged KV cache: token seq_lens[b] - 1 of sequence b (the
+ * lengths count it) gets K row k_new[b] and V row v_new[b], written into slot
+ * (seq_lens[b] - 1) % 16 of page block_table[b, (seq_lens[b] - 1) / 16] of
+ * k_cache / v_cache, and the attention runs over all seq_lens[b] tokens with
+ * those rows ("Reverse engineering Flash Attention 4's proprietary fused
+ * attention kernel", first point: the KV-cache update fused with the
+ * attention; paged format as for attn_decode_paged).
+ *
+ *   k_new, v_new  bf16 [B, Hkv, d], 16-byte aligned, not aliasing the caches
+ *   k_cache,      as for attn_decode_paged, but written: after the call the
+ *   v_cache       current tokens' slots hold the new rows; no other byte of
+ *                 the caches changes.  The previous contents of those slots
+ *                 are never read (they may hold any bits).
+ *   rounding      one of ATTN_ROUND_* for O
+ * Everything else (shapes, workspace, limits, statuses) is as for
+ * attn_decode_paged; a NULL k_new or v_new returns ATTN_ERR_NULL.  The result
+ * equals writing the rows into the caches and then calling
+ * attn_decode_paged_rounded, bit for bit, in one launch sequence.  If the
+ * table entry of the current token's page is outside [0, num_pages) nothing
+ * is written and that page's tokens are left out, as in attn_decode_paged.
+ */
+int attn_decode_paged_append(const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, void* o, float* lse, int B, int Hq,
+                             int Hkv, int d, int page_size, int max_blocks_per_seq,
+                             int num_pages, float scale, int rounding, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 2
+    assert ea.attn_version() == 3
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -107,6 +107,26 @@ def test_decode_argument_errors(kw, code):
     assert dec(**kw) == code
     for r in (0, 1, 2):
         assert dec(rounding=r, **kw) == code
+        assert app(rounding=r, **kw) == code
+
+
+def app(rounding=0, kn=P, vn=P, **kw):
+    """attn_decode_paged_append with the same arguments as dec()."""
+    a = dict(q=P, k=P, v=P, tab=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, page=16,
+             mb=4, npages=8, scale=0.1, ws=P, wsb=10 ** 6, stream=None)
+    a.update(kw)
+    return ea.library().attn_decode_paged_append(
+        a["q"], kn, vn, a["k"], a["v"], a["tab"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"],
+        a["Hkv"], a["d"], a["page"], a["mb"], a["npages"], a["scale"], rounding, a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), -1), (dict(vn=None), -1), (dict(kn=P + 8), -4), (dict(vn=P + 2), -4),
+    (dict(rounding=5), -3),
+])
+def test_append_argument_errors(kw, code):
+    assert app(**kw) == code
 
 
 def test_valid_arguments_need_a_gfx950_device():
@@ -119,6 +139,7 @@ def test_valid_arguments_need_a_gfx950_device():
     for r in (0, 1, 2):
         assert fwd(rounding=r) == -7
         assert dec(rounding=r) == -7
+        assert app(rounding=r) == -7
 
 
 def test_binding_rejects_unknown_rounding_name():
