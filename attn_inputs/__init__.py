@@ -31,7 +31,7 @@ BF16_QNAN = np.uint16(0x7FC0)
 
 # stream ids for default_rng([seed, stream])
 (_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX, _S_EQK, _S_EQV, _S_KNEW,
- _S_VNEW) = range(12)
+ _S_VNEW, _S_DO) = range(13)
 
 BSHD = 0
 BHSD = 1
@@ -268,6 +268,12 @@ def equal_keys_decode(lens, Hq, Hkv, *, seed=0, binades=0, name="") -> Decode:
             p.k_pool[pg, t % PAGE] = rows[b]
             p.v_pool[pg, t % PAGE] = vals[pg, t % PAGE]
     return p
+
+
+def output_grad(p: Prefill, seed=0, dist="normal") -> np.ndarray:
+    """Upstream gradient dO for the backward of problem p: bf16 bits in Q's
+    layout and shape, iid N(0, 1) by default."""
+    return f32_to_bf16_bits(_draw(dist, seed, _S_DO, layout_shape(p.layout, p.B, p.Hq, p.Sq)))
 
 
 # --------------------------------------------------------------------------

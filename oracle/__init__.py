@@ -10,8 +10,10 @@ HIP kernels: the two meet only in the seeded input generator (``attn_inputs``).
   definition).
 * ``oracle.online``: a float64 model of the blockwise online softmax and of the
   split-KV merge, used only to pin the oracle to the pages' merge rule.
+* ``oracle.backward``: the gradient of the forward (dQ, dK, dV for an upstream
+  dO) by the chain rule on the materialised matrices, in float64.
 * ``oracle.rounding``: the three bf16 rounding rules of the output conversion
   (to nearest with ties to even, to nearest with ties away from zero, toward
   zero) applied to float64 values.
 """
-from . import attention, online, rounding  # noqa: F401
+from . import attention, backward, online, rounding  # noqa: F401

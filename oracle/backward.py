@@ -1,0 +1,144 @@
+"""Gradient of exact attention in float64: the backward oracle (TEST
+INFRASTRUCTURE ONLY).
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg may use this
+module; the library never does.
+
+What it computes, and where the pages fix it:
+
+* The backward pass keeps only the per-row softmax statistics of the forward
+  and recomputes the score and probability tiles from them instead of storing
+  P ("IO-aware tiling strategy in FlashAttention-4", the paragraph on the
+  backward pass; "Reverse engineering Flash Attention 4's proprietary fused
+  attention kernel", point 2, recompute of S/P from max_log and row_sum).
+  That is how the GPU path works.  What it must produce is fixed by the
+  forward's definition alone: the gradient of L = sum(dO * O) with respect to
+  Q, K and V, where O = softmax(scale * Q K^T, masked) V is the forward of
+  ``oracle.attention`` (same GQA head mapping, same bottom-right causal
+  alignment, same empty-row rule).
+* This module writes that gradient out by the chain rule on the materialised
+  matrices of one (batch, query head):
+      P  = row softmax of S = scale * Q K^T (masked entries -inf, P = 0 there)
+      dV = P^T dO
+      dP = dO V^T
+      dS = P * (dP - rowsum(P * dP))        (Jacobian of the row softmax)
+      dQ = scale * dS K,   dK = scale * dS^T Q
+  and a K/V head's gradients are the sums over the query heads that read it.
+  The row sum rowsum(P * dP) equals dO_i . O_i in exact arithmetic; the
+  oracle uses the former (the Jacobian as defined), the GPU the latter.
+* A row with no visible key has O = 0 whatever Q, K, V are: its dQ is zero
+  and it adds nothing to dK or dV.
+
+Inputs are bf16 bit patterns (uint16, upcast exactly) or float64 arrays (used
+by the finite-difference pins); the scale is rounded to float32 first, as the
+library receives it.  Everything else is float64.  Row chunks only split the
+sums over query rows of dK and dV.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import (BHSD, BSHD, _logical, _run, bf16_to_f64, kv_head_of,  # noqa: F401
+                        row_softmax, scale_as_f32, scores, visible_keys)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) upcast exactly; float arrays taken as float64."""
+    if x.dtype == np.uint16:
+        return bf16_to_f64(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def probabilities(q, k, scale, n_visible=None):
+    """P [n, Sk] of query rows q [n, d] against keys k [Sk, d], with row i
+    limited to keys 0..n_visible[i]-1 (all-masked rows give P = 0)."""
+    s = scores(q, k, scale)
+    if n_visible is not None:
+        j = np.arange(k.shape[0])
+        s = np.where(j[None, :] >= np.asarray(n_visible)[:, None], -np.inf, s)
+    p, _, _ = row_softmax(s)
+    return p
+
+
+def grad_rows(q, k, v, do, scale, n_visible=None):
+    """Gradient of sum(do * O) for O = attention of query rows q [n, d]
+    against k, v [Sk, d] (float64).  Returns (dq [n, d], dk [Sk, d],
+    dv [Sk, d])."""
+    p = probabilities(q, k, scale, n_visible)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def grad_magnitudes(q, k, v, do, scale, n_visible=None):
+    """Sums of absolute terms behind each gradient entry, the scale of its
+    rounding error when the products are formed from bf16-rounded operands
+    (P, dS) and the row term from a rounded O.  With
+    Dabs_i = sum_c |dO_ic O_ic| and A = P * (|dP| + Dabs):
+        mdv = P^T |dO|,  mdq = scale * A |K|,  mdk = scale * A^T |Q|.
+    Returns (mdq [n, d], mdk [Sk, d], mdv [Sk, d])."""
+    p = probabilities(q, k, scale, n_visible)
+    o = p @ v
+    dabs = np.abs(do * o).sum(axis=1, keepdims=True)
+    a = p * (np.abs(do @ v.T) + dabs)
+    return scale * (a @ np.abs(k)), scale * (a.T @ np.abs(q)), p.T @ np.abs(do)
+
+
+def attention_backward(q_in, k_in, v_in, do_in, B, Hq, Hkv, Sq, Sk, scale, causal, layout,
+                       chunk=512, workers=None, magnitudes=False):
+    """Full backward oracle.  q_in/do_in: [B,Sq,Hq,D] (BSHD) or [B,Hq,Sq,D]
+    (BHSD); k_in/v_in likewise with Hkv heads and Sk rows.  Returns
+    (dq [B,Hq,Sq,D], dk [B,Hkv,Sk,D], dv [B,Hkv,Sk,D]) float64 in logical
+    head-major order, followed by the three magnitude arrays of
+    ``grad_magnitudes`` (same shapes) when magnitudes=True."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    qv, kv, vv, dov = (_logical(x, layout) for x in (q_in, k_in, v_in, do_in))
+    d = q_in.shape[-1]
+    sc = scale_as_f32(scale)
+    dq = np.zeros((B, Hq, Sq, d))
+    dk = np.zeros((B, Hkv, Sk, d))
+    dv = np.zeros((B, Hkv, Sk, d))
+    if magnitudes:
+        mq, mk, mv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+    nvis = np.array([visible_keys(i, Sq, Sk, causal) for i in range(Sq)], np.int64)
+
+    def job(b, g):
+        kk = as_f64(kv[b, g])
+        vv_ = as_f64(vv[b, g])
+        for h in range(Hq):
+            if kv_head_of(h, Hq, Hkv) != g:
+                continue
+            for i0 in range(0, Sq, chunk):
+                i1 = min(Sq, i0 + chunk)
+                args = (as_f64(qv[b, h, i0:i1]), kk, vv_, as_f64(dov[b, h, i0:i1]), sc,
+                        nvis[i0:i1])
+                gq, gk, gv = grad_rows(*args)
+                dq[b, h, i0:i1] = gq
+                dk[b, g] += gk
+                dv[b, g] += gv
+                if magnitudes:
+                    aq, ak, av = grad_magnitudes(*args)
+                    mq[b, h, i0:i1] = aq
+                    mk[b, g] += ak
+                    mv[b, g] += av
+
+    _run(job, [(b, g) for b in range(B) for g in range(Hkv)], workers)
+    if magnitudes:
+        return dq, dk, dv, mq, mk, mv
+    return dq, dk, dv
+
+
+def flops_backward(B, Hq, Sq, Sk, d, causal):
+    """Algorithmic FLOP of the backward: the five products (S recomputed,
+    dP, dV, dQ, dK) of 2*Sq*Sk*d each per head, 10*B*Hq*Sq*Sk*d, halved when
+    causal."""
+    f = 10.0 * B * Hq * Sq * Sk * d
+    return f / 2 if causal else f
+
+
+__all__ = ["as_f64", "probabilities", "grad_rows", "grad_magnitudes", "attention_backward",
+           "flops_backward"]
