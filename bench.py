@@ -12,7 +12,9 @@ are already resident in HBM:
   256 MB last-level cache cannot serve a call from the previous one;
 * the other prefill workloads (causal GQA B=8 S=8192, diffusion-style self
   attention S=32760 and its cross attention against 512 keys), timed the
-  same way and reported beside the headline (skip with --no-extra).
+  same way and reported beside the headline (skip with --no-extra);
+* the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads,
+  reported beside the headline too.
 
 Times come from HIP events on the stream the kernels are launched on.  The
 fp64 CPU oracle is timed on the host cores on a bounded sample of the same
@@ -258,6 +260,39 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     return res
 
 
+def backward_workloads(args, gen, ea, torch, to_dev, log):
+    """attn_bwd (dQ, dK, dV from the forward's O and LSE and an upstream dO;
+    three launches: row terms, dK/dV, dQ) on the MHA and the causal GQA
+    workloads.  FLOP = 10*B*Hq*Sq*Sk*d (the five products S, dP, dV, dQ, dK),
+    halved when causal."""
+    res = []
+    steps = max(3, min(args.steps, 10))
+    for make, seed in ((gen.config2, 2), (gen.config3, 3)):
+        p = make()
+        log(f"timing the backward of {p.name}")
+        q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+        do = to_dev(gen.output_grad(p, seed))
+        lay = "bshd" if p.layout == gen.BSHD else "bhsd"
+        o, lse = ea.attn_fwd(q, k, v, causal=p.causal, scale=p.scale, layout=lay)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(ea.attn_bwd_workspace_bytes(p.B, p.Hq, p.Sq), dtype=torch.uint8,
+                         device=q.device)
+
+        def run(_i):
+            ea.attn_bwd(q, k, v, o, lse, do, causal=p.causal, scale=p.scale, layout=lay, dq=dq,
+                        dk=dk, dv=dv, workspace=ws)
+
+        ms = time_calls(run, steps, 2, torch)
+        fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 128 / (2 if p.causal else 1)
+        tf = fl / (ms * 1e-3) / 1e12
+        res.append({"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
+                    "TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def decode_append(args, d, ea, torch, qd, pools, tab, lens, od, lsed, ws, to_dev, log):
     """The decode workload with the current token appended to the cache in the
     same call (attn_decode_paged_append): new K/V rows drawn for every
@@ -465,6 +500,7 @@ def main():
                                              ws, to_dev, log)
         out["rounding_modes"] = rounding_modes(args, p, ea, torch, q, k, v, o, lse, log)
         out["other_workloads"] = extra_workloads(args, gen, ea, torch, dev, to_dev, log)
+        out["backward"] = backward_workloads(args, gen, ea, torch, to_dev, log)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         cb = cpu_baseline(p, args.cpu_seconds, torch)

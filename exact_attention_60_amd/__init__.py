@@ -10,6 +10,7 @@ library is not built the binding raises instead of computing anything itself.
     o, lse = attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, rounding="rtne")
     o, lse = attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table,
                                       seq_lens)   # writes the new rows into the caches
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bshd")
 
 ``rounding`` is the rule of the final fp32 -> bf16 conversion of O: "rtne"
 (nearest, ties to even; the plain entry points), "rtna" (nearest, ties away
@@ -39,8 +40,8 @@ STATUS = {
 
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_decode_workspace_bytes", "attn_decode_paged",
-           "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_status_string",
-           "attn_version")
+           "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
+           "attn_bwd", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -75,6 +76,11 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
                                                  i, i, i, f, i, vp, sz, vp]
         lib.attn_decode_paged_append.restype = i
+        lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+        lib.attn_bwd_workspace_bytes.restype = sz
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp,
+                                 sz, vp]
+        lib.attn_bwd.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -93,6 +99,10 @@ def attn_status_string(status: int) -> str:
 
 def attn_decode_workspace_bytes(B: int, Hq: int, max_blocks_per_seq: int) -> int:
     return int(library().attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq))
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Sq: int) -> int:
+    return int(library().attn_bwd_workspace_bytes(B, Hq, Sq))
 
 
 def _torch():
@@ -221,7 +231,48 @@ def attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, seq
                              v_new=v_new, **kw)
 
 
-__all__ = ["attn_fwd", "attn_decode_paged", "attn_decode_paged_append",
+def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None,
+             layout: str = "bshd", dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of attn_fwd for an upstream gradient do (q's layout and
+    shape), from the forward's inputs q, k, v and outputs o, lse.  Returns
+    (dq in q's layout, dk and dv in k's layout), all bf16."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_bf16(n, t)
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4 or o.shape != q.shape or \
+            do.shape != q.shape:
+        raise ValueError("q, o, do must share a 4-D shape and k, v another")
+    lay = {"bshd": ATTN_BSHD, "bhsd": ATTN_BHSD}[layout.lower()]
+    if lay == ATTN_BSHD:
+        B, Sq, Hq, d = q.shape
+        _, Sk, Hkv, _ = k.shape
+    else:
+        B, Hq, Sq, d = q.shape
+        _, Hkv, Sk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q and k disagree on batch or head dim")
+    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (B, Hq, Sq) or \
+            not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 GPU tensor [B, Hq, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = library().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), B, Hq, Hkv, Sq, Sk, d, float(scale),
+                            int(bool(causal)), lay, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append",
            "attn_decode_workspace_bytes", "attn_status_string",
            "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

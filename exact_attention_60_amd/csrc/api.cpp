@@ -215,4 +215,59 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                                    ATTN_ROUND_RTNE, workspace, workspace_bytes, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq) {
+  if (B < 1 || Hq < 1 || Sq < 1) return 0;
+  return (size_t)2 * B * Hq * Sq * sizeof(float);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Sk, int d, float scale, int causal, int layout, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
+      (causal != 0 && causal != 1) || !scale_ok(scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_ALIGN;
+  if (B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  const int64_t D = attn::kHeadDim;
+  attn::BwdArgs a;
+  if (layout == ATTN_BSHD) {
+    a.q_sb = (int64_t)Sq * Hq * D; a.q_sh = D; a.q_ss = (int64_t)Hq * D;
+    a.k_sb = (int64_t)Sk * Hkv * D; a.k_sh = D; a.k_ss = (int64_t)Hkv * D;
+  } else {
+    a.q_sb = (int64_t)Hq * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
+    a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
+  }
+  // the rows of one (batch, head) are addressed with 32-bit byte offsets,
+  // including the zero-filled rows past the end of a last 64-row block
+  if (((int64_t)Sq + 64) * a.q_ss * 2 > INT32_MAX || ((int64_t)Sk + 64) * a.k_ss * 2 > INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Sq);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.ws_d = static_cast<float*>(workspace);
+  a.ws_l = a.ws_d + (size_t)B * Hq * Sq;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
+  a.group = Hq / Hkv;
+  a.c = scale * 1.4426950408889634f;
+  a.scale = scale;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+  const hipError_t e = attn::launch_backward(a, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // extern "C"

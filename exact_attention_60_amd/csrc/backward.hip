@@ -1,0 +1,452 @@
+// Attention backward for gfx950: dQ, dK, dV of O = softmax(scale * Q K^T) V
+// for an upstream gradient dO.
+//
+// What is computed: the pages keep only the per-row softmax statistics from
+// the forward and recompute the score and probability tiles in the backward
+// instead of storing P ("IO-aware tiling strategy in FlashAttention-4", the
+// backward-pass paragraph; "Reverse engineering Flash Attention 4's
+// proprietary fused attention kernel", point 2).  With the forward's LSE
+// (natural log of the softmax denominator) each probability is recomputed
+// directly, P_ij = exp(scale * q_i.k_j - LSE_i), and the gradient of the row
+// softmax needs one more per-row number, D_i = dO_i . O_i (which equals
+// sum_j P_ij dP_ij):
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//     dQ = scale * dS K,  dK = scale * dS^T Q,
+// with a K/V head's dK and dV summed over the query heads that share it.
+//
+// Design (MI355X-first):
+//  * bwd_prep_kernel: D and the LSE in log2 units (+inf for rows that see no
+//    key, so that their recomputed probabilities are exactly 0), one pass over
+//    O and dO.
+//  * bwd_dkdv_kernel: one workgroup = 4 waves = 128 keys of one (batch, K/V
+//    head); each wave keeps its 32 keys' K and V fragments and fp32 dK, dV
+//    accumulators in registers and walks every query head of the group and
+//    every 64-row query block that can see its keys.  Q, dO, LSE and D blocks
+//    are copied HBM -> LDS by the buffer unit (buffer_load ... lds), double
+//    buffered one block ahead.  The GQA sum stays inside the workgroup, so
+//    there are no atomics and the result is deterministic.
+//  * bwd_dq_kernel: one workgroup = 4 waves = 128 query rows of one (batch,
+//    query head); each wave keeps its rows' Q and dO fragments and fp32 dQ
+//    accumulators in registers, and the 64-key K/V tiles stream through
+//    double-buffered LDS the same way.  S and dP are recomputed here rather
+//    than exchanged between the kernels.
+//  * All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  S
+//    and dP come out of the MFMA with one key (dK/dV kernel) or one query row
+//    (dQ kernel) per lane column, so their accumulator registers, rounded to
+//    bf16, are directly the A operand of the next product (the k-slot order of
+//    the accumulator rows is used as the contraction order); the other
+//    operand of that product is read column-wise from the row-major LDS tile
+//    with the gfx950 transpose read (ds_read_b64_tr_b16).
+//  * LDS rows are 256 B with an XOR swizzle of their 16-byte chunks so that
+//    both the row reads and the transpose reads spread over the banks.
+//  * blockIdx is remapped so that workgroups reading the same Q/dO (or K/V)
+//    run on one XCD and share its L2; causal dQ blocks are dispatched
+//    heaviest first.
+#include "gfx950.hpp"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int D = kHeadDim;
+constexpr int NW = 4;                 // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int KV_ROWS = NW * 32;      // keys per dK/dV workgroup
+constexpr int QB = 64;                // query rows per step of the dK/dV loop
+constexpr int Q_ROWS = NW * 32;       // query rows per dQ workgroup
+constexpr int KB = 64;                // keys per step of the dQ loop
+constexpr int TILE = 64 * 256;        // one 64-row bf16 tile in LDS
+constexpr uint32_t kRsrcFlags = 0x00020000;
+
+static_assert(kBwdKvRows == KV_ROWS && kBwdQRows == Q_ROWS && D == 128, "layout assumed below");
+
+// 4-bit swizzle of a row index: rows r and r + 4k land in different 4-chunk
+// groups, and the 4 rows of one transpose read in different chunks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// byte offset of 16-byte chunk c of row `row` in a tile
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return row * 256 + ((c ^ swz(row & 15)) << 4);
+}
+// byte offset of element `col` (a multiple of 4) of row `row`
+__device__ __forceinline__ int elem_off(int row, int col) {
+  return tile_off(row, col >> 3) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int per = n >> 3;
+  return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
+}
+
+// vmcnt(0) lgkmcnt(0): this wave's LDS copies have landed and its LDS reads
+// are done.
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 lds_row(const char* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + tile_off(row, chunk));
+}
+
+// B operand of a product whose contraction runs over tile rows: lane
+// (c = lane%32, h = lane/32) needs column `col0 + c` of the 8 rows
+// rbase + 4h + {0..3} and rbase + 8 + 4h + {0..3}, in that k-slot order (the
+// row order of a 32x32 accumulator's registers 0..7 in a lane half).  Two
+// transpose reads: in each 16-lane group lane j gets element j%4 of the
+// 4-element row addressed by lane 4e + j/4 (e = 0..3), so lane L of the
+// group addresses row rbase + 4h + L/4 at column col0 + 16*((lane/16)%2) +
+// 4*(L%4).
+__device__ __forceinline__ bf16x8 lds_cols(const char* tile, int rbase, int col0, int lane) {
+  const int L = lane & 15;
+  const int row = rbase + 4 * (lane >> 5) + (L >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+  const bf16x4 lo = lds_read_tr(tile + elem_off(row, col));
+  const bf16x4 hi = lds_read_tr(tile + elem_off(row + 8, col));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 8 fp32 accumulator values -> bf16 A operand (round to nearest even)
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+  u32x4 u = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+             pack_bf16(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Asynchronous copy of 16 rows (this wave's share of a 64-row tile) from
+// HBM into LDS: each buffer_load_dwordx4 ... lds moves 4 rows, lane i landing
+// at byte 16*i, i.e. row +i/16 and physical chunk i%16, so it fetches the
+// logical chunk the swizzle puts there.  Rows past the buffer's range read 0.
+struct RowCopy {
+  uint32_t voff[4];
+  int row0;
+  __device__ void init(int64_t row_stride, int wave, int lane) {
+    row0 = 16 * wave;
+    const uint32_t ss = (uint32_t)(row_stride * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = row0 + 4 * j + (lane >> 4);
+      voff[j] = (uint32_t)row * ss + (uint32_t)(((lane & 15) ^ swz(row & 15)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* tile, uint32_t base) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)(tile + (row0 + 4 * j) * 256),
+                                               16, voff[j] + base, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+
+}  // namespace
+
+// ---- D = rowsum(dO * O) and LSE in log2 units --------------------------------
+// 16 rows per workgroup, 16 lanes per row, 8 elements per lane.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int hq = blockIdx.y, b = blockIdx.z;
+  const int ch = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < a.Sq) {
+    const int64_t off = b * a.q_sb + hq * a.q_sh + (int64_t)row * a.q_ss + ch * 8;
+    const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(a.o + off);
+    const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(a.dout + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf((float)o8[e], (float)d8[e], s);
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+  if (ch == 0 && row < a.Sq) {
+    const int64_t i = ((int64_t)b * a.Hq + hq) * a.Sq + row;
+    a.ws_d[i] = s;
+    const float l = a.lse[i];
+    a.ws_l[i] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+}
+
+// ---- dK, dV ----------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char qbuf[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char dobuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) float lbuf[2 * QB];
+  __shared__ __attribute__((aligned(16))) float dbuf[2 * QB];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int n_kb = (a.Sk + KV_ROWS - 1) / KV_ROWS;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bg = L / n_kb;
+  const int kb = L - bg * n_kb;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int k0 = kb * KV_ROWS;
+  const int kw0 = k0 + 32 * wave;       // this wave's first key
+  const int off = a.Sk - a.Sq;          // key j visible from row i iff j <= i + off (causal)
+
+  // K and V fragments of the wave's keys: B operand of S = Q K^T and of
+  // dP = dO V^T (lane: key kw0 + c, head-dim slots 16*ks + 8*h .. +7)
+  const __bf16* kp = a.k + b * a.k_sb + g * a.k_sh;
+  const __bf16* vp = a.v + b * a.k_sb + g * a.k_sh;
+  bf16x8 kf[8], vf[8];
+  {
+    const int key = kw0 + c;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (key < a.Sk) {
+        kf[ks] = *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
+        vf[ks] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
+      } else {
+        kf[ks] = bf16x8{};
+        vf[ks] = bf16x8{};
+      }
+    }
+  }
+
+  // query blocks that can see a key of this workgroup, for each head of the group
+  const int qstart = CAUSAL ? max(0, k0 - off) : 0;
+  const int qb_first = qstart / QB;
+  const int n_qb = (a.Sq + QB - 1) / QB;
+  const int per_head = n_qb - qb_first;
+  const int total = a.group * per_head;
+
+  RowCopy cp;
+  cp.init(a.q_ss, wave, lane);
+  const uint32_t q_bytes = (uint32_t)((int64_t)(a.Sq - 1) * a.q_ss * 2 + 256);
+  const uint32_t blk_bytes = (uint32_t)(QB * a.q_ss * 2);
+  auto issue = [&](int s, int st) {
+    const int hq = g * a.group + s / per_head;
+    const int qb = qb_first + s % per_head;
+    const int64_t hoff = b * a.q_sb + hq * a.q_sh;
+    cp.issue(rsrc(a.q + hoff, q_bytes), qbuf + st * TILE, (uint32_t)qb * blk_bytes);
+    cp.issue(rsrc(a.dout + hoff, q_bytes), dobuf + st * TILE, (uint32_t)qb * blk_bytes);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? a.ws_l : a.ws_d) + ((int64_t)b * a.Hq + hq) * a.Sq;
+      float* dst = (wave == 0 ? lbuf : dbuf) + st * QB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src, (uint32_t)a.Sq * 4), (ATTN_LDS void*)dst,
+                                               4, (uint32_t)(qb * QB + lane) * 4, 0, 0, 0);
+    }
+  };
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
+
+  issue(0, 0);
+  for (int s = 0; s < total; ++s) {
+    const int st = s & 1;
+    wait_all();
+    barrier();
+    if (s + 1 < total) issue(s + 1, st ^ 1);
+    const int q0 = (qb_first + s % per_head) * QB;
+    const char* qt = qbuf + st * TILE;
+    const char* dt = dobuf + st * TILE;
+    const float* lb = lbuf + st * QB;
+    const float* db = dbuf + st * QB;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int r0 = q0 + 32 * qs;
+      if (kw0 >= a.Sk) continue;                        // keys past the end
+      if (CAUSAL && kw0 > r0 + 31 + off) continue;     // no row sees these keys
+      const bool mask = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > a.Sk);
+      // S[q][key] and dP[q][key]: accumulator register r of lane (c, h) holds
+      // row 8*(r/4) + 4h + r%4 of the sub-block against key kw0 + c
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(lds_row(qt, 32 * qs + c, 2 * ks + h), kf[ks], sacc);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) pacc = mfma32(lds_row(dt, 32 * qs + c, 2 * ks + h), vf[ks], pacc);
+      float p[16], ds[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 32 * qs + 8 * q4 + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(db + 32 * qs + 8 * q4 + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * q4 + i;
+          float pv = fast_exp2(sacc[r] * a.c - l4[i]);
+          if (mask) {
+            const int row = r0 + 8 * q4 + 4 * h + i, key = kw0 + c;
+            if (key >= a.Sk || (CAUSAL && key > row + off)) pv = 0.f;
+          }
+          p[r] = pv;
+          ds[r] = pv * (pacc[r] - d4[i]);
+        }
+      }
+      // dV[key][d] += sum_q P[q][key] dO[q][d]; dK[key][d] += sum_q dS[q][key] Q[q][d]
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pa = to_bf16x8(p + 8 * t);
+        const bf16x8 da = to_bf16x8(ds + 8 * t);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          dv[n] = mfma32(pa, lds_cols(dt, 32 * qs + 16 * t, 32 * n, lane), dv[n]);
+          dk[n] = mfma32(da, lds_cols(qt, 32 * qs + 16 * t, 32 * n, lane), dk[n]);
+        }
+      }
+    }
+  }
+
+  // register r of lane (c, h), d block n: key kw0 + 8*(r/4) + 4h + r%4, dim 32n + c
+  __bf16* dkp = a.dk + b * a.k_sb + g * a.k_sh;
+  __bf16* dvp = a.dv + b * a.k_sb + g * a.k_sh;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (key < a.Sk) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        dkp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)(dk[n][r] * a.scale);
+        dvp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)dv[n][r];
+      }
+    }
+  }
+}
+
+// ---- dQ --------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int n_qb = (a.Sq + Q_ROWS - 1) / Q_ROWS;
+  const int BH = a.B * a.Hq;
+  int bh, qb;
+  if (CAUSAL) {
+    const int row = blockIdx.x / BH;      // heaviest query blocks first
+    qb = n_qb - 1 - row;
+    bh = xcd_remap(blockIdx.x - row * BH, BH);
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    bh = L / n_qb;
+    qb = L - bh * n_qb;
+  }
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const int g = hq / a.group;
+  const int off = a.Sk - a.Sq;
+  const int q0 = qb * Q_ROWS;
+  const int qw0 = q0 + 32 * wave;         // this wave's first row
+  const int q = qw0 + c;                  // this lane's row (both halves)
+
+  // Q and dO fragments of the wave's rows: B operand of S^T = K Q^T and of
+  // dP^T = V dO^T (lane: row q, head-dim slots 16*ks + 8*h .. +7)
+  const int64_t qoff = b * a.q_sb + hq * a.q_sh;
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (q < a.Sq) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qoff + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
+      df[ks] = *reinterpret_cast<const bf16x8*>(a.dout + qoff + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
+    } else {
+      qf[ks] = bf16x8{};
+      df[ks] = bf16x8{};
+    }
+  }
+  const int64_t srow = ((int64_t)b * a.Hq + hq) * a.Sq;
+  const float l2 = q < a.Sq ? a.ws_l[srow + q] : INFINITY;
+  const float drow = q < a.Sq ? a.ws_d[srow + q] : 0.f;
+
+  const int last_row = min(q0 + Q_ROWS, a.Sq) - 1;
+  const int n_keys = CAUSAL ? min(a.Sk, max(0, last_row + off + 1)) : a.Sk;
+  const int n_kt = (n_keys + KB - 1) / KB;
+  const int wave_last = min(qw0 + 31, a.Sq - 1);
+
+  RowCopy cp;
+  cp.init(a.k_ss, wave, lane);
+  const __bf16* kp = a.k + b * a.k_sb + g * a.k_sh;
+  const __bf16* vp = a.v + b * a.k_sb + g * a.k_sh;
+  const uint32_t k_bytes = (uint32_t)((int64_t)(a.Sk - 1) * a.k_ss * 2 + 256);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kp, k_bytes), rv = rsrc(vp, k_bytes);
+  const uint32_t blk_bytes = (uint32_t)(KB * a.k_ss * 2);
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) dq[n] = f32x16{};
+
+  if (n_kt > 0) {
+    cp.issue(rk, kbuf, 0);
+    cp.issue(rv, vbuf, 0);
+  }
+  for (int t = 0; t < n_kt; ++t) {
+    const int st = t & 1;
+    wait_all();
+    barrier();
+    if (t + 1 < n_kt) {
+      cp.issue(rk, kbuf + (st ^ 1) * TILE, (uint32_t)(t + 1) * blk_bytes);
+      cp.issue(rv, vbuf + (st ^ 1) * TILE, (uint32_t)(t + 1) * blk_bytes);
+    }
+    const char* kt = kbuf + st * TILE;
+    const char* vt = vbuf + st * TILE;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int kr0 = t * KB + 32 * ks2;
+      if (kr0 >= n_keys || qw0 >= a.Sq) continue;
+      if (CAUSAL && kr0 > wave_last + off) continue;   // no row of the wave sees these keys
+      const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > a.Sk);
+      // S^T[key][q] and dP^T[key][q]: register r of lane (c, h) holds key
+      // kr0 + 8*(r/4) + 4h + r%4 against this lane's row q
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(lds_row(kt, 32 * ks2 + c, 2 * ks + h), qf[ks], sacc);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) pacc = mfma32(lds_row(vt, 32 * ks2 + c, 2 * ks + h), df[ks], pacc);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(sacc[r] * a.c - l2);
+        if (mask) {
+          const int key = kr0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= a.Sk || (CAUSAL && key > q + off)) pv = 0.f;
+        }
+        ds[r] = pv * (pacc[r] - drow);
+      }
+      // dQ[q][d] += sum_key dS[q][key] K[key][d]
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 da = to_bf16x8(ds + 8 * u);
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          dq[n] = mfma32(da, lds_cols(kt, 32 * ks2 + 16 * u, 32 * n, lane), dq[n]);
+      }
+    }
+  }
+
+  // register r of lane (c, h), d block n: row qw0 + 8*(r/4) + 4h + r%4, dim 32n + c
+  __bf16* dqp = a.dq + qoff;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = qw0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (row < a.Sq) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) dqp[(int64_t)row * a.q_ss + 32 * n + c] = (__bf16)(dq[n][r] * a.scale);
+    }
+  }
+}
+
+hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
+  const int64_t n_rows16 = ((int64_t)a.Sq + 15) / 16;
+  const int64_t g_kv = (int64_t)a.B * a.Hkv * ((a.Sk + KV_ROWS - 1) / KV_ROWS);
+  const int64_t g_q = (int64_t)a.B * a.Hq * ((a.Sq + Q_ROWS - 1) / Q_ROWS);
+  if (n_rows16 > 0x7fffffff || a.Hq > 65535 || a.B > 65535 || g_kv > 0x7fffffff ||
+      g_q > 0x7fffffff)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_rows16, a.Hq, a.B), dim3(256), 0, stream, a);
+  if (causal) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -74,4 +74,30 @@ struct DecodeArgs {
 int decode_max_splits(int max_blocks);
 hipError_t launch_decode(DecodeArgs a, int num_cus, hipStream_t stream);
 
+// ---- backward ----------------------------------------------------------------
+constexpr int kBwdKvRows = 128;   // keys per dK/dV workgroup
+constexpr int kBwdQRows = 128;    // query rows per dQ workgroup
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;       // forward output
+  const __bf16* dout;    // upstream gradient dO, q's layout
+  const float* lse;      // forward LSE [B, Hq, Sq] (natural log)
+  __bf16* dq;            // q's layout
+  __bf16* dk;            // k's layout
+  __bf16* dv;
+  float* ws_d;           // [B, Hq, Sq] rowsum(dO * O)
+  float* ws_l;           // [B, Hq, Sq] LSE * log2(e), +inf where LSE = -inf
+  int64_t q_sb, q_sh, q_ss;  // element strides (q, o, dout, dq)
+  int64_t k_sb, k_sh, k_ss;  // element strides (k, v, dk, dv)
+  int B, Hq, Hkv, Sq, Sk;
+  int group;             // Hq / Hkv
+  float c;               // scale * log2(e)
+  float scale;
+};
+
+hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream);
+
 }  // namespace attn

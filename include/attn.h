@@ -1,7 +1,7 @@
 /*
  * attn.h - C ABI of the gfx950 (MI355X) exact-attention library (libattn.so).
  *
- * Two operations:
+ * Three operations:
  *
  *   attn_fwd           O = softmax(scale * Q K^T) V, computed tile by tile with
  *                      an online softmax so the score matrix never reaches HBM;
@@ -9,6 +9,8 @@
  *   attn_decode_paged  the same definition for one query row per sequence
  *                      against a paged KV cache, split over the keys, with the
  *                      partial results merged by their log-sum-exps.
+ *   attn_bwd           dQ, dK, dV of the forward for an upstream dO, with the
+ *                      probabilities recomputed from the forward's LSE.
  *
  * Definitions followed (page titles and sections):
  *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
@@ -71,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 3
+#define ATTN_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
@@ -217,6 +219,48 @@ int attn_decode_paged_append(const void* q, const void* k_new, const void* v_new
                              int Hkv, int d, int page_size, int max_blocks_per_seq,
                              int num_pages, float scale, int rounding, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes - device workspace that attn_bwd needs: two fp32
+ * values per query row (the row term D_i = dO_i . O_i and the LSE in log2
+ * units), 8 * B * Hq * Sq bytes.  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq);
+
+/*
+ * attn_bwd - gradients dQ, dK, dV of attn_fwd's O for an upstream gradient
+ * dO, recomputing the probabilities from the forward's LSE instead of storing
+ * them ("IO-aware tiling strategy in FlashAttention-4", backward-pass
+ * paragraph: only the row statistics are kept and S/P are recomputed;
+ * "Reverse engineering Flash Attention 4's proprietary fused attention
+ * kernel", point 2).  What is returned is the gradient of sum(dO * O) with
+ * respect to Q, K and V of the forward's definition (same GQA mapping, causal
+ * alignment and scale); a K/V head's dK and dV are summed over the query
+ * heads that share it.
+ *
+ *   q, k, v      the forward's inputs, as for attn_fwd
+ *   o, lse       the forward's outputs for these inputs (attn_fwd with the
+ *                same arguments; O under any rounding rule)
+ *   dout         bf16, same layout and shape as q
+ *   dq           bf16 output, same layout and shape as q
+ *   dk, dv       bf16 outputs, same layout and shape as k
+ *   workspace    device memory of at least attn_bwd_workspace_bytes(B, Hq, Sq)
+ *                bytes; its contents on entry do not matter
+ *   B, Hq, Hkv, Sq, Sk, d, scale, causal, layout: as for attn_fwd
+ *
+ * Rows that see no key (causal with Sq > Sk) get dQ = 0 and add nothing to dK
+ * and dV.  Products run in bf16 with fp32 accumulation (P and dS rounded to
+ * bf16 to nearest even); the outputs are rounded to bf16 to nearest even.
+ * Size limits (ATTN_ERR_SHAPE): (Sq + 64) * q row stride * 2 and
+ * (Sk + 64) * k row stride * 2 must stay below 2^31 (row stride = heads * 128
+ * elements in BSHD, 128 in BHSD), B and Hq at most 65535.
+ * Returns ATTN_OK or an attn_status error; every check runs before any HIP
+ * call.  Deterministic: no atomics, fixed summation order.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Sk, int d, float scale, int causal, int layout, void* workspace,
+             size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 3
+    assert ea.attn_version() == 4
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -140,6 +140,46 @@ def test_valid_arguments_need_a_gfx950_device():
         assert fwd(rounding=r) == -7
         assert dec(rounding=r) == -7
         assert app(rounding=r) == -7
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8,
+             d=128, scale=0.1, causal=0, layout=0, ws=P, wsb=10 ** 6, stream=None)
+    a.update(kw)
+    return ea.library().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                 a["d"], a["scale"], a["causal"], a["layout"], a["ws"], a["wsb"],
+                                 a["stream"])
+
+
+def test_bwd_workspace_bytes():
+    assert ea.attn_bwd_workspace_bytes(4, 32, 4096) == 8 * 4 * 32 * 4096
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1) == 8
+    assert ea.attn_bwd_workspace_bytes(0, 1, 1) == 0
+    assert ea.attn_bwd_workspace_bytes(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(do=None), -1),
+    (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
+    (dict(B=0), -2), (dict(Sq=0), -2), (dict(Sk=-1), -2), (dict(Hq=3, Hkv=2), -2),
+    (dict(B=65536), -2),
+    (dict(Sk=(1 << 22), Hkv=2, Hq=2, layout=0), -2),   # K/V rows of one head exceed 32-bit offsets
+    (dict(Sq=(1 << 22), Hkv=2, Hq=2, layout=0, wsb=1 << 40), -2),
+    (dict(d=64), -3), (dict(layout=2), -3), (dict(causal=2), -3), (dict(scale=0.0), -3),
+    (dict(scale=float("nan")), -3),
+    (dict(q=P + 8), -4), (dict(dk=P + 2), -4), (dict(lse=P + 4), -4), (dict(do=P + 8), -4),
+    (dict(ws=None), -5), (dict(wsb=8 * 4 * 8 - 1), -5), (dict(ws=P + 4), -5),
+])
+def test_bwd_argument_errors(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_valid_arguments_need_a_gfx950_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert bwd() == -7
 
 
 def test_binding_rejects_unknown_rounding_name():
