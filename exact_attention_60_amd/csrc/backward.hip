@@ -310,8 +310,11 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---- dQ --------------------------------------------------------------------
+// Two workgroups per CU (two waves per SIMD, 64 KB of LDS each): one wave's
+// exponentials and operand reads run under the other's MFMAs.
 template <bool CAUSAL>
-__global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE];
 
