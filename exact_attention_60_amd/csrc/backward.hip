@@ -255,39 +255,69 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       if (kw0 >= a.Sk) continue;                        // keys past the end
       if (CAUSAL && kw0 > r0 + 31 + off) continue;     // no row sees these keys
       const bool mask = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > a.Sk);
+      // Operand reads are issued in batches ahead of the MFMAs that use them
+      // (sched_barrier keeps the compiler from sinking each read next to its
+      // use, which would expose the LDS latency once per MFMA).
+      bf16x8 qa[8], oa[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        qa[ks] = lds_row(qt, 32 * qs + c, 2 * ks + h);
+        oa[ks] = lds_row(dt, 32 * qs + c, 2 * ks + h);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // S[q][key] and dP[q][key]: accumulator register r of lane (c, h) holds
       // row 8*(r/4) + 4h + r%4 of the sub-block against key kw0 + c
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(lds_row(qt, 32 * qs + c, 2 * ks + h), kf[ks], sacc);
+      for (int ks = 0; ks < 8; ++ks) {
+        sacc = mfma32(qa[ks], kf[ks], sacc);
+        pacc = mfma32(oa[ks], vf[ks], pacc);
+      }
+      // column operands of the first half of the dV/dK products, read while
+      // the MFMAs above drain and the exponentials run
+      bf16x8 ocol[2][4], qcol[2][4];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) pacc = mfma32(lds_row(dt, 32 * qs + c, 2 * ks + h), vf[ks], pacc);
+      for (int n = 0; n < 4; ++n) {
+        ocol[0][n] = lds_cols(dt, 32 * qs, 32 * n, lane);
+        qcol[0][n] = lds_cols(qt, 32 * qs, 32 * n, lane);
+      }
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        l4[q4] = *reinterpret_cast<const f32x4*>(lb + 32 * qs + 8 * q4 + 4 * h);
+        d4[q4] = *reinterpret_cast<const f32x4*>(db + 32 * qs + 8 * q4 + 4 * h);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float p[16], ds[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lb + 32 * qs + 8 * q4 + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(db + 32 * qs + 8 * q4 + 4 * h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * q4 + i;
-          float pv = fast_exp2(sacc[r] * a.c - l4[i]);
+          float pv = fast_exp2(sacc[r] * a.c - l4[q4][i]);
           if (mask) {
             const int row = r0 + 8 * q4 + 4 * h + i, key = kw0 + c;
             if (key >= a.Sk || (CAUSAL && key > row + off)) pv = 0.f;
           }
           p[r] = pv;
-          ds[r] = pv * (pacc[r] - d4[i]);
+          ds[r] = pv * (pacc[r] - d4[q4][i]);
         }
       }
-      // dV[key][d] += sum_q P[q][key] dO[q][d]; dK[key][d] += sum_q dS[q][key] Q[q][d]
+      // dV[key][d] += sum_q P[q][key] dO[q][d]; dK[key][d] += sum_q dS[q][key] Q[q][d];
+      // the second half's column operands are read under the first half's MFMAs
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        ocol[1][n] = lds_cols(dt, 32 * qs + 16, 32 * n, lane);
+        qcol[1][n] = lds_cols(qt, 32 * qs + 16, 32 * n, lane);
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 pa = to_bf16x8(p + 8 * t);
         const bf16x8 da = to_bf16x8(ds + 8 * t);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          dv[n] = mfma32(pa, lds_cols(dt, 32 * qs + 16 * t, 32 * n, lane), dv[n]);
-          dk[n] = mfma32(da, lds_cols(qt, 32 * qs + 16 * t, 32 * n, lane), dk[n]);
+          dv[n] = mfma32(pa, ocol[t][n], dv[n]);
+          dk[n] = mfma32(da, qcol[t][n], dk[n]);
         }
       }
     }
@@ -396,11 +426,20 @@ void bwd_dq_kernel(BwdArgs a) {
       const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > a.Sk);
       // S^T[key][q] and dP^T[key][q]: register r of lane (c, h) holds key
       // kr0 + 8*(r/4) + 4h + r%4 against this lane's row q
+      // K rows are read as one batch, and the V rows go out before the S^T
+      // MFMAs so that they arrive under them
+      bf16x8 ka[8], va[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) ka[ks] = lds_row(kt, 32 * ks2 + c, 2 * ks + h);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) va[ks] = lds_row(vt, 32 * ks2 + c, 2 * ks + h);
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(lds_row(kt, 32 * ks2 + c, 2 * ks + h), qf[ks], sacc);
+      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(ka[ks], qf[ks], sacc);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) pacc = mfma32(lds_row(vt, 32 * ks2 + c, 2 * ks + h), df[ks], pacc);
+      for (int ks = 0; ks < 8; ++ks) pacc = mfma32(va[ks], df[ks], pacc);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
