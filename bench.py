@@ -151,19 +151,21 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
     f_write = copy_bytes / (float(wmap[cref["Dispatch_Id"]]["Counter_Value"]) * 1024)
     per = {}
     for r in fetch:
-        key = ("prefill_kernel" if "prefill_kernel" in r["Kernel_Name"] else
-               "decode_partial_kernel" if "decode_partial" in r["Kernel_Name"] else
-               "decode_merge_kernel" if "decode_merge" in r["Kernel_Name"] else None)
+        name = r["Kernel_Name"]
+        key = next((kk for kk in ("prefill_kernel", "decode_partial_kernel", "decode_merge_kernel",
+                                  "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
+                    if kk in name), None)
         if key is None:
             continue
         fb = float(r["Counter_Value"]) * 1024 * f_fetch
         wb = float(wmap[r["Dispatch_Id"]]["Counter_Value"]) * 1024 * f_write
         per.setdefault(key, []).append((fb, wb))
     srcs = {"prefill_kernel": "prefill.hip", "decode_partial_kernel": "decode.hip",
-            "decode_merge_kernel": "decode.hip"}
+            "decode_merge_kernel": "decode.hip", "bwd_prep_kernel": "backward.hip",
+            "bwd_dkdv_kernel": "backward.hip", "bwd_dq_kernel": "backward.hip"}
     traffic = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
                         "dispatch), each scaled by the reading of a 1 GiB device copy; prefill "
-                        "on mha_prefill_b4_h32_s4096_bhsd, decode on "
+                        "and backward on mha_prefill_b4_h32_s4096_bhsd, decode on "
                         "paged_decode_b32_hq32_hkv8_len4096_page16",
                "fetch_scale": f_fetch, "write_scale": f_write,
                "commands": [command["fetch"], command["write"]]}
@@ -221,6 +223,16 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
             [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true>"),
              wl_row("diffusion_self_b2_h12_s32760_bshd", "prefill_kernel<false>"),
              wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false>")], []),
+        "backward_kernels__mha_b4_h32_s4096_bhsd_and_causal_gqa_s8192.md": (
+            "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
+            "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
+            [wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_prep_kernel"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<false>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dkdv_kernel<true>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dq_kernel<true>")],
+            ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]),
     }
     for fname, (title, rows, tkeys) in files.items():
         body = [title, ""] + head + rows
@@ -285,9 +297,18 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         ms = time_calls(run, steps, 2, torch)
         fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 128 / (2 if p.causal else 1)
         tf = fl / (ms * 1e-3) / 1e12
-        res.append({"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
-                    "TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                    "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+        ent = {"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
+               "TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+               "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}
+        if p.name == "mha_prefill_b4_h32_s4096_bhsd":
+            # HBM bytes the three kernels moved per call (counter passes), against the
+            # algorithmic Q, K, V, O, dO, LSE read once and dQ, dK, dV written once
+            src_b = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "backward.hip")
+            parts = [traffic_from_profiles(kk, src_b) for kk in
+                     ("bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")]
+            ent["algorithmic_bytes"] = 8 * q.numel() * 2 + 4 * p.B * p.Hq * p.Sq
+            ent["traffic"] = None if None in parts else sum(parts)
+        res.append(ent)
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
     return res
@@ -357,8 +378,20 @@ def main():
                                                  [(f"mha_prefill_b4_h32_s4096_bhsd_{m}", xs)
                                                   for m in ROUNDING_MODES] +
                                                  [("diffusion_self_b2_h12_s32760_bshd", xs),
-                                                  ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs)],
-                        "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs)],
+                                                  ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs),
+                                                  ("mha_prefill_b4_h32_s4096_bhsd_backward_fwd", 1)],
+                        "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs),
+                                                 ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                  "_backward_fwd", 1)],
+                        "bwd_prep_kernel": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),
+                                            ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
+                                             xs)],
+                        "bwd_dkdv_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs)],
+                        "bwd_dq_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs)],
+                        "bwd_dkdv_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                   "_backward", xs)],
+                        "bwd_dq_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                 "_backward", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
                                                    st + wu),
                                                   ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
@@ -429,6 +462,9 @@ def main():
             prefill(i)
         for i in range(3):
             decode(i)
+        do = to_dev(gen.output_grad(p, 2))
+        for i in range(3):
+            ea.attn_bwd(q, k, v, o, lse, do, causal=False, scale=p.scale, layout="bhsd")
         torch.cuda.synchronize()
         print(json.dumps({"counters_run": True, "copy_bytes": n}))
         return
