@@ -31,7 +31,7 @@ BF16_QNAN = np.uint16(0x7FC0)
 
 # stream ids for default_rng([seed, stream])
 (_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX, _S_EQK, _S_EQV, _S_KNEW,
- _S_VNEW, _S_DO) = range(13)
+ _S_VNEW, _S_DO, _S_VLENS) = range(14)
 
 BSHD = 0
 BHSD = 1
@@ -276,6 +276,51 @@ def output_grad(p: Prefill, seed=0, dist="normal") -> np.ndarray:
     return f32_to_bf16_bits(_draw(dist, seed, _S_DO, layout_shape(p.layout, p.B, p.Hq, p.Sq)))
 
 
+@dataclass
+class Varlen:
+    """Packed sequences: q [total_q, Hq, D], k/v [total_k, Hkv, D] bf16 bits;
+    sequence b is rows cu_q[b]..cu_q[b+1]-1 of q and cu_k[b]..cu_k[b+1]-1 of
+    k/v (int32 offsets)."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+    Hq: int
+    Hkv: int
+    causal: bool
+    scale: float
+    name: str = ""
+
+    @property
+    def B(self) -> int:
+        return len(self.cu_q) - 1
+
+    @property
+    def max_q(self) -> int:
+        return max(1, int(np.diff(self.cu_q).max()))
+
+    @property
+    def flops(self) -> float:
+        """4*Hq*Sq_b*Sk_b*D summed over the sequences, halved when causal."""
+        f = 4.0 * self.Hq * float(np.sum(np.diff(self.cu_q).astype(np.float64) *
+                                         np.diff(self.cu_k))) * D
+        return f / 2 if self.causal else f
+
+
+def varlen_inputs(lens_q, lens_k, Hq, Hkv, *, causal=False, seed=0, name="") -> Varlen:
+    """Packed sequences with the given query and key lengths; Q, K, V iid
+    N(0, 1)."""
+    lens_q = np.asarray(lens_q, np.int64)
+    lens_k = np.asarray(lens_k, np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = f32_to_bf16_bits(_normal(seed, _S_Q, (int(cu_q[-1]), Hq, D)))
+    k = f32_to_bf16_bits(_normal(seed, _S_K, (int(cu_k[-1]), Hkv, D)))
+    v = f32_to_bf16_bits(_normal(seed, _S_V, (int(cu_k[-1]), Hkv, D)))
+    return Varlen(q, k, v, cu_q, cu_k, Hq, Hkv, bool(causal), 1.0 / math.sqrt(D), name=name)
+
+
 # --------------------------------------------------------------------------
 # The named workloads (d = 128, bf16, scale = 1/sqrt(128) throughout).
 
@@ -318,3 +363,12 @@ def config5(seed=5):
     """Paged split-KV decode B=32, Hq=32, Hkv=8, lens ~ U{1..4096}."""
     return decode_inputs(32, 32, 8, max_len=4096, seed=seed,
                          name="paged_decode_b32_hq32_hkv8_len4096_page16")
+
+
+def varlen_causal_gqa(seed=6):
+    """Packed batch of 16 causal GQA sequences (Hq=32, Hkv=8), self attention
+    with lengths iid U{1..8192}: a stand-in for a batch of prompts of mixed
+    lengths without padding."""
+    lens = _rng(seed, _S_VLENS).integers(1, 8193, size=16)
+    return varlen_inputs(lens, lens, 32, 8, causal=True, seed=seed,
+                         name="varlen_causal_gqa_b16_hq32_hkv8_len8192")

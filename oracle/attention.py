@@ -23,6 +23,8 @@ What it computes, and where the pages define it:
 * LSE is the natural log of the softmax denominator over visible keys,
   m + ln(l), the statistics the pages say are kept ("Reverse engineering ...",
   point 2; "IO-aware tiling ...", backward-pass paragraph).
+* Packed sequences (variable-length batches): each sequence is its own
+  problem of the definition above, with its own lengths.
 * Paged decode: K/V of sequence b live in 16-token pages listed by an int32
   block table ("Engineering the FlashAttention-4 kernel port to ROCm",
   multi-query section, paged KV cache); the oracle gathers them into a dense
@@ -180,6 +182,38 @@ def attention_sampled(q_bits, k_bits, v_bits, B, Hq, Hkv, Sq, Sk, scale, causal,
     return o, lse
 
 
+def attention_varlen(q_bits, k_bits, v_bits, cu_q, cu_k, Hkv, scale, causal, workers=None):
+    """Oracle for packed sequences of different lengths: sequence b is query
+    rows cu_q[b]..cu_q[b+1]-1 of q [total_q, Hq, D] against key rows
+    cu_k[b]..cu_k[b+1]-1 of k, v [total_k, Hkv, D], each sequence being one
+    problem of the definition above with its own lengths (causal alignment
+    per sequence).  Variable-length batching is what the MoonMath page lists
+    among its kernel's limits ("MoonMath AI open-sources a HIP attention
+    kernel for AMD MI300X that beats AITER v3", limitations paragraph).
+    Returns (o [total_q, Hq, D], lse [Hq, total_q]) float64."""
+    total_q, Hq, d = q_bits.shape
+    sc = scale_as_f32(scale)
+    o = np.zeros((total_q, Hq, d), np.float64)
+    lse = np.full((Hq, total_q), -np.inf)
+
+    def job(b):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        sq, sk = q1 - q0, k1 - k0
+        if sq == 0:
+            return
+        nv = np.array([visible_keys(i, sq, sk, causal) for i in range(sq)], np.int64)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            oo, ll = attend_rows(bf16_to_f64(q_bits[q0:q1, h]), bf16_to_f64(k_bits[k0:k1, g]),
+                                 bf16_to_f64(v_bits[k0:k1, g]), sc, nv)
+            o[q0:q1, h] = oo
+            lse[h, q0:q1] = ll
+
+    _run(job, list(range(len(cu_q) - 1)), workers)
+    return o, lse
+
+
 def gather_pages(pool_bits, block_table, seq_len, b, g):
     """Dense [len, D] view of KV head g of sequence b from a paged pool
     [num_pages, 16, Hkv, D]: token t lives in page block_table[b, t // 16],
@@ -261,6 +295,6 @@ def flops_prefill(B, Hq, Sq, Sk, d, causal):
 
 
 __all__ = ["bf16_to_f64", "scale_as_f32", "kv_head_of", "visible_keys", "scores",
-           "row_softmax", "attend_rows", "attention", "attention_sampled",
+           "row_softmax", "attend_rows", "attention", "attention_sampled", "attention_varlen",
            "gather_pages", "decode_paged", "append_token", "decode_paged_append",
            "flops_prefill"]
