@@ -13,6 +13,8 @@ are already resident in HBM:
 * the other prefill workloads (causal GQA B=8 S=8192, diffusion-style self
   attention S=32760 and its cross attention against 512 keys), timed the
   same way and reported beside the headline (skip with --no-extra);
+* packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
+  U{1..8192}, reported beside the headline;
 * the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads,
   reported beside the headline too.
 
@@ -222,7 +224,8 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
             "# prefill_kernel on the causal GQA and diffusion-style workloads",
             [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true>"),
              wl_row("diffusion_self_b2_h12_s32760_bshd", "prefill_kernel<false>"),
-             wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false>")], []),
+             wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false>"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192", "prefill_kernel<true>")], []),
         "backward_kernels__mha_b4_h32_s4096_bhsd_and_causal_gqa_s8192.md": (
             "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
             "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
@@ -268,6 +271,26 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
                     "flop": p.flops, "TFLOP/s": round(tf, 2),
                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, o, lse
+    # packed sequences of mixed lengths (attn_fwd_varlen)
+    pv = gen.varlen_causal_gqa()
+    log(f"timing {pv.name}")
+    q, k, v = to_dev(pv.q), to_dev(pv.k), to_dev(pv.v)
+    cq = torch.from_numpy(pv.cu_q).to(dev)
+    ck = torch.from_numpy(pv.cu_k).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((pv.Hq, q.shape[0]), dtype=torch.float32, device=dev)
+
+    def run_v(_i):
+        ea.attn_fwd_varlen(q, k, v, cq, ck, pv.max_q, causal=True, scale=pv.scale, out=o, lse=lse)
+
+    ms = time_calls(run_v, steps, 2, torch)
+    tf = pv.flops / (ms * 1e-3) / 1e12
+    res.append({"workload": pv.name, "B": pv.B, "Hq": pv.Hq, "Hkv": pv.Hkv,
+                "total_tokens": int(pv.cu_q[-1]), "max_seqlen": pv.max_q, "causal": True,
+                "layout": "packed [tokens, H, 128]", "ms_per_call": round(ms, 4),
+                "flop": pv.flops, "TFLOP/s": round(tf, 2),
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    del q, k, v, o, lse
     torch.cuda.empty_cache()
     return res
 
@@ -381,6 +404,7 @@ def main():
                                                   ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs),
                                                   ("mha_prefill_b4_h32_s4096_bhsd_backward_fwd", 1)],
                         "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs),
+                                                 ("varlen_causal_gqa_b16_hq32_hkv8_len8192", xs),
                                                  ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                   "_backward_fwd", 1)],
                         "bwd_prep_kernel": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),

@@ -11,6 +11,7 @@ library is not built the binding raises instead of computing anything itself.
     o, lse = attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table,
                                       seq_lens)   # writes the new rows into the caches
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bshd")
+    o, lse = attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)  # packed
 
 ``rounding`` is the rule of the final fp32 -> bf16 conversion of O: "rtne"
 (nearest, ties to even; the plain entry points), "rtna" (nearest, ties away
@@ -39,7 +40,7 @@ STATUS = {
 }
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_decode_workspace_bytes", "attn_decode_paged",
+EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_varlen", "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
            "attn_bwd", "attn_status_string", "attn_version")
 
@@ -65,6 +66,9 @@ def library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd_rounded.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
         lib.attn_fwd_rounded.restype = i
+        lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
+                                        vp]
+        lib.attn_fwd_varlen.restype = i
         lib.attn_decode_workspace_bytes.argtypes = [i, i, i]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
@@ -171,6 +175,42 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
+                    causal: bool = False, scale: float | None = None, rounding: str = "rtne",
+                    out=None, lse=None, stream=None):
+    """Attention forward over packed sequences.  q: [total_q, Hq, 128];
+    k, v: [total_k, Hkv, 128]; cu_seqlens_q / cu_seqlens_k: int32 GPU tensors
+    [B + 1] of row offsets; max_seqlen_q: the longest query length (a host
+    int).  Returns (o bf16 [total_q, Hq, 128], lse fp32 [Hq, total_q])."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(n, t)
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{n} must be a contiguous 1-D int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = library().attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), cu_seqlens_q.data_ptr(),
+                                   cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
+                                   int(max_seqlen_q), d, float(scale), int(bool(causal)),
+                                   _rounding_code(rounding), _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_varlen")
+    return out, lse
+
+
 def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: float | None = None,
                       rounding: str = "rtne", out=None, lse=None, workspace=None, stream=None,
                       k_new=None, v_new=None):
@@ -272,7 +312,7 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
     return dq, dk, dv
 
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append",
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append",
            "attn_decode_workspace_bytes", "attn_status_string",
            "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

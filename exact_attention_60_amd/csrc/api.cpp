@@ -98,6 +98,55 @@ int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float
   if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
   a.c = scale * 1.4426950408889634f;
   a.rounding = rounding;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+  const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
+                    int Hkv, int total_q, int total_k, int max_seqlen_q, int d, float scale,
+                    int causal, int rounding, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 ||
+      Hq % Hkv != 0)
+    return ATTN_ERR_SHAPE;
+  if (d != attn::kHeadDim || (causal != 0 && causal != 1) || !scale_ok(scale) ||
+      !rounding_ok(rounding))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return ATTN_ERR_ALIGN;
+  const int64_t D = attn::kHeadDim;
+  attn::PrefillArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  // packed [total, H, 128]: the batch stride is unused (rows come from the offsets)
+  a.q_sb = 0; a.q_sh = D; a.q_ss = (int64_t)Hq * D;
+  a.k_sb = 0; a.k_sh = D; a.k_ss = (int64_t)Hkv * D;
+  // the K/V rows of one sequence are addressed with 32-bit byte offsets
+  if ((int64_t)(total_k - 1) * a.k_ss * 2 + 256 > INT32_MAX) return ATTN_ERR_SHAPE;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.Sq = max_seqlen_q;
+  a.Sk = 0;
+  a.group = Hq / Hkv;
+  a.n_qt = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
+  a.c = scale * 1.4426950408889634f;
+  a.rounding = rounding;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;

@@ -30,6 +30,12 @@ struct PrefillArgs {
   int n_qt;                  // ceil(Sq / kPrefillBM)
   float c;                   // scale * log2(e)
   int rounding;              // kRoundRTNE / kRoundRTNA / kRoundRTZ for O
+  // packed sequences (null cu_q: dense batch): sequence b is rows
+  // cu_q[b] .. cu_q[b+1]-1 of q/o and cu_k[b] .. cu_k[b+1]-1 of k/v; Sq is
+  // then the longest query length, LSE is [Hq, total_q]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);

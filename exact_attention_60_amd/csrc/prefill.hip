@@ -83,6 +83,18 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
 }
 
+// Workgroups are dealt to the 8 XCDs round robin (XCD = i % 8).  Index i of
+// a row of B*Hq workgroups goes to K/V head group (i % 8) + 8 * (i / 8 / G),
+// query head (i / 8) % G of that group, so the G query heads of a group share
+// an XCD (and its L2) and consecutive groups -- the K/V heads of one
+// sequence -- land on different XCDs.  Needs the group count to be a
+// multiple of 8, else i is kept.
+__device__ __forceinline__ int spread_groups(int i, int G, int n_groups) {
+  if (n_groups & 7) return i;
+  const int x = i & 7, j = i >> 3;
+  return (x + 8 * (j / G)) * G + (j - (j / G) * G);
+}
+
 // Asynchronous copy of a wave's 16 rows of one K or V tile from HBM into LDS
 // (buffer_load_dwordx4 ... lds).  Each instruction moves 1 KB: lane i lands
 // at byte 16*i, i.e. row +i/16, physical chunk i%16, so it fetches the
@@ -97,7 +109,7 @@ struct TileLoader {
                        int lane) {
     wave &= 3;
     const uint32_t ss = (uint32_t)(k_ss * 2);
-    const uint32_t nrec = (uint32_t)((int64_t)(Sk - 1) * ss + 256);
+    const uint32_t nrec = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * ss + 256) : 0u;
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)nrec, 0x00020000);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)nrec, 0x00020000);
     tile_bytes = ss * BN;
@@ -498,10 +510,14 @@ void prefill_kernel(PrefillArgs a) {
   // ---- which (batch, head, query tile) this workgroup computes
   const int BH = a.B * a.Hq;
   int bh, qt;
-  if (CAUSAL) {
+  if (CAUSAL || a.cu_q) {
     const int row = blockIdx.x / BH;     // heaviest query tiles first
     qt = a.n_qt - 1 - row;
-    bh = xcd_remap(blockIdx.x - row * BH, BH);
+    // packed sequences of different lengths: the heads of one sequence are
+    // spread over the XCDs (a K/V head's query heads kept together), so that
+    // no XCD is left with the longest sequences
+    bh = a.cu_q ? spread_groups(blockIdx.x - row * BH, a.group, a.B * a.Hkv)
+                : xcd_remap(blockIdx.x - row * BH, BH);
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     bh = L / a.n_qt;
@@ -510,23 +526,41 @@ void prefill_kernel(PrefillArgs a) {
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hk = hq / a.group;
-  const __bf16* __restrict__ qp = a.q + b * a.q_sb + hq * a.q_sh;
-  const __bf16* kp = a.k + b * a.k_sb + hk * a.k_sh;
-  const __bf16* vp = a.v + b * a.k_sb + hk * a.k_sh;
-
+  // this sequence's rows: the whole [B, ...] batch entry, or (packed
+  // sequences) rows cu_q[b] .. cu_q[b+1]-1 of q and cu_k[b] .. cu_k[b+1]-1 of
+  // k/v, offsets clamped to the packed sizes
+  int Sq = a.Sq, Sk = a.Sk;
+  int64_t qbase = b * a.q_sb, kbase = b * a.k_sb;
+  int64_t lse_base = (int64_t)(b * a.Hq + hq) * a.Sq;
+  if (a.cu_q) {
+    const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
+    const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
+    const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
+    const int k_hi = min(max(a.cu_k[b + 1], k_lo), a.total_k);
+    Sq = min(q_hi - q_lo, a.Sq);         // a.Sq is the longest query length here
+    Sk = k_hi - k_lo;
+    qbase = (int64_t)q_lo * a.q_ss;
+    kbase = (int64_t)k_lo * a.k_ss;
+    lse_base = (int64_t)hq * a.total_q + q_lo;
+  }
   const int q0 = qt * BM;
-  x.off = a.Sk - a.Sq;                   // causal: key j visible iff j <= i + off
-  x.Sk = a.Sk;
+  if (q0 >= Sq) return;                  // whole workgroup: past this sequence's rows
+  const __bf16* __restrict__ qp = a.q + qbase + hq * a.q_sh;
+  const __bf16* kp = a.k + kbase + hk * a.k_sh;
+  const __bf16* vp = a.v + kbase + hk * a.k_sh;
+
+  x.off = Sk - Sq;                       // causal: key j visible iff j <= i + off
+  x.Sk = Sk;
   x.c = a.c;
-  const int last_row = min(q0 + BM, a.Sq) - 1;
-  int n_keys = a.Sk;
-  if (CAUSAL) n_keys = min(a.Sk, max(0, last_row + x.off + 1));
+  const int last_row = min(q0 + BM, Sq) - 1;
+  int n_keys = Sk;
+  if (CAUSAL) n_keys = min(Sk, max(0, last_row + x.off + 1));
   x.n_tiles = (n_keys + BN - 1) / BN;
   // 32-row blocks interleaved between the groups: SIMD s holds blocks 2s, 2s+1
   const int rb = 2 * (x.wave & 3) + x.group;
   w.first = q0 + 32 * rb;
-  w.last = min(w.first + 31, a.Sq - 1);
-  x.ld.init(kp, vp, a.k_ss, a.Sk, x.wave, lane);
+  w.last = min(w.first + 31, Sq - 1);
+  x.ld.init(kp, vp, a.k_ss, Sk, x.wave, lane);
 
   // ---- per-lane LDS offsets
   // K operand (A of S^T): row kb*32 + l32, chunk 2*ks + hi
@@ -560,7 +594,7 @@ void prefill_kernel(PrefillArgs a) {
     const int row = w.first + w.l32;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if (row < a.Sq)
+      if (row < Sq)
         w.qf[ks] = *(const bf16x8*)(qp + (int64_t)row * a.q_ss + 16 * ks + 8 * w.hi);
       else
         w.qf[ks] = bf16x8{};
@@ -597,16 +631,16 @@ void prefill_kernel(PrefillArgs a) {
       }
   });
   wait_lds();
-  __bf16* ob = a.o + b * a.q_sb + hq * a.q_sh;
+  __bf16* ob = a.o + qbase + hq * a.q_sh;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int rr = 4 * k + (lane >> 4), cc = lane & 15;
     const u32x4 v = *(const u32x4*)(st + tile_off(rr, cc));
-    if (w.first + rr < a.Sq) *(u32x4*)(ob + (int64_t)(w.first + rr) * a.q_ss + 8 * cc) = v;
+    if (w.first + rr < Sq) *(u32x4*)(ob + (int64_t)(w.first + rr) * a.q_ss + 8 * cc) = v;
   }
-  if (row < a.Sq && w.hi == 0) {
+  if (row < Sq && w.hi == 0) {
     const float lse = (l > 0.f) ? (w.m_use + __log2f(l)) * kLn2 : -INFINITY;
-    a.lse[((int64_t)(b * a.Hq + hq)) * a.Sq + row] = lse;
+    a.lse[lse_base + row] = lse;
   }
 }
 

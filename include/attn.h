@@ -11,6 +11,7 @@
  *                      partial results merged by their log-sum-exps.
  *   attn_bwd           dQ, dK, dV of the forward for an upstream dO, with the
  *                      probabilities recomputed from the forward's LSE.
+ * attn_fwd_varlen is attn_fwd over packed sequences of different lengths.
  *
  * Definitions followed (page titles and sections):
  *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 4
+#define ATTN_VERSION 5
 
 typedef enum {
   ATTN_OK = 0,
@@ -134,6 +135,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                      int layout, int rounding, void* stream);
+
+/*
+ * attn_fwd_varlen - attn_fwd over a batch of packed sequences of different
+ * lengths (variable-length batching, which the MoonMath page lists among what
+ * its kernel lacks: "MoonMath AI open-sources a HIP attention kernel for AMD
+ * MI300X that beats AITER v3", limitations paragraph).  Sequence b is query
+ * rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1; each sequence is one attn_fwd problem of its own
+ * lengths (causal alignment, empty-row rule and GQA mapping as for attn_fwd).
+ *
+ *   q     bf16 [total_q, Hq, d] (packed rows, d innermost)
+ *   k, v  bf16 [total_k, Hkv, d]
+ *   o     bf16 output [total_q, Hq, d]
+ *   lse   fp32 output [Hq, total_q]
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [B + 1], 4-byte aligned:
+ *         0 = cu[0] <= cu[1] <= ... <= cu[B] = total; a sequence may be
+ *         empty; one with keys but no query rows writes nothing, one with
+ *         query rows but no keys gets O = 0 and LSE = -inf
+ *   max_seqlen_q  >= every query length (it sizes the launch; rows of a
+ *         longer sequence past it are not written)
+ *   B, Hq, Hkv, total_q, total_k, max_seqlen_q >= 1, Hq % Hkv == 0, d == 128
+ *   rounding  one of ATTN_ROUND_* for O
+ *
+ * The offsets live on the device and are not read by the host; out-of-order
+ * or out-of-range values are clamped to [0, total] (memory-safe, results for
+ * such sequences unspecified).  Size limits (ATTN_ERR_SHAPE):
+ * (total_k - 1) * Hkv * 256 + 256 < 2^31 and B * Hq * ceil(max_seqlen_q / 256)
+ * < 2^31.  Other statuses as for attn_fwd_rounded.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
+                    int Hkv, int total_q, int total_k, int max_seqlen_q, int d, float scale,
+                    int causal, int rounding, void* stream);
 
 /*
  * attn_decode_workspace_bytes - device workspace that attn_decode_paged needs

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 4
+    assert ea.attn_version() == 5
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -180,6 +180,35 @@ def test_bwd_valid_arguments_need_a_gfx950_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert bwd() == -7
+
+
+def fwd_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=3, Hq=4, Hkv=2, tq=100, tk=90, maxq=50,
+             d=128, scale=0.1, causal=1, rounding=0, stream=None)
+    a.update(kw)
+    return ea.library().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"],
+                                        a["ck"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"],
+                                        a["maxq"], a["d"], a["scale"], a["causal"],
+                                        a["rounding"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(cq=None), -1), (dict(ck=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(tq=0), -2), (dict(tk=0), -2), (dict(maxq=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(tk=(1 << 21) + 2, Hkv=4), -2),
+    (dict(d=64), -3), (dict(causal=2), -3), (dict(scale=0.0), -3), (dict(rounding=3), -3),
+    (dict(q=P + 8), -4), (dict(o=P + 2), -4), (dict(cq=P + 2), -4), (dict(ck=P + 1), -4),
+])
+def test_fwd_varlen_argument_errors(kw, code):
+    assert fwd_varlen(**kw) == code
+
+
+def test_fwd_varlen_valid_arguments_need_a_gfx950_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert fwd_varlen() == -7
+    assert fwd_varlen(cq=P + 4, ck=P + 8) == -7   # 4-byte alignment is enough for offsets
 
 
 def test_binding_rejects_unknown_rounding_name():
