@@ -142,6 +142,102 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 
+// ---- pieces of the dK/dV loop (lane (c, h) = (lane % 32, lane / 32)) ----
+
+// A operands of S = Q K^T and dP = dO V^T: Q and dO row `row`, head-dim
+// slots 16*ks + 8*h .. +7
+__device__ __forceinline__ void read_rows(bf16x8 (&qa)[8], bf16x8 (&oa)[8], const char* qt,
+                                          const char* dt, int row, int h) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qa[ks] = lds_row(qt, row, 2 * ks + h);
+    oa[ks] = lds_row(dt, row, 2 * ks + h);
+  }
+}
+// S and dP of one 32-row sub-block against the wave's 32 keys
+__device__ __forceinline__ void mfma_sdp(f32x16& s, f32x16& p, const bf16x8 (&qa)[8],
+                                         const bf16x8 (&oa)[8], const bf16x8 (&kf)[8],
+                                         const bf16x8 (&vf)[8]) {
+  s = f32x16{};
+  p = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    s = mfma32(qa[ks], kf[ks], s);
+    p = mfma32(oa[ks], vf[ks], p);
+  }
+}
+// B operands of dV += P^T dO and dK += dS^T Q for a sub-block starting at
+// tile row r32: dO and Q columns, both halves of the 32 rows
+__device__ __forceinline__ void read_cols(bf16x8 (&oc)[2][4], bf16x8 (&qc)[2][4], const char* qt,
+                                          const char* dt, int r32, int lane) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      oc[t][n] = lds_cols(dt, r32 + 16 * t, 32 * n, lane);
+      qc[t][n] = lds_cols(qt, r32 + 16 * t, 32 * n, lane);
+    }
+}
+// log2-LSE and D of the 16 rows a lane's accumulator registers hold
+__device__ __forceinline__ void read_rowvals(f32x4 (&l4)[4], f32x4 (&d4)[4], const float* lb,
+                                             const float* db, int r32, int h) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    l4[q4] = *reinterpret_cast<const f32x4*>(lb + r32 + 8 * q4 + 4 * h);
+    d4[q4] = *reinterpret_cast<const f32x4*>(db + r32 + 8 * q4 + 4 * h);
+  }
+}
+// P = exp2(S*c - L) and dS = P (dP - D), rounded to bf16 as the A operands of
+// the dV and dK products.  With MASK, entries whose key is past the end or
+// (causal) past the row's diagonal get P = 0: row0 is the global row of
+// register 0 (4h included), key the lane's key.
+template <bool MASK>
+__device__ __forceinline__ void softmax_grad(bf16x8 (&pa)[2], bf16x8 (&da)[2], const f32x16& s,
+                                             const f32x16& p, const f32x4 (&l4)[4],
+                                             const f32x4 (&d4)[4], float c, int row0, int key,
+                                             int Sk, int off, int causal) {
+  float pv[16], dv[16];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q4 + i;
+      float x = fast_exp2(s[r] * c - l4[q4][i]);
+      if (MASK) {
+        const int row = row0 + 8 * q4 + i;
+        if (key >= Sk || (causal && key > row + off)) x = 0.f;
+      }
+      pv[r] = x;
+      dv[r] = x * (p[r] - d4[q4][i]);
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    pa[t] = to_bf16x8(pv + 8 * t);
+    da[t] = to_bf16x8(dv + 8 * t);
+  }
+}
+// dV += P^T dO, dK += dS^T Q for one sub-block
+__device__ __forceinline__ void mfma_dvdk(f32x16 (&dv)[4], f32x16 (&dk)[4], const bf16x8 (&pa)[2],
+                                          const bf16x8 (&da)[2], const bf16x8 (&oc)[2][4],
+                                          const bf16x8 (&qc)[2][4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      dv[n] = mfma32(pa[t], oc[t][n], dv[n]);
+      dk[n] = mfma32(da[t], qc[t][n], dk[n]);
+    }
+}
+// Scheduling request for the region since the last sched_barrier: 16 MFMAs
+// each followed by up to 6 VALU instructions.
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+}
+
 }  // namespace
 
 // ---- D = rowsum(dO * O) and LSE in log2 units --------------------------------
@@ -249,77 +345,73 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     const char* dt = dobuf + st * TILE;
     const float* lb = lbuf + st * QB;
     const float* db = dbuf + st * QB;
+    // which 32-row sub-blocks of this block see some of the wave's keys, and
+    // whether any entry of them needs the mask (key tail or causal diagonal)
+    bool act[2], msk[2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int r0 = q0 + 32 * qs;
-      if (kw0 >= a.Sk) continue;                        // keys past the end
-      if (CAUSAL && kw0 > r0 + 31 + off) continue;     // no row sees these keys
-      const bool mask = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > a.Sk);
-      // Operand reads are issued in batches ahead of the MFMAs that use them
-      // (sched_barrier keeps the compiler from sinking each read next to its
-      // use, which would expose the LDS latency once per MFMA).
-      bf16x8 qa[8], oa[8];
+      act[qs] = kw0 < a.Sk && !(CAUSAL && kw0 > r0 + 31 + off);
+      msk[qs] = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > a.Sk);
+    }
+    if (act[0] && act[1] && !msk[0] && !msk[1]) {
+      // Both sub-blocks whole: software-pipelined, so that each block of
+      // MFMAs has independent VALU work beside it (the wave's VALU
+      // instructions issue while its MFMAs execute).  Order: S, dP of
+      // sub-block 0 | S, dP of 1 beside the softmax gradient of 0 | dV, dK of
+      // 0 beside the softmax gradient of 1 | dV, dK of 1.
+      bf16x8 qa[8], oa[8], qa1[8], oa1[8];
+      read_rows(qa, oa, qt, dt, c, h);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s0, p0, s1, p1;
+      mfma_sdp(s0, p0, qa, oa, kf, vf);
+      read_rows(qa1, oa1, qt, dt, 32 + c, h);
+      bf16x8 oc0[2][4], qc0[2][4];
+      read_cols(oc0, qc0, qt, dt, 0, lane);
+      f32x4 l0[4], d0[4], l1[4], d1[4];
+      read_rowvals(l0, d0, lb, db, 0, h);
+      read_rowvals(l1, d1, lb, db, 32, h);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_sdp(s1, p1, qa1, oa1, kf, vf);
+      bf16x8 pa0[2], da0[2];
+      softmax_grad<false>(pa0, da0, s0, p0, l0, d0, a.c, 0, 0, 0, 0, 0);
+      interleave_mfma_valu();
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 oc1[2][4], qc1[2][4];
+      read_cols(oc1, qc1, qt, dt, 32, lane);
+      mfma_dvdk(dv, dk, pa0, da0, oc0, qc0);
+      bf16x8 pa1[2], da1[2];
+      softmax_grad<false>(pa1, da1, s1, p1, l1, d1, a.c, 0, 0, 0, 0, 0);
+      interleave_mfma_valu();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_dvdk(dv, dk, pa1, da1, oc1, qc1);
+      continue;
+    }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        qa[ks] = lds_row(qt, 32 * qs + c, 2 * ks + h);
-        oa[ks] = lds_row(dt, 32 * qs + c, 2 * ks + h);
-      }
+    for (int qs = 0; qs < 2; ++qs) {
+      if (!act[qs]) continue;
+      const int r0 = q0 + 32 * qs;
+      // operand reads are issued in batches ahead of the MFMAs that use them
+      // (sched_barrier keeps the compiler from sinking each read next to its
+      // use, which would expose the LDS latency once per MFMA)
+      bf16x8 qa[8], oa[8];
+      read_rows(qa, oa, qt, dt, 32 * qs + c, h);
       __builtin_amdgcn_sched_barrier(0);
       // S[q][key] and dP[q][key]: accumulator register r of lane (c, h) holds
       // row 8*(r/4) + 4h + r%4 of the sub-block against key kw0 + c
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        sacc = mfma32(qa[ks], kf[ks], sacc);
-        pacc = mfma32(oa[ks], vf[ks], pacc);
-      }
-      // column operands of the first half of the dV/dK products, read while
-      // the MFMAs above drain and the exponentials run
-      bf16x8 ocol[2][4], qcol[2][4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        ocol[0][n] = lds_cols(dt, 32 * qs, 32 * n, lane);
-        qcol[0][n] = lds_cols(qt, 32 * qs, 32 * n, lane);
-      }
+      f32x16 sacc, pacc;
+      mfma_sdp(sacc, pacc, qa, oa, kf, vf);
+      bf16x8 oc[2][4], qc[2][4];
+      read_cols(oc, qc, qt, dt, 32 * qs, lane);
       f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        l4[q4] = *reinterpret_cast<const f32x4*>(lb + 32 * qs + 8 * q4 + 4 * h);
-        d4[q4] = *reinterpret_cast<const f32x4*>(db + 32 * qs + 8 * q4 + 4 * h);
-      }
+      read_rowvals(l4, d4, lb, db, 32 * qs, h);
       __builtin_amdgcn_sched_barrier(0);
-      float p[16], ds[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q4 + i;
-          float pv = fast_exp2(sacc[r] * a.c - l4[q4][i]);
-          if (mask) {
-            const int row = r0 + 8 * q4 + 4 * h + i, key = kw0 + c;
-            if (key >= a.Sk || (CAUSAL && key > row + off)) pv = 0.f;
-          }
-          p[r] = pv;
-          ds[r] = pv * (pacc[r] - d4[q4][i]);
-        }
-      }
-      // dV[key][d] += sum_q P[q][key] dO[q][d]; dK[key][d] += sum_q dS[q][key] Q[q][d];
-      // the second half's column operands are read under the first half's MFMAs
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        ocol[1][n] = lds_cols(dt, 32 * qs + 16, 32 * n, lane);
-        qcol[1][n] = lds_cols(qt, 32 * qs + 16, 32 * n, lane);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 pa = to_bf16x8(p + 8 * t);
-        const bf16x8 da = to_bf16x8(ds + 8 * t);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          dv[n] = mfma32(pa, ocol[t][n], dv[n]);
-          dk[n] = mfma32(da, qcol[t][n], dk[n]);
-        }
-      }
+      bf16x8 pa[2], da[2];
+      if (msk[qs])
+        softmax_grad<CAUSAL>(pa, da, sacc, pacc, l4, d4, a.c, r0 + 4 * h, kw0 + c, a.Sk, off, 1);
+      else
+        softmax_grad<false>(pa, da, sacc, pacc, l4, d4, a.c, 0, 0, 0, 0, 0);
+      mfma_dvdk(dv, dk, pa, da, oc, qc);
     }
   }
 
