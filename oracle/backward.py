@@ -132,6 +132,31 @@ def attention_backward(q_in, k_in, v_in, do_in, B, Hq, Hkv, Sq, Sk, scale, causa
     return dq, dk, dv
 
 
+def attention_backward_varlen(q_in, k_in, v_in, do_in, cu_q, cu_k, Hkv, scale, causal,
+                              workers=None, magnitudes=False):
+    """Backward oracle for packed sequences (the forward of
+    ``oracle.attention.attention_varlen``): each sequence's gradients are
+    those of its own problem.  q_in/do_in [total_q, Hq, D], k_in/v_in
+    [total_k, Hkv, D] (bf16 bits or float64).  Returns (dq, dk, dv) in the
+    packed layouts, then the three magnitude arrays when magnitudes=True."""
+    total_q, Hq, d = q_in.shape
+    total_k = k_in.shape[0]
+    outs = [np.zeros((total_q, Hq, d)), np.zeros((total_k, Hkv, d)), np.zeros((total_k, Hkv, d))]
+    if magnitudes:
+        outs += [np.zeros_like(outs[0]), np.zeros_like(outs[1]), np.zeros_like(outs[2])]
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0 or k1 == k0:
+            continue   # no row sees a key: every gradient of the sequence is 0
+        r = attention_backward(q_in[q0:q1][None], k_in[k0:k1][None], v_in[k0:k1][None],
+                               do_in[q0:q1][None], 1, Hq, Hkv, q1 - q0, k1 - k0, scale, causal,
+                               BSHD, workers=workers, magnitudes=magnitudes)
+        for i, x in enumerate(r):
+            rows = slice(q0, q1) if i % 3 == 0 else slice(k0, k1)
+            outs[i][rows] = x[0].transpose(1, 0, 2)
+    return tuple(outs)
+
+
 def flops_backward(B, Hq, Sq, Sk, d, causal):
     """Algorithmic FLOP of the backward: the five products (S recomputed,
     dP, dV, dQ, dK) of 2*Sq*Sk*d each per head, 10*B*Hq*Sq*Sk*d, halved when
@@ -141,4 +166,4 @@ def flops_backward(B, Hq, Sq, Sk, d, causal):
 
 
 __all__ = ["as_f64", "probabilities", "grad_rows", "grad_magnitudes", "attention_backward",
-           "flops_backward"]
+           "attention_backward_varlen", "flops_backward"]

@@ -10,6 +10,7 @@ import torch
 
 import attn_inputs as gen
 import oracle.attention as att
+import oracle.backward as obwd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -141,3 +142,53 @@ def test_planted_varlen_mistake_is_caught(plant):
                 np.abs(lse[:, seen] - lse_t[:, seen]).max() <= 1e-12):
             caught = True
     assert caught
+
+
+def torch_packed_grads(p, do):
+    """float64 autograd of sum(dO * O) through torch's attention over the
+    packed batch with the block-diagonal mask (rows that see no key have
+    zero output and are left out of the loss, as their O is 0)."""
+    f = [torch.from_numpy(att.bf16_to_f64(x)).permute(1, 0, 2).contiguous()
+         for x in (p.q, p.k, p.v, do)]
+    q, k, v, dot = f
+    for t in (q, k, v):
+        t.requires_grad_(True)
+    G = p.Hq // p.Hkv
+    Tq, Tk = int(p.cu_q[-1]), int(p.cu_k[-1])
+    mask = torch.zeros((Tq, Tk), dtype=torch.bool)
+    for b in range(p.B):
+        q0, q1, k0, k1 = (int(x) for x in (p.cu_q[b], p.cu_q[b + 1], p.cu_k[b], p.cu_k[b + 1]))
+        i = torch.arange(q1 - q0)[:, None]
+        j = torch.arange(k1 - k0)[None, :]
+        mask[q0:q1, k0:k1] = (j <= i + (k1 - k0) - (q1 - q0)) if p.causal else True
+    seen = mask.any(dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(G, dim=0), v.repeat_interleave(G, dim=0),
+        attn_mask=mask | ~seen[:, None], scale=float(np.float32(p.scale)))
+    (o[:, seen] * dot[:, seen]).sum().backward()
+    return [t.grad.permute(1, 0, 2).numpy() for t in (q, k, v)]
+
+
+@pytest.mark.parametrize("lq,lk,causal,Hq,Hkv", CASES)
+def test_varlen_backward_matches_torch_autograd(lq, lk, causal, Hq, Hkv):
+    p = gen.varlen_inputs(lq, lk, Hq, Hkv, causal=causal, seed=21)
+    do = gen.f32_to_bf16_bits(np.random.default_rng(5).standard_normal(
+        (int(p.cu_q[-1]), Hq, 128)).astype(np.float32))
+    got = obwd.attention_backward_varlen(p.q, p.k, p.v, do, p.cu_q, p.cu_k, Hkv, p.scale, causal,
+                                         workers=1)
+    ref = torch_packed_grads(p, do)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        err = np.abs(g - r).max() / max(1e-300, np.abs(r).max())
+        assert err <= 1e-12, f"{name}: relative error {err:.3g}"
+
+
+def test_varlen_backward_one_sequence_equals_dense():
+    p = gen.varlen_inputs([40], [57], 4, 2, causal=True, seed=22)
+    do = gen.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((40, 4, 128)).astype(
+        np.float32))
+    a = obwd.attention_backward_varlen(p.q, p.k, p.v, do, p.cu_q, p.cu_k, 2, p.scale, True,
+                                       workers=1)
+    b = obwd.attention_backward(p.q[None], p.k[None], p.v[None], do[None], 1, 4, 2, 40, 57,
+                                p.scale, True, att.BSHD, workers=1)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y[0].transpose(1, 0, 2))
