@@ -15,8 +15,9 @@ are already resident in HBM:
   same way and reported beside the headline (skip with --no-extra);
 * packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
   U{1..8192}, reported beside the headline;
-* the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads,
-  reported beside the headline too.
+* the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads
+  and of the packed sequences (attn_bwd_varlen), reported beside the
+  headline too.
 
 Times come from HIP events on the stream the kernels are launched on.  The
 fp64 CPU oracle is timed on the host cores on a bounded sample of the same
@@ -234,7 +235,10 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
              wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dkdv_kernel<true>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dq_kernel<true>")],
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dq_kernel<true>"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_prep_kernel"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_dkdv_kernel<true>"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_dq_kernel<true>")],
             ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]),
     }
     for fname, (title, rows, tkeys) in files.items():
@@ -334,6 +338,31 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         res.append(ent)
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    # packed sequences of mixed lengths (attn_bwd_varlen)
+    pv = gen.varlen_causal_gqa()
+    log(f"timing the backward of {pv.name}")
+    q, k, v = to_dev(pv.q), to_dev(pv.k), to_dev(pv.v)
+    r = np.random.default_rng(6)
+    do = to_dev(gen.f32_to_bf16_bits(r.standard_normal(pv.q.shape).astype(np.float32)))
+    cq = torch.from_numpy(pv.cu_q).to(q.device)
+    ck = torch.from_numpy(pv.cu_k).to(q.device)
+    o, lse = ea.attn_fwd_varlen(q, k, v, cq, ck, pv.max_q, causal=True, scale=pv.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(1, pv.Hq, q.shape[0]), dtype=torch.uint8,
+                     device=q.device)
+
+    def run_v(_i):
+        ea.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, pv.max_q, pv.max_q, causal=True,
+                           scale=pv.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms = time_calls(run_v, steps, 2, torch)
+    fl = 2.5 * pv.flops
+    res.append({"workload": pv.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
+                "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+                "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
     return res
 
 
@@ -406,15 +435,23 @@ def main():
                         "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs),
                                                  ("varlen_causal_gqa_b16_hq32_hkv8_len8192", xs),
                                                  ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                  "_backward_fwd", 1),
+                                                 ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                   "_backward_fwd", 1)],
                         "bwd_prep_kernel": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),
                                             ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
+                                             xs),
+                                            ("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
                                              xs)],
                         "bwd_dkdv_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs)],
                         "bwd_dq_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs)],
                         "bwd_dkdv_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                   "_backward", xs),
+                                                  ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                    "_backward", xs)],
                         "bwd_dq_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                 "_backward", xs),
+                                                ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                  "_backward", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
                                                    st + wu),

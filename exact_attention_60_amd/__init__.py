@@ -12,6 +12,8 @@ library is not built the binding raises instead of computing anything itself.
                                       seq_lens)   # writes the new rows into the caches
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, layout="bshd")
     o, lse = attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q)  # packed
+    dq, dk, dv = attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k,
+                                 max_seqlen_q, max_seqlen_k)
 
 ``rounding`` is the rule of the final fp32 -> bf16 conversion of O: "rtne"
 (nearest, ties to even; the plain entry points), "rtna" (nearest, ties away
@@ -42,7 +44,7 @@ STATUS = {
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_varlen", "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
-           "attn_bwd", "attn_status_string", "attn_version")
+           "attn_bwd", "attn_bwd_varlen", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -85,6 +87,9 @@ def library() -> ctypes.CDLL:
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp,
                                  sz, vp]
         lib.attn_bwd.restype = i
+        lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                        i, i, i, f, i, vp, sz, vp]
+        lib.attn_bwd_varlen.restype = i
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -312,7 +317,51 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
     return dq, dk, dv
 
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append",
+def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    max_seqlen_k: int, *, causal: bool = False, scale: float | None = None,
+                    dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of attn_fwd_varlen for an upstream gradient do
+    ([total_q, Hq, 128]), from its inputs and its outputs o, lse
+    ([Hq, total_q]).  Returns (dq, dk, dv) in the packed layouts, bf16."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_bf16(n, t)
+    if q.dim() != 3 or k.shape != v.shape or k.dim() != 3 or o.shape != q.shape or \
+            do.shape != q.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("q, o, do must share a [total_q, Hq, d] shape and k, v [total_k, Hkv, d]")
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{n} must be a contiguous 1-D int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (Hq, total_q) or \
+            not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 GPU tensor [Hq, total_q]")
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(1, Hq, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = library().attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), cu_seqlens_q.data_ptr(),
+                                   cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
+                                   int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
+                                   int(bool(causal)), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_varlen")
+    return dq, dk, dv
+
+
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append",
            "attn_decode_workspace_bytes", "attn_status_string",
            "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

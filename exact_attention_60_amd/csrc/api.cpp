@@ -312,6 +312,70 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.group = Hq / Hkv;
   a.c = scale * 1.4426950408889634f;
   a.scale = scale;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+  const hipError_t e = attn::launch_backward(a, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens_q ||
+      !cu_seqlens_k)
+    return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 ||
+      max_seqlen_k < 1 || Hq % Hkv != 0)
+    return ATTN_ERR_SHAPE;
+  if (d != attn::kHeadDim || (causal != 0 && causal != 1) || !scale_ok(scale))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return ATTN_ERR_ALIGN;
+  if (Hq > 65535) return ATTN_ERR_SHAPE;
+  const int64_t D = attn::kHeadDim;
+  attn::BwdArgs a;
+  a.q_sb = 0; a.q_sh = D; a.q_ss = (int64_t)Hq * D;
+  a.k_sb = 0; a.k_sh = D; a.k_ss = (int64_t)Hkv * D;
+  // rows of one sequence are addressed with 32-bit byte offsets, including
+  // the zero-filled rows past the end of a last 64-row block
+  if (((int64_t)total_q + 64) * a.q_ss * 2 > INT32_MAX ||
+      ((int64_t)total_k + 64) * a.k_ss * 2 > INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  if ((int64_t)B * Hkv * ((max_seqlen_k + attn::kBwdKvRows - 1) / attn::kBwdKvRows) > INT32_MAX ||
+      (int64_t)B * Hq * ((max_seqlen_q + attn::kBwdQRows - 1) / attn::kBwdQRows) > INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  const size_t need = attn_bwd_workspace_bytes(1, Hq, total_q);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = static_cast<const __bf16*>(o);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<__bf16*>(dq);
+  a.dk = static_cast<__bf16*>(dk);
+  a.dv = static_cast<__bf16*>(dv);
+  a.ws_d = static_cast<float*>(workspace);
+  a.ws_l = a.ws_d + (size_t)Hq * total_q;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.Sq = max_seqlen_q;
+  a.Sk = max_seqlen_k;
+  a.group = Hq / Hkv;
+  a.c = scale * 1.4426950408889634f;
+  a.scale = scale;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;

@@ -238,16 +238,62 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+// Workgroups are dealt to the 8 XCDs round robin (XCD = i % 8).  Index i of
+// a row of B*Hq workgroups goes to K/V head group (i % 8) + 8 * (i / 8 / G),
+// query head (i / 8) % G of that group: the G query heads of a group share an
+// XCD, consecutive groups (the K/V heads of one sequence) do not.  Needs the
+// group count to be a multiple of 8, else i is kept.
+__device__ __forceinline__ int spread_groups(int i, int G, int n_groups) {
+  if (n_groups & 7) return i;
+  const int x = i & 7, j = i >> 3;
+  return (x + 8 * (j / G)) * G + (j - (j / G) * G);
+}
+
+// One sequence's sizes and offsets: the whole batch entry b, or (packed
+// sequences) rows cu_q[b] .. cu_q[b+1]-1 and cu_k[b] .. cu_k[b+1]-1, offsets
+// clamped to the packed sizes and lengths to the longest ones.  Row i of query
+// head hq has its LSE and workspace values at row0 + hq * hstride + i.
+struct SeqView {
+  int Sq, Sk;
+  int64_t qbase, kbase;   // element offsets of row 0 in q/o/dout/dq and k/v/dk/dv
+  int64_t row0, hstride;
+};
+__device__ __forceinline__ SeqView seq_view(const BwdArgs& a, int b) {
+  SeqView v;
+  if (a.cu_q) {
+    const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
+    const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
+    const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
+    const int k_hi = min(max(a.cu_k[b + 1], k_lo), a.total_k);
+    v.Sq = min(q_hi - q_lo, a.Sq);
+    v.Sk = min(k_hi - k_lo, a.Sk);
+    v.qbase = (int64_t)q_lo * a.q_ss;
+    v.kbase = (int64_t)k_lo * a.k_ss;
+    v.row0 = q_lo;
+    v.hstride = a.total_q;
+  } else {
+    v.Sq = a.Sq;
+    v.Sk = a.Sk;
+    v.qbase = b * a.q_sb;
+    v.kbase = b * a.k_sb;
+    v.row0 = (int64_t)b * a.Hq * a.Sq;
+    v.hstride = a.Sq;
+  }
+  return v;
+}
+
 }  // namespace
 
 // ---- D = rowsum(dO * O) and LSE in log2 units --------------------------------
 // 16 rows per workgroup, 16 lanes per row, 8 elements per lane.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  // packed sequences: all total_q rows as one batch entry ([Hq, total_q])
+  const int rows = a.cu_q ? a.total_q : a.Sq;
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int hq = blockIdx.y, b = blockIdx.z;
   const int ch = threadIdx.x & 15;
   float s = 0.f;
-  if (row < a.Sq) {
+  if (row < rows) {
     const int64_t off = b * a.q_sb + hq * a.q_sh + (int64_t)row * a.q_ss + ch * 8;
     const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(a.o + off);
     const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(a.dout + off);
@@ -256,8 +302,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-  if (ch == 0 && row < a.Sq) {
-    const int64_t i = ((int64_t)b * a.Hq + hq) * a.Sq + row;
+  if (ch == 0 && row < rows) {
+    const int64_t i = ((int64_t)b * a.Hq + hq) * rows + row;
     a.ws_d[i] = s;
     const float l = a.lse[i];
     a.ws_l[i] = (l == -INFINITY) ? INFINITY : l * kLog2e;
@@ -275,24 +321,36 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 31, h = lane >> 5;
   const int n_kb = (a.Sk + KV_ROWS - 1) / KV_ROWS;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bg = L / n_kb;
-  const int kb = L - bg * n_kb;
+  int bg, kb;
+  if (a.cu_q) {
+    // packed sequences: rows of B*Hkv workgroups per key block, so the K/V
+    // heads of one sequence land on different XCDs
+    const int BG = a.B * a.Hkv;
+    kb = blockIdx.x / BG;
+    bg = blockIdx.x - kb * BG;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    bg = L / n_kb;
+    kb = L - bg * n_kb;
+  }
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const SeqView sv = seq_view(a, b);
+  const int Sq = sv.Sq, Sk = sv.Sk;
   const int k0 = kb * KV_ROWS;
+  if (k0 >= Sk) return;                 // whole workgroup: past this sequence's keys
   const int kw0 = k0 + 32 * wave;       // this wave's first key
-  const int off = a.Sk - a.Sq;          // key j visible from row i iff j <= i + off (causal)
+  const int off = Sk - Sq;              // key j visible from row i iff j <= i + off (causal)
 
   // K and V fragments of the wave's keys: B operand of S = Q K^T and of
   // dP = dO V^T (lane: key kw0 + c, head-dim slots 16*ks + 8*h .. +7)
-  const __bf16* kp = a.k + b * a.k_sb + g * a.k_sh;
-  const __bf16* vp = a.v + b * a.k_sb + g * a.k_sh;
+  const __bf16* kp = a.k + sv.kbase + g * a.k_sh;
+  const __bf16* vp = a.v + sv.kbase + g * a.k_sh;
   bf16x8 kf[8], vf[8];
   {
     const int key = kw0 + c;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if (key < a.Sk) {
+      if (key < Sk) {
         kf[ks] = *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
         vf[ks] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
       } else {
@@ -305,24 +363,24 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   // query blocks that can see a key of this workgroup, for each head of the group
   const int qstart = CAUSAL ? max(0, k0 - off) : 0;
   const int qb_first = qstart / QB;
-  const int n_qb = (a.Sq + QB - 1) / QB;
+  const int n_qb = (Sq + QB - 1) / QB;
   const int per_head = n_qb - qb_first;
   const int total = a.group * per_head;
 
   RowCopy cp;
   cp.init(a.q_ss, wave, lane);
-  const uint32_t q_bytes = (uint32_t)((int64_t)(a.Sq - 1) * a.q_ss * 2 + 256);
+  const uint32_t q_bytes = Sq > 0 ? (uint32_t)((int64_t)(Sq - 1) * a.q_ss * 2 + 256) : 0u;
   const uint32_t blk_bytes = (uint32_t)(QB * a.q_ss * 2);
   auto issue = [&](int s, int st) {
     const int hq = g * a.group + s / per_head;
     const int qb = qb_first + s % per_head;
-    const int64_t hoff = b * a.q_sb + hq * a.q_sh;
+    const int64_t hoff = sv.qbase + hq * a.q_sh;
     cp.issue(rsrc(a.q + hoff, q_bytes), qbuf + st * TILE, (uint32_t)qb * blk_bytes);
     cp.issue(rsrc(a.dout + hoff, q_bytes), dobuf + st * TILE, (uint32_t)qb * blk_bytes);
     if (wave < 2) {
-      const float* src = (wave == 0 ? a.ws_l : a.ws_d) + ((int64_t)b * a.Hq + hq) * a.Sq;
+      const float* src = (wave == 0 ? a.ws_l : a.ws_d) + sv.row0 + hq * sv.hstride;
       float* dst = (wave == 0 ? lbuf : dbuf) + st * QB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src, (uint32_t)a.Sq * 4), (ATTN_LDS void*)dst,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src, (uint32_t)Sq * 4), (ATTN_LDS void*)dst,
                                                4, (uint32_t)(qb * QB + lane) * 4, 0, 0, 0);
     }
   };
@@ -334,7 +392,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     dv[n] = f32x16{};
   }
 
-  issue(0, 0);
+  if (total > 0) issue(0, 0);
   for (int s = 0; s < total; ++s) {
     const int st = s & 1;
     wait_all();
@@ -351,8 +409,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int r0 = q0 + 32 * qs;
-      act[qs] = kw0 < a.Sk && !(CAUSAL && kw0 > r0 + 31 + off);
-      msk[qs] = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > a.Sk);
+      act[qs] = kw0 < Sk && !(CAUSAL && kw0 > r0 + 31 + off);
+      msk[qs] = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > Sk);
     }
     if (act[0] && act[1] && !msk[0] && !msk[1]) {
       // Both sub-blocks whole: software-pipelined, so that each block of
@@ -408,7 +466,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 pa[2], da[2];
       if (msk[qs])
-        softmax_grad<CAUSAL>(pa, da, sacc, pacc, l4, d4, a.c, r0 + 4 * h, kw0 + c, a.Sk, off, 1);
+        softmax_grad<CAUSAL>(pa, da, sacc, pacc, l4, d4, a.c, r0 + 4 * h, kw0 + c, Sk, off, 1);
       else
         softmax_grad<false>(pa, da, sacc, pacc, l4, d4, a.c, 0, 0, 0, 0, 0);
       mfma_dvdk(dv, dk, pa, da, oc, qc);
@@ -416,12 +474,12 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // register r of lane (c, h), d block n: key kw0 + 8*(r/4) + 4h + r%4, dim 32n + c
-  __bf16* dkp = a.dk + b * a.k_sb + g * a.k_sh;
-  __bf16* dvp = a.dv + b * a.k_sb + g * a.k_sh;
+  __bf16* dkp = a.dk + sv.kbase + g * a.k_sh;
+  __bf16* dvp = a.dv + sv.kbase + g * a.k_sh;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (key < a.Sk) {
+    if (key < Sk) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         dkp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)(dk[n][r] * a.scale);
@@ -445,10 +503,12 @@ void bwd_dq_kernel(BwdArgs a) {
   const int n_qb = (a.Sq + Q_ROWS - 1) / Q_ROWS;
   const int BH = a.B * a.Hq;
   int bh, qb;
-  if (CAUSAL) {
+  if (CAUSAL || a.cu_q) {
     const int row = blockIdx.x / BH;      // heaviest query blocks first
     qb = n_qb - 1 - row;
-    bh = xcd_remap(blockIdx.x - row * BH, BH);
+    // packed sequences: the heads of one sequence spread over the XCDs
+    bh = a.cu_q ? spread_groups(blockIdx.x - row * BH, a.group, a.B * a.Hkv)
+                : xcd_remap(blockIdx.x - row * BH, BH);
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     bh = L / n_qb;
@@ -456,18 +516,21 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   const int b = bh / a.Hq, hq = bh - b * a.Hq;
   const int g = hq / a.group;
-  const int off = a.Sk - a.Sq;
+  const SeqView sv = seq_view(a, b);
+  const int Sq = sv.Sq, Sk = sv.Sk;
   const int q0 = qb * Q_ROWS;
+  if (q0 >= Sq) return;                   // whole workgroup: past this sequence's rows
+  const int off = Sk - Sq;
   const int qw0 = q0 + 32 * wave;         // this wave's first row
   const int q = qw0 + c;                  // this lane's row (both halves)
 
   // Q and dO fragments of the wave's rows: B operand of S^T = K Q^T and of
   // dP^T = V dO^T (lane: row q, head-dim slots 16*ks + 8*h .. +7)
-  const int64_t qoff = b * a.q_sb + hq * a.q_sh;
+  const int64_t qoff = sv.qbase + hq * a.q_sh;
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    if (q < a.Sq) {
+    if (q < Sq) {
       qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qoff + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
       df[ks] = *reinterpret_cast<const bf16x8*>(a.dout + qoff + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
     } else {
@@ -475,20 +538,20 @@ void bwd_dq_kernel(BwdArgs a) {
       df[ks] = bf16x8{};
     }
   }
-  const int64_t srow = ((int64_t)b * a.Hq + hq) * a.Sq;
-  const float l2 = q < a.Sq ? a.ws_l[srow + q] : INFINITY;
-  const float drow = q < a.Sq ? a.ws_d[srow + q] : 0.f;
+  const int64_t srow = sv.row0 + hq * sv.hstride;
+  const float l2 = q < Sq ? a.ws_l[srow + q] : INFINITY;
+  const float drow = q < Sq ? a.ws_d[srow + q] : 0.f;
 
-  const int last_row = min(q0 + Q_ROWS, a.Sq) - 1;
-  const int n_keys = CAUSAL ? min(a.Sk, max(0, last_row + off + 1)) : a.Sk;
+  const int last_row = min(q0 + Q_ROWS, Sq) - 1;
+  const int n_keys = CAUSAL ? min(Sk, max(0, last_row + off + 1)) : Sk;
   const int n_kt = (n_keys + KB - 1) / KB;
-  const int wave_last = min(qw0 + 31, a.Sq - 1);
+  const int wave_last = min(qw0 + 31, Sq - 1);
 
   RowCopy cp;
   cp.init(a.k_ss, wave, lane);
-  const __bf16* kp = a.k + b * a.k_sb + g * a.k_sh;
-  const __bf16* vp = a.v + b * a.k_sb + g * a.k_sh;
-  const uint32_t k_bytes = (uint32_t)((int64_t)(a.Sk - 1) * a.k_ss * 2 + 256);
+  const __bf16* kp = a.k + sv.kbase + g * a.k_sh;
+  const __bf16* vp = a.v + sv.kbase + g * a.k_sh;
+  const uint32_t k_bytes = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * a.k_ss * 2 + 256) : 0u;
   const __amdgpu_buffer_rsrc_t rk = rsrc(kp, k_bytes), rv = rsrc(vp, k_bytes);
   const uint32_t blk_bytes = (uint32_t)(KB * a.k_ss * 2);
 
@@ -513,9 +576,9 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       const int kr0 = t * KB + 32 * ks2;
-      if (kr0 >= n_keys || qw0 >= a.Sq) continue;
+      if (kr0 >= n_keys || qw0 >= Sq) continue;
       if (CAUSAL && kr0 > wave_last + off) continue;   // no row of the wave sees these keys
-      const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > a.Sk);
+      const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > Sk);
       // S^T[key][q] and dP^T[key][q]: register r of lane (c, h) holds key
       // kr0 + 8*(r/4) + 4h + r%4 against this lane's row q
       // K rows are read as one batch, and the V rows go out before the S^T
@@ -538,7 +601,7 @@ void bwd_dq_kernel(BwdArgs a) {
         float pv = fast_exp2(sacc[r] * a.c - l2);
         if (mask) {
           const int key = kr0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= a.Sk || (CAUSAL && key > q + off)) pv = 0.f;
+          if (key >= Sk || (CAUSAL && key > q + off)) pv = 0.f;
         }
         ds[r] = pv * (pacc[r] - drow);
       }
@@ -558,7 +621,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = qw0 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (row < a.Sq) {
+    if (row < Sq) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) dqp[(int64_t)row * a.q_ss + 32 * n + c] = (__bf16)(dq[n][r] * a.scale);
     }
@@ -566,13 +629,15 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
-  const int64_t n_rows16 = ((int64_t)a.Sq + 15) / 16;
+  const int64_t n_rows16 = ((int64_t)(a.cu_q ? a.total_q : a.Sq) + 15) / 16;
+  const int prep_b = a.cu_q ? 1 : a.B;
   const int64_t g_kv = (int64_t)a.B * a.Hkv * ((a.Sk + KV_ROWS - 1) / KV_ROWS);
   const int64_t g_q = (int64_t)a.B * a.Hq * ((a.Sq + Q_ROWS - 1) / Q_ROWS);
   if (n_rows16 > 0x7fffffff || a.Hq > 65535 || a.B > 65535 || g_kv > 0x7fffffff ||
       g_q > 0x7fffffff)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_rows16, a.Hq, a.B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_rows16, a.Hq, prep_b), dim3(256), 0, stream,
+                     a);
   if (causal) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
     hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)g_q), dim3(NT), 0, stream, a);

@@ -102,6 +102,12 @@ struct BwdArgs {
   int group;             // Hq / Hkv
   float c;               // scale * log2(e)
   float scale;
+  // packed sequences (null cu_q: dense batch): sequence b is rows
+  // cu_q[b] .. cu_q[b+1]-1 of q and cu_k[b] .. cu_k[b+1]-1 of k; Sq and Sk are
+  // then the longest lengths, LSE and the workspace [Hq, total_q]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream);

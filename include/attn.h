@@ -11,7 +11,8 @@
  *                      partial results merged by their log-sum-exps.
  *   attn_bwd           dQ, dK, dV of the forward for an upstream dO, with the
  *                      probabilities recomputed from the forward's LSE.
- * attn_fwd_varlen is attn_fwd over packed sequences of different lengths.
+ * attn_fwd_varlen and attn_bwd_varlen are attn_fwd and attn_bwd over packed
+ * sequences of different lengths.
  *
  * Definitions followed (page titles and sections):
  *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
@@ -74,7 +75,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 5
+#define ATTN_VERSION 6
 
 typedef enum {
   ATTN_OK = 0,
@@ -295,6 +296,29 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
              int Sk, int d, float scale, int causal, int layout, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_varlen - attn_bwd for packed sequences (the backward of
+ * attn_fwd_varlen): each sequence's gradients are those of its own problem.
+ *
+ *   q, k, v, o, dout, dq, dk, dv  packed as for attn_fwd_varlen
+ *                 (q, o, dout, dq [total_q, Hq, d]; k, v, dk, dv
+ *                 [total_k, Hkv, d])
+ *   lse           fp32 [Hq, total_q], as attn_fwd_varlen writes it
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [B + 1], as for attn_fwd_varlen
+ *   max_seqlen_q, max_seqlen_k  >= every query / key length (they size the
+ *                 launches; rows or keys of a longer sequence past them are
+ *                 not written)
+ *   workspace     at least attn_bwd_workspace_bytes(1, Hq, total_q) bytes
+ * Key rows of a sequence with no query rows get dK = dV = 0.  Size limits
+ * (ATTN_ERR_SHAPE): (total + 64) * heads * 256 < 2^31 for q and k, Hq <=
+ * 65535.  Other arguments, checks and statuses as for attn_bwd.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int d, float scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 5
+    assert ea.attn_version() == 6
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -209,6 +209,37 @@ def test_fwd_varlen_valid_arguments_need_a_gfx950_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert fwd_varlen() == -7
     assert fwd_varlen(cq=P + 4, ck=P + 8) == -7   # 4-byte alignment is enough for offsets
+
+
+def bwd_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cq=P, ck=P, B=3, Hq=4, Hkv=2,
+             tq=100, tk=90, mq=50, mk=60, d=128, scale=0.1, causal=1, ws=P, wsb=10 ** 6,
+             stream=None)
+    a.update(kw)
+    return ea.library().attn_bwd_varlen(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["cq"],
+        a["ck"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"], a["mk"], a["d"], a["scale"],
+        a["causal"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(cq=None), -1), (dict(ck=None), -1), (dict(dv=None), -1),
+    (dict(B=0), -2), (dict(tq=0), -2), (dict(tk=0), -2), (dict(mq=0), -2), (dict(mk=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(tk=(1 << 21), Hkv=4), -2),
+    (dict(d=64), -3), (dict(causal=2), -3), (dict(scale=-1.0), -3),
+    (dict(q=P + 8), -4), (dict(dk=P + 2), -4), (dict(cq=P + 2), -4),
+    (dict(ws=None), -5), (dict(wsb=8 * 4 * 100 - 1), -5),
+])
+def test_bwd_varlen_argument_errors(kw, code):
+    assert bwd_varlen(**kw) == code
+
+
+def test_bwd_varlen_valid_arguments_need_a_gfx950_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert bwd_varlen() == -7
+    assert bwd_varlen(wsb=8 * 4 * 100) == -7
 
 
 def test_binding_rejects_unknown_rounding_name():

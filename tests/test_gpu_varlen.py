@@ -1,5 +1,6 @@
-"""Parity of the packed-sequence forward (attn_fwd_varlen) with the fp64
-oracle (GPU), under the forward's tolerance."""
+"""Parity of the packed-sequence forward (attn_fwd_varlen) and backward
+(attn_bwd_varlen) with the fp64 oracles (GPU), under the forward's and the
+backward's tolerances."""
 import numpy as np
 import pytest
 import torch
@@ -7,6 +8,7 @@ import torch
 import attn_inputs as gen
 import exact_attention_60_amd as ea
 import oracle.attention as att
+import oracle.backward as obwd
 from gpu_util import dev_bf16, dev_i32, host_f64, need_gpu
 from tolerance import check_lse, check_o
 
@@ -87,3 +89,55 @@ def test_packed_prompt_batch_sampled():
                                             p.scale, True)
         check_o(host_f64(o[q0:q1, hs]), o_ref[:, hs], f"packed batch seq {b}")
         check_lse(host_f64(lse[hs, q0:q1]), l_ref[hs], f"packed batch seq {b} lse")
+
+
+# ---- backward of packed sequences -------------------------------------------
+
+def run_bwd(p, do_bits, max_q=None, max_k=None):
+    q, k, v = dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v)
+    cq, ck = dev_i32(p.cu_q), dev_i32(p.cu_k)
+    mq = max_q or p.max_q
+    mk = max_k or max(1, int(np.diff(p.cu_k).max()))
+    o, lse = ea.attn_fwd_varlen(q, k, v, cq, ck, mq, causal=p.causal, scale=p.scale)
+    g = ea.attn_bwd_varlen(q, k, v, o, lse, dev_bf16(do_bits), cq, ck, mq, mk, causal=p.causal,
+                           scale=p.scale)
+    torch.cuda.synchronize()
+    return g
+
+
+def packed_do(p, seed):
+    r = np.random.default_rng(seed)
+    return gen.f32_to_bf16_bits(r.standard_normal((int(p.cu_q[-1]), p.Hq, 128)).astype(np.float32))
+
+
+@pytest.mark.parametrize("lq,lk,causal,Hq,Hkv", [
+    ([5, 0, 17, 1, 33], [7, 3, 17, 1, 20], True, 4, 2),
+    ([300, 256, 257, 1], [300, 256, 257, 1], True, 8, 2),
+    ([12, 3, 0, 400], [30, 3, 8, 700], False, 4, 4),
+    ([513, 64], [0, 64], False, 2, 1),
+])
+def test_varlen_backward_all_elements(lq, lk, causal, Hq, Hkv):
+    from test_gpu_backward import check as check_grad
+    p = gen.varlen_inputs(lq, lk, Hq, Hkv, causal=causal, seed=sum(lq) * 3 + 1)
+    do = packed_do(p, 17)
+    got = run_bwd(p, do)
+    ref = obwd.attention_backward_varlen(p.q, p.k, p.v, do, p.cu_q, p.cu_k, Hkv, p.scale, causal,
+                                         magnitudes=True)
+    r = [check_grad(f"varlen {n}", host_f64(t), ref[i], ref[i + 3])
+         for i, (n, t) in enumerate(zip(("dq", "dk", "dv"), got))]
+    print(f"varlen backward lq={lq} lk={lk}: max err/tol {max(r):.3f}", flush=True)
+
+
+def test_varlen_backward_equals_dense_per_sequence():
+    p = gen.varlen_inputs([200, 77, 300], [260, 77, 300], 4, 2, causal=True, seed=9)
+    do = packed_do(p, 9)
+    dq, dk, dv = run_bwd(p, do)
+    for b in range(p.B):
+        q0, q1, k0, k1 = (int(x) for x in (p.cu_q[b], p.cu_q[b + 1], p.cu_k[b], p.cu_k[b + 1]))
+        qs, ks, vs = (dev_bf16(x[None]) for x in (p.q[q0:q1], p.k[k0:k1], p.v[k0:k1]))
+        od, ld = ea.attn_fwd(qs, ks, vs, causal=True, scale=p.scale, layout="bshd")
+        g = ea.attn_bwd(qs, ks, vs, od, ld, dev_bf16(do[q0:q1][None]), causal=True,
+                        scale=p.scale, layout="bshd")
+        torch.cuda.synchronize()
+        for x, y in zip(g, (dq[q0:q1], dk[k0:k1], dv[k0:k1])):
+            assert torch.equal(x[0].view(torch.int16), y.view(torch.int16))
