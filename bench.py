@@ -231,14 +231,18 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
             "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
             "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
             [wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_prep_kernel"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<false>"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<false, false>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false, false>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dkdv_kernel<true>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_dq_kernel<true>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
+                    "bwd_dkdv_kernel<true, false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
+                    "bwd_dq_kernel<true, false>"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_prep_kernel"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_dkdv_kernel<true>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_dq_kernel<true>")],
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
+                    "bwd_dkdv_kernel<true, true>"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
+                    "bwd_dq_kernel<true, true>")],
             ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]),
     }
     for fname, (title, rows, tkeys) in files.items():
@@ -443,16 +447,18 @@ def main():
                                              xs),
                                             ("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
                                              xs)],
-                        "bwd_dkdv_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs)],
-                        "bwd_dq_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs)],
-                        "bwd_dkdv_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                   "_backward", xs),
-                                                  ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
-                                                   "_backward", xs)],
-                        "bwd_dq_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                 "_backward", xs),
-                                                ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
-                                                 "_backward", xs)],
+                        "bwd_dkdv_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
+                                                           xs)],
+                        "bwd_dq_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
+                                                         xs)],
+                        "bwd_dkdv_kernel<true, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                          "_backward", xs)],
+                        "bwd_dq_kernel<true, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                        "_backward", xs)],
+                        "bwd_dkdv_kernel<true, true>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
+                                                         "_backward", xs)],
+                        "bwd_dq_kernel<true, true>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
+                                                       "_backward", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
                                                    st + wu),
                                                   ("paged_decode_b32_hq32_hkv8_len4096_page16_append",

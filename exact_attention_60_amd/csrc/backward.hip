@@ -258,9 +258,10 @@ struct SeqView {
   int64_t qbase, kbase;   // element offsets of row 0 in q/o/dout/dq and k/v/dk/dv
   int64_t row0, hstride;
 };
+template <bool PACKED>
 __device__ __forceinline__ SeqView seq_view(const BwdArgs& a, int b) {
   SeqView v;
-  if (a.cu_q) {
+  if (PACKED) {
     const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
     const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
     const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---- dK, dV ----------------------------------------------------------------
-template <bool CAUSAL>
+template <bool CAUSAL, bool PACKED>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char qbuf[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char dobuf[2 * TILE];
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int c = lane & 31, h = lane >> 5;
   const int n_kb = (a.Sk + KV_ROWS - 1) / KV_ROWS;
   int bg, kb;
-  if (a.cu_q) {
+  if (PACKED) {
     // packed sequences: rows of B*Hkv workgroups per key block, so the K/V
     // heads of one sequence land on different XCDs
     const int BG = a.B * a.Hkv;
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     kb = L - bg * n_kb;
   }
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const SeqView sv = seq_view(a, b);
+  const SeqView sv = seq_view<PACKED>(a, b);
   const int Sq = sv.Sq, Sk = sv.Sk;
   const int k0 = kb * KV_ROWS;
   if (k0 >= Sk) return;                 // whole workgroup: past this sequence's keys
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 // ---- dQ --------------------------------------------------------------------
 // Two workgroups per CU (two waves per SIMD, 64 KB of LDS each): one wave's
 // exponentials and operand reads run under the other's MFMAs.
-template <bool CAUSAL>
+template <bool CAUSAL, bool PACKED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE];
@@ -503,11 +504,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const int n_qb = (a.Sq + Q_ROWS - 1) / Q_ROWS;
   const int BH = a.B * a.Hq;
   int bh, qb;
-  if (CAUSAL || a.cu_q) {
+  if (CAUSAL || PACKED) {
     const int row = blockIdx.x / BH;      // heaviest query blocks first
     qb = n_qb - 1 - row;
     // packed sequences: the heads of one sequence spread over the XCDs
-    bh = a.cu_q ? spread_groups(blockIdx.x - row * BH, a.group, a.B * a.Hkv)
+    bh = PACKED ? spread_groups(blockIdx.x - row * BH, a.group, a.B * a.Hkv)
                 : xcd_remap(blockIdx.x - row * BH, BH);
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -516,7 +517,7 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   const int b = bh / a.Hq, hq = bh - b * a.Hq;
   const int g = hq / a.group;
-  const SeqView sv = seq_view(a, b);
+  const SeqView sv = seq_view<PACKED>(a, b);
   const int Sq = sv.Sq, Sk = sv.Sk;
   const int q0 = qb * Q_ROWS;
   if (q0 >= Sq) return;                   // whole workgroup: past this sequence's rows
@@ -638,12 +639,20 @@ hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_rows16, a.Hq, prep_b), dim3(256), 0, stream,
                      a);
-  if (causal) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+  const bool packed = a.cu_q != nullptr;
+  if (causal && packed) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, true>), dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<true, true>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+  } else if (causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, false>), dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<true, false>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+  } else if (packed) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<false, true>), dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<false, true>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<false, false>), dim3((unsigned)g_kv), dim3(NT), 0, stream,
+                       a);
+    hipLaunchKernelGGL((bwd_dq_kernel<false, false>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
   }
   return hipGetLastError();
 }
