@@ -20,6 +20,8 @@ What it computes, and where the pages define it:
   Reading taken when Sq != Sk: bottom-right alignment, key j is visible from
   query i iff j <= i + (Sk - Sq).  A row with no visible key returns O = 0 and
   LSE = -inf.
+* ALiBi (optional): a per-query-head linear bias -slope * |i + Sk - Sq - j|
+  added to the scaled scores before the softmax (see ``alibi_bias``).
 * LSE is the natural log of the softmax denominator over visible keys,
   m + ln(l), the statistics the pages say are kept ("Reverse engineering ...",
   point 2; "IO-aware tiling ...", backward-pass paragraph).
@@ -88,13 +90,28 @@ def row_softmax(s: np.ndarray):
     return p, m, l
 
 
-def attend_rows(q, k, v, scale, n_visible=None):
+def alibi_bias(rows, Sq, Sk, slope):
+    """ALiBi bias of query rows `rows` against keys 0..Sk-1: -slope * |i + Sk
+    - Sq - j| (linear in the distance from the row's own position; the query
+    positions are aligned to the end of the keys, as the causal mask is).
+    The IO-aware tiling page asks that ALiBi positional biases be supported
+    ("IO-aware tiling strategy in FlashAttention-4", integration paragraph);
+    the bias itself is not defined there."""
+    i = np.asarray(rows, np.float64)[:, None]
+    j = np.arange(Sk, dtype=np.float64)[None, :]
+    return -float(slope) * np.abs(i + (Sk - Sq) - j)
+
+
+def attend_rows(q, k, v, scale, n_visible=None, bias=None):
     """Materialised attention for query rows q [n, d] against k, v [Sk, d]
-    (float64).  n_visible[i] limits row i to keys 0..n_visible[i]-1.
-    Returns (o [n, d], lse [n])."""
+    (float64).  n_visible[i] limits row i to keys 0..n_visible[i]-1; bias
+    [n, Sk], if given, is added to the scaled scores.  Returns (o [n, d],
+    lse [n])."""
     if k.shape[0] == 0:  # no key at all: every row is empty
         return np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf)
     s = scores(q, k, scale)
+    if bias is not None:
+        s = s + bias
     if n_visible is not None:
         j = np.arange(k.shape[0])
         s = np.where(j[None, :] >= np.asarray(n_visible)[:, None], -np.inf, s)
@@ -118,9 +135,11 @@ def _workers():
 
 
 def attention(q_bits, k_bits, v_bits, B, Hq, Hkv, Sq, Sk, scale, causal, layout,
-              chunk=256, workers=None):
+              chunk=256, workers=None, alibi_slopes=None):
     """Full prefill oracle.  Returns (o [B, Hq, Sq, D] float64 in logical
-    head-major order, lse [B, Hq, Sq] float64)."""
+    head-major order, lse [B, Hq, Sq] float64).  alibi_slopes [Hq] (float32
+    values, used as float64), if given, adds ``alibi_bias`` with query head
+    h's slope to the scaled scores."""
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     qv = _logical(q_bits, layout)
@@ -139,7 +158,10 @@ def attention(q_bits, k_bits, v_bits, B, Hq, Hkv, Sq, Sk, scale, causal, layout,
         qq = bf16_to_f64(qv[b, h, i0:i1])
         kk = bf16_to_f64(kv[b, g, :kmax])
         vv_ = bf16_to_f64(vv[b, g, :kmax])
-        oo, ll = attend_rows(qq, kk, vv_, sc, np.minimum(nvis[i0:i1], kmax))
+        bias = None
+        if alibi_slopes is not None:
+            bias = alibi_bias(np.arange(i0, i1), Sq, Sk, alibi_slopes[h])[:, :kmax]
+        oo, ll = attend_rows(qq, kk, vv_, sc, np.minimum(nvis[i0:i1], kmax), bias)
         o[b, h, i0:i1] = oo
         lse[b, h, i0:i1] = ll
 
@@ -295,6 +317,6 @@ def flops_prefill(B, Hq, Sq, Sk, d, causal):
 
 
 __all__ = ["bf16_to_f64", "scale_as_f32", "kv_head_of", "visible_keys", "scores",
-           "row_softmax", "attend_rows", "attention", "attention_sampled", "attention_varlen",
+           "row_softmax", "alibi_bias", "attend_rows", "attention", "attention_sampled", "attention_varlen",
            "gather_pages", "decode_paged", "append_token", "decode_paged_append",
            "flops_prefill"]
