@@ -13,6 +13,7 @@ are already resident in HBM:
 * the other prefill workloads (causal GQA B=8 S=8192, diffusion-style self
   attention S=32760 and its cross attention against 512 keys), timed the
   same way and reported beside the headline (skip with --no-extra);
+* the causal GQA workload with an ALiBi bias (attn_fwd_alibi);
 * packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
   U{1..8192}, reported beside the headline;
 * the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads
@@ -209,10 +210,10 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
     files = {
         "prefill_kernel__mha_prefill_b4_h32_s4096_bhsd.md": (
             "# prefill_kernel on mha_prefill_b4_h32_s4096_bhsd (B=4, H=32, S=4096, BHSD)",
-            [wl_row("mha_prefill_b4_h32_s4096_bhsd", "prefill_kernel<false>")] +
-            [wl_row(f"mha_prefill_b4_h32_s4096_bhsd_{m}", "prefill_kernel<false>")
+            [wl_row("mha_prefill_b4_h32_s4096_bhsd", "prefill_kernel<false, false>")] +
+            [wl_row(f"mha_prefill_b4_h32_s4096_bhsd_{m}", "prefill_kernel<false, false>")
              for m in ROUNDING_MODES] +
-            [kstats_row("prefill_kernel<false>")], ["prefill_kernel"]),
+            [kstats_row("prefill_kernel<false, false>")], ["prefill_kernel"]),
         "decode_partial_and_merge_kernels__paged_decode_b32_hq32_hkv8_len4096.md": (
             "# decode_partial_kernel + decode_merge_kernel on paged_decode_b32_hq32_hkv8_"
             "len4096_page16",
@@ -223,10 +224,13 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
             ["decode_partial_kernel", "decode_merge_kernel"]),
         "prefill_kernel__causal_gqa_s8192_and_diffusion_s32760.md": (
             "# prefill_kernel on the causal GQA and diffusion-style workloads",
-            [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true>"),
-             wl_row("diffusion_self_b2_h12_s32760_bshd", "prefill_kernel<false>"),
-             wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192", "prefill_kernel<true>")], []),
+            [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true, false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi",
+                    "prefill_kernel<true, true>"),
+             wl_row("diffusion_self_b2_h12_s32760_bshd", "prefill_kernel<false, false>"),
+             wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false, false>"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192", "prefill_kernel<true, false>")],
+            []),
         "backward_kernels__mha_b4_h32_s4096_bhsd_and_causal_gqa_s8192.md": (
             "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
             "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
@@ -279,6 +283,25 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
                     "flop": p.flops, "TFLOP/s": round(tf, 2),
                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, o, lse
+    # ALiBi on the causal GQA workload (slopes 2^(-8h/H) of the ALiBi method)
+    p = gen.config3()
+    log(f"timing {p.name} with ALiBi")
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    sl = torch.from_numpy((2.0 ** (-8.0 * np.arange(1, p.Hq + 1) / p.Hq)).astype(np.float32)).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+    def run_a(_i):
+        ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd", out=o, lse=lse,
+                    alibi_slopes=sl)
+
+    ms = time_calls(run_a, steps, 2, torch)
+    tf = p.flops / (ms * 1e-3) / 1e12
+    res.append({"workload": p.name + "_alibi", "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq,
+                "Sk": p.Sk, "causal": True, "layout": "bshd", "ms_per_call": round(ms, 4),
+                "flop": p.flops, "TFLOP/s": round(tf, 2),
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    del q, k, v, o, lse
     # packed sequences of mixed lengths (attn_fwd_varlen)
     pv = gen.varlen_causal_gqa()
     log(f"timing {pv.name}")
@@ -430,14 +453,18 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
-        cmd = {"plan": {"prefill_kernel<false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu)] +
+        cmd = {"plan": {"prefill_kernel<true, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                        "_alibi", xs)],
+                        "prefill_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu)] +
                                                  [(f"mha_prefill_b4_h32_s4096_bhsd_{m}", xs)
                                                   for m in ROUNDING_MODES] +
                                                  [("diffusion_self_b2_h12_s32760_bshd", xs),
                                                   ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs),
                                                   ("mha_prefill_b4_h32_s4096_bhsd_backward_fwd", 1)],
-                        "prefill_kernel<true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", xs),
-                                                 ("varlen_causal_gqa_b16_hq32_hkv8_len8192", xs),
+                        "prefill_kernel<true, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
+                                                         xs),
+                                                        ("varlen_causal_gqa_b16_hq32_hkv8_len8192",
+                                                         xs),
                                                  ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                   "_backward_fwd", 1),
                                                  ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
@@ -586,7 +613,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profiles("prefill_kernel", src_p),
-                     "kernel": "prefill_kernel<false>",
+                     "kernel": "prefill_kernel<false, false>",
                      "per_launch": {"flop": p.flops, "ms": round(ms_p, 4)}},
         "decode": {"workload": d.name, "value": round(gbs, 1), "unit": "GB/s",
                    "us_per_call": round(ms_d * 1e3, 2), "tokens": d.tokens,

@@ -42,7 +42,7 @@ STATUS = {
 }
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_varlen", "attn_decode_workspace_bytes", "attn_decode_paged",
+EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_alibi", "attn_fwd_varlen", "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
            "attn_bwd", "attn_bwd_varlen", "attn_status_string", "attn_version")
 
@@ -68,6 +68,8 @@ def library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd_rounded.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
         lib.attn_fwd_rounded.restype = i
+        lib.attn_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+        lib.attn_fwd_alibi.restype = i
         lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                         vp]
         lib.attn_fwd_varlen.restype = i
@@ -144,9 +146,11 @@ def _rounding_code(rounding: str) -> int:
 
 
 def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
-             layout: str = "bshd", rounding: str = "rtne", out=None, lse=None, stream=None):
+             layout: str = "bshd", rounding: str = "rtne", out=None, lse=None, stream=None,
+             alibi_slopes=None):
     """Fused exact attention forward.  q: [B, Sq, Hq, 128] (bshd) or
     [B, Hq, Sq, 128] (bhsd); k, v likewise with Hkv heads and Sk keys.
+    alibi_slopes: optional fp32 GPU tensor [Hq] (ALiBi bias, attn_fwd_alibi).
     Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -171,7 +175,14 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
             Sq, Sk, d, float(scale), int(bool(causal)), lay)
-    if rnd == ROUNDING["rtne"]:
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or \
+                tuple(alibi_slopes.shape) != (Hq,) or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous fp32 GPU tensor [Hq]")
+        st = library().attn_fwd_alibi(*args[:5], alibi_slopes.data_ptr(), *args[5:], rnd,
+                                      _stream_ptr(stream))
+        where = "attn_fwd_alibi"
+    elif rnd == ROUNDING["rtne"]:
         st, where = library().attn_fwd(*args, _stream_ptr(stream)), "attn_fwd"
     else:
         st, where = library().attn_fwd_rounded(*args, rnd, _stream_ptr(stream)), "attn_fwd_rounded"

@@ -66,9 +66,9 @@ const char* attn_status_string(int status) {
   }
 }
 
-int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal, int layout,
-                     int rounding, void* stream) {
+static int fwd_call(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const float* alibi_slopes, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                    float scale, int causal, int layout, int rounding, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
@@ -101,6 +101,7 @@ int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float
   a.cu_q = nullptr;
   a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
+  a.alibi = alibi_slopes;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
@@ -147,11 +148,28 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.cu_k = cu_seqlens_k;
   a.total_q = total_q;
   a.total_k = total_k;
+  a.alibi = nullptr;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
   const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal, int layout,
+                     int rounding, void* stream) {
+  return fwd_call(q, k, v, o, lse, nullptr, B, Hq, Hkv, Sq, Sk, d, scale, causal, layout,
+                  rounding, stream);
+}
+
+int attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const float* alibi_slopes, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                   float scale, int causal, int layout, int rounding, void* stream) {
+  if (!alibi_slopes) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) return ATTN_ERR_ALIGN;
+  return fwd_call(q, k, v, o, lse, alibi_slopes, B, Hq, Hkv, Sq, Sk, d, scale, causal, layout,
+                  rounding, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,

@@ -36,6 +36,9 @@ struct PrefillArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int total_q, total_k;
+  // ALiBi slopes [Hq] (null: no bias): -slope * |i + Sk - Sq - j| is added to
+  // the scaled scores of query head h
+  const float* alibi;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);

@@ -362,8 +362,21 @@ __device__ __forceinline__ float probs(Wave& w, float c, float msub) {
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-template <bool CAUSAL, bool F16>
-__device__ __forceinline__ void softmax_phase(Wave& w, int kbase, int Sk, int off, float c) {
+template <bool CAUSAL, bool F16, bool ALIBI>
+__device__ __forceinline__ void softmax_phase(Wave& w, int kbase, int Sk, int off, float c,
+                                              float alibi) {
+  if constexpr (ALIBI) {
+    // linear bias on the raw scores: alibi * |i + off - j| (alibi = -slope /
+    // scale), one subtraction and one fma (|.| as a source modifier) per score
+    const float d0 = (float)(w.first + w.l32 + off - kbase - 4 * w.hi);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float key = (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+        w.s[kb][r] = __builtin_fmaf(alibi, __builtin_fabsf(d0 - key), w.s[kb][r]);
+      }
+  }
   const bool need_mask = (kbase + BN > Sk) || (CAUSAL && kbase + BN - 1 > w.first + off);
   if (need_mask) {
     const int row = w.first + w.l32;
@@ -400,6 +413,7 @@ struct Ctx {
   TileLoader ld;
   int n_tiles, Sk, off, wave, lane, group;
   float c;
+  float alibi;   // -slope / scale of this head (ALiBi variants)
 };
 
 // The phased tile loop.  Phase 2t: group 0 runs the MFMA phase of tile t
@@ -418,7 +432,7 @@ struct Ctx {
 //    V^T(t) is first read in phase 2t+2.
 //  * Each group issues the first K-operand reads of its next MFMA phase at
 //    the end of its softmax phase, when that K tile is already visible.
-template <bool CAUSAL, bool F16>
+template <bool CAUSAL, bool F16, bool ALIBI>
 __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, char* vbuf,
                                           char* vtbuf) {
 #pragma unroll
@@ -447,7 +461,8 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
     } else {
       if (t + 1 < T) x.ld.issue_k(t + 1, knext);
       if (t < T) x.ld.issue_v(t, vbuf);
-      if (visible(t - 1)) softmax_phase<CAUSAL, F16>(w, (t - 1) * BN, x.Sk, x.off, x.c);
+      if (visible(t - 1)) softmax_phase<CAUSAL, F16, ALIBI>(w, (t - 1) * BN, x.Sk, x.off, x.c,
+                                                                   x.alibi);
       wait_copies();
       pre = visible(t);
       if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
@@ -455,7 +470,7 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
     barrier();   // K(t+1), V(t) copies have landed (group 1 waited for them)
     // ---- phase 2t+1
     if (g0) {
-      if (visible(t)) softmax_phase<CAUSAL, F16>(w, t * BN, x.Sk, x.off, x.c);
+      if (visible(t)) softmax_phase<CAUSAL, F16, ALIBI>(w, t * BN, x.Sk, x.off, x.c, x.alibi);
       pre = visible(t + 1);
       if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
     } else {
@@ -490,7 +505,7 @@ __device__ __forceinline__ bool state_finite(const Wave& w) {
   return ok;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];   // K, double buffered
@@ -552,6 +567,7 @@ void prefill_kernel(PrefillArgs a) {
   x.off = Sk - Sq;                       // causal: key j visible iff j <= i + off
   x.Sk = Sk;
   x.c = a.c;
+  x.alibi = ALIBI ? -a.alibi[hq] * kLog2e / a.c : 0.f;
   const int last_row = min(q0 + BM, Sq) - 1;
   int n_keys = Sk;
   if (CAUSAL) n_keys = min(Sk, max(0, last_row + x.off + 1));
@@ -601,11 +617,11 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  tile_loop<CAUSAL, true>(w, x, kbuf, vbuf, vtbuf);
+  tile_loop<CAUSAL, true, ALIBI>(w, x, kbuf, vbuf, vtbuf);
   // A V value beyond the fp16 range (|v| >= 65520) or a non-finite input
   // shows up as a non-finite accumulator: redo this workgroup with bf16
   // probabilities and bf16 V, which covers the whole bf16 range.
-  if (__syncthreads_or(!state_finite(w))) tile_loop<CAUSAL, false>(w, x, kbuf, vbuf, vtbuf);
+  if (__syncthreads_or(!state_finite(w))) tile_loop<CAUSAL, false, ALIBI>(w, x, kbuf, vbuf, vtbuf);
 
   // ---- epilogue: O = acc / l (bf16 under the caller's rounding rule) in q's
   // layout; LSE = ln(sum exp)
@@ -649,10 +665,18 @@ void prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.Hq * a.n_qt;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (causal)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, stream, a);
+  if (a.alibi) {
+    if (causal)
+      hipLaunchKernelGGL((prefill_kernel<true, true>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<false, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                         a);
+  } else if (causal) {
+    hipLaunchKernelGGL((prefill_kernel<true, false>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       a);
+  }
   return hipGetLastError();
 }
 

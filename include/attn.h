@@ -12,7 +12,7 @@
  *   attn_bwd           dQ, dK, dV of the forward for an upstream dO, with the
  *                      probabilities recomputed from the forward's LSE.
  * attn_fwd_varlen and attn_bwd_varlen are attn_fwd and attn_bwd over packed
- * sequences of different lengths.
+ * sequences of different lengths; attn_fwd_alibi adds an ALiBi bias.
  *
  * Definitions followed (page titles and sections):
  *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 6
+#define ATTN_VERSION 7
 
 typedef enum {
   ATTN_OK = 0,
@@ -136,6 +136,24 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                      int layout, int rounding, void* stream);
+
+/*
+ * attn_fwd_alibi - attn_fwd_rounded with an ALiBi linear position bias: for
+ * query head h, -alibi_slopes[h] * |i + Sk - Sq - j| is added to the scaled
+ * score of query row i and key j before the softmax (query positions aligned
+ * to the end of the keys, as the causal mask is), and LSE is that of the
+ * biased scores.  ALiBi support is what "IO-aware tiling strategy in
+ * FlashAttention-4" (integration paragraph) asks a drop-in kernel to check;
+ * the bias form is the ALiBi method's own (per-head slopes, linear in the
+ * distance).
+ *
+ *   alibi_slopes  device fp32 [Hq], 4-byte aligned, finite values (device
+ *                 data: not checked); NULL returns ATTN_ERR_NULL
+ * Everything else is as for attn_fwd_rounded.
+ */
+int attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const float* alibi_slopes, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                   float scale, int causal, int layout, int rounding, void* stream);
 
 /*
  * attn_fwd_varlen - attn_fwd over a batch of packed sequences of different

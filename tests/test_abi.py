@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 6
+    assert ea.attn_version() == 7
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -240,6 +240,31 @@ def test_bwd_varlen_valid_arguments_need_a_gfx950_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert bwd_varlen() == -7
     assert bwd_varlen(wsb=8 * 4 * 100) == -7
+
+
+def fwd_alibi(al=P, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.1,
+             causal=0, layout=0, rounding=0, stream=None)
+    a.update(kw)
+    return ea.library().attn_fwd_alibi(a["q"], a["k"], a["v"], a["o"], a["lse"], al, a["B"],
+                                       a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"],
+                                       a["causal"], a["layout"], a["rounding"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(al=None), -1), (dict(q=None), -1), (dict(al=P + 2), -4), (dict(B=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(d=64), -3), (dict(rounding=9), -3), (dict(o=P + 8), -4),
+])
+def test_fwd_alibi_argument_errors(kw, code):
+    assert fwd_alibi(**kw) == code
+
+
+def test_fwd_alibi_valid_arguments_need_a_gfx950_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert fwd_alibi() == -7
+    assert fwd_alibi(al=P + 4) == -7
 
 
 def test_binding_rejects_unknown_rounding_name():

@@ -1,0 +1,80 @@
+"""Parity of the ALiBi forward (attn_fwd_alibi) with the fp64 oracle (GPU),
+under the forward's tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as gen
+import exact_attention_60_amd as ea
+import oracle.attention as att
+from gpu_util import dev_bf16, host_f64, logical_o, need_gpu
+from tolerance import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def slopes(H):
+    """The geometric slopes of the ALiBi paper for H heads (2^(-8h/H))."""
+    return (2.0 ** (-8.0 * np.arange(1, H + 1) / H)).astype(np.float32)
+
+
+def lay(p):
+    return "bshd" if p.layout == gen.BSHD else "bhsd"
+
+
+def run(p, sl, rounding="rtne"):
+    o, lse = ea.attn_fwd(dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v), causal=p.causal,
+                         scale=p.scale, layout=lay(p), rounding=rounding,
+                         alibi_slopes=torch.from_numpy(sl).cuda())
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,layout,causal", [
+    (1, 4, 4, 256, 256, gen.BSHD, False),
+    (2, 8, 2, 200, 200, gen.BSHD, True),       # GQA causal, ragged tiles
+    (1, 4, 2, 300, 77, gen.BHSD, False),       # cross attention, keys before and after i + off
+    (1, 4, 2, 150, 100, gen.BSHD, True),       # rows that see no key
+    (1, 4, 1, 70, 600, gen.BHSD, True),        # bottom-right alignment
+])
+def test_alibi_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=Sq + 2 * Sk,
+                           n_hot=2)
+    sl = slopes(Hq)
+    o, lse = run(p, sl)
+    o_ref, l_ref = att.attention(p.q, p.k, p.v, B, Hq, Hkv, Sq, Sk, p.scale, causal, p.layout,
+                                 alibi_slopes=sl)
+    e = check_o(logical_o(o, p.layout), o_ref, "alibi")
+    el = check_lse(host_f64(lse), l_ref, "alibi lse")
+    print(f"alibi B{B} Hq{Hq} Sq{Sq} Sk{Sk} causal{causal}: err/tol {e[1]:.3f} lse {el:.3g}",
+          flush=True)
+
+
+def test_zero_slopes_equal_the_plain_kernel_bitwise():
+    p = gen.prefill_inputs(1, 4, 2, 333, 333, layout=gen.BSHD, causal=True, seed=3)
+    o1, l1 = run(p, np.zeros(4, np.float32))
+    o2, l2 = ea.attn_fwd(dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v), causal=True, scale=p.scale,
+                         layout="bshd")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_alibi_causal_gqa_full_size_sampled_group():
+    """The causal GQA workload (B=8, Hq=32, Hkv=8, S=8192) with ALiBi: every
+    row of one K/V head's four query heads."""
+    p = gen.config3()
+    sl = slopes(32)
+    o, lse = run(p, sl)
+    b, g, G = 5, 6, 4
+    sub = [np.ascontiguousarray(x[b:b + 1, :, h0:h1])
+           for x, h0, h1 in ((p.q, g * G, g * G + G), (p.k, g, g + 1), (p.v, g, g + 1))]
+    o_ref, l_ref = att.attention(*sub, 1, G, 1, p.Sq, p.Sk, p.scale, True, gen.BSHD,
+                                 alibi_slopes=sl[g * G:g * G + G])
+    e = check_o(logical_o(o[b:b + 1, :, g * G:g * G + G], gen.BSHD), o_ref, "alibi cfg3")
+    check_lse(host_f64(lse[b:b + 1, g * G:g * G + G]), l_ref, "alibi cfg3 lse")
+    print(f"alibi causal gqa b{b} g{g}: err/tol {e[1]:.3f}", flush=True)
