@@ -38,8 +38,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import (BHSD, BSHD, _logical, _run, bf16_to_f64, kv_head_of,  # noqa: F401
-                        row_softmax, scale_as_f32, scores, visible_keys)
+from .attention import (BHSD, BSHD, _logical, _run, alibi_bias, bf16_to_f64,  # noqa: F401
+                        kv_head_of, row_softmax, scale_as_f32, scores, visible_keys)
 
 
 def as_f64(x: np.ndarray) -> np.ndarray:
@@ -49,10 +49,13 @@ def as_f64(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def probabilities(q, k, scale, n_visible=None):
+def probabilities(q, k, scale, n_visible=None, bias=None):
     """P [n, Sk] of query rows q [n, d] against keys k [Sk, d], with row i
-    limited to keys 0..n_visible[i]-1 (all-masked rows give P = 0)."""
+    limited to keys 0..n_visible[i]-1 (all-masked rows give P = 0) and bias
+    [n, Sk] (ALiBi), if given, added to the scaled scores."""
     s = scores(q, k, scale)
+    if bias is not None:
+        s = s + bias
     if n_visible is not None:
         j = np.arange(k.shape[0])
         s = np.where(j[None, :] >= np.asarray(n_visible)[:, None], -np.inf, s)
@@ -60,11 +63,11 @@ def probabilities(q, k, scale, n_visible=None):
     return p
 
 
-def grad_rows(q, k, v, do, scale, n_visible=None):
+def grad_rows(q, k, v, do, scale, n_visible=None, bias=None):
     """Gradient of sum(do * O) for O = attention of query rows q [n, d]
-    against k, v [Sk, d] (float64).  Returns (dq [n, d], dk [Sk, d],
-    dv [Sk, d])."""
-    p = probabilities(q, k, scale, n_visible)
+    against k, v [Sk, d] (float64).  A bias (constant in Q, K, V) enters only
+    P.  Returns (dq [n, d], dk [Sk, d], dv [Sk, d])."""
+    p = probabilities(q, k, scale, n_visible, bias)
     dv = p.T @ do
     dp = do @ v.T
     ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
@@ -73,14 +76,14 @@ def grad_rows(q, k, v, do, scale, n_visible=None):
     return dq, dk, dv
 
 
-def grad_magnitudes(q, k, v, do, scale, n_visible=None):
+def grad_magnitudes(q, k, v, do, scale, n_visible=None, bias=None):
     """Sums of absolute terms behind each gradient entry, the scale of its
     rounding error when the products are formed from bf16-rounded operands
     (P, dS) and the row term from a rounded O.  With
     Dabs_i = sum_c |dO_ic O_ic| and A = P * (|dP| + Dabs):
         mdv = P^T |dO|,  mdq = scale * A |K|,  mdk = scale * A^T |Q|.
     Returns (mdq [n, d], mdk [Sk, d], mdv [Sk, d])."""
-    p = probabilities(q, k, scale, n_visible)
+    p = probabilities(q, k, scale, n_visible, bias)
     o = p @ v
     dabs = np.abs(do * o).sum(axis=1, keepdims=True)
     a = p * (np.abs(do @ v.T) + dabs)
@@ -88,12 +91,13 @@ def grad_magnitudes(q, k, v, do, scale, n_visible=None):
 
 
 def attention_backward(q_in, k_in, v_in, do_in, B, Hq, Hkv, Sq, Sk, scale, causal, layout,
-                       chunk=512, workers=None, magnitudes=False):
+                       chunk=512, workers=None, magnitudes=False, alibi_slopes=None):
     """Full backward oracle.  q_in/do_in: [B,Sq,Hq,D] (BSHD) or [B,Hq,Sq,D]
     (BHSD); k_in/v_in likewise with Hkv heads and Sk rows.  Returns
     (dq [B,Hq,Sq,D], dk [B,Hkv,Sk,D], dv [B,Hkv,Sk,D]) float64 in logical
     head-major order, followed by the three magnitude arrays of
-    ``grad_magnitudes`` (same shapes) when magnitudes=True."""
+    ``grad_magnitudes`` (same shapes) when magnitudes=True.  alibi_slopes
+    [Hq]: the forward had the ALiBi bias of ``oracle.attention.alibi_bias``."""
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     qv, kv, vv, dov = (_logical(x, layout) for x in (q_in, k_in, v_in, do_in))
@@ -114,8 +118,11 @@ def attention_backward(q_in, k_in, v_in, do_in, B, Hq, Hkv, Sq, Sk, scale, causa
                 continue
             for i0 in range(0, Sq, chunk):
                 i1 = min(Sq, i0 + chunk)
+                bias = None
+                if alibi_slopes is not None:
+                    bias = alibi_bias(np.arange(i0, i1), Sq, Sk, alibi_slopes[h])
                 args = (as_f64(qv[b, h, i0:i1]), kk, vv_, as_f64(dov[b, h, i0:i1]), sc,
-                        nvis[i0:i1])
+                        nvis[i0:i1], bias)
                 gq, gk, gv = grad_rows(*args)
                 dq[b, h, i0:i1] = gq
                 dk[b, g] += gk

@@ -15,24 +15,27 @@ def _logical(x, layout):
     return x.transpose(0, 2, 1, 3) if layout == BSHD else x
 
 
-def _loss(q, k, v, do, B, Hq, Hkv, Sq, Sk, scale, causal, layout):
+def _loss(q, k, v, do, B, Hq, Hkv, Sq, Sk, scale, causal, layout, slopes=None):
     """L = sum(dO * O) with O from the forward oracle's attend_rows (float64
-    inputs)."""
+    inputs), with the ALiBi bias of the given slopes."""
     ql, kl, vl, dol = (_logical(x, layout) for x in (q, k, v, do))
     nv = np.array([att.visible_keys(i, Sq, Sk, causal) for i in range(Sq)])
     total = 0.0
     for b in range(B):
         for h in range(Hq):
             g = att.kv_head_of(h, Hq, Hkv)
-            o, _ = att.attend_rows(ql[b, h], kl[b, g], vl[b, g], float(np.float32(scale)), nv)
+            bias = None if slopes is None else att.alibi_bias(np.arange(Sq), Sq, Sk, slopes[h])
+            o, _ = att.attend_rows(ql[b, h], kl[b, g], vl[b, g], float(np.float32(scale)), nv,
+                                   bias)
             total += float((o * dol[b, h]).sum())
     return total
 
 
 def finite_difference(bwd, B=1, Hq=4, Hkv=2, Sq=5, Sk=7, d=8, causal=False, layout=BSHD,
-                      seed=0, eps=1e-6, tol=1e-7):
+                      seed=0, eps=1e-6, tol=1e-7, slopes=None):
     """Central differences of L = sum(dO * O) (forward oracle, float64) against
-    the analytic gradient, every entry of dQ, dK and dV."""
+    the analytic gradient, every entry of dQ, dK and dV (with ALiBi when
+    slopes are given)."""
     r = np.random.default_rng(seed)
     q = r.standard_normal(gen.layout_shape(layout, B, Hq, Sq, d))
     k = r.standard_normal(gen.layout_shape(layout, B, Hkv, Sk, d))
@@ -40,7 +43,7 @@ def finite_difference(bwd, B=1, Hq=4, Hkv=2, Sq=5, Sk=7, d=8, causal=False, layo
     do = r.standard_normal(gen.layout_shape(layout, B, Hq, Sq, d))
     scale = 0.375  # exact in float32
     args = (B, Hq, Hkv, Sq, Sk, scale, causal, layout)
-    dq, dk, dv = bwd.attention_backward(q, k, v, do, *args, workers=1)
+    dq, dk, dv = bwd.attention_backward(q, k, v, do, *args, workers=1, alibi_slopes=slopes)
     for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
         num = np.zeros_like(x)
         it = np.nditer(x, flags=["multi_index"])
@@ -48,9 +51,9 @@ def finite_difference(bwd, B=1, Hq=4, Hkv=2, Sq=5, Sk=7, d=8, causal=False, layo
             idx = it.multi_index
             old = x[idx]
             x[idx] = old + eps
-            lp = _loss(q, k, v, do, *args)
+            lp = _loss(q, k, v, do, *args, slopes)
             x[idx] = old - eps
-            lm = _loss(q, k, v, do, *args)
+            lm = _loss(q, k, v, do, *args, slopes)
             x[idx] = old
             num[idx] = (lp - lm) / (2 * eps)
         err = np.abs(_logical(num, layout) - g).max()
@@ -181,6 +184,10 @@ ALL = [
     ("finite differences, non-causal BSHD", lambda m: finite_difference(m)),
     ("finite differences, causal BHSD", lambda m: finite_difference(m, causal=True, layout=BHSD)),
     ("finite differences, causal Sq > Sk", lambda m: finite_difference(m, Sq=7, Sk=4, causal=True)),
+    ("finite differences, ALiBi causal", lambda m: finite_difference(
+        m, Sq=6, Sk=9, causal=True, slopes=np.array([0.5, 0.25, 0.125, 0.0625], np.float32))),
+    ("finite differences, ALiBi cross", lambda m: finite_difference(
+        m, Sq=7, Sk=4, layout=BHSD, slopes=np.array([1.0, 0.5, 0.3, 0.2], np.float32))),
     ("torch autograd", lambda m: torch_autograd(m)),
     ("invariants", lambda m: invariants(m)),
     ("invariants causal", lambda m: invariants(m, causal=True, layout=BHSD)),

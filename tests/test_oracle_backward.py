@@ -43,8 +43,8 @@ def fresh():
 
 def _with_grad_rows(body):
     def plant(m):
-        def grad_rows(q, k, v, do, scale, n_visible=None):
-            p = m.probabilities(q, k, scale, n_visible)
+        def grad_rows(q, k, v, do, scale, n_visible=None, bias=None):
+            p = m.probabilities(q, k, scale, n_visible, bias)
             return body(p, q, k, v, do, scale)
         m.grad_rows = grad_rows
     return plant
@@ -87,7 +87,7 @@ def _row_term_column_sum(p, q, k, v, do, s):
 
 def _mask_ignored(m):
     orig = m.probabilities
-    m.probabilities = lambda q, k, scale, n_visible=None: orig(q, k, scale, None)
+    m.probabilities = lambda q, k, scale, n_visible=None, bias=None: orig(q, k, scale, None, bias)
 
 
 def _group_overwrites(m):
@@ -106,7 +106,14 @@ def _group_overwrites(m):
     m.attention_backward = ab
 
 
+def _alibi_ignored_in_backward(m):
+    # the recomputed probabilities leave the bias out
+    orig = m.probabilities
+    m.probabilities = lambda q, k, scale, n_visible=None, bias=None: orig(q, k, scale, n_visible)
+
+
 MUTANTS = {
+    "ALiBi bias left out of the recomputed P": _alibi_ignored_in_backward,
     "row term dropped": _with_grad_rows(_no_row_term),
     "row term sign": _with_grad_rows(_row_term_sign),
     "dK without the scale": _with_grad_rows(_dk_unscaled),
