@@ -235,18 +235,23 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
             "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
             "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
             [wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_prep_kernel"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<false, false>"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false, false>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<false, false, false>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false, false, false>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                    "bwd_dkdv_kernel<true, false>"),
+                    "bwd_dkdv_kernel<true, false, false>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                    "bwd_dq_kernel<true, false>"),
+                    "bwd_dq_kernel<true, false, false>"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_prep_kernel"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                    "bwd_dkdv_kernel<true, true>"),
+                    "bwd_dkdv_kernel<true, true, false>"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                    "bwd_dq_kernel<true, true>")],
+                    "bwd_dq_kernel<true, true, false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", "bwd_prep_kernel"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward",
+                    "bwd_dkdv_kernel<true, false, true>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward",
+                    "bwd_dq_kernel<true, false, true>")],
             ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]),
     }
     for fname, (title, rows, tkeys) in files.items():
@@ -365,6 +370,30 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         res.append(ent)
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    # the causal GQA backward with ALiBi (attn_bwd_alibi)
+    p = gen.config3()
+    log(f"timing the backward of {p.name} with ALiBi")
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    do = to_dev(gen.output_grad(p, 3))
+    sl = torch.from_numpy((2.0 ** (-8.0 * np.arange(1, p.Hq + 1) / p.Hq)).astype(np.float32)).to(
+        q.device)
+    o, lse = ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd", alibi_slopes=sl)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(p.B, p.Hq, p.Sq), dtype=torch.uint8,
+                     device=q.device)
+
+    def run_a(_i):
+        ea.attn_bwd(q, k, v, o, lse, do, causal=True, scale=p.scale, layout="bshd", dq=dq, dk=dk,
+                    dv=dv, workspace=ws, alibi_slopes=sl)
+
+    ms = time_calls(run_a, steps, 2, torch)
+    fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 128 / 2
+    res.append({"workload": p.name + "_alibi_backward", "ms_per_call": round(ms, 4), "flop": fl,
+                "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+                "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
     # packed sequences of mixed lengths (attn_bwd_varlen)
     pv = gen.varlen_causal_gqa()
     log(f"timing the backward of {pv.name}")
@@ -454,7 +483,9 @@ def main():
     if args.summarize:
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
         cmd = {"plan": {"prefill_kernel<true, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                        "_alibi", xs)],
+                                                        "_alibi", xs),
+                                                       ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                                                        "_alibi_backward_fwd", 1)],
                         "prefill_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu)] +
                                                  [(f"mha_prefill_b4_h32_s4096_bhsd_{m}", xs)
                                                   for m in ROUNDING_MODES] +
@@ -472,20 +503,26 @@ def main():
                         "bwd_prep_kernel": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),
                                             ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
                                              xs),
+                                            ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi"
+                                             "_backward", xs),
                                             ("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
                                              xs)],
-                        "bwd_dkdv_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
+                        "bwd_dkdv_kernel<false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
                                                            xs)],
-                        "bwd_dq_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
+                        "bwd_dq_kernel<false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
                                                          xs)],
-                        "bwd_dkdv_kernel<true, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                        "bwd_dkdv_kernel<true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                           "_backward", xs)],
-                        "bwd_dq_kernel<true, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                        "bwd_dq_kernel<true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                         "_backward", xs)],
-                        "bwd_dkdv_kernel<true, true>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
+                        "bwd_dkdv_kernel<true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                          "_backward", xs)],
-                        "bwd_dq_kernel<true, true>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
+                        "bwd_dq_kernel<true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                        "_backward", xs)],
+                        "bwd_dkdv_kernel<true, false, true>": [(
+                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
+                        "bwd_dq_kernel<true, false, true>": [(
+                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
                                                    st + wu),
                                                   ("paged_decode_b32_hq32_hkv8_len4096_page16_append",

@@ -44,7 +44,7 @@ STATUS = {
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_alibi", "attn_fwd_varlen", "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
-           "attn_bwd", "attn_bwd_varlen", "attn_status_string", "attn_version")
+           "attn_bwd", "attn_bwd_alibi", "attn_bwd_varlen", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -89,6 +89,9 @@ def library() -> ctypes.CDLL:
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp,
                                  sz, vp]
         lib.attn_bwd.restype = i
+        lib.attn_bwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f,
+                                       i, i, vp, sz, vp]
+        lib.attn_bwd_alibi.restype = i
         lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
                                         i, i, i, f, i, vp, sz, vp]
         lib.attn_bwd_varlen.restype = i
@@ -288,10 +291,12 @@ def attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, seq
 
 
 def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None,
-             layout: str = "bshd", dq=None, dk=None, dv=None, workspace=None, stream=None):
+             layout: str = "bshd", dq=None, dk=None, dv=None, workspace=None, stream=None,
+             alibi_slopes=None):
     """Gradients of attn_fwd for an upstream gradient do (q's layout and
-    shape), from the forward's inputs q, k, v and outputs o, lse.  Returns
-    (dq in q's layout, dk and dv in k's layout), all bf16."""
+    shape), from the forward's inputs q, k, v and outputs o, lse (and its
+    ALiBi slopes, if it had any: attn_bwd_alibi).  Returns (dq in q's layout,
+    dk and dv in k's layout), all bf16."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_bf16(n, t)
@@ -318,13 +323,19 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
     need = attn_bwd_workspace_bytes(B, Hq, Sq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = library().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), B, Hq, Hkv, Sq, Sk, d, float(scale),
-                            int(bool(causal)), lay, workspace.data_ptr(),
-                            workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    tail = (B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)), lay, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or \
+                tuple(alibi_slopes.shape) != (Hq,) or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous fp32 GPU tensor [Hq]")
+        st, where = library().attn_bwd_alibi(*head, alibi_slopes.data_ptr(), *tail), "attn_bwd_alibi"
+    else:
+        st, where = library().attn_bwd(*head, *tail), "attn_bwd"
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, where)
     return dq, dk, dv
 
 

@@ -287,10 +287,10 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq) {
   return (size_t)2 * B * Hq * Sq * sizeof(float);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
-             int Sk, int d, float scale, int causal, int layout, void* workspace,
-             size_t workspace_bytes, void* stream) {
+static int bwd_call(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, const float* alibi_slopes,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                    int layout, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
@@ -333,11 +333,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.cu_q = nullptr;
   a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
+  a.alibi = alibi_slopes;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
   const hipError_t e = attn::launch_backward(a, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+             int Sk, int d, float scale, int causal, int layout, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  return bwd_call(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, Hq, Hkv, Sq, Sk, d, scale,
+                  causal, layout, workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_alibi(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, const float* alibi_slopes,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                   int layout, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!alibi_slopes) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u) return ATTN_ERR_ALIGN;
+  return bwd_call(q, k, v, o, lse, dout, dq, dk, dv, alibi_slopes, B, Hq, Hkv, Sq, Sk, d, scale,
+                  causal, layout, workspace, workspace_bytes, stream);
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -394,6 +413,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.cu_k = cu_seqlens_k;
   a.total_q = total_q;
   a.total_k = total_k;
+  a.alibi = nullptr;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;

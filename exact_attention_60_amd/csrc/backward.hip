@@ -190,19 +190,24 @@ __device__ __forceinline__ void read_rowvals(f32x4 (&l4)[4], f32x4 (&d4)[4], con
 // P = exp2(S*c - L) and dS = P (dP - D), rounded to bf16 as the A operands of
 // the dV and dK products.  With MASK, entries whose key is past the end or
 // (causal) past the row's diagonal get P = 0: row0 is the global row of
-// register 0 (4h included), key the lane's key.
-template <bool MASK>
+// register 0 (4h included), key the lane's key.  With ALIBI the exponent also
+// gets alibi2 * |d0 + 8*q4 + i| (alibi2 = -slope*log2(e), d0 = the distance
+// row + off - key of register 0).
+template <bool MASK, bool ALIBI = false>
 __device__ __forceinline__ void softmax_grad(bf16x8 (&pa)[2], bf16x8 (&da)[2], const f32x16& s,
                                              const f32x16& p, const f32x4 (&l4)[4],
                                              const f32x4 (&d4)[4], float c, int row0, int key,
-                                             int Sk, int off, int causal) {
+                                             int Sk, int off, int causal, float alibi2 = 0.f,
+                                             float d0 = 0.f) {
   float pv[16], dv[16];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * q4 + i;
-      float x = fast_exp2(s[r] * c - l4[q4][i]);
+      float e = s[r] * c - l4[q4][i];
+      if (ALIBI) e = __builtin_fmaf(alibi2, __builtin_fabsf(d0 + (float)(8 * q4 + i)), e);
+      float x = fast_exp2(e);
       if (MASK) {
         const int row = row0 + 8 * q4 + i;
         if (key >= Sk || (causal && key > row + off)) x = 0.f;
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---- dK, dV ----------------------------------------------------------------
-template <bool CAUSAL, bool PACKED>
+template <bool CAUSAL, bool PACKED, bool ALIBI>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char qbuf[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char dobuf[2 * TILE];
@@ -400,6 +405,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     barrier();
     if (s + 1 < total) issue(s + 1, st ^ 1);
     const int q0 = (qb_first + s % per_head) * QB;
+    // ALiBi: -slope * log2(e) of this step's query head, and the distance
+    // row + off - key of register 0 of sub-block 0 (sub-block 1: +32)
+    const float alibi2 = ALIBI ? -a.alibi[g * a.group + s / per_head] * kLog2e : 0.f;
+    const float ad0 = (float)(q0 + 4 * h + off - (kw0 + c));
     const char* qt = qbuf + st * TILE;
     const char* dt = dobuf + st * TILE;
     const float* lb = lbuf + st * QB;
@@ -433,14 +442,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       mfma_sdp(s1, p1, qa1, oa1, kf, vf);
       bf16x8 pa0[2], da0[2];
-      softmax_grad<false>(pa0, da0, s0, p0, l0, d0, a.c, 0, 0, 0, 0, 0);
+      softmax_grad<false, ALIBI>(pa0, da0, s0, p0, l0, d0, a.c, 0, 0, 0, 0, 0, alibi2, ad0);
       interleave_mfma_valu();
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 oc1[2][4], qc1[2][4];
       read_cols(oc1, qc1, qt, dt, 32, lane);
       mfma_dvdk(dv, dk, pa0, da0, oc0, qc0);
       bf16x8 pa1[2], da1[2];
-      softmax_grad<false>(pa1, da1, s1, p1, l1, d1, a.c, 0, 0, 0, 0, 0);
+      softmax_grad<false, ALIBI>(pa1, da1, s1, p1, l1, d1, a.c, 0, 0, 0, 0, 0, alibi2,
+                                 ad0 + 32.f);
       interleave_mfma_valu();
       __builtin_amdgcn_sched_barrier(0);
       mfma_dvdk(dv, dk, pa1, da1, oc1, qc1);
@@ -467,9 +477,11 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 pa[2], da[2];
       if (msk[qs])
-        softmax_grad<CAUSAL>(pa, da, sacc, pacc, l4, d4, a.c, r0 + 4 * h, kw0 + c, Sk, off, 1);
+        softmax_grad<CAUSAL, ALIBI>(pa, da, sacc, pacc, l4, d4, a.c, r0 + 4 * h, kw0 + c, Sk, off,
+                                    1, alibi2, ad0 + 32.f * qs);
       else
-        softmax_grad<false>(pa, da, sacc, pacc, l4, d4, a.c, 0, 0, 0, 0, 0);
+        softmax_grad<false, ALIBI>(pa, da, sacc, pacc, l4, d4, a.c, 0, 0, 0, 0, 0, alibi2,
+                                   ad0 + 32.f * qs);
       mfma_dvdk(dv, dk, pa, da, oc, qc);
     }
   }
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 // ---- dQ --------------------------------------------------------------------
 // Two workgroups per CU (two waves per SIMD, 64 KB of LDS each): one wave's
 // exponentials and operand reads run under the other's MFMAs.
-template <bool CAUSAL, bool PACKED>
+template <bool CAUSAL, bool PACKED, bool ALIBI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE];
@@ -542,6 +554,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int64_t srow = sv.row0 + hq * sv.hstride;
   const float l2 = q < Sq ? a.ws_l[srow + q] : INFINITY;
   const float drow = q < Sq ? a.ws_d[srow + q] : 0.f;
+  const float alibi2 = ALIBI ? -a.alibi[hq] * kLog2e : 0.f;   // -slope * log2(e)
 
   const int last_row = min(q0 + Q_ROWS, Sq) - 1;
   const int n_keys = CAUSAL ? min(Sk, max(0, last_row + off + 1)) : Sk;
@@ -597,9 +610,14 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) pacc = mfma32(va[ks], df[ks], pacc);
       float ds[16];
+      // ALiBi distance row + off - key of register 0
+      const float ad0 = (float)(q + off - kr0 - 4 * h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(sacc[r] * a.c - l2);
+        float e = sacc[r] * a.c - l2;
+        if (ALIBI)
+          e = __builtin_fmaf(alibi2, __builtin_fabsf(ad0 - (float)(8 * (r >> 2) + (r & 3))), e);
+        float pv = fast_exp2(e);
         if (mask) {
           const int key = kr0 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (key >= Sk || (CAUSAL && key > q + off)) pv = 0.f;
@@ -640,19 +658,29 @@ hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_rows16, a.Hq, prep_b), dim3(256), 0, stream,
                      a);
   const bool packed = a.cu_q != nullptr;
-  if (causal && packed) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<true, true>), dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<true, true>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+  const dim3 gk((unsigned)g_kv), gq((unsigned)g_q), bt(NT);
+  if (packed) {
+    if (causal) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<true, true, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<true, true, false>), gq, bt, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<false, true, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<false, true, false>), gq, bt, 0, stream, a);
+    }
+  } else if (a.alibi) {
+    if (causal) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<true, false, true>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<true, false, true>), gq, bt, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<false, false, true>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<false, false, true>), gq, bt, 0, stream, a);
+    }
   } else if (causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<true, false>), dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<true, false>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
-  } else if (packed) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<false, true>), dim3((unsigned)g_kv), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<false, true>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, false, false>), gk, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<true, false, false>), gq, bt, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<false, false>), dim3((unsigned)g_kv), dim3(NT), 0, stream,
-                       a);
-    hipLaunchKernelGGL((bwd_dq_kernel<false, false>), dim3((unsigned)g_q), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<false, false, false>), gk, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<false, false, false>), gq, bt, 0, stream, a);
   }
   return hipGetLastError();
 }

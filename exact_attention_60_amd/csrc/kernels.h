@@ -111,6 +111,7 @@ struct BwdArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int total_q, total_k;
+  const float* alibi;    // ALiBi slopes [Hq] of the forward (null: none; dense only)
 };
 
 hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream);

@@ -12,7 +12,8 @@
  *   attn_bwd           dQ, dK, dV of the forward for an upstream dO, with the
  *                      probabilities recomputed from the forward's LSE.
  * attn_fwd_varlen and attn_bwd_varlen are attn_fwd and attn_bwd over packed
- * sequences of different lengths; attn_fwd_alibi adds an ALiBi bias.
+ * sequences of different lengths; attn_fwd_alibi and attn_bwd_alibi add an
+ * ALiBi bias.
  *
  * Definitions followed (page titles and sections):
  *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
@@ -75,7 +76,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 7
+#define ATTN_VERSION 8
 
 typedef enum {
   ATTN_OK = 0,
@@ -314,6 +315,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
              int Sk, int d, float scale, int causal, int layout, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_alibi - attn_bwd for attn_fwd_alibi: the gradients of the forward
+ * with the ALiBi bias (the bias does not depend on Q, K or V, so it enters
+ * only the recomputed probabilities).  alibi_slopes as for attn_fwd_alibi
+ * (the same values the forward used); o and lse from attn_fwd_alibi.
+ * Everything else is as for attn_bwd.
+ */
+int attn_bwd_alibi(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, const float* alibi_slopes,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                   int layout, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_bwd_varlen - attn_bwd for packed sequences (the backward of

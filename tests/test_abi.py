@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 7
+    assert ea.attn_version() == 8
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -265,6 +265,24 @@ def test_fwd_alibi_valid_arguments_need_a_gfx950_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert fwd_alibi() == -7
     assert fwd_alibi(al=P + 4) == -7
+
+
+def bwd_alibi(al=P, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8,
+             d=128, scale=0.1, causal=0, layout=0, ws=P, wsb=10 ** 6, stream=None)
+    a.update(kw)
+    return ea.library().attn_bwd_alibi(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"],
+                                       a["dq"], a["dk"], a["dv"], al, a["B"], a["Hq"], a["Hkv"],
+                                       a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"],
+                                       a["layout"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(al=None), -1), (dict(dq=None), -1), (dict(al=P + 2), -4), (dict(B=0), -2),
+    (dict(d=64), -3), (dict(ws=None), -5),
+])
+def test_bwd_alibi_argument_errors(kw, code):
+    assert bwd_alibi(**kw) == code
 
 
 def test_binding_rejects_unknown_rounding_name():

@@ -78,3 +78,27 @@ def test_alibi_causal_gqa_full_size_sampled_group():
     e = check_o(logical_o(o[b:b + 1, :, g * G:g * G + G], gen.BSHD), o_ref, "alibi cfg3")
     check_lse(host_f64(lse[b:b + 1, g * G:g * G + G]), l_ref, "alibi cfg3 lse")
     print(f"alibi causal gqa b{b} g{g}: err/tol {e[1]:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,layout,causal", [
+    (2, 8, 2, 200, 200, gen.BSHD, True),
+    (1, 4, 2, 300, 77, gen.BHSD, False),
+    (1, 4, 1, 70, 600, gen.BHSD, True),
+])
+def test_alibi_backward_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
+    import oracle.backward as obwd
+    from test_gpu_backward import check as check_grad, logical
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=Sq + 3 * Sk)
+    do = gen.output_grad(p, 4)
+    sl = slopes(Hq)
+    slt = torch.from_numpy(sl).cuda()
+    q, k, v = dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v)
+    o, lse = ea.attn_fwd(q, k, v, causal=causal, scale=p.scale, layout=lay(p), alibi_slopes=slt)
+    g = ea.attn_bwd(q, k, v, o, lse, dev_bf16(do), causal=causal, scale=p.scale, layout=lay(p),
+                    alibi_slopes=slt)
+    torch.cuda.synchronize()
+    ref = obwd.attention_backward(p.q, p.k, p.v, do, B, Hq, Hkv, Sq, Sk, p.scale, causal,
+                                  p.layout, magnitudes=True, alibi_slopes=sl)
+    r = [check_grad(f"alibi {n}", logical(t, p.layout), ref[i], ref[i + 3])
+         for i, (n, t) in enumerate(zip(("dq", "dk", "dv"), g))]
+    print(f"alibi backward Sq{Sq} Sk{Sk} causal{causal}: max err/tol {max(r):.3f}", flush=True)
