@@ -84,6 +84,40 @@ def time_calls(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def per_call_stats(fn, reps, torch):
+    """Median and minimum of `reps` calls timed one by one (an event pair per
+    call on the launch stream), in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median_ms": round(t[len(t) // 2], 5), "min_ms": round(t[0], 5), "reps": reps}
+
+
+def device_clock_info(torch):
+    """CU count and peak engine clock of device 0 (hipDeviceGetAttribute,
+    hipDeviceAttributeClockRate = 5, in kHz), and the dense bf16 MFMA rate they
+    give at 4096 FLOP per CU per clock; None where the runtime does not
+    answer."""
+    import ctypes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0 and v.value > 0:
+            khz = v.value
+    except OSError:
+        pass
+    peak = cus * khz * 1e3 * 4096 / 1e12 if khz else None
+    return {"cus": cus, "clock_mhz": khz / 1e3 if khz else None,
+            "bf16_peak_at_clock_TFLOP/s": round(peak, 1) if peak else None}
+
+
 def cpu_baseline(p, budget_s, torch):
     """Time the oracle (as it is) on whole (b, h) heads of the prefill
     workload until about budget_s seconds of host work are done."""
@@ -486,7 +520,8 @@ def main():
                                                         "_alibi", xs),
                                                        ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                         "_alibi_backward_fwd", 1)],
-                        "prefill_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd", st + wu)] +
+                        "prefill_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd",
+                                                          st + wu + max(st, 20))] +
                                                  [(f"mha_prefill_b4_h32_s4096_bhsd_{m}", xs)
                                                   for m in ROUNDING_MODES] +
                                                  [("diffusion_self_b2_h12_s32760_bshd", xs),
@@ -524,11 +559,11 @@ def main():
                         "bwd_dq_kernel<true, false, true>": [(
                             "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
-                                                   st + wu),
+                                                   max(st, 20) + wu + max(st, 40)),
                                                   ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
                                                    max(st, 20) + 3)],
                         "decode_merge_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
-                                                 st + wu),
+                                                 max(st, 20) + wu + max(st, 40)),
                                                 ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
                                                  max(st, 20) + 3)]},
                "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace "
@@ -612,6 +647,10 @@ def main():
 
     tflops = p.flops / (ms_p * 1e-3) / 1e12
     gbs = d.bytes / (ms_d * 1e-3) / 1e9
+    # per-call distribution of the same two calls (median and minimum)
+    st_p = per_call_stats(prefill, max(args.steps, 20), torch)
+    st_d = per_call_stats(decode, max(args.steps, 40), torch)
+    dev_info = device_clock_info(torch)
 
     # ---- quick sampled parity of what was timed
     import oracle.attention as att
@@ -651,14 +690,24 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profiles("prefill_kernel", src_p),
                      "kernel": "prefill_kernel<false, false>",
-                     "per_launch": {"flop": p.flops, "ms": round(ms_p, 4)}},
+                     "per_launch": {"flop": p.flops, "ms": round(ms_p, 4)},
+                     "per_call": {**st_p, "TFLOP/s_at_median": round(
+                         p.flops / (st_p["median_ms"] * 1e-3) / 1e12, 2)},
+                     "device": dev_info,
+                     "frac_of_peak_at_device_clock": (
+                         round(tflops / dev_info["bf16_peak_at_clock_TFLOP/s"], 4)
+                         if dev_info["bf16_peak_at_clock_TFLOP/s"] else None)},
         "decode": {"workload": d.name, "value": round(gbs, 1), "unit": "GB/s",
                    "us_per_call": round(ms_d * 1e3, 2), "tokens": d.tokens,
                    "algorithmic_bytes": d.bytes,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                 "traffic": traffic_from_profiles("decode_partial_kernel", src_d),
-                                "kernel": "decode_partial_kernel + decode_merge_kernel"}},
+                                "kernel": "decode_partial_kernel + decode_merge_kernel"},
+                   "per_call": {"median_us": round(st_d["median_ms"] * 1e3, 2),
+                                "min_us": round(st_d["min_ms"] * 1e3, 2), "reps": st_d["reps"],
+                                "GB/s_at_median": round(d.bytes / (st_d["median_ms"] * 1e-3) / 1e9,
+                                                        1)}},
         "parity": {"prefill_sampled_rows": len(rows), "prefill_max_err_over_tol": round(par_p, 4),
                    "prefill_max_lse_err": par_pl, "decode_max_err_over_tol": round(par_d, 4)},
     }
