@@ -39,9 +39,20 @@
 //    with the gfx950 transpose read (ds_read_b64_tr_b16).
 //  * LDS rows are 256 B with an XOR swizzle of their 16-byte chunks so that
 //    both the row reads and the transpose reads spread over the banks.
+//  * The dK/dV kernel runs one wave per SIMD (K, V fragments and two
+//    accumulators take 370+ registers), so it overlaps its own MFMAs and VALU
+//    work: when both 32-row halves of a query block are whole, the S/dP
+//    MFMAs of one half run beside the softmax gradient of the other, and the
+//    dV/dK MFMAs of one beside the next (an interleave requested from the
+//    scheduler).  The dQ kernel fits two waves per SIMD and relies on that.
 //  * blockIdx is remapped so that workgroups reading the same Q/dO (or K/V)
 //    run on one XCD and share its L2; causal dQ blocks are dispatched
-//    heaviest first.
+//    heaviest first.  Packed sequences (PACKED variants) spread the heads of
+//    a sequence over the XCDs instead, so that long sequences do not all land
+//    on one.
+//  * ALIBI variants add the ALiBi bias -slope * |i + Sk - Sq - j| to the
+//    exponent of each recomputed probability (the bias does not depend on Q,
+//    K or V, so nothing else changes).
 #include "gfx950.hpp"
 #include "kernels.h"
 
