@@ -54,6 +54,12 @@
 //  * blockIdx is remapped so that workgroups sharing K/V land on one XCD
 //    (workgroups are dealt to the 8 XCDs round robin), keeping K/V re-reads in
 //    that XCD's L2.
+//  * Packed sequences of different lengths (cu_q/cu_k offsets): a workgroup
+//    reads its sequence's offsets first and returns at once if its query tile
+//    lies past the sequence; the heads of one sequence are spread over the
+//    XCDs (spread_groups) so the longest sequences do not share one XCD.
+//  * ALiBi (ALIBI variants): the linear bias is added to the raw scores at
+//    the start of each softmax phase, before the mask and the row max.
 #include "gfx950.hpp"
 #include "kernels.h"
 
