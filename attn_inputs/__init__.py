@@ -89,20 +89,24 @@ class Prefill:
     hot_rows: list = field(default_factory=list)  # (b, s, h) query vectors scaled x8
 
     @property
+    def d(self) -> int:
+        return int(self.q.shape[-1])
+
+    @property
     def flops(self) -> float:
-        f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * D
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * self.d
         return f / 2 if self.causal else f
 
 
 def prefill_inputs(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0,
                    scale=None, q_dist="normal", k_dist="normal", v_dist="normal",
-                   n_hot=0, name="") -> Prefill:
-    """Draw a prefill problem.  `n_hot` query vectors Q[b, s, h, :] (drawn by
-    the seed) are multiplied by 8 before rounding; x8 is a power of two, so it
-    commutes with the bf16 rounding."""
+                   n_hot=0, name="", d=D) -> Prefill:
+    """Draw a prefill problem (head dim d, 128 unless given).  `n_hot` query
+    vectors Q[b, s, h, :] (drawn by the seed) are multiplied by 8 before
+    rounding; x8 is a power of two, so it commutes with the bf16 rounding."""
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    qf = _draw(q_dist, seed, _S_Q, layout_shape(layout, B, Hq, Sq))
+        scale = 1.0 / math.sqrt(d)
+    qf = _draw(q_dist, seed, _S_Q, layout_shape(layout, B, Hq, Sq, d))
     hot = []
     if n_hot:
         r = _rng(seed, _S_HOT)
@@ -117,8 +121,8 @@ def prefill_inputs(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0,
                 qf[b, h, s, :] *= 8.0
     q = f32_to_bf16_bits(qf)
     del qf
-    k = f32_to_bf16_bits(_draw(k_dist, seed, _S_K, layout_shape(layout, B, Hkv, Sk)))
-    v = f32_to_bf16_bits(_draw(v_dist, seed, _S_V, layout_shape(layout, B, Hkv, Sk)))
+    k = f32_to_bf16_bits(_draw(k_dist, seed, _S_K, layout_shape(layout, B, Hkv, Sk, d)))
+    v = f32_to_bf16_bits(_draw(v_dist, seed, _S_V, layout_shape(layout, B, Hkv, Sk, d)))
     return Prefill(q, k, v, B, Hq, Hkv, Sq, Sk, layout, bool(causal), float(scale),
                    name=name, hot_rows=hot)
 
@@ -372,3 +376,10 @@ def varlen_causal_gqa(seed=6):
     lens = _rng(seed, _S_VLENS).integers(1, 8193, size=16)
     return varlen_inputs(lens, lens, 32, 8, causal=True, seed=seed,
                          name="varlen_causal_gqa_b16_hq32_hkv8_len8192")
+
+
+def headdim64_causal_gqa(seed=7):
+    """Causal GQA prefill with head dim 64: B=8, Hq=32, Hkv=8, S=8192, BSHD
+    (the causal GQA workload's shape at the smaller head size)."""
+    return prefill_inputs(8, 32, 8, 8192, 8192, layout=BSHD, causal=True, seed=seed, d=64,
+                          name="gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd")
