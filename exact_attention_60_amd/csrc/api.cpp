@@ -71,12 +71,15 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, int layout, int rounding, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-  if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
-      (causal != 0 && causal != 1) || !scale_ok(scale) || !rounding_ok(rounding))
+  // head dim 128 (every variant) or 64 (dense, no ALiBi)
+  const bool hd64 = d == 64;
+  if ((d != attn::kHeadDim && !(hd64 && !alibi_slopes)) ||
+      (layout != ATTN_BSHD && layout != ATTN_BHSD) || (causal != 0 && causal != 1) ||
+      !scale_ok(scale) || !rounding_ok(rounding))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_ALIGN;
-  const int64_t D = attn::kHeadDim;
+  const int64_t D = d;
   attn::PrefillArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -91,10 +94,11 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
     a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
   }
   // K/V of one (batch, kv head) are addressed with 32-bit byte offsets
-  if ((int64_t)(Sk - 1) * a.k_ss * 2 + 256 > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)(Sk - 1) * a.k_ss * 2 + D * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
   a.group = Hq / Hkv;
-  a.n_qt = (Sq + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  const int rows_per_block = hd64 ? attn::prefill_hd_rows_per_block() : attn::kPrefillBM;
+  a.n_qt = (Sq + rows_per_block - 1) / rows_per_block;
   if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
   a.c = scale * 1.4426950408889634f;
   a.rounding = rounding;
@@ -105,7 +109,9 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
-  const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      hd64 ? attn::launch_prefill_hd(a, d, causal != 0, static_cast<hipStream_t>(stream))
+           : attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -1,0 +1,329 @@
+// Exact attention forward for head dim 64 on gfx950: O = softmax(scale Q K^T) V
+// with the same online softmax as the d = 128 kernel ("IO-aware tiling
+// strategy in FlashAttention-4", body: Q in row tiles, K/V in column tiles
+// brought on chip, a running row max m and denominator l merged block by
+// block, the output accumulator rescaled by a per-row factor and divided by
+// l once at the end).  Head dims other than 128 are what the MoonMath page's
+// kernel leaves out ("MoonMath AI open-sources a HIP attention kernel for AMD
+// MI300X that beats AITER v3", scope paragraph: head dim fixed at 128).
+//
+// Design (gfx950):
+//  * one workgroup = 4 waves = 128 query rows of one (batch, query head); a
+//    wave owns 32 rows, with its Q fragments and the fp32 O^T accumulator in
+//    registers (about 110 VGPRs, so several workgroups share a CU).
+//  * K and V tiles of 64 keys (128-byte rows) are copied HBM -> LDS by
+//    buffer_load ... lds, double buffered one tile ahead; rows are XOR-swizzled
+//    in 16-byte chunks; keys past Sk fall outside the buffer range and read 0.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row in each lane
+//    column (its 32 keys split over the two lane halves), so the row max and
+//    sum are in-lane plus one v_permlane32_swap, the rescale factor is a
+//    per-lane scalar for O^T, and the probabilities are directly the B
+//    operand of O^T += V^T P^T, whose V^T operand comes from the row-major V
+//    tile through ds_read_b64_tr_b16.
+//  * P.V runs in fp16 (V converted in LDS once per tile, P rounded to fp16,
+//    l summed from the rounded P), as the d = 128 kernel does; a V value
+//    beyond the fp16 range or a non-finite input leaves a non-finite
+//    accumulator and the workgroup redoes its tiles in bf16.
+//  * Causal: tiles past the diagonal are never loaded, waves whose rows see
+//    none of a 32-key half skip it, only boundary halves are masked, heaviest
+//    query blocks are dispatched first.
+#include "gfx950.hpp"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int NW = 4;
+constexpr int NT = NW * 64;
+constexpr int QR = NW * 32;    // query rows per workgroup
+constexpr int KB = 64;         // keys per tile
+
+template <int D>
+struct Geom {
+  static constexpr int RB = D * 2;               // bytes per row
+  static constexpr int NC = RB / 16;             // 16-byte chunks per row
+  static constexpr int TILE = KB * RB;           // one K or V tile
+  static constexpr int KS = D / 16;              // MFMA k-steps over d
+  static constexpr int NTD = D / 32;             // 32-wide d blocks of O^T
+  static constexpr int RPI = 1024 / RB;          // rows per 1 KB copy instruction
+  static constexpr int IPW = KB / RPI / NW;      // copy instructions per wave per tile
+  static_assert(NC == 8 && IPW * RPI * NW == KB, "laid out for 128-byte rows");
+};
+
+// 3-bit swizzle of a row: a bijection on rows 0..7 that also sends the 4
+// consecutive rows of a transpose read to 4 different chunk pairs.
+__device__ __forceinline__ int swz8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int hd_off(int row, int chunk) {
+  return row * Geom<D>::RB + ((chunk ^ swz8(row & 7)) << 4);
+}
+template <int D>
+__device__ __forceinline__ int hd_elem(int row, int col) {   // col a multiple of 4
+  return hd_off<D>(row, col >> 3) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int per = n >> 3;
+  return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A operand of O^T += V^T P^T: column col0 + c of the V rows
+// rbase + 4h + {0..3} and rbase + 8 + 4h + {0..3} (k-slot order of a 32x32
+// accumulator's registers 0..7 in a lane half), by two transpose reads: in
+// each 16-lane group lane j gets element j%4 of the 4-element row addressed by
+// lane 4e + j/4.
+template <int D>
+__device__ __forceinline__ bf16x8 v_cols(const char* tile, int rbase, int col0, int lane) {
+  const int L = lane & 15;
+  const int row = rbase + 4 * (lane >> 5) + (L >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+  const bf16x4 lo = lds_read_tr(tile + hd_elem<D>(row, col));
+  const bf16x4 hi = lds_read_tr(tile + hd_elem<D>(row + 8, col));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <int D>
+struct Copier {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t voff[Geom<D>::IPW];
+  uint32_t tile_bytes;
+  int row0;
+  __device__ void init(const __bf16* kp, const __bf16* vp, int64_t ss, int Sk, int wave,
+                       int lane) {
+    constexpr int RPI = Geom<D>::RPI, NC = Geom<D>::NC;
+    const uint32_t sb = (uint32_t)(ss * 2);
+    const uint32_t nrec = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * sb + Geom<D>::RB) : 0u;
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)nrec, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)nrec, 0x00020000);
+    tile_bytes = sb * KB;
+    row0 = wave * Geom<D>::IPW * RPI;
+#pragma unroll
+    for (int j = 0; j < Geom<D>::IPW; ++j) {
+      const int row = row0 + j * RPI + lane / NC;
+      const int c = (lane % NC) ^ swz8(row & 7);
+      voff[j] = (uint32_t)row * sb + (uint32_t)c * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(int t, char* kt, char* vt) const {
+    const uint32_t base = (uint32_t)t * tile_bytes;
+#pragma unroll
+    for (int j = 0; j < Geom<D>::IPW; ++j) {
+      const int r = row0 + j * Geom<D>::RPI;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ATTN_LDS void*)(kt + r * Geom<D>::RB), 16,
+                                               voff[j] + base, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vt + r * Geom<D>::RB), 16,
+                                               voff[j] + base, 0, 0, 0);
+    }
+  }
+};
+
+template <int D>
+struct HdState {
+  bf16x8 qf[Geom<D>::KS];       // B operand of S^T = K Q^T (row = lane % 32)
+  f32x16 oacc[Geom<D>::NTD];    // O^T, d blocks of 32
+  float m;                      // running row max, log2 units (scale*log2e folded in)
+  float l;                      // this lane's part of the row sum
+};
+
+// The tile loop; F16 selects fp16 (else bf16) for P and V.
+template <int D, bool CAUSAL, bool F16>
+__device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char* kbuf,
+                                        char* vbuf, int n_kt, int n_keys, int Sk, int Sq, int off,
+                                        int qw0, int wave_last, float c, int lane) {
+  constexpr int TILE = Geom<D>::TILE;
+  const int cl = lane & 31, h = lane >> 5;
+  const int q = qw0 + cl;
+#pragma unroll
+  for (int n = 0; n < Geom<D>::NTD; ++n) w.oacc[n] = f32x16{};
+  w.m = -INFINITY;
+  w.l = 0.f;
+  if (n_kt > 0) cp.issue(0, kbuf, vbuf);
+  for (int t = 0; t < n_kt; ++t) {
+    const int st = t & 1;
+    char* kt = kbuf + st * TILE;
+    char* vt = vbuf + st * TILE;
+    wait_all();
+    barrier();   // tile t has landed for every wave; tile t-1 is no longer read
+    if (t + 1 < n_kt) cp.issue(t + 1, kbuf + (st ^ 1) * TILE, vbuf + (st ^ 1) * TILE);
+    if constexpr (F16) {
+      // V tile bf16 -> fp16 in place, 16 bytes per thread per step
+#pragma unroll
+      for (int i = threadIdx.x; i < TILE / 16; i += NT) {
+        u32x4* pch = reinterpret_cast<u32x4*>(vt + 16 * i);
+        u32x4 x = *pch;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+        *pch = x;
+      }
+      // lgkmcnt(0) only: the next tile's copies stay in flight
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      barrier();
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int kr0 = t * KB + 32 * ks2;
+      if (kr0 >= n_keys || qw0 >= Sq) continue;
+      if (CAUSAL && kr0 > wave_last + off) continue;   // no row of the wave sees these keys
+      const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > Sk);
+      // S^T[key][q]: register r of lane (cl, h) holds key kr0 + 8*(r/4) + 4h + r%4
+      bf16x8 ka[Geom<D>::KS];
+#pragma unroll
+      for (int ks = 0; ks < Geom<D>::KS; ++ks)
+        ka[ks] = *reinterpret_cast<const bf16x8*>(kt + hd_off<D>(32 * ks2 + cl, 2 * ks + h));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < Geom<D>::KS; ++ks) s = mfma32(ka[ks], w.qf[ks], s);
+      if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kr0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= Sk || (CAUSAL && key > q + off)) s[r] = -INFINITY;
+        }
+      }
+      // online softmax of row q over these 32 keys (16 per lane half)
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = max_halves(mx);
+      const float m_new = fmaxf(w.m, mx * c);
+      const float alpha = (m_new == w.m) ? 1.f : fast_exp2(w.m - m_new);
+      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      uint32_t pk[8];
+      float tsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[2 * i], c, -msub));
+        const float p1 = fast_exp2(__builtin_fmaf(s[2 * i + 1], c, -msub));
+        pk[i] = F16 ? pack_f16(p0, p1) : pack_bf16(p0, p1);
+        tsum = F16 ? sum2_f16(pk[i], tsum) : sum2_bf16(pk[i], tsum);
+      }
+      w.l = w.l * alpha + tsum;
+      w.m = m_new;
+      // the running max of most rows stops moving after the first tiles:
+      // rescale only when some row of the wave changed it
+      if (wave_any(alpha != 1.f)) {
+#pragma unroll
+        for (int n = 0; n < Geom<D>::NTD; ++n) w.oacc[n] *= alpha;
+      }
+      // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pb = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
+#pragma unroll
+        for (int n = 0; n < Geom<D>::NTD; ++n) {
+          const bf16x8 va = v_cols<D>(vt, 32 * ks2 + 16 * u, 32 * n, lane);
+          if constexpr (F16)
+            w.oacc[n] = mfma32(__builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, pb),
+                               w.oacc[n]);
+          else
+            w.oacc[n] = mfma32(va, __builtin_bit_cast(bf16x8, pb), w.oacc[n]);
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ bool hd_finite(const HdState<D>& w) {
+  bool ok = __builtin_isfinite(w.l);
+#pragma unroll
+  for (int n = 0; n < Geom<D>::NTD; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ok = ok && __builtin_isfinite(w.oacc[n][r]);
+  return ok;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT) void prefill_hd_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * Geom<D>::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2 * Geom<D>::TILE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cl = lane & 31, h = lane >> 5;
+  const int n_qb = a.n_qt;
+  const int BH = a.B * a.Hq;
+  int bh, qb;
+  if (CAUSAL) {
+    const int row = blockIdx.x / BH;     // heaviest query blocks first
+    qb = n_qb - 1 - row;
+    bh = xcd_remap(blockIdx.x - row * BH, BH);
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    bh = L / n_qb;
+    qb = L - bh * n_qb;
+  }
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const int hk = hq / a.group;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const __bf16* qp = a.q + b * a.q_sb + hq * a.q_sh;
+  const __bf16* kp = a.k + b * a.k_sb + hk * a.k_sh;
+  const __bf16* vp = a.v + b * a.k_sb + hk * a.k_sh;
+  const int q0 = qb * QR;
+  const int qw0 = q0 + 32 * wave;
+  const int q = qw0 + cl;
+  const int last_row = min(q0 + QR, Sq) - 1;
+  const int n_keys = CAUSAL ? min(Sk, max(0, last_row + off + 1)) : Sk;
+  const int n_kt = (n_keys + KB - 1) / KB;
+  const int wave_last = min(qw0 + 31, Sq - 1);
+
+  HdState<D> w;
+#pragma unroll
+  for (int ks = 0; ks < Geom<D>::KS; ++ks) {
+    if (q < Sq)
+      w.qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
+    else
+      w.qf[ks] = bf16x8{};
+  }
+  Copier<D> cp;
+  cp.init(kp, vp, a.k_ss, Sk, wave, lane);
+
+  hd_loop<D, CAUSAL, true>(w, cp, kbuf, vbuf, n_kt, n_keys, Sk, Sq, off, qw0, wave_last, a.c,
+                           lane);
+  if (__syncthreads_or(!hd_finite(w)))
+    hd_loop<D, CAUSAL, false>(w, cp, kbuf, vbuf, n_kt, n_keys, Sk, Sq, off, qw0, wave_last, a.c,
+                              lane);
+
+  // epilogue: O = O^T / l in q's layout (register r of lane (cl, h), d block
+  // n: d = 32n + 8*(r/4) + 4h + r%4), LSE = (m + log2 l) ln 2
+  const float L = sum_halves(w.l);
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  if (q < Sq) {
+    __bf16* orow = a.o + b * a.q_sb + hq * a.q_sh + (int64_t)q * a.q_ss;
+    with_rounding(a.rounding, [&](auto mode) {
+#pragma unroll
+      for (int n = 0; n < Geom<D>::NTD; ++n)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 u;
+          u[0] = pack_bf16_as<mode()>(w.oacc[n][4 * g] * inv, w.oacc[n][4 * g + 1] * inv);
+          u[1] = pack_bf16_as<mode()>(w.oacc[n][4 * g + 2] * inv, w.oacc[n][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + 32 * n + 8 * g + 4 * h) = u;
+        }
+    });
+    if (h == 0)
+      a.lse[((int64_t)(b * a.Hq + hq)) * Sq + q] = (L > 0.f) ? (w.m + __log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+int prefill_hd_rows_per_block() { return QR; }
+
+hipError_t launch_prefill_hd(const PrefillArgs& a, int d, bool causal, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.B * a.Hq * a.n_qt;
+  if (grid <= 0 || grid > 0x7fffffff || d != 64) return hipErrorInvalidValue;
+  if (causal)
+    hipLaunchKernelGGL((prefill_hd_kernel<64, true>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_hd_kernel<64, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

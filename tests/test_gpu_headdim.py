@@ -1,0 +1,95 @@
+"""Parity of the head-dim-64 forward (attn_fwd with d = 64) with the fp64
+oracle (GPU), under the forward's tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as gen
+import exact_attention_60_amd as ea
+import oracle.attention as att
+from gpu_util import dev_bf16, host_f64, logical_o, need_gpu
+from tolerance import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def lay(p):
+    return "bshd" if p.layout == gen.BSHD else "bhsd"
+
+
+def run(p, rounding="rtne"):
+    o, lse = ea.attn_fwd(dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v), causal=p.causal,
+                         scale=p.scale, layout=lay(p), rounding=rounding)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(p, o, lse, what):
+    o_ref, l_ref = att.attention(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale, p.causal,
+                                 p.layout)
+    e = check_o(logical_o(o, p.layout), o_ref, what)
+    el = check_lse(host_f64(lse), l_ref, what)
+    print(f"{what}: err/tol {e[1]:.3f} lse {el:.3g}", flush=True)
+    return o_ref
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,layout,causal", [
+    (1, 4, 4, 256, 256, gen.BSHD, False),
+    (2, 8, 2, 200, 200, gen.BHSD, True),       # GQA causal, ragged blocks and tiles
+    (1, 4, 2, 300, 77, gen.BSHD, False),       # cross attention, short keys
+    (1, 4, 2, 150, 100, gen.BSHD, True),       # rows that see no key
+    (1, 4, 1, 70, 600, gen.BHSD, True),        # MQA, bottom-right alignment
+    (1, 2, 2, 1, 1, gen.BSHD, False),
+    (1, 2, 1, 129, 1000, gen.BSHD, False),
+])
+def test_d64_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=Sq + Sk,
+                           n_hot=min(3, B * Sq * Hq), d=64)
+    o, lse = run(p)
+    check(p, o, lse, f"d64 B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} causal{causal}")
+
+
+def test_d64_rounding_rules_from_the_same_values():
+    p = gen.prefill_inputs(1, 4, 2, 130, 130, layout=gen.BSHD, causal=True, seed=5, d=64)
+    outs = {m: run(p, m)[0] for m in ("rtne", "rtna", "rtz")}
+    o_ref = check(p, outs["rtne"], run(p)[1], "d64 rtne")
+    for m in ("rtna", "rtz"):
+        check_o(logical_o(outs[m], p.layout), o_ref, f"d64 {m}")
+    # RTZ never exceeds RTNE in magnitude, and the two differ by at most one spacing
+    a = host_f64(outs["rtz"])
+    b = host_f64(outs["rtne"])
+    assert np.all(np.abs(a) <= np.abs(b))
+
+
+def test_d64_v_beyond_fp16_range_takes_the_bf16_path():
+    p = gen.prefill_inputs(1, 2, 1, 64, 90, layout=gen.BSHD, seed=6, d=64)
+    v = p.v.copy()
+    v[0, 7, 0, 5] = gen.f32_to_bf16_bits(np.array([70000.0], np.float32))[0]
+    p = gen.Prefill(p.q, p.k, v, 1, 2, 1, 64, 90, gen.BSHD, False, p.scale)
+    o, lse = run(p)
+    assert torch.isfinite(o.float()).all()
+    check(p, o, lse, "d64 large V")
+
+
+def test_d64_deterministic():
+    p = gen.prefill_inputs(1, 8, 2, 333, 333, layout=gen.BSHD, causal=True, seed=9, d=64)
+    a, la = run(p)
+    b, lb = run(p)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+def test_d64_causal_gqa_full_size_sampled_group():
+    p = gen.headdim64_causal_gqa()
+    o, lse = run(p)
+    b, g, G = 3, 5, 4
+    sub = [np.ascontiguousarray(x[b:b + 1, :, h0:h1])
+           for x, h0, h1 in ((p.q, g * G, g * G + G), (p.k, g, g + 1), (p.v, g, g + 1))]
+    o_ref, l_ref = att.attention(*sub, 1, G, 1, p.Sq, p.Sk, p.scale, True, gen.BSHD)
+    e = check_o(logical_o(o[b:b + 1, :, g * G:g * G + G], gen.BSHD), o_ref, "d64 full size")
+    check_lse(host_f64(lse[b:b + 1, g * G:g * G + G]), l_ref, "d64 full size lse")
+    print(f"d64 causal gqa full size b{b} g{g}: err/tol {e[1]:.3f}", flush=True)
