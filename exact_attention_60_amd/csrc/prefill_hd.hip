@@ -20,7 +20,8 @@
 //    per-lane scalar for O^T, and the probabilities are directly the B
 //    operand of O^T += V^T P^T, whose V^T operand comes from the row-major V
 //    tile through ds_read_b64_tr_b16.
-//  * P.V runs in fp16 (V converted in LDS once per tile, P rounded to fp16,
+//  * P.V runs in fp16 (each wave converts the V rows it copied, in LDS, before
+//    the tile's barrier; P rounded to fp16,
 //    l summed from the rounded P), as the d = 128 kernel does; a V value
 //    beyond the fp16 range or a non-finite input leaves a non-finite
 //    accumulator and the workgroup redoes its tiles in bf16.
@@ -148,23 +149,24 @@ __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char
     const int st = t & 1;
     char* kt = kbuf + st * TILE;
     char* vt = vbuf + st * TILE;
-    wait_all();
-    barrier();   // tile t has landed for every wave; tile t-1 is no longer read
-    if (t + 1 < n_kt) cp.issue(t + 1, kbuf + (st ^ 1) * TILE, vbuf + (st ^ 1) * TILE);
+    wait_all();    // this wave's copies of tile t have landed
     if constexpr (F16) {
-      // V tile bf16 -> fp16 in place, 16 bytes per thread per step
+      // bf16 -> fp16 in place for the V rows this wave copied (each lane the
+      // 16 bytes its copy instructions wrote), before the barrier publishes
+      // the tile; no other wave touches these rows meanwhile
 #pragma unroll
-      for (int i = threadIdx.x; i < TILE / 16; i += NT) {
-        u32x4* pch = reinterpret_cast<u32x4*>(vt + 16 * i);
+      for (int j = 0; j < Geom<D>::IPW; ++j) {
+        u32x4* pch = reinterpret_cast<u32x4*>(
+            vt + (cp.row0 + j * Geom<D>::RPI) * Geom<D>::RB + 16 * lane);
         u32x4 x = *pch;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
         *pch = x;
       }
-      // lgkmcnt(0) only: the next tile's copies stay in flight
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      barrier();
+      wait_all();
     }
+    barrier();   // tile t is complete for every wave; tile t-1 is no longer read
+    if (t + 1 < n_kt) cp.issue(t + 1, kbuf + (st ^ 1) * TILE, vbuf + (st ^ 1) * TILE);
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       const int kr0 = t * KB + 32 * ks2;
