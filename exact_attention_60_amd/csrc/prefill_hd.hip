@@ -242,8 +242,11 @@ __device__ __forceinline__ bool hd_finite(const HdState<D>& w) {
   return ok;
 }
 
+// Occupancy: four waves per SIMD without the causal mask code (124 VGPRs),
+// three with it (the mask paths need more registers; four would spill).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void prefill_hd_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CAUSAL ? 3 : 4, 4)))
+void prefill_hd_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * Geom<D>::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[2 * Geom<D>::TILE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
