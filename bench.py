@@ -13,7 +13,7 @@ are already resident in HBM:
 * the other prefill workloads (causal GQA B=8 S=8192, diffusion-style self
   attention S=32760 and its cross attention against 512 keys), timed the
   same way and reported beside the headline (skip with --no-extra);
-* the causal GQA shape at head dim 64 (attn_fwd with d = 64);
+* the causal GQA shape at head dims 64 and 256 (attn_fwd with d = 64, 256);
 * the causal GQA workload with an ALiBi bias (attn_fwd_alibi);
 * packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
   U{1..8192}, reported beside the headline;
@@ -266,7 +266,9 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
              wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false, false>"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192", "prefill_kernel<true, false>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd",
-                    "prefill_hd_kernel<64, true>")],
+                    "prefill_hd_kernel<64, true>"),
+             wl_row("gqa_causal_prefill_b4_hq32_hkv8_s4096_d256_bshd",
+                    "prefill_hd_kernel<256, true>")],
             []),
         "backward_kernels__mha_b4_h32_s4096_bhsd_and_causal_gqa_s8192.md": (
             "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
@@ -339,6 +341,24 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     tf = p.flops / (ms * 1e-3) / 1e12
     res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
                 "d": 64, "causal": True, "layout": "bshd", "ms_per_call": round(ms, 4),
+                "flop": p.flops, "TFLOP/s": round(tf, 2),
+                "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    del q, k, v, o, lse
+    # head dim 256 on a causal GQA shape (B=4, Hq=32, Hkv=8, S=4096)
+    p = gen.prefill_inputs(4, 32, 8, 4096, 4096, layout=gen.BSHD, causal=True, seed=8, d=256,
+                           name="gqa_causal_prefill_b4_hq32_hkv8_s4096_d256_bshd")
+    log(f"timing {p.name}")
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+    def run_h2(_i):
+        ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd", out=o, lse=lse)
+
+    ms = time_calls(run_h2, steps, 2, torch)
+    tf = p.flops / (ms * 1e-3) / 1e12
+    res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
+                "d": 256, "causal": True, "layout": "bshd", "ms_per_call": round(ms, 4),
                 "flop": p.flops, "TFLOP/s": round(tf, 2),
                 "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
     del q, k, v, o, lse
@@ -538,6 +558,8 @@ def main():
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
         cmd = {"plan": {"prefill_hd_kernel<64, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192"
                                                          "_d64_bshd", xs)],
+                        "prefill_hd_kernel<256, true>": [("gqa_causal_prefill_b4_hq32_hkv8_s4096"
+                                                          "_d256_bshd", xs)],
                         "prefill_kernel<true, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                         "_alibi", xs),
                                                        ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"

@@ -71,8 +71,8 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, int layout, int rounding, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-  // head dim 128 (every variant) or 64 (dense, no ALiBi)
-  const bool hd64 = d == 64;
+  // head dim 128 (every variant), or 64 and 256 (dense, no ALiBi)
+  const bool hd64 = d == 64 || d == 256;
   if ((d != attn::kHeadDim && !(hd64 && !alibi_slopes)) ||
       (layout != ATTN_BSHD && layout != ATTN_BHSD) || (causal != 0 && causal != 1) ||
       !scale_ok(scale) || !rounding_ok(rounding))

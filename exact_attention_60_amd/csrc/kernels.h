@@ -43,8 +43,8 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 
-// head dim 64 (dense layouts, no ALiBi): query rows per workgroup, and the
-// launch (n_qt = ceil(Sq / rows per workgroup))
+// head dims 64 and 256 (dense layouts, no ALiBi): query rows per workgroup,
+// and the launch (n_qt = ceil(Sq / rows per workgroup))
 int prefill_hd_rows_per_block();
 hipError_t launch_prefill_hd(const PrefillArgs& a, int d, bool causal, hipStream_t stream);
 

@@ -1,4 +1,4 @@
-// Exact attention forward for head dim 64 on gfx950: O = softmax(scale Q K^T) V
+// Exact attention forward for head dims 64 and 256 on gfx950: O = softmax(scale Q K^T) V
 // with the same online softmax as the d = 128 kernel ("IO-aware tiling
 // strategy in FlashAttention-4", body: Q in row tiles, K/V in column tiles
 // brought on chip, a running row max m and denominator l merged block by
@@ -11,7 +11,8 @@
 //  * one workgroup = 4 waves = 128 query rows of one (batch, query head); a
 //    wave owns 32 rows, with its Q fragments and the fp32 O^T accumulator in
 //    registers (about 110 VGPRs, so several workgroups share a CU).
-//  * K and V tiles of 64 keys (128-byte rows) are copied HBM -> LDS by
+//  * K and V tiles of 64 keys (d = 64, 128-byte rows) or 32 keys (d = 256,
+//    512-byte rows) are copied HBM -> LDS by
 //    buffer_load ... lds, double buffered one tile ahead; rows are XOR-swizzled
 //    in 16-byte chunks; keys past Sk fall outside the buffer range and read 0.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row in each lane
@@ -37,10 +38,10 @@ namespace {
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int QR = NW * 32;    // query rows per workgroup
-constexpr int KB = 64;         // keys per tile
 
 template <int D>
 struct Geom {
+  static constexpr int KB = D <= 64 ? 64 : 32;   // keys per tile (LDS: 2 stages of K and V)
   static constexpr int RB = D * 2;               // bytes per row
   static constexpr int NC = RB / 16;             // 16-byte chunks per row
   static constexpr int TILE = KB * RB;           // one K or V tile
@@ -48,15 +49,20 @@ struct Geom {
   static constexpr int NTD = D / 32;             // 32-wide d blocks of O^T
   static constexpr int RPI = 1024 / RB;          // rows per 1 KB copy instruction
   static constexpr int IPW = KB / RPI / NW;      // copy instructions per wave per tile
-  static_assert(NC == 8 && IPW * RPI * NW == KB, "laid out for 128-byte rows");
+  static_assert(IPW >= 1 && IPW * RPI * NW == KB && KB % 32 == 0, "tile layout");
 };
 
-// 3-bit swizzle of a row: a bijection on rows 0..7 that also sends the 4
-// consecutive rows of a transpose read to 4 different chunk pairs.
-__device__ __forceinline__ int swz8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk swizzle of a row: for 8-chunk rows a bijection on rows 0..7 that
+// also sends the 4 consecutive rows of a transpose read to 4 different chunk
+// pairs; for longer rows the 4-bit version of the same idea.
+template <int NC>
+__device__ __forceinline__ int hd_swz(int r) {
+  if constexpr (NC == 8) return ((r & 3) << 1) | ((r >> 2) & 1);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 template <int D>
 __device__ __forceinline__ int hd_off(int row, int chunk) {
-  return row * Geom<D>::RB + ((chunk ^ swz8(row & 7)) << 4);
+  return row * Geom<D>::RB + ((chunk ^ hd_swz<Geom<D>::NC>(row & 15)) << 4);
 }
 template <int D>
 __device__ __forceinline__ int hd_elem(int row, int col) {   // col a multiple of 4
@@ -102,12 +108,12 @@ struct Copier {
     const uint32_t nrec = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * sb + Geom<D>::RB) : 0u;
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)nrec, 0x00020000);
     rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)nrec, 0x00020000);
-    tile_bytes = sb * KB;
+    tile_bytes = sb * Geom<D>::KB;
     row0 = wave * Geom<D>::IPW * RPI;
 #pragma unroll
     for (int j = 0; j < Geom<D>::IPW; ++j) {
       const int row = row0 + j * RPI + lane / NC;
-      const int c = (lane % NC) ^ swz8(row & 7);
+      const int c = (lane % NC) ^ hd_swz<NC>(row & 15);
       voff[j] = (uint32_t)row * sb + (uint32_t)c * 16;
     }
   }
@@ -168,20 +174,24 @@ __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char
     barrier();   // tile t is complete for every wave; tile t-1 is no longer read
     if (t + 1 < n_kt) cp.issue(t + 1, kbuf + (st ^ 1) * TILE, vbuf + (st ^ 1) * TILE);
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const int kr0 = t * KB + 32 * ks2;
+    for (int ks2 = 0; ks2 < Geom<D>::KB / 32; ++ks2) {
+      const int kr0 = t * Geom<D>::KB + 32 * ks2;
       if (kr0 >= n_keys || qw0 >= Sq) continue;
       if (CAUSAL && kr0 > wave_last + off) continue;   // no row of the wave sees these keys
       const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > Sk);
       // S^T[key][q]: register r of lane (cl, h) holds key kr0 + 8*(r/4) + 4h + r%4
-      bf16x8 ka[Geom<D>::KS];
-#pragma unroll
-      for (int ks = 0; ks < Geom<D>::KS; ++ks)
-        ka[ks] = *reinterpret_cast<const bf16x8*>(kt + hd_off<D>(32 * ks2 + cl, 2 * ks + h));
-      __builtin_amdgcn_sched_barrier(0);
+      // K rows read four k-steps at a time ahead of their MFMAs
       f32x16 s = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < Geom<D>::KS; ++ks) s = mfma32(ka[ks], w.qf[ks], s);
+      for (int k0 = 0; k0 < Geom<D>::KS; k0 += 4) {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ka[i] = *reinterpret_cast<const bf16x8*>(kt + hd_off<D>(32 * ks2 + cl, 2 * (k0 + i) + h));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = mfma32(ka[i], w.qf[k0 + i], s);
+      }
       if (mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -242,10 +252,13 @@ __device__ __forceinline__ bool hd_finite(const HdState<D>& w) {
   return ok;
 }
 
-// Occupancy: four waves per SIMD without the causal mask code (124 VGPRs),
-// three with it (the mask paths need more registers; four would spill).
+// Occupancy at d = 64: four waves per SIMD without the causal mask code (124
+// VGPRs), three with it (the mask paths need more registers; four would
+// spill).  At d = 256 the Q fragments and O^T alone take 192 registers, and
+// the budget of two waves per SIMD spills: one.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CAUSAL ? 3 : 4, 4)))
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : (CAUSAL ? 3 : 4), D > 64 ? 1 : 4)))
 void prefill_hd_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * Geom<D>::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[2 * Geom<D>::TILE];
@@ -274,7 +287,7 @@ void prefill_hd_kernel(PrefillArgs a) {
   const int q = qw0 + cl;
   const int last_row = min(q0 + QR, Sq) - 1;
   const int n_keys = CAUSAL ? min(Sk, max(0, last_row + off + 1)) : Sk;
-  const int n_kt = (n_keys + KB - 1) / KB;
+  const int n_kt = (n_keys + Geom<D>::KB - 1) / Geom<D>::KB;
   const int wave_last = min(qw0 + 31, Sq - 1);
 
   HdState<D> w;
@@ -322,12 +335,15 @@ int prefill_hd_rows_per_block() { return QR; }
 
 hipError_t launch_prefill_hd(const PrefillArgs& a, int d, bool causal, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.Hq * a.n_qt;
-  if (grid <= 0 || grid > 0x7fffffff || d != 64) return hipErrorInvalidValue;
-  if (causal)
-    hipLaunchKernelGGL((prefill_hd_kernel<64, true>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_hd_kernel<64, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       a);
+  if (grid <= 0 || grid > 0x7fffffff || (d != 64 && d != 256)) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), bt(NT);
+  if (d == 64) {
+    if (causal) hipLaunchKernelGGL((prefill_hd_kernel<64, true>), g, bt, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_hd_kernel<64, false>), g, bt, 0, stream, a);
+  } else {
+    if (causal) hipLaunchKernelGGL((prefill_hd_kernel<256, true>), g, bt, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_hd_kernel<256, false>), g, bt, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

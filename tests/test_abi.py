@@ -64,7 +64,7 @@ def fwd(rounding=None, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(lse=None), -1), (dict(v=None), -1),
     (dict(B=0), -2), (dict(Sq=0), -2), (dict(Sk=-1), -2), (dict(Hq=3, Hkv=2), -2),
-    (dict(d=96), -3), (dict(d=256), -3), (dict(layout=2), -3), (dict(causal=2), -3),
+    (dict(d=96), -3), (dict(d=512), -3), (dict(layout=2), -3), (dict(causal=2), -3),
     (dict(scale=0.0), -3), (dict(scale=float("nan")), -3), (dict(scale=float("inf")), -3),
     (dict(scale=-1.0), -3),
     (dict(q=P + 8), -4), (dict(o=P + 2), -4), (dict(lse=P + 4), -4),
@@ -136,7 +136,8 @@ def test_valid_arguments_need_a_gfx950_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     # all checks pass, so the library asks HIP for the device and finds none
     assert fwd() == -7
-    assert fwd(d=64) == -7            # head dim 64 is supported by attn_fwd
+    assert fwd(d=64) == -7            # head dims 64 and 256 are supported by attn_fwd
+    assert fwd(d=256) == -7
     assert dec() == -7
     for r in (0, 1, 2):
         assert fwd(rounding=r) == -7

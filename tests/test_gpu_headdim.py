@@ -1,5 +1,5 @@
-"""Parity of the head-dim-64 forward (attn_fwd with d = 64) with the fp64
-oracle (GPU), under the forward's tolerance."""
+"""Parity of the head-dim-64 and -256 forwards (attn_fwd with d = 64 or 256)
+with the fp64 oracle (GPU), under the forward's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -93,3 +93,27 @@ def test_d64_causal_gqa_full_size_sampled_group():
     e = check_o(logical_o(o[b:b + 1, :, g * G:g * G + G], gen.BSHD), o_ref, "d64 full size")
     check_lse(host_f64(lse[b:b + 1, g * G:g * G + G]), l_ref, "d64 full size lse")
     print(f"d64 causal gqa full size b{b} g{g}: err/tol {e[1]:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,layout,causal", [
+    (1, 4, 4, 256, 256, gen.BSHD, False),
+    (2, 4, 2, 200, 200, gen.BHSD, True),
+    (1, 4, 2, 300, 77, gen.BSHD, False),
+    (1, 4, 2, 150, 100, gen.BSHD, True),
+    (1, 2, 1, 33, 500, gen.BHSD, True),
+])
+def test_d256_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=Sq + 2 * Sk,
+                           n_hot=min(3, B * Sq * Hq), d=256)
+    o, lse = run(p)
+    check(p, o, lse, f"d256 B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} causal{causal}")
+
+
+def test_d256_v_beyond_fp16_range_takes_the_bf16_path():
+    p = gen.prefill_inputs(1, 2, 1, 64, 90, layout=gen.BSHD, seed=16, d=256)
+    v = p.v.copy()
+    v[0, 11, 0, 200] = gen.f32_to_bf16_bits(np.array([-80000.0], np.float32))[0]
+    p = gen.Prefill(p.q, p.k, v, 1, 2, 1, 64, 90, gen.BSHD, False, p.scale)
+    o, lse = run(p)
+    assert torch.isfinite(o.float()).all()
+    check(p, o, lse, "d256 large V")

@@ -9,10 +9,11 @@ import attn_inputs as gen
 import oracle.attention as att
 
 
-@pytest.mark.parametrize("causal,layout", [(False, gen.BSHD), (True, gen.BHSD)])
-def test_d64_matches_torch(causal, layout):
-    p = gen.prefill_inputs(2, 4, 2, 40, 57, layout=layout, causal=causal, seed=41, d=64)
-    assert p.q.shape[-1] == 64 and abs(p.scale - 0.125) < 1e-12
+@pytest.mark.parametrize("causal,layout,d", [(False, gen.BSHD, 64), (True, gen.BHSD, 64),
+                                             (True, gen.BSHD, 256)])
+def test_d64_matches_torch(causal, layout, d):
+    p = gen.prefill_inputs(2, 4, 2, 40, 57, layout=layout, causal=causal, seed=41, d=d)
+    assert p.q.shape[-1] == d and abs(p.scale - d ** -0.5) < 1e-12
     o, lse = att.attention(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale, causal, layout,
                            workers=1)
     f = [torch.from_numpy(np.ascontiguousarray(att._logical(att.bf16_to_f64(x), layout)))
