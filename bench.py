@@ -119,6 +119,35 @@ def device_clock_info(torch):
             "bf16_peak_at_clock_TFLOP/s": round(peak, 1) if peak else None}
 
 
+def snapshot_outputs(p, o, lse, od, torch):
+    """Host copies of 64 random rows of the timed prefill's O and LSE and of
+    the timed decode's O, for the sampled parity check of the oracle leg."""
+    r = np.random.default_rng(0)
+    rows = [(int(r.integers(p.B)), int(r.integers(p.Hq)), int(r.integers(p.Sq))) for _ in range(64)]
+    og = torch.stack([o[b, h, i] for (b, h, i) in rows]).float().cpu().numpy()
+    lg = torch.stack([lse[b, h, i] for (b, h, i) in rows]).cpu().numpy()
+    return {"rows": rows, "o": og, "lse": lg, "od": od.float().cpu().numpy()}
+
+
+def sampled_parity(p, d, snap):
+    """The snapshot against the oracle (part of the oracle leg): worst error
+    over the tolerance, and the worst LSE error."""
+    import oracle.attention as att
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tolerance import o_tolerance
+    rows = snap["rows"]
+    o_ref, l_ref = att.attention_sampled(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
+                                         False, p.layout, rows)
+    od_ref, _ = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
+                                 d.scale)
+    return {"prefill_sampled_rows": len(rows),
+            "prefill_max_err_over_tol": round(float(
+                (np.abs(snap["o"] - o_ref) / o_tolerance(o_ref)).max()), 4),
+            "prefill_max_lse_err": float(np.abs(snap["lse"] - l_ref).max()),
+            "decode_max_err_over_tol": round(float(
+                (np.abs(snap["od"] - od_ref) / o_tolerance(od_ref)).max()), 4)}
+
+
 def cpu_baseline(p, budget_s, torch):
     """Time the oracle (as it is) on whole (b, h) heads of the prefill
     workload until about budget_s seconds of host work are done."""
@@ -687,7 +716,7 @@ def main():
     ms_p = time_calls(prefill, args.steps, args.warmup, torch)
     log(f"prefill {ms_p:.3f} ms/call; timing decode")
     ms_d = time_calls(decode, max(args.steps, 20), args.warmup, torch)
-    log(f"decode {ms_d * 1e3:.1f} us/call; sampled parity")
+    log(f"decode {ms_d * 1e3:.1f} us/call")
 
     tflops = p.flops / (ms_p * 1e-3) / 1e12
     gbs = d.bytes / (ms_d * 1e-3) / 1e9
@@ -695,22 +724,7 @@ def main():
     st_p = per_call_stats(prefill, max(args.steps, 20), torch)
     st_d = per_call_stats(decode, max(args.steps, 40), torch)
     dev_info = device_clock_info(torch)
-
-    # ---- quick sampled parity of what was timed
-    import oracle.attention as att
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from tolerance import o_tolerance
-    r = np.random.default_rng(0)
-    rows = [(int(r.integers(p.B)), int(r.integers(p.Hq)), int(r.integers(p.Sq))) for _ in range(64)]
-    o_ref, l_ref = att.attention_sampled(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
-                                         False, p.layout, rows)
-    og = torch.stack([o[b, h, i] for (b, h, i) in rows]).float().cpu().numpy()
-    lg = torch.stack([lse[b, h, i] for (b, h, i) in rows]).cpu().numpy()
-    par_p = float((np.abs(og - o_ref) / o_tolerance(o_ref)).max())
-    par_pl = float(np.abs(lg - l_ref).max())
-    od_ref, ld_ref = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
-                                      d.scale)
-    par_d = float((np.abs(od.float().cpu().numpy() - od_ref) / o_tolerance(od_ref)).max())
+    snap = snapshot_outputs(p, o, lse, od, torch)
 
     src_p = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill.hip")
     src_d = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "decode.hip")
@@ -752,8 +766,6 @@ def main():
                                 "min_us": round(st_d["min_ms"] * 1e3, 2), "reps": st_d["reps"],
                                 "GB/s_at_median": round(d.bytes / (st_d["median_ms"] * 1e-3) / 1e9,
                                                         1)}},
-        "parity": {"prefill_sampled_rows": len(rows), "prefill_max_err_over_tol": round(par_p, 4),
-                   "prefill_max_lse_err": par_pl, "decode_max_err_over_tol": round(par_d, 4)},
     }
     if not args.no_extra:
         out["decode_append"] = decode_append(args, d, ea, torch, qd, pools, tab, lens, od, lsed,
@@ -762,6 +774,10 @@ def main():
         out["other_workloads"] = extra_workloads(args, gen, ea, torch, dev, to_dev, log)
         out["backward"] = backward_workloads(args, gen, ea, torch, to_dev, log)
     if not args.no_cpu_baseline:
+        # the oracle leg: a sampled parity check of what was timed, then the
+        # oracle timed on the host cores
+        log("sampled parity against the oracle")
+        out["parity"] = sampled_parity(p, d, snap)
         log("timing the CPU oracle baseline")
         cb = cpu_baseline(p, args.cpu_seconds, torch)
         cb["value"] = round(cb["value"], 6)
