@@ -277,7 +277,8 @@ def equal_keys_decode(lens, Hq, Hkv, *, seed=0, binades=0, name="") -> Decode:
 def output_grad(p: Prefill, seed=0, dist="normal") -> np.ndarray:
     """Upstream gradient dO for the backward of problem p: bf16 bits in Q's
     layout and shape, iid N(0, 1) by default."""
-    return f32_to_bf16_bits(_draw(dist, seed, _S_DO, layout_shape(p.layout, p.B, p.Hq, p.Sq)))
+    return f32_to_bf16_bits(_draw(dist, seed, _S_DO, layout_shape(p.layout, p.B, p.Hq, p.Sq,
+                                                               p.d)))
 
 
 @dataclass

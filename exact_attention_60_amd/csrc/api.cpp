@@ -299,14 +299,16 @@ static int bwd_call(const void* q, const void* k, const void* v, const void* o, 
                     int layout, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-  if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
-      (causal != 0 && causal != 1) || !scale_ok(scale))
+  // head dim 128, or 64 without ALiBi
+  if ((d != attn::kHeadDim && !(d == 64 && !alibi_slopes)) ||
+      (layout != ATTN_BSHD && layout != ATTN_BHSD) || (causal != 0 && causal != 1) ||
+      !scale_ok(scale))
     return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_ERR_ALIGN;
   if (B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
-  const int64_t D = attn::kHeadDim;
+  const int64_t D = d;
   attn::BwdArgs a;
   if (layout == ATTN_BSHD) {
     a.q_sb = (int64_t)Sq * Hq * D; a.q_sh = D; a.q_ss = (int64_t)Hq * D;
@@ -334,6 +336,7 @@ static int bwd_call(const void* q, const void* k, const void* v, const void* o, 
   a.ws_l = a.ws_d + (size_t)B * Hq * Sq;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
   a.group = Hq / Hkv;
+  a.D = d;
   a.c = scale * 1.4426950408889634f;
   a.scale = scale;
   a.cu_q = nullptr;
@@ -413,6 +416,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.Sq = max_seqlen_q;
   a.Sk = max_seqlen_k;
   a.group = Hq / Hkv;
+  a.D = attn::kHeadDim;
   a.c = scale * 1.4426950408889634f;
   a.scale = scale;
   a.cu_q = cu_seqlens_q;

@@ -59,28 +59,46 @@
 namespace attn {
 namespace {
 
-constexpr int D = kHeadDim;
 constexpr int NW = 4;                 // waves per workgroup
 constexpr int NT = NW * 64;
 constexpr int KV_ROWS = NW * 32;      // keys per dK/dV workgroup
 constexpr int QB = 64;                // query rows per step of the dK/dV loop
 constexpr int Q_ROWS = NW * 32;       // query rows per dQ workgroup
 constexpr int KB = 64;                // keys per step of the dQ loop
-constexpr int TILE = 64 * 256;        // one 64-row bf16 tile in LDS
 constexpr uint32_t kRsrcFlags = 0x00020000;
 
-static_assert(kBwdKvRows == KV_ROWS && kBwdQRows == Q_ROWS && D == 128, "layout assumed below");
+static_assert(kBwdKvRows == KV_ROWS && kBwdQRows == Q_ROWS, "layout assumed below");
 
-// 4-bit swizzle of a row index: rows r and r + 4k land in different 4-chunk
-// groups, and the 4 rows of one transpose read in different chunks.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Sizes that follow from the head dim D (64 or 128) of bf16 rows in LDS.
+template <int D>
+struct BG {
+  static constexpr int RB = 2 * D;        // bytes per row
+  static constexpr int NC = D / 8;        // 16-byte chunks per row
+  static constexpr int TILE = 64 * RB;    // one 64-row tile
+  static constexpr int KS = D / 16;       // MFMA k-steps over d
+  static constexpr int NTD = D / 32;      // 32-wide d blocks
+  static constexpr int RPI = 1024 / RB;   // rows per 1 KB copy instruction
+  static constexpr int CPW = 64 / RPI / NW;   // copy instructions per wave per tile
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+};
+
+// Chunk swizzle of a row: rows r and r + 4k land in different 4-chunk groups
+// (16-chunk rows) or chunk pairs (8-chunk rows), and the 4 rows of one
+// transpose read in different chunks.
+template <int NC>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (NC == 8) return ((r & 3) << 1) | ((r >> 2) & 1);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 // byte offset of 16-byte chunk c of row `row` in a tile
+template <int D>
 __device__ __forceinline__ int tile_off(int row, int c) {
-  return row * 256 + ((c ^ swz(row & 15)) << 4);
+  return row * BG<D>::RB + ((c ^ swz<BG<D>::NC>(row & 15)) << 4);
 }
 // byte offset of element `col` (a multiple of 4) of row `row`
+template <int D>
 __device__ __forceinline__ int elem_off(int row, int col) {
-  return tile_off(row, col >> 3) + ((col & 7) << 1);
+  return tile_off<D>(row, col >> 3) + ((col & 7) << 1);
 }
 
 __device__ __forceinline__ int xcd_remap(int i, int n) {
@@ -97,8 +115,9 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+template <int D>
 __device__ __forceinline__ bf16x8 lds_row(const char* tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + tile_off(row, chunk));
+  return *reinterpret_cast<const bf16x8*>(tile + tile_off<D>(row, chunk));
 }
 
 // B operand of a product whose contraction runs over tile rows: lane
@@ -109,12 +128,13 @@ __device__ __forceinline__ bf16x8 lds_row(const char* tile, int row, int chunk) 
 // 4-element row addressed by lane 4e + j/4 (e = 0..3), so lane L of the
 // group addresses row rbase + 4h + L/4 at column col0 + 16*((lane/16)%2) +
 // 4*(L%4).
+template <int D>
 __device__ __forceinline__ bf16x8 lds_cols(const char* tile, int rbase, int col0, int lane) {
   const int L = lane & 15;
   const int row = rbase + 4 * (lane >> 5) + (L >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-  const bf16x4 lo = lds_read_tr(tile + elem_off(row, col));
-  const bf16x4 hi = lds_read_tr(tile + elem_off(row + 8, col));
+  const bf16x4 lo = lds_read_tr(tile + elem_off<D>(row, col));
+  const bf16x4 hi = lds_read_tr(tile + elem_off<D>(row + 8, col));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -126,26 +146,29 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
 }
 
 // Asynchronous copy of 16 rows (this wave's share of a 64-row tile) from
-// HBM into LDS: each buffer_load_dwordx4 ... lds moves 4 rows, lane i landing
-// at byte 16*i, i.e. row +i/16 and physical chunk i%16, so it fetches the
-// logical chunk the swizzle puts there.  Rows past the buffer's range read 0.
+// HBM into LDS: each buffer_load_dwordx4 ... lds moves 1 KB (RPI rows), lane i
+// landing at byte 16*i, i.e. row +i/NC and physical chunk i%NC, so it fetches
+// the logical chunk the swizzle puts there.  Rows past the buffer's range
+// read 0.
+template <int D>
 struct RowCopy {
-  uint32_t voff[4];
+  static constexpr int RPI = BG<D>::RPI, NC = BG<D>::NC, CPW = BG<D>::CPW;
+  uint32_t voff[CPW];
   int row0;
   __device__ void init(int64_t row_stride, int wave, int lane) {
     row0 = 16 * wave;
     const uint32_t ss = (uint32_t)(row_stride * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = row0 + 4 * j + (lane >> 4);
-      voff[j] = (uint32_t)row * ss + (uint32_t)(((lane & 15) ^ swz(row & 15)) << 4);
+    for (int j = 0; j < CPW; ++j) {
+      const int row = row0 + RPI * j + lane / NC;
+      voff[j] = (uint32_t)row * ss + (uint32_t)(((lane % NC) ^ swz<NC>(row & 15)) << 4);
     }
   }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* tile, uint32_t base) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ATTN_LDS void*)(tile + (row0 + 4 * j) * 256),
-                                               16, voff[j] + base, 0, 0, 0);
+    for (int j = 0; j < CPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (ATTN_LDS void*)(tile + (row0 + RPI * j) * BG<D>::RB), 16, voff[j] + base, 0, 0, 0);
   }
 };
 
@@ -157,36 +180,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 
 // A operands of S = Q K^T and dP = dO V^T: Q and dO row `row`, head-dim
 // slots 16*ks + 8*h .. +7
-__device__ __forceinline__ void read_rows(bf16x8 (&qa)[8], bf16x8 (&oa)[8], const char* qt,
-                                          const char* dt, int row, int h) {
+template <int D>
+__device__ __forceinline__ void read_rows(bf16x8 (&qa)[BG<D>::KS], bf16x8 (&oa)[BG<D>::KS],
+                                          const char* qt, const char* dt, int row, int h) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    qa[ks] = lds_row(qt, row, 2 * ks + h);
-    oa[ks] = lds_row(dt, row, 2 * ks + h);
+  for (int ks = 0; ks < BG<D>::KS; ++ks) {
+    qa[ks] = lds_row<D>(qt, row, 2 * ks + h);
+    oa[ks] = lds_row<D>(dt, row, 2 * ks + h);
   }
 }
 // S and dP of one 32-row sub-block against the wave's 32 keys
-__device__ __forceinline__ void mfma_sdp(f32x16& s, f32x16& p, const bf16x8 (&qa)[8],
-                                         const bf16x8 (&oa)[8], const bf16x8 (&kf)[8],
-                                         const bf16x8 (&vf)[8]) {
+template <int KS>
+__device__ __forceinline__ void mfma_sdp(f32x16& s, f32x16& p, const bf16x8 (&qa)[KS],
+                                         const bf16x8 (&oa)[KS], const bf16x8 (&kf)[KS],
+                                         const bf16x8 (&vf)[KS]) {
   s = f32x16{};
   p = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     s = mfma32(qa[ks], kf[ks], s);
     p = mfma32(oa[ks], vf[ks], p);
   }
 }
 // B operands of dV += P^T dO and dK += dS^T Q for a sub-block starting at
 // tile row r32: dO and Q columns, both halves of the 32 rows
-__device__ __forceinline__ void read_cols(bf16x8 (&oc)[2][4], bf16x8 (&qc)[2][4], const char* qt,
-                                          const char* dt, int r32, int lane) {
+template <int D>
+__device__ __forceinline__ void read_cols(bf16x8 (&oc)[2][BG<D>::NTD], bf16x8 (&qc)[2][BG<D>::NTD],
+                                          const char* qt, const char* dt, int r32, int lane) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      oc[t][n] = lds_cols(dt, r32 + 16 * t, 32 * n, lane);
-      qc[t][n] = lds_cols(qt, r32 + 16 * t, 32 * n, lane);
+    for (int n = 0; n < BG<D>::NTD; ++n) {
+      oc[t][n] = lds_cols<D>(dt, r32 + 16 * t, 32 * n, lane);
+      qc[t][n] = lds_cols<D>(qt, r32 + 16 * t, 32 * n, lane);
     }
 }
 // log2-LSE and D of the 16 rows a lane's accumulator registers hold
@@ -233,22 +259,24 @@ __device__ __forceinline__ void softmax_grad(bf16x8 (&pa)[2], bf16x8 (&da)[2], c
   }
 }
 // dV += P^T dO, dK += dS^T Q for one sub-block
-__device__ __forceinline__ void mfma_dvdk(f32x16 (&dv)[4], f32x16 (&dk)[4], const bf16x8 (&pa)[2],
-                                          const bf16x8 (&da)[2], const bf16x8 (&oc)[2][4],
-                                          const bf16x8 (&qc)[2][4]) {
+template <int NTD>
+__device__ __forceinline__ void mfma_dvdk(f32x16 (&dv)[NTD], f32x16 (&dk)[NTD],
+                                          const bf16x8 (&pa)[2], const bf16x8 (&da)[2],
+                                          const bf16x8 (&oc)[2][NTD], const bf16x8 (&qc)[2][NTD]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < NTD; ++n) {
       dv[n] = mfma32(pa[t], oc[t][n], dv[n]);
       dk[n] = mfma32(da[t], qc[t][n], dk[n]);
     }
 }
-// Scheduling request for the region since the last sched_barrier: 16 MFMAs
+// Scheduling request for the region since the last sched_barrier: N MFMAs
 // each followed by up to 6 VALU instructions.
+template <int N>
 __device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
   }
@@ -302,13 +330,16 @@ __device__ __forceinline__ SeqView seq_view(const BwdArgs& a, int b) {
 }  // namespace
 
 // ---- D = rowsum(dO * O) and LSE in log2 units --------------------------------
-// 16 rows per workgroup, 16 lanes per row, 8 elements per lane.
+// D/8 lanes per row, 8 elements per lane (16 rows per workgroup at d = 128,
+// 32 at d = 64).
+template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8, RPW = 256 / LPR;
   // packed sequences: all total_q rows as one batch entry ([Hq, total_q])
   const int rows = a.cu_q ? a.total_q : a.Sq;
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int row = blockIdx.x * RPW + threadIdx.x / LPR;
   const int hq = blockIdx.y, b = blockIdx.z;
-  const int ch = threadIdx.x & 15;
+  const int ch = threadIdx.x % LPR;
   float s = 0.f;
   if (row < rows) {
     const int64_t off = b * a.q_sb + hq * a.q_sh + (int64_t)row * a.q_ss + ch * 8;
@@ -318,7 +349,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) s = fmaf((float)o8[e], (float)d8[e], s);
   }
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+  for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
   if (ch == 0 && row < rows) {
     const int64_t i = ((int64_t)b * a.Hq + hq) * rows + row;
     a.ws_d[i] = s;
@@ -328,8 +359,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---- dK, dV ----------------------------------------------------------------
-template <bool CAUSAL, bool PACKED, bool ALIBI>
+template <int D, bool CAUSAL, bool PACKED, bool ALIBI>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int TILE = BG<D>::TILE, KS = BG<D>::KS, NTD = BG<D>::NTD;
   __shared__ __attribute__((aligned(1024))) char qbuf[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char dobuf[2 * TILE];
   __shared__ __attribute__((aligned(16))) float lbuf[2 * QB];
@@ -362,11 +394,11 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   // dP = dO V^T (lane: key kw0 + c, head-dim slots 16*ks + 8*h .. +7)
   const __bf16* kp = a.k + sv.kbase + g * a.k_sh;
   const __bf16* vp = a.v + sv.kbase + g * a.k_sh;
-  bf16x8 kf[8], vf[8];
+  bf16x8 kf[KS], vf[KS];
   {
     const int key = kw0 + c;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       if (key < Sk) {
         kf[ks] = *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
         vf[ks] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
@@ -384,9 +416,9 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int per_head = n_qb - qb_first;
   const int total = a.group * per_head;
 
-  RowCopy cp;
+  RowCopy<D> cp;
   cp.init(a.q_ss, wave, lane);
-  const uint32_t q_bytes = Sq > 0 ? (uint32_t)((int64_t)(Sq - 1) * a.q_ss * 2 + 256) : 0u;
+  const uint32_t q_bytes = Sq > 0 ? (uint32_t)((int64_t)(Sq - 1) * a.q_ss * 2 + BG<D>::RB) : 0u;
   const uint32_t blk_bytes = (uint32_t)(QB * a.q_ss * 2);
   auto issue = [&](int s, int st) {
     const int hq = g * a.group + s / per_head;
@@ -402,9 +434,9 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  f32x16 dk[4], dv[4];
+  f32x16 dk[NTD], dv[NTD];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
+  for (int n = 0; n < NTD; ++n) {
     dk[n] = f32x16{};
     dv[n] = f32x16{};
   }
@@ -439,14 +471,14 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       // instructions issue while its MFMAs execute).  Order: S, dP of
       // sub-block 0 | S, dP of 1 beside the softmax gradient of 0 | dV, dK of
       // 0 beside the softmax gradient of 1 | dV, dK of 1.
-      bf16x8 qa[8], oa[8], qa1[8], oa1[8];
-      read_rows(qa, oa, qt, dt, c, h);
+      bf16x8 qa[KS], oa[KS], qa1[KS], oa1[KS];
+      read_rows<D>(qa, oa, qt, dt, c, h);
       __builtin_amdgcn_sched_barrier(0);
       f32x16 s0, p0, s1, p1;
       mfma_sdp(s0, p0, qa, oa, kf, vf);
-      read_rows(qa1, oa1, qt, dt, 32 + c, h);
-      bf16x8 oc0[2][4], qc0[2][4];
-      read_cols(oc0, qc0, qt, dt, 0, lane);
+      read_rows<D>(qa1, oa1, qt, dt, 32 + c, h);
+      bf16x8 oc0[2][NTD], qc0[2][NTD];
+      read_cols<D>(oc0, qc0, qt, dt, 0, lane);
       f32x4 l0[4], d0[4], l1[4], d1[4];
       read_rowvals(l0, d0, lb, db, 0, h);
       read_rowvals(l1, d1, lb, db, 32, h);
@@ -454,15 +486,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       mfma_sdp(s1, p1, qa1, oa1, kf, vf);
       bf16x8 pa0[2], da0[2];
       softmax_grad<false, ALIBI>(pa0, da0, s0, p0, l0, d0, a.c, 0, 0, 0, 0, 0, alibi2, ad0);
-      interleave_mfma_valu();
+      interleave_mfma_valu<2 * KS>();
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 oc1[2][4], qc1[2][4];
-      read_cols(oc1, qc1, qt, dt, 32, lane);
+      bf16x8 oc1[2][NTD], qc1[2][NTD];
+      read_cols<D>(oc1, qc1, qt, dt, 32, lane);
       mfma_dvdk(dv, dk, pa0, da0, oc0, qc0);
       bf16x8 pa1[2], da1[2];
       softmax_grad<false, ALIBI>(pa1, da1, s1, p1, l1, d1, a.c, 0, 0, 0, 0, 0, alibi2,
                                  ad0 + 32.f);
-      interleave_mfma_valu();
+      interleave_mfma_valu<4 * NTD>();
       __builtin_amdgcn_sched_barrier(0);
       mfma_dvdk(dv, dk, pa1, da1, oc1, qc1);
       continue;
@@ -474,15 +506,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       // operand reads are issued in batches ahead of the MFMAs that use them
       // (sched_barrier keeps the compiler from sinking each read next to its
       // use, which would expose the LDS latency once per MFMA)
-      bf16x8 qa[8], oa[8];
-      read_rows(qa, oa, qt, dt, 32 * qs + c, h);
+      bf16x8 qa[KS], oa[KS];
+      read_rows<D>(qa, oa, qt, dt, 32 * qs + c, h);
       __builtin_amdgcn_sched_barrier(0);
       // S[q][key] and dP[q][key]: accumulator register r of lane (c, h) holds
       // row 8*(r/4) + 4h + r%4 of the sub-block against key kw0 + c
       f32x16 sacc, pacc;
       mfma_sdp(sacc, pacc, qa, oa, kf, vf);
-      bf16x8 oc[2][4], qc[2][4];
-      read_cols(oc, qc, qt, dt, 32 * qs, lane);
+      bf16x8 oc[2][NTD], qc[2][NTD];
+      read_cols<D>(oc, qc, qt, dt, 32 * qs, lane);
       f32x4 l4[4], d4[4];
       read_rowvals(l4, d4, lb, db, 32 * qs, h);
       __builtin_amdgcn_sched_barrier(0);
@@ -505,7 +537,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     const int key = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
     if (key < Sk) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
+      for (int n = 0; n < NTD; ++n) {
         dkp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)(dk[n][r] * a.scale);
         dvp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)dv[n][r];
       }
@@ -516,9 +548,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 // ---- dQ --------------------------------------------------------------------
 // Two workgroups per CU (two waves per SIMD, 64 KB of LDS each): one wave's
 // exponentials and operand reads run under the other's MFMAs.
-template <bool CAUSAL, bool PACKED, bool ALIBI>
+template <int D, bool CAUSAL, bool PACKED, bool ALIBI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
+  constexpr int TILE = BG<D>::TILE, KS = BG<D>::KS, NTD = BG<D>::NTD;
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE];
 
@@ -551,9 +584,9 @@ void bwd_dq_kernel(BwdArgs a) {
   // Q and dO fragments of the wave's rows: B operand of S^T = K Q^T and of
   // dP^T = V dO^T (lane: row q, head-dim slots 16*ks + 8*h .. +7)
   const int64_t qoff = sv.qbase + hq * a.q_sh;
-  bf16x8 qf[8], df[8];
+  bf16x8 qf[KS], df[KS];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     if (q < Sq) {
       qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qoff + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
       df[ks] = *reinterpret_cast<const bf16x8*>(a.dout + qoff + (int64_t)q * a.q_ss + 16 * ks + 8 * h);
@@ -572,17 +605,17 @@ void bwd_dq_kernel(BwdArgs a) {
   const int n_kt = (n_keys + KB - 1) / KB;
   const int wave_last = min(qw0 + 31, Sq - 1);
 
-  RowCopy cp;
+  RowCopy<D> cp;
   cp.init(a.k_ss, wave, lane);
   const __bf16* kp = a.k + sv.kbase + g * a.k_sh;
   const __bf16* vp = a.v + sv.kbase + g * a.k_sh;
-  const uint32_t k_bytes = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * a.k_ss * 2 + 256) : 0u;
+  const uint32_t k_bytes = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * a.k_ss * 2 + BG<D>::RB) : 0u;
   const __amdgpu_buffer_rsrc_t rk = rsrc(kp, k_bytes), rv = rsrc(vp, k_bytes);
   const uint32_t blk_bytes = (uint32_t)(KB * a.k_ss * 2);
 
-  f32x16 dq[4];
+  f32x16 dq[NTD];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) dq[n] = f32x16{};
+  for (int n = 0; n < NTD; ++n) dq[n] = f32x16{};
 
   if (n_kt > 0) {
     cp.issue(rk, kbuf, 0);
@@ -608,18 +641,18 @@ void bwd_dq_kernel(BwdArgs a) {
       // kr0 + 8*(r/4) + 4h + r%4 against this lane's row q
       // K rows are read as one batch, and the V rows go out before the S^T
       // MFMAs so that they arrive under them
-      bf16x8 ka[8], va[8];
+      bf16x8 ka[KS], va[KS];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) ka[ks] = lds_row(kt, 32 * ks2 + c, 2 * ks + h);
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_row<D>(kt, 32 * ks2 + c, 2 * ks + h);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) va[ks] = lds_row(vt, 32 * ks2 + c, 2 * ks + h);
+      for (int ks = 0; ks < KS; ++ks) va[ks] = lds_row<D>(vt, 32 * ks2 + c, 2 * ks + h);
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(ka[ks], qf[ks], sacc);
+      for (int ks = 0; ks < KS; ++ks) sacc = mfma32(ka[ks], qf[ks], sacc);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) pacc = mfma32(va[ks], df[ks], pacc);
+      for (int ks = 0; ks < KS; ++ks) pacc = mfma32(va[ks], df[ks], pacc);
       float ds[16];
       // ALiBi distance row + off - key of register 0
       const float ad0 = (float)(q + off - kr0 - 4 * h);
@@ -640,8 +673,8 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int u = 0; u < 2; ++u) {
         const bf16x8 da = to_bf16x8(ds + 8 * u);
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-          dq[n] = mfma32(da, lds_cols(kt, 32 * ks2 + 16 * u, 32 * n, lane), dq[n]);
+        for (int n = 0; n < NTD; ++n)
+          dq[n] = mfma32(da, lds_cols<D>(kt, 32 * ks2 + 16 * u, 32 * n, lane), dq[n]);
       }
     }
   }
@@ -653,47 +686,77 @@ void bwd_dq_kernel(BwdArgs a) {
     const int row = qw0 + 8 * (r >> 2) + 4 * h + (r & 3);
     if (row < Sq) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) dqp[(int64_t)row * a.q_ss + 32 * n + c] = (__bf16)(dq[n][r] * a.scale);
+      for (int n = 0; n < NTD; ++n) dqp[(int64_t)row * a.q_ss + 32 * n + c] = (__bf16)(dq[n][r] * a.scale);
     }
   }
 }
 
 hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
-  const int64_t n_rows16 = ((int64_t)(a.cu_q ? a.total_q : a.Sq) + 15) / 16;
+  const int rows = a.cu_q ? a.total_q : a.Sq;
+  const int rpw = a.D == 64 ? 32 : 16;   // rows per workgroup of the row-term kernel
+  const int64_t n_prep = ((int64_t)rows + rpw - 1) / rpw;
   const int prep_b = a.cu_q ? 1 : a.B;
   const int64_t g_kv = (int64_t)a.B * a.Hkv * ((a.Sk + KV_ROWS - 1) / KV_ROWS);
   const int64_t g_q = (int64_t)a.B * a.Hq * ((a.Sq + Q_ROWS - 1) / Q_ROWS);
-  if (n_rows16 > 0x7fffffff || a.Hq > 65535 || a.B > 65535 || g_kv > 0x7fffffff ||
-      g_q > 0x7fffffff)
+  if (n_prep > 0x7fffffff || a.Hq > 65535 || a.B > 65535 || g_kv > 0x7fffffff ||
+      g_q > 0x7fffffff || (a.D != 64 && a.D != 128) || (a.D == 64 && (a.cu_q || a.alibi)))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)n_rows16, a.Hq, prep_b), dim3(256), 0, stream,
-                     a);
+  const dim3 gp((unsigned)n_prep, a.Hq, prep_b), gk((unsigned)g_kv), gq((unsigned)g_q), bt(NT);
   const bool packed = a.cu_q != nullptr;
-  const dim3 gk((unsigned)g_kv), gq((unsigned)g_q), bt(NT);
-  if (packed) {
+  if (a.D == 64) {
+    hipLaunchKernelGGL((bwd_prep_kernel<64>), gp, dim3(256), 0, stream, a);
     if (causal) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<true, true, false>), gk, bt, 0, stream, a);
-      hipLaunchKernelGGL((bwd_dq_kernel<true, true, false>), gq, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, false, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true, false, false>), gq, bt, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<false, true, false>), gk, bt, 0, stream, a);
-      hipLaunchKernelGGL((bwd_dq_kernel<false, true, false>), gq, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, false, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false, false, false>), gq, bt, 0, stream, a);
+    }
+  } else if (packed) {
+    hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
+    if (causal) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, true, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true, true, false>), gq, bt, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, true, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false, true, false>), gq, bt, 0, stream, a);
     }
   } else if (a.alibi) {
+    hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
     if (causal) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<true, false, true>), gk, bt, 0, stream, a);
-      hipLaunchKernelGGL((bwd_dq_kernel<true, false, true>), gq, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, false, true>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true, false, true>), gq, bt, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<false, false, true>), gk, bt, 0, stream, a);
-      hipLaunchKernelGGL((bwd_dq_kernel<false, false, true>), gq, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, false, true>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false, false, true>), gq, bt, 0, stream, a);
     }
   } else if (causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<true, false, false>), gk, bt, 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<true, false, false>), gq, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, false, false>), gk, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, true, false, false>), gq, bt, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<false, false, false>), gk, bt, 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<false, false, false>), gq, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, false, false>), gk, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, false, false, false>), gq, bt, 0, stream, a);
   }
   return hipGetLastError();
 }
+
+// Every kernel variant the launch above uses, instantiated explicitly (the
+// host pass otherwise left some of them without their launch stubs).
+template __global__ void bwd_prep_kernel<64>(BwdArgs);
+template __global__ void bwd_prep_kernel<128>(BwdArgs);
+#define ATTN_BWD_VARIANT(D, C, P, A)                              \
+  template __global__ void bwd_dkdv_kernel<D, C, P, A>(BwdArgs); \
+  template __global__ void bwd_dq_kernel<D, C, P, A>(BwdArgs);
+ATTN_BWD_VARIANT(64, true, false, false)
+ATTN_BWD_VARIANT(64, false, false, false)
+ATTN_BWD_VARIANT(128, true, true, false)
+ATTN_BWD_VARIANT(128, false, true, false)
+ATTN_BWD_VARIANT(128, true, false, true)
+ATTN_BWD_VARIANT(128, false, false, true)
+ATTN_BWD_VARIANT(128, true, false, false)
+ATTN_BWD_VARIANT(128, false, false, false)
+#undef ATTN_BWD_VARIANT
 
 }  // namespace attn

@@ -108,6 +108,7 @@ struct BwdArgs {
   int64_t k_sb, k_sh, k_ss;  // element strides (k, v, dk, dv)
   int B, Hq, Hkv, Sq, Sk;
   int group;             // Hq / Hkv
+  int D;                 // head dim: 128, or 64 (dense, no ALiBi)
   float c;               // scale * log2(e)
   float scale;
   // packed sequences (null cu_q: dense batch): sequence b is rows

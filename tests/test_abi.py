@@ -169,7 +169,7 @@ def test_bwd_workspace_bytes():
     (dict(B=65536), -2),
     (dict(Sk=(1 << 22), Hkv=2, Hq=2, layout=0), -2),   # K/V rows of one head exceed 32-bit offsets
     (dict(Sq=(1 << 22), Hkv=2, Hq=2, layout=0, wsb=1 << 40), -2),
-    (dict(d=64), -3), (dict(layout=2), -3), (dict(causal=2), -3), (dict(scale=0.0), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(layout=2), -3), (dict(causal=2), -3), (dict(scale=0.0), -3),
     (dict(scale=float("nan")), -3),
     (dict(q=P + 8), -4), (dict(dk=P + 2), -4), (dict(lse=P + 4), -4), (dict(do=P + 8), -4),
     (dict(ws=None), -5), (dict(wsb=8 * 4 * 8 - 1), -5), (dict(ws=P + 4), -5),
@@ -183,6 +183,7 @@ def test_bwd_valid_arguments_need_a_gfx950_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert bwd() == -7
+    assert bwd(d=64) == -7            # head dim 64 is supported by attn_bwd
 
 
 def fwd_varlen(**kw):

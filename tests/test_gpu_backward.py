@@ -153,3 +153,22 @@ def test_mha_prefill_full_size_sampled_heads():
 def test_causal_gqa_full_size_sampled_group():
     p = gen.config3()
     _check_full_size(p, gen.output_grad(p, 3), [(7, 7)], "gqa causal b8 s8192")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,layout,causal", [
+    (1, 4, 4, 256, 256, gen.BSHD, False),
+    (2, 8, 2, 200, 200, gen.BSHD, True),      # GQA causal, ragged
+    (1, 4, 1, 129, 129, gen.BHSD, False),     # MQA
+    (2, 4, 4, 300, 77, gen.BHSD, False),      # cross attention
+    (1, 4, 2, 150, 100, gen.BSHD, True),      # rows that see no key
+    (1, 4, 2, 70, 300, gen.BSHD, True),       # bottom-right alignment
+])
+def test_d64_backward_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal,
+                           seed=500 + Sq + Sk, n_hot=2, d=64)
+    check_problem(p, gen.output_grad(p, 8), f"d64 B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} causal{causal}")
+
+
+def test_d64_backward_full_size_sampled_group():
+    p = gen.headdim64_causal_gqa()
+    _check_full_size(p, gen.output_grad(p, 7), [(2, 3)], "d64 gqa causal b8 s8192")
