@@ -18,8 +18,8 @@ are already resident in HBM:
 * packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
   U{1..8192}, reported beside the headline;
 * the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads
-  and of the packed sequences (attn_bwd_varlen), reported beside the
-  headline too.
+  (also with ALiBi and at head dim 64) and of the packed sequences
+  (attn_bwd_varlen), reported beside the headline too.
 
 Times come from HIP events on the stream the kernels are launched on.  The
 fp64 CPU oracle is timed on the host cores on a bounded sample of the same
@@ -302,24 +302,30 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
         "backward_kernels__mha_b4_h32_s4096_bhsd_and_causal_gqa_s8192.md": (
             "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
             "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
-            [wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_prep_kernel"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<false, false, false>"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<false, false, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel"),
+            [wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_prep_kernel<128>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<128, false, false, false>"),
+             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<128, false, false, false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel<128>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                    "bwd_dkdv_kernel<true, false, false>"),
+                    "bwd_dkdv_kernel<128, true, false, false>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                    "bwd_dq_kernel<true, false, false>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_prep_kernel"),
+                    "bwd_dq_kernel<128, true, false, false>"),
+             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_prep_kernel<128>"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                    "bwd_dkdv_kernel<true, true, false>"),
+                    "bwd_dkdv_kernel<128, true, true, false>"),
              wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                    "bwd_dq_kernel<true, true, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", "bwd_prep_kernel"),
+                    "bwd_dq_kernel<128, true, true, false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", "bwd_prep_kernel<128>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward",
-                    "bwd_dkdv_kernel<true, false, true>"),
+                    "bwd_dkdv_kernel<128, true, false, true>"),
              wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward",
-                    "bwd_dq_kernel<true, false, true>")],
+                    "bwd_dq_kernel<128, true, false, true>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward",
+                    "bwd_prep_kernel<64>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward",
+                    "bwd_dkdv_kernel<64, true, false, false>"),
+             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward",
+                    "bwd_dq_kernel<64, true, false, false>")],
             ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]),
     }
     for fname, (title, rows, tkeys) in files.items():
@@ -497,6 +503,28 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
                 "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
+    # the causal GQA backward at head dim 64
+    p = gen.headdim64_causal_gqa()
+    log(f"timing the backward of {p.name}")
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    do = to_dev(gen.output_grad(p, 7))
+    o, lse = ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(p.B, p.Hq, p.Sq), dtype=torch.uint8,
+                     device=q.device)
+
+    def run_d(_i):
+        ea.attn_bwd(q, k, v, o, lse, do, causal=True, scale=p.scale, layout="bshd", dq=dq, dk=dk,
+                    dv=dv, workspace=ws)
+
+    ms = time_calls(run_d, steps, 2, torch)
+    fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 64 / 2
+    res.append({"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
+                "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+                "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
     # packed sequences of mixed lengths (attn_bwd_varlen)
     pv = gen.varlen_causal_gqa()
     log(f"timing the backward of {pv.name}")
@@ -586,7 +614,15 @@ def main():
     if args.summarize:
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
         cmd = {"plan": {"prefill_hd_kernel<64, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192"
-                                                         "_d64_bshd", xs)],
+                                                         "_d64_bshd", xs),
+                                                        ("gqa_causal_prefill_b8_hq32_hkv8_s8192"
+                                                         "_d64_bshd_backward_fwd", 1)],
+                        "bwd_prep_kernel<64>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd"
+                                                 "_backward", xs)],
+                        "bwd_dkdv_kernel<64, true, false, false>": [(
+                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward", xs)],
+                        "bwd_dq_kernel<64, true, false, false>": [(
+                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward", xs)],
                         "prefill_hd_kernel<256, true>": [("gqa_causal_prefill_b4_hq32_hkv8_s4096"
                                                           "_d256_bshd", xs)],
                         "prefill_kernel<true, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
@@ -608,28 +644,28 @@ def main():
                                                   "_backward_fwd", 1),
                                                  ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                   "_backward_fwd", 1)],
-                        "bwd_prep_kernel": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),
+                        "bwd_prep_kernel<128>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),
                                             ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
                                              xs),
                                             ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi"
                                              "_backward", xs),
                                             ("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
                                              xs)],
-                        "bwd_dkdv_kernel<false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
+                        "bwd_dkdv_kernel<128, false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
                                                            xs)],
-                        "bwd_dq_kernel<false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
+                        "bwd_dq_kernel<128, false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
                                                          xs)],
-                        "bwd_dkdv_kernel<true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                        "bwd_dkdv_kernel<128, true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                           "_backward", xs)],
-                        "bwd_dq_kernel<true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
+                        "bwd_dq_kernel<128, true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
                                                         "_backward", xs)],
-                        "bwd_dkdv_kernel<true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
+                        "bwd_dkdv_kernel<128, true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                          "_backward", xs)],
-                        "bwd_dq_kernel<true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
+                        "bwd_dq_kernel<128, true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
                                                        "_backward", xs)],
-                        "bwd_dkdv_kernel<true, false, true>": [(
+                        "bwd_dkdv_kernel<128, true, false, true>": [(
                             "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
-                        "bwd_dq_kernel<true, false, true>": [(
+                        "bwd_dq_kernel<128, true, false, true>": [(
                             "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
                         "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
                                                    max(st, 20) + wu + max(st, 40)),
