@@ -31,7 +31,7 @@ BF16_QNAN = np.uint16(0x7FC0)
 
 # stream ids for default_rng([seed, stream])
 (_S_Q, _S_K, _S_V, _S_HOT, _S_LENS, _S_PERM, _S_KX, _S_VX, _S_EQK, _S_EQV, _S_KNEW,
- _S_VNEW, _S_DO, _S_VLENS) = range(14)
+ _S_VNEW, _S_DO, _S_VLENS, _S_F8Q, _S_F8K, _S_F8V) = range(17)
 
 BSHD = 0
 BHSD = 1
@@ -384,3 +384,59 @@ def headdim64_causal_gqa(seed=7):
     (the causal GQA workload's shape at the smaller head size)."""
     return prefill_inputs(8, 32, 8, 8192, 8192, layout=BSHD, causal=True, seed=seed, d=64,
                           name="gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd")
+
+
+def e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    """Encode float32 values as OCP E4M3 (FN) bytes, round to nearest even,
+    with torch's float8_e4m3fn conversion (finite inputs within +-448)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+@dataclass
+class Fp8Prefill:
+    """One FP8 prefill problem: q/k/v are E4M3 byte arrays in `layout`, each
+    with a float32 descale factor (real value = descale * decoded byte)."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    layout: int
+    causal: bool
+    scale: float
+    descale_q: float
+    descale_k: float
+    descale_v: float
+    name: str = ""
+
+    @property
+    def flops(self) -> float:
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * D
+        return f / 2 if self.causal else f
+
+
+def fp8_prefill_inputs(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0, scale=None,
+                       descales=(1.0, 1.0, 1.0), amp=(1.0, 1.0, 1.0), name="") -> Fp8Prefill:
+    """Draw Q, K, V iid N(0, 1) times amp (per tensor) in float32 and encode
+    them as E4M3; `descales` are stored beside them as float32.  A small amp
+    puts many values among the E4M3 subnormals (|x| < 2^-6)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    q = e4m3_bytes(amp[0] * _normal(seed, _S_F8Q, layout_shape(layout, B, Hq, Sq)))
+    k = e4m3_bytes(amp[1] * _normal(seed, _S_F8K, layout_shape(layout, B, Hkv, Sk)))
+    v = e4m3_bytes(amp[2] * _normal(seed, _S_F8V, layout_shape(layout, B, Hkv, Sk)))
+    dq, dk, dv = (float(np.float32(x)) for x in descales)
+    return Fp8Prefill(q, k, v, B, Hq, Hkv, Sq, Sk, layout, bool(causal), float(scale), dq, dk, dv,
+                      name=name)
+
+
+def fp8_mha_prefill(seed=8):
+    """The MHA prefill workload's shape (B=4, H=32, S=4096, BHSD, non-causal)
+    with E4M3 inputs drawn from N(0, 1) and descales 1."""
+    return fp8_prefill_inputs(4, 32, 32, 4096, 4096, layout=BHSD, seed=seed,
+                              name="fp8_mha_prefill_b4_h32_s4096_bhsd")

@@ -12,8 +12,10 @@ HIP kernels: the two meet only in the seeded input generator (``attn_inputs``).
   split-KV merge, used only to pin the oracle to the pages' merge rule.
 * ``oracle.backward``: the gradient of the forward (dQ, dK, dV for an upstream
   dO) by the chain rule on the materialised matrices, in float64.
+* ``oracle.fp8``: E4M3 decoding and the forward on FP8 inputs with
+  per-tensor descales.
 * ``oracle.rounding``: the three bf16 rounding rules of the output conversion
   (to nearest with ties to even, to nearest with ties away from zero, toward
   zero) applied to float64 values.
 """
-from . import attention, backward, online, rounding  # noqa: F401
+from . import attention, backward, fp8, online, rounding  # noqa: F401
