@@ -388,9 +388,10 @@ def headdim64_causal_gqa(seed=7):
 
 def e4m3_bytes(x: np.ndarray) -> np.ndarray:
     """Encode float32 values as OCP E4M3 (FN) bytes, round to nearest even,
-    with torch's float8_e4m3fn conversion (finite inputs within +-448)."""
+    with torch's float8_e4m3fn conversion; values beyond +-448 are clipped to
+    +-448 first (the conversion would give the NaN encoding)."""
     import torch
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0))
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 

@@ -42,7 +42,8 @@ STATUS = {
 }
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_alibi", "attn_fwd_varlen", "attn_decode_workspace_bytes", "attn_decode_paged",
+EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_alibi", "attn_fwd_varlen", "attn_fwd_fp8",
+           "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
            "attn_bwd", "attn_bwd_alibi", "attn_bwd_varlen", "attn_status_string", "attn_version")
 
@@ -73,6 +74,8 @@ def library() -> ctypes.CDLL:
         lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                         vp]
         lib.attn_fwd_varlen.restype = i
+        lib.attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        lib.attn_fwd_fp8.restype = i
         lib.attn_decode_workspace_bytes.argtypes = [i, i, i]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
@@ -191,6 +194,44 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
         st, where = library().attn_fwd_rounded(*args, rnd, _stream_ptr(stream)), "attn_fwd_rounded"
     if st != 0:
         raise AttnError(st, where)
+    return out, lse
+
+
+def attn_fwd_fp8(q, k, v, *, descale_q: float = 1.0, descale_k: float = 1.0,
+                 descale_v: float = 1.0, causal: bool = False, scale: float | None = None,
+                 layout: str = "bshd", out=None, lse=None, stream=None):
+    """Attention forward on FP8 inputs: q, k, v are uint8 GPU tensors of OCP
+    E4M3 bytes (or torch.float8_e4m3fn), shaped as for attn_fwd, each with a
+    per-tensor fp32 descale.  Returns (o bf16 in q's layout, lse fp32
+    [B, Hq, Sq])."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_cuda or \
+                not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous uint8 / float8_e4m3fn GPU tensor")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q, k, v must be 4-D and k, v of equal shape")
+    lay = {"bshd": ATTN_BSHD, "bhsd": ATTN_BHSD}[layout.lower()]
+    if lay == ATTN_BSHD:
+        B, Sq, Hq, d = q.shape
+        _, Sk, Hkv, _ = k.shape
+    else:
+        B, Hq, Sq, d = q.shape
+        _, Hkv, Sk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q and k disagree on batch or head dim")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(descale_q),
+                                float(descale_k), float(descale_v), out.data_ptr(), lse.data_ptr(),
+                                B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)), lay,
+                                _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
     return out, lse
 
 

@@ -185,6 +185,51 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                           ATTN_ROUND_RTNE, stream);
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                 float descale_v, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk,
+                 int d, float scale, int causal, int layout, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  // the descales and the scale fold into two fp32 constants, which must stay
+  // normal, positive and finite
+  const double cd = (double)scale * 1.4426950408889634 * (double)descale_q * (double)descale_k *
+                    65536.0;
+  const double od = (double)descale_v * 256.0;
+  const bool consts_ok = std::isfinite(cd) && std::isfinite(od) && cd >= 1.2e-38 &&
+                         od >= 1.2e-38 && cd <= 3.0e38 && od <= 3.0e38;
+  if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
+      (causal != 0 && causal != 1) || !scale_ok(scale) || !scale_ok(descale_q) ||
+      !scale_ok(descale_k) || !scale_ok(descale_v) || !consts_ok)
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  const int64_t D = d;
+  attn::Fp8Args a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.o = static_cast<__bf16*>(o);
+  a.lse = lse;
+  if (layout == ATTN_BSHD) {
+    a.q_sb = (int64_t)Sq * Hq * D; a.q_sh = D; a.q_ss = (int64_t)Hq * D;
+    a.k_sb = (int64_t)Sk * Hkv * D; a.k_sh = D; a.k_ss = (int64_t)Hkv * D;
+  } else {
+    a.q_sb = (int64_t)Hq * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
+    a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
+  }
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
+  a.group = Hq / Hkv;
+  a.n_qt = (Sq + attn::kFp8RowsPerBlock - 1) / attn::kFp8RowsPerBlock;
+  if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
+  a.c = (float)cd;
+  a.out_scale = (float)od;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+  const hipError_t e = attn::launch_prefill_fp8(a, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
   if (B < 1 || Hq < 1 || max_blocks_per_seq < 1) return 0;
   const size_t splits = (size_t)attn::decode_max_splits(max_blocks_per_seq);

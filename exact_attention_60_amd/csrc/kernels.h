@@ -43,6 +43,26 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 
+// ---- FP8 (E4M3) forward ------------------------------------------------------
+constexpr int kFp8RowsPerBlock = 128;   // query rows per workgroup
+
+struct Fp8Args {
+  const uint8_t* q;          // E4M3 bytes, d = 128 innermost
+  const uint8_t* k;
+  const uint8_t* v;
+  __bf16* o;                 // bf16, q's layout
+  float* lse;                // [B, Hq, Sq]
+  int64_t q_sb, q_sh, q_ss;  // element strides of batch, head, sequence (q and o)
+  int64_t k_sb, k_sh, k_ss;  // same for k and v
+  int B, Hq, Hkv, Sq, Sk;
+  int group;                 // Hq / Hkv
+  int n_qt;                  // ceil(Sq / kFp8RowsPerBlock)
+  float c;                   // scale * log2(e) * descale_q * descale_k * 2^16
+  float out_scale;           // descale_v * 2^8
+};
+
+hipError_t launch_prefill_fp8(const Fp8Args& a, bool causal, hipStream_t stream);
+
 // head dims 64 and 256 (dense layouts, no ALiBi): query rows per workgroup,
 // and the launch (n_qt = ceil(Sq / rows per workgroup))
 int prefill_hd_rows_per_block();

@@ -13,7 +13,7 @@
  *                      probabilities recomputed from the forward's LSE.
  * attn_fwd_varlen and attn_bwd_varlen are attn_fwd and attn_bwd over packed
  * sequences of different lengths; attn_fwd_alibi and attn_bwd_alibi add an
- * ALiBi bias.
+ * ALiBi bias; attn_fwd_fp8 takes FP8 (E4M3) inputs with per-tensor descales.
  *
  * Definitions followed (page titles and sections):
  *  - attention as the fused softmax(QK^T/sqrt(d))V, bf16, head dim 128, BSHD
@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 8
+#define ATTN_VERSION 9
 
 typedef enum {
   ATTN_OK = 0,
@@ -155,6 +155,33 @@ int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float
 int attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
                    const float* alibi_slopes, int B, int Hq, int Hkv, int Sq, int Sk, int d,
                    float scale, int causal, int layout, int rounding, void* stream);
+
+/*
+ * attn_fwd_fp8 - attn_fwd on FP8 inputs.  Q, K and V are bytes in the OCP
+ * 8-bit E4M3 format ("FN": sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, no infinity, largest finite 448), each tensor with one
+ * fp32 descale factor: the attention of attn_fwd is computed on the real
+ * values descale_q*q, descale_k*k, descale_v*v.  The pages name FP8 inputs
+ * as a variant and say that FP8 handling falls back to FP16 on ROCm
+ * ("Engineering the FlashAttention-4 kernel port to ROCm", HIP migration
+ * section; "IO-aware tiling strategy in FlashAttention-4", monitoring
+ * paragraph): the bytes are widened exactly to fp16 inside the kernel and
+ * both products run on fp16 MFMA with fp32 accumulation.
+ *
+ *   q, k, v      device E4M3 bytes in `layout` (BSHD [B,S,H,128] or BHSD
+ *                [B,H,S,128]), 16-byte aligned, finite values: the E4M3 NaN
+ *                encoding is not recognised (it reads as +-480)
+ *   descale_*    positive finite fp32; scale*descale_q*descale_k*log2(e)*2^16
+ *                and descale_v*2^8 must be normal fp32 values, otherwise
+ *                ATTN_ERR_UNSUPPORTED
+ *   o, lse       as for attn_fwd (O bf16 rounded to nearest even in q's
+ *                layout, LSE fp32 [B,Hq,Sq] of the descaled scores)
+ * d must be 128.  Everything else (shapes, GQA, causal alignment, empty rows,
+ * errors, stream) is as for attn_fwd.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                 float descale_v, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk,
+                 int d, float scale, int causal, int layout, void* stream);
 
 /*
  * attn_fwd_varlen - attn_fwd over a batch of packed sequences of different

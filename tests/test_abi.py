@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     src = open(os.path.join(ROOT, "include", "attn.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 8
+    assert ea.attn_version() == 9
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -294,3 +294,30 @@ def test_binding_rejects_unknown_rounding_name():
     with pytest.raises(ValueError):
         ea._rounding_code("nearest")
     assert [ea._rounding_code(n) for n in ("RTNE", "rtna", "rtz")] == [0, 1, 2]
+
+
+def fwd_fp8(**kw):
+    a = dict(q=P, k=P, v=P, dq=1.0, dk=1.0, dv=1.0, o=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8,
+             d=128, scale=0.1, causal=0, layout=0, stream=None)
+    a.update(kw)
+    return ea.library().attn_fwd_fp8(a["q"], a["k"], a["v"], a["dq"], a["dk"], a["dv"], a["o"],
+                                     a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"],
+                                     a["scale"], a["causal"], a["layout"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(B=0), -2), (dict(Hq=3), -2), (dict(Sk=0), -2),
+    (dict(d=64), -3), (dict(layout=2), -3), (dict(causal=2), -3), (dict(dq=0.0), -3),
+    (dict(dk=-1.0), -3), (dict(dv=float("inf")), -3), (dict(dv=float("nan")), -3),
+    (dict(dq=1e-30, dk=1e-30), -3), (dict(dq=1e30, dk=1e30), -3), (dict(v=P + 8), -4),
+])
+def test_fwd_fp8_argument_errors(kw, code):
+    assert fwd_fp8(**kw) == code
+
+
+def test_fwd_fp8_valid_arguments_need_a_gfx950_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert fwd_fp8() == -7
+    assert fwd_fp8(dq=0.5, dk=3.0, dv=1e-3, causal=1, layout=1) == -7

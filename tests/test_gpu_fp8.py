@@ -1,0 +1,115 @@
+"""Parity of the FP8 (E4M3) forward (attn_fwd_fp8) with the fp64 oracle on
+the decoded, descaled inputs (GPU), under the forward's tolerance:
+|O - O_ref| <= 2 ulp_bf16(|O_ref|) + 1e-3 and |LSE - LSE_ref| <= 1e-3.  The
+widening of E4M3 to fp16 is exact, so the arithmetic after it is that of the
+bf16 forward (fp32 accumulation, fp16 probabilities for P.V, bf16 output)."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as gen
+import exact_attention_60_amd as ea
+import oracle.fp8 as f8
+from gpu_util import host_f64, logical_o, need_gpu
+from tolerance import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def dev_u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run(p):
+    o, lse = ea.attn_fwd_fp8(dev_u8(p.q), dev_u8(p.k), dev_u8(p.v), descale_q=p.descale_q,
+                             descale_k=p.descale_k, descale_v=p.descale_v, causal=p.causal,
+                             scale=p.scale, layout="bshd" if p.layout == gen.BSHD else "bhsd")
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_all(p, what):
+    print(f"case: {what}", flush=True)
+    o, lse = run(p)
+    o_ref, l_ref = f8.attention_fp8(p.q, p.k, p.v, p.descale_q, p.descale_k, p.descale_v, p.B,
+                                    p.Hq, p.Hkv, p.Sq, p.Sk, p.scale, p.causal, p.layout)
+    e = check_o(logical_o(o, p.layout), o_ref, what)
+    el = check_lse(host_f64(lse), l_ref, what)
+    print(f"{what}: err/tol {e[1]:.3f} lse {el:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,layout,causal", [
+    (1, 4, 4, 256, 256, gen.BSHD, False),      # the tiny MHA shape
+    (2, 8, 2, 200, 200, gen.BHSD, True),       # GQA causal, ragged blocks and tiles
+    (1, 4, 2, 300, 77, gen.BSHD, False),       # cross attention, short keys
+    (1, 4, 2, 150, 100, gen.BSHD, True),       # rows that see no key
+    (1, 4, 1, 70, 600, gen.BHSD, True),        # MQA, bottom-right alignment
+    (1, 2, 2, 1, 1, gen.BSHD, False),          # one row, one key
+    (1, 2, 1, 129, 1000, gen.BSHD, False),     # one row past a block, many tiles
+])
+def test_shapes_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
+    p = gen.fp8_prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=Sq + Sk)
+    check_all(p, f"fp8 B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} causal{causal}")
+
+
+def test_descales_and_peaky_rows():
+    # descales far from 1 and a large Q (amp 6): sharp softmax rows
+    p = gen.fp8_prefill_inputs(1, 4, 2, 160, 230, layout=gen.BSHD, causal=True, seed=21,
+                               descales=(1.75, 0.625, 0.0390625), amp=(6.0, 1.0, 1.0))
+    check_all(p, "fp8 descales, peaky rows")
+
+
+def test_subnormal_inputs():
+    # amp 0.02: most bytes are E4M3 subnormals (|x| < 2^-6), widened to fp16
+    # subnormals; the descales bring the scores back to order one
+    p = gen.fp8_prefill_inputs(1, 4, 4, 128, 192, layout=gen.BHSD, seed=22,
+                               descales=(64.0, 64.0, 32.0), amp=(0.02, 0.02, 0.02))
+    frac = np.mean((p.q & 0x78) == 0)
+    assert frac > 0.3, frac
+    check_all(p, "fp8 subnormal inputs")
+
+
+def test_extreme_values():
+    # the largest finite E4M3 bytes (+-448) in V, with a V descale of 2^-8 so
+    # that the real values are of order one, as the absolute part of the
+    # tolerance assumes (with |v| up to 448 the fp16 rounding of P alone moves
+    # a cancelling sum by far more than 1e-3)
+    p = gen.fp8_prefill_inputs(1, 2, 1, 64, 100, layout=gen.BSHD, seed=23, amp=(1.0, 1.0, 200.0),
+                               descales=(1.0, 1.0, 1.0 / 256))
+    p.v[0, ::7, 0, ::5] = 0x7E
+    p.v[0, 3::11, 0, 1::9] = 0xFE
+    check_all(p, "fp8 extreme V")
+
+
+def test_mha_full_size_sampled_rows():
+    p = gen.fp8_mha_prefill()
+    print(f"case: {p.name}", flush=True)
+    o, lse = run(p)
+    rng = np.random.default_rng(5)
+    rows = [(int(rng.integers(p.B)), int(rng.integers(p.Hq)), int(i))
+            for i in rng.integers(0, p.Sq, size=48)] + [(3, 31, p.Sq - 1), (0, 0, 0)]
+    o_ref, l_ref = f8.attention_fp8(p.q, p.k, p.v, 1, 1, 1, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
+                                    False, p.layout, rows=rows)
+    got = logical_o(o, p.layout)
+    gl = host_f64(lse)
+    idx = tuple(np.array(rows).T)
+    e = check_o(got[idx], o_ref[idx], p.name)
+    el = check_lse(gl[idx], l_ref[idx], p.name)
+    print(f"{p.name}: sampled err/tol {e[1]:.3f} lse {el:.3g}", flush=True)
+
+
+def test_float8_dtype_accepted_and_deterministic():
+    p = gen.fp8_prefill_inputs(1, 4, 2, 100, 140, causal=True, seed=24)
+    q = dev_u8(p.q).view(torch.float8_e4m3fn)
+    k = dev_u8(p.k).view(torch.float8_e4m3fn)
+    v = dev_u8(p.v).view(torch.float8_e4m3fn)
+    a = ea.attn_fwd_fp8(q, k, v, causal=True)
+    b = run(p)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
