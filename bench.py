@@ -15,6 +15,8 @@ are already resident in HBM:
   same way and reported beside the headline (skip with --no-extra);
 * the causal GQA shape at head dims 64 and 256 (attn_fwd with d = 64, 256);
 * the causal GQA workload with an ALiBi bias (attn_fwd_alibi);
+* FP8 (E4M3) inputs on the MHA shape (attn_fwd_fp8), reported beside the
+  headline;
 * packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
   U{1..8192}, reported beside the headline;
 * the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads
@@ -220,7 +222,8 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
     per = {}
     for r in fetch:
         name = r["Kernel_Name"]
-        key = next((kk for kk in ("prefill_kernel", "decode_partial_kernel", "decode_merge_kernel",
+        key = next((kk for kk in ("prefill_kernel", "prefill_fp8_kernel", "decode_partial_kernel",
+                                  "decode_merge_kernel",
                                   "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
                     if kk in name), None)
         if key is None:
@@ -228,12 +231,13 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
         fb = float(r["Counter_Value"]) * 1024 * f_fetch
         wb = float(wmap[r["Dispatch_Id"]]["Counter_Value"]) * 1024 * f_write
         per.setdefault(key, []).append((fb, wb))
-    srcs = {"prefill_kernel": "prefill.hip", "decode_partial_kernel": "decode.hip",
+    srcs = {"prefill_kernel": "prefill.hip", "prefill_fp8_kernel": "prefill_fp8.hip",
+            "decode_partial_kernel": "decode.hip",
             "decode_merge_kernel": "decode.hip", "bwd_prep_kernel": "backward.hip",
             "bwd_dkdv_kernel": "backward.hip", "bwd_dq_kernel": "backward.hip"}
     traffic = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
                         "dispatch), each scaled by the reading of a 1 GiB device copy; prefill "
-                        "and backward on mha_prefill_b4_h32_s4096_bhsd, decode on "
+                        "and backward on mha_prefill_b4_h32_s4096_bhsd (FP8: its E4M3 copy), decode on "
                         "paged_decode_b32_hq32_hkv8_len4096_page16",
                "fetch_scale": f_fetch, "write_scale": f_write,
                "commands": [command["fetch"], command["write"]]}
@@ -286,6 +290,10 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
              wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_partial_kernel"),
              wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_merge_kernel")],
             ["decode_partial_kernel", "decode_merge_kernel"]),
+        "prefill_fp8_kernel__fp8_mha_prefill_b4_h32_s4096_bhsd.md": (
+            "# prefill_fp8_kernel (attn_fwd_fp8, E4M3 inputs) on fp8_mha_prefill_b4_h32_s4096_bhsd",
+            [wl_row("fp8_mha_prefill_b4_h32_s4096_bhsd", "prefill_fp8_kernel<false>")],
+            ["prefill_fp8_kernel"]),
         "prefill_kernel__causal_gqa_s8192_and_diffusion_s32760.md": (
             "# prefill_kernel on the causal GQA and diffusion-style workloads",
             [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true, false>"),
@@ -362,6 +370,31 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
                     "flop": p.flops, "TFLOP/s": round(tf, 2),
                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, o, lse
+    # FP8 (E4M3) inputs on the MHA shape (attn_fwd_fp8)
+    p = gen.fp8_mha_prefill()
+    log(f"timing {p.name}")
+
+    def u8(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q, k, v = u8(p.q), u8(p.k), u8(p.v)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+    def run_f(_i):
+        ea.attn_fwd_fp8(q, k, v, causal=False, scale=p.scale, layout="bhsd", out=o, lse=lse)
+
+    ms = time_calls(run_f, steps, 2, torch)
+    tf = p.flops / (ms * 1e-3) / 1e12
+    res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
+                "inputs": "e4m3", "compute": "fp16 MFMA", "causal": False, "layout": "bhsd",
+                "ms_per_call": round(ms, 4), "flop": p.flops, "TFLOP/s": round(tf, 2),
+                "frac_of_fp16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_bytes": 3 * q.numel() + 2 * o.numel() + 4 * lse.numel(),
+                "traffic": traffic_from_profiles(
+                    "prefill_fp8_kernel",
+                    os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill_fp8.hip"))})
+    del q, k, v, o, lse
     # head dim 64 on the causal GQA shape
     p = gen.headdim64_causal_gqa()
     log(f"timing {p.name}")
@@ -613,7 +646,8 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
-        cmd = {"plan": {"prefill_hd_kernel<64, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192"
+        cmd = {"plan": {"prefill_fp8_kernel<false>": [("fp8_mha_prefill_b4_h32_s4096_bhsd", xs)],
+                        "prefill_hd_kernel<64, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192"
                                                          "_d64_bshd", xs),
                                                         ("gqa_causal_prefill_b8_hq32_hkv8_s8192"
                                                          "_d64_bshd_backward_fwd", 1)],
@@ -740,6 +774,10 @@ def main():
         do = to_dev(gen.output_grad(p, 2))
         for i in range(3):
             ea.attn_bwd(q, k, v, o, lse, do, causal=False, scale=p.scale, layout="bhsd")
+        p8 = gen.fp8_mha_prefill()
+        q8, k8, v8 = (torch.from_numpy(x).to(dev) for x in (p8.q, p8.k, p8.v))
+        for i in range(3):
+            ea.attn_fwd_fp8(q8, k8, v8, scale=p8.scale, layout="bhsd", out=o, lse=lse)
         torch.cuda.synchronize()
         print(json.dumps({"counters_run": True, "copy_bytes": n}))
         return
