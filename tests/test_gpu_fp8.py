@@ -113,3 +113,20 @@ def test_float8_dtype_accepted_and_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1], b[1])
+
+
+def test_causal_gqa_full_size_sampled_rows():
+    # the causal GQA workload's shape (B=8, Hq=32, Hkv=8, S=8192, BSHD) in E4M3
+    p = gen.fp8_prefill_inputs(8, 32, 8, 8192, 8192, layout=gen.BSHD, causal=True, seed=9,
+                               descales=(0.5, 0.5, 2.0))
+    print("case: fp8 causal gqa b8 hq32 hkv8 s8192", flush=True)
+    o, lse = run(p)
+    rng = np.random.default_rng(6)
+    rows = [(int(rng.integers(p.B)), int(rng.integers(p.Hq)), int(i))
+            for i in rng.integers(0, p.Sq, size=40)] + [(7, 31, p.Sq - 1), (0, 0, 0), (3, 5, 64)]
+    o_ref, l_ref = f8.attention_fp8(p.q, p.k, p.v, p.descale_q, p.descale_k, p.descale_v, p.B,
+                                    p.Hq, p.Hkv, p.Sq, p.Sk, p.scale, True, p.layout, rows=rows)
+    idx = tuple(np.array(rows).T)
+    e = check_o(logical_o(o, p.layout)[idx], o_ref[idx], "fp8 causal gqa")
+    el = check_lse(host_f64(lse)[idx], l_ref[idx], "fp8 causal gqa")
+    print(f"fp8 causal gqa s8192: sampled err/tol {e[1]:.3f} lse {el:.3g}", flush=True)
