@@ -441,3 +441,10 @@ def fp8_mha_prefill(seed=8):
     with E4M3 inputs drawn from N(0, 1) and descales 1."""
     return fp8_prefill_inputs(4, 32, 32, 4096, 4096, layout=BHSD, seed=seed,
                               name="fp8_mha_prefill_b4_h32_s4096_bhsd")
+
+
+def fp8_causal_gqa(seed=9):
+    """The causal GQA workload's shape (B=8, Hq=32, Hkv=8, S=8192, BSHD) with
+    E4M3 inputs drawn from N(0, 1) and descales 1."""
+    return fp8_prefill_inputs(8, 32, 8, 8192, 8192, layout=BSHD, causal=True, seed=seed,
+                              name="fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd")

@@ -15,8 +15,8 @@ are already resident in HBM:
   same way and reported beside the headline (skip with --no-extra);
 * the causal GQA shape at head dims 64 and 256 (attn_fwd with d = 64, 256);
 * the causal GQA workload with an ALiBi bias (attn_fwd_alibi);
-* FP8 (E4M3) inputs on the MHA shape (attn_fwd_fp8), reported beside the
-  headline;
+* FP8 (E4M3) inputs on the MHA and causal GQA shapes (attn_fwd_fp8),
+  reported beside the headline;
 * packed sequences (attn_fwd_varlen): 16 causal GQA sequences of lengths
   U{1..8192}, reported beside the headline;
 * the backward (attn_bwd: dQ, dK, dV) of the MHA and causal GQA workloads
@@ -290,9 +290,11 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
              wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_partial_kernel"),
              wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_merge_kernel")],
             ["decode_partial_kernel", "decode_merge_kernel"]),
-        "prefill_fp8_kernel__fp8_mha_prefill_b4_h32_s4096_bhsd.md": (
-            "# prefill_fp8_kernel (attn_fwd_fp8, E4M3 inputs) on fp8_mha_prefill_b4_h32_s4096_bhsd",
-            [wl_row("fp8_mha_prefill_b4_h32_s4096_bhsd", "prefill_fp8_kernel<false>")],
+        "prefill_fp8_kernel__fp8_mha_s4096_and_causal_gqa_s8192.md": (
+            "# prefill_fp8_kernel (attn_fwd_fp8, E4M3 inputs) on fp8_mha_prefill_b4_h32_s4096_bhsd "
+            "and fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
+            [wl_row("fp8_mha_prefill_b4_h32_s4096_bhsd", "prefill_fp8_kernel<false>"),
+             wl_row("fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_fp8_kernel<true>")],
             ["prefill_fp8_kernel"]),
         "prefill_kernel__causal_gqa_s8192_and_diffusion_s32760.md": (
             "# prefill_kernel on the causal GQA and diffusion-style workloads",
@@ -370,31 +372,34 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
                     "flop": p.flops, "TFLOP/s": round(tf, 2),
                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del q, k, v, o, lse
-    # FP8 (E4M3) inputs on the MHA shape (attn_fwd_fp8)
-    p = gen.fp8_mha_prefill()
-    log(f"timing {p.name}")
-
+    # FP8 (E4M3) inputs on the MHA and causal GQA shapes (attn_fwd_fp8)
     def u8(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
-    q, k, v = u8(p.q), u8(p.k), u8(p.v)
-    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+    for make in (gen.fp8_mha_prefill, gen.fp8_causal_gqa):
+        p = make()
+        log(f"timing {p.name}")
+        lay = "bshd" if p.layout == gen.BSHD else "bhsd"
+        q, k, v = u8(p.q), u8(p.k), u8(p.v)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
 
-    def run_f(_i):
-        ea.attn_fwd_fp8(q, k, v, causal=False, scale=p.scale, layout="bhsd", out=o, lse=lse)
+        def run_f(_i):
+            ea.attn_fwd_fp8(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
 
-    ms = time_calls(run_f, steps, 2, torch)
-    tf = p.flops / (ms * 1e-3) / 1e12
-    res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
-                "inputs": "e4m3", "compute": "fp16 MFMA", "causal": False, "layout": "bhsd",
-                "ms_per_call": round(ms, 4), "flop": p.flops, "TFLOP/s": round(tf, 2),
-                "frac_of_fp16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_bytes": 3 * q.numel() + 2 * o.numel() + 4 * lse.numel(),
-                "traffic": traffic_from_profiles(
-                    "prefill_fp8_kernel",
-                    os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill_fp8.hip"))})
-    del q, k, v, o, lse
+        ms = time_calls(run_f, steps, 2, torch)
+        tf = p.flops / (ms * 1e-3) / 1e12
+        ent = {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
+               "inputs": "e4m3", "compute": "fp16 MFMA", "causal": p.causal, "layout": lay,
+               "ms_per_call": round(ms, 4), "flop": p.flops, "TFLOP/s": round(tf, 2),
+               "frac_of_fp16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if not p.causal:
+            ent["algorithmic_bytes"] = 3 * q.numel() + 2 * o.numel() + 4 * lse.numel()
+            ent["traffic"] = traffic_from_profiles(
+                "prefill_fp8_kernel",
+                os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill_fp8.hip"))
+        res.append(ent)
+        del q, k, v, o, lse
     # head dim 64 on the causal GQA shape
     p = gen.headdim64_causal_gqa()
     log(f"timing {p.name}")
@@ -647,6 +652,8 @@ def main():
     if args.summarize:
         st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
         cmd = {"plan": {"prefill_fp8_kernel<false>": [("fp8_mha_prefill_b4_h32_s4096_bhsd", xs)],
+                        "prefill_fp8_kernel<true>": [("fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192"
+                                                      "_bshd", xs)],
                         "prefill_hd_kernel<64, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192"
                                                          "_d64_bshd", xs),
                                                         ("gqa_causal_prefill_b8_hq32_hkv8_s8192"
