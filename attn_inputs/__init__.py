@@ -100,10 +100,11 @@ class Prefill:
 
 def prefill_inputs(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0,
                    scale=None, q_dist="normal", k_dist="normal", v_dist="normal",
-                   n_hot=0, name="", d=D) -> Prefill:
+                   n_hot=0, name="", d=D, v_amp=1.0) -> Prefill:
     """Draw a prefill problem (head dim d, 128 unless given).  `n_hot` query
     vectors Q[b, s, h, :] (drawn by the seed) are multiplied by 8 before
-    rounding; x8 is a power of two, so it commutes with the bf16 rounding."""
+    rounding; x8 is a power of two, so it commutes with the bf16 rounding.
+    V's draws are multiplied by v_amp (in float32) before rounding."""
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     qf = _draw(q_dist, seed, _S_Q, layout_shape(layout, B, Hq, Sq, d))
@@ -122,7 +123,8 @@ def prefill_inputs(B, Hq, Hkv, Sq, Sk, *, layout=BSHD, causal=False, seed=0,
     q = f32_to_bf16_bits(qf)
     del qf
     k = f32_to_bf16_bits(_draw(k_dist, seed, _S_K, layout_shape(layout, B, Hkv, Sk, d)))
-    v = f32_to_bf16_bits(_draw(v_dist, seed, _S_V, layout_shape(layout, B, Hkv, Sk, d)))
+    v = f32_to_bf16_bits(np.float32(v_amp) *
+                         _draw(v_dist, seed, _S_V, layout_shape(layout, B, Hkv, Sk, d)))
     return Prefill(q, k, v, B, Hq, Hkv, Sq, Sk, layout, bool(causal), float(scale),
                    name=name, hot_rows=hot)
 
@@ -166,10 +168,11 @@ class Decode:
 
 
 def decode_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, scale=None, lens=None,
-                  permute=True, poison_tail=True, name="") -> Decode:
+                  permute=True, poison_tail=True, name="", q_amp=1.0, v_amp=1.0) -> Decode:
     """Paged decode problem: lens ~ U{1..max_len} (unless given), 16-token
     pages dealt out in sequence order from one random permutation of the pool;
-    slots past each sequence's end hold bf16 NaN."""
+    slots past each sequence's end hold bf16 NaN.  Q's and V's draws are
+    multiplied by q_amp and v_amp (in float32) before rounding."""
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if lens is None:
@@ -187,7 +190,7 @@ def decode_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, scale=None, lens=None,
         table[b, :nb[b]] = ids[off:off + nb[b]]
         off += int(nb[b])
     kp = f32_to_bf16_bits(_normal(seed, _S_K, (P, PAGE, Hkv, D)))
-    vp = f32_to_bf16_bits(_normal(seed, _S_V, (P, PAGE, Hkv, D)))
+    vp = f32_to_bf16_bits(np.float32(v_amp) * _normal(seed, _S_V, (P, PAGE, Hkv, D)))
     if poison_tail:
         for b in range(B):
             t = int(lens[b]) % PAGE
@@ -195,7 +198,7 @@ def decode_inputs(B, Hq, Hkv, *, max_len=4096, seed=0, scale=None, lens=None,
                 last = table[b, nb[b] - 1]
                 kp[last, t:] = BF16_QNAN
                 vp[last, t:] = BF16_QNAN
-    q = f32_to_bf16_bits(_normal(seed, _S_Q, (B, Hq, D)))
+    q = f32_to_bf16_bits(np.float32(q_amp) * _normal(seed, _S_Q, (B, Hq, D)))
     return Decode(q, kp, vp, table, lens, B, Hq, Hkv, float(scale), name=name)
 
 

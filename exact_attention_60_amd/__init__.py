@@ -144,6 +144,38 @@ def _check_bf16(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(name, t, dtype, shape, device):
+    """A caller-supplied output (or workspace) must match what the kernels
+    write: dtype, exact shape, the inputs' device, contiguous."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_same_device(dev, **tensors):
+    for n, t in tensors.items():
+        if t.device != dev:
+            raise ValueError(f"{n} must be on {dev} (the device of q), got {t.device}")
+
+
+def _workspace(ws, need, device):
+    """The caller's workspace (a contiguous GPU byte tensor of at least `need`
+    bytes) or a fresh one."""
+    torch = _torch()
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
+    return ws
+
+
 def _rounding_code(rounding: str) -> int:
     try:
         return ROUNDING[rounding.lower()]
@@ -154,8 +186,9 @@ def _rounding_code(rounding: str) -> int:
 def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
              layout: str = "bshd", rounding: str = "rtne", out=None, lse=None, stream=None,
              alibi_slopes=None):
-    """Fused exact attention forward.  q: [B, Sq, Hq, 128] (bshd) or
-    [B, Hq, Sq, 128] (bhsd); k, v likewise with Hkv heads and Sk keys.
+    """Fused exact attention forward.  q: [B, Sq, Hq, d] (bshd) or
+    [B, Hq, Sq, d] (bhsd); k, v likewise with Hkv heads and Sk keys.  The head
+    dim d is 128, 64 or 256 (64 and 256 without ALiBi).
     alibi_slopes: optional fp32 GPU tensor [Hq] (ALiBi bias, attn_fwd_alibi).
     Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
     torch = _torch()
@@ -173,18 +206,19 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
         _, Hkv, Sk, _ = k.shape
     if k.shape[0] != B or k.shape[3] != d:
         raise ValueError("q and k disagree on batch or head dim")
+    _check_same_device(q.device, k=k, v=v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_out("out", out, torch.bfloat16, q.shape, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, torch.float32, (B, Hq, Sq), q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
             Sq, Sk, d, float(scale), int(bool(causal)), lay)
     if alibi_slopes is not None:
-        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or \
-                tuple(alibi_slopes.shape) != (Hq,) or not alibi_slopes.is_contiguous():
-            raise ValueError("alibi_slopes must be a contiguous fp32 GPU tensor [Hq]")
+        _check_out("alibi_slopes", alibi_slopes, torch.float32, (Hq,), q.device)
         st = library().attn_fwd_alibi(*args[:5], alibi_slopes.data_ptr(), *args[5:], rnd,
                                       _stream_ptr(stream))
         where = "attn_fwd_alibi"
@@ -220,12 +254,15 @@ def attn_fwd_fp8(q, k, v, *, descale_q: float = 1.0, descale_k: float = 1.0,
         _, Hkv, Sk, _ = k.shape
     if k.shape[0] != B or k.shape[3] != d:
         raise ValueError("q and k disagree on batch or head dim")
+    _check_same_device(q.device, k=k, v=v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check_out("out", out, torch.bfloat16, q.shape, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, torch.float32, (B, Hq, Sq), q.device)
     st = library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(descale_q),
                                 float(descale_k), float(descale_v), out.data_ptr(), lse.data_ptr(),
                                 B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)), lay,
@@ -255,12 +292,15 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
     total_q, Hq, d = q.shape
     total_k, Hkv, _ = k.shape
     B = cu_seqlens_q.numel() - 1
+    _check_same_device(q.device, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_out("out", out, torch.bfloat16, q.shape, q.device)
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, torch.float32, (Hq, total_q), q.device)
     st = library().attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), cu_seqlens_q.data_ptr(),
                                    cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
@@ -289,10 +329,19 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("q must be [B, Hq, d], the caches [num_pages, 16, Hkv, d], "
+                         "block_table [B, max_blocks] and seq_lens [B]")
     B, Hq, d = q.shape
     num_pages, page, Hkv, d2 = k_cache.shape
     if v_cache.shape != k_cache.shape or d2 != d or block_table.shape[0] != B:
         raise ValueError("inconsistent decode shapes")
+    if seq_lens.numel() != B:
+        raise ValueError(f"seq_lens must hold B = {B} lengths, got {seq_lens.numel()}")
+    _check_same_device(q.device, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                       seq_lens=seq_lens)
+    if append:
+        _check_same_device(q.device, k_new=k_new, v_new=v_new)
     if append and (tuple(k_new.shape) != (B, Hkv, d) or tuple(v_new.shape) != (B, Hkv, d)):
         raise ValueError("k_new and v_new must be [B, Hkv, 128]")
     max_blocks = block_table.shape[1]
@@ -300,12 +349,13 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = attn_decode_workspace_bytes(B, Hq, max_blocks)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _check_out("out", out, torch.bfloat16, q.shape, q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, torch.float32, (B, Hq), q.device)
     head = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
             seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page, max_blocks,
             num_pages, float(scale))
@@ -334,8 +384,8 @@ def attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, seq
 def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None = None,
              layout: str = "bshd", dq=None, dk=None, dv=None, workspace=None, stream=None,
              alibi_slopes=None):
-    """Gradients of attn_fwd for an upstream gradient do (q's layout and
-    shape), from the forward's inputs q, k, v and outputs o, lse (and its
+    """Gradients of attn_fwd (head dim 128, or 64 without ALiBi) for an
+    upstream gradient do (q's layout and shape), from the forward's inputs q, k, v and outputs o, lse (and its
     ALiBi slopes, if it had any: attn_bwd_alibi).  Returns (dq in q's layout,
     dk and dv in k's layout), all bf16."""
     torch = _torch()
@@ -353,25 +403,24 @@ def attn_bwd(q, k, v, o, lse, do, *, causal: bool = False, scale: float | None =
         _, Hkv, Sk, _ = k.shape
     if k.shape[0] != B or k.shape[3] != d:
         raise ValueError("q and k disagree on batch or head dim")
-    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (B, Hq, Sq) or \
-            not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 GPU tensor [B, Hq, Sq]")
+    _check_same_device(q.device, k=k, v=v, o=o, do=do)
+    _check_out("lse", lse, torch.float32, (B, Hq, Sq), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_out("dq", dq, torch.bfloat16, q.shape, q.device)
+    _check_out("dk", dk, torch.bfloat16, k.shape, q.device)
+    _check_out("dv", dv, torch.bfloat16, v.shape, q.device)
     need = attn_bwd_workspace_bytes(B, Hq, Sq)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     tail = (B, Hq, Hkv, Sq, Sk, d, float(scale), int(bool(causal)), lay, workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     if alibi_slopes is not None:
-        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or \
-                tuple(alibi_slopes.shape) != (Hq,) or not alibi_slopes.is_contiguous():
-            raise ValueError("alibi_slopes must be a contiguous fp32 GPU tensor [Hq]")
+        _check_out("alibi_slopes", alibi_slopes, torch.float32, (Hq,), q.device)
         st, where = library().attn_bwd_alibi(*head, alibi_slopes.data_ptr(), *tail), "attn_bwd_alibi"
     else:
         st, where = library().attn_bwd(*head, *tail), "attn_bwd"
@@ -399,18 +448,20 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
     total_q, Hq, d = q.shape
     total_k, Hkv, _ = k.shape
-    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (Hq, total_q) or \
-            not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 GPU tensor [Hq, total_q]")
+    _check_same_device(q.device, k=k, v=v, o=o, do=do, cu_seqlens_q=cu_seqlens_q,
+                       cu_seqlens_k=cu_seqlens_k)
+    _check_out("lse", lse, torch.float32, (Hq, total_q), q.device)
     B = cu_seqlens_q.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_out("dq", dq, torch.bfloat16, q.shape, q.device)
+    _check_out("dk", dk, torch.bfloat16, k.shape, q.device)
+    _check_out("dv", dv, torch.bfloat16, v.shape, q.device)
     need = attn_bwd_workspace_bytes(1, Hq, total_q)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     st = library().attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                    dv.data_ptr(), cu_seqlens_q.data_ptr(),

@@ -57,7 +57,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape (sizes must be >= 1, Hq a multiple of Hkv, within limits)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (d must be 128, page_size 16, layout BSHD/BHSD, scale finite and > 0, causal 0/1, rounding RTNE/RTNA/RTZ)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (head dim 128 everywhere, also 64/256 in attn_fwd[_rounded] and 64 in attn_bwd; page_size 16, layout BSHD/BHSD, scale finite and > 0, causal 0/1, rounding RTNE/RTNA/RTZ)";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";

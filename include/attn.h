@@ -42,7 +42,9 @@
  *
  * Conventions common to every entry point
  *  - bf16 tensors are passed as raw device pointers to IEEE bfloat16 data;
- *    d (head dim) must be 128 and is innermost and contiguous.
+ *    d (head dim) is innermost and contiguous.  Every entry point takes
+ *    d = 128; attn_fwd and attn_fwd_rounded also take d = 64 and d = 256, and
+ *    attn_bwd also takes d = 64.  Any other d returns ATTN_ERR_UNSUPPORTED.
  *  - Pointers are device pointers, 16-byte aligned.  The caller allocates and
  *    owns every buffer (inputs, outputs, tables, workspace); the library never
  *    allocates, frees or synchronises.
@@ -82,7 +84,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,        /* a required pointer is NULL                    */
   ATTN_ERR_SHAPE = -2,       /* a size is < 1, Hq % Hkv != 0, size overflow    */
-  ATTN_ERR_UNSUPPORTED = -3, /* d != 128, page_size != 16, bad layout, scale   */
+  ATTN_ERR_UNSUPPORTED = -3, /* head dim not taken by the entry point, page_size
+                                != 16, bad layout/rounding, scale not finite > 0 */
   ATTN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned               */
   ATTN_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required     */
   ATTN_ERR_LAUNCH = -6,      /* the HIP runtime rejected a launch              */
@@ -109,14 +112,15 @@ enum { ATTN_ROUND_RTNE = 0, ATTN_ROUND_RTNA = 1, ATTN_ROUND_RTZ = 2 };
  *   o    bf16 output, same layout and shape as q
  *   lse  fp32 output [B, Hq, Sq] (contiguous, for both layouts); natural log of
  *        sum_j exp(scale * q_i . k_j) over the visible keys j
- *   B, Hq, Hkv, Sq, Sk >= 1, Hq % Hkv == 0, d == 128
+ *   B, Hq, Hkv, Sq, Sk >= 1, Hq % Hkv == 0, d in {64, 128, 256}
  *   scale  finite float32 (1/sqrt(d) is the usual value)
  *   causal 0 or 1
  *
  * Size limits (ATTN_ERR_SHAPE): the K/V rows of one (batch, kv head) are
- * addressed with 32-bit byte offsets, so (Sk - 1) * row stride * 2 + 256 must
- * stay below 2^31 (row stride = Hkv * 128 elements in BSHD, 128 in BHSD), and
- * B * Hq * ceil(Sq / 256) must stay below 2^31.
+ * addressed with 32-bit byte offsets, so (Sk - 1) * row stride * 2 + 2 * d
+ * must stay below 2^31 (row stride = Hkv * d elements in BSHD, d in BHSD), and
+ * the workgroup count (B * Hq * ceil(Sq / rows per workgroup)) must stay below
+ * 2^31.
  *
  * Returns ATTN_OK or an attn_status error.
  */
@@ -327,14 +331,15 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq);
  *   dk, dv       bf16 outputs, same layout and shape as k
  *   workspace    device memory of at least attn_bwd_workspace_bytes(B, Hq, Sq)
  *                bytes; its contents on entry do not matter
- *   B, Hq, Hkv, Sq, Sk, d, scale, causal, layout: as for attn_fwd
+ *   B, Hq, Hkv, Sq, Sk, scale, causal, layout: as for attn_fwd
+ *   d            128 or 64 (64 not with attn_bwd_alibi)
  *
  * Rows that see no key (causal with Sq > Sk) get dQ = 0 and add nothing to dK
  * and dV.  Products run in bf16 with fp32 accumulation (P and dS rounded to
  * bf16 to nearest even); the outputs are rounded to bf16 to nearest even.
  * Size limits (ATTN_ERR_SHAPE): (Sq + 64) * q row stride * 2 and
- * (Sk + 64) * k row stride * 2 must stay below 2^31 (row stride = heads * 128
- * elements in BSHD, 128 in BHSD), B and Hq at most 65535.
+ * (Sk + 64) * k row stride * 2 must stay below 2^31 (row stride = heads * d
+ * elements in BSHD, d in BHSD), B and Hq at most 65535.
  * Returns ATTN_OK or an attn_status error; every check runs before any HIP
  * call.  Deterministic: no atomics, fixed summation order.
  */

@@ -46,9 +46,16 @@ def logical_o(o: torch.Tensor, layout: int) -> np.ndarray:
     return x.transpose(0, 2, 1, 3) if layout == gen.BSHD else x
 
 
+def oracle_workers():
+    """Host threads for the oracle beside a GPU test: one per core this
+    process may use, at most 16 (a one-GPU machine's share of its host)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def check_full(p: gen.Prefill, o, lse, what=""):
     o_ref, l_ref = att.attention(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
-                                 p.causal, p.layout)
+                                 p.causal, p.layout, workers=oracle_workers())
     e_o = check_o(logical_o(o, p.layout), o_ref, what)
     e_l = check_lse(host_f64(lse), l_ref, what)
     return e_o, e_l
@@ -72,7 +79,7 @@ def sample_rows(p: gen.Prefill, n: int, seed: int):
 def check_sampled(p: gen.Prefill, o, lse, n=256, seed=0, what=""):
     rows = sample_rows(p, n, seed)
     o_ref, l_ref = att.attention_sampled(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
-                                         p.causal, p.layout, rows)
+                                         p.causal, p.layout, rows, workers=oracle_workers())
     bsel = torch.tensor([r[0] for r in rows], device=o.device)
     hsel = torch.tensor([r[1] for r in rows], device=o.device)
     isel = torch.tensor([r[2] for r in rows], device=o.device)

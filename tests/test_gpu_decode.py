@@ -187,3 +187,28 @@ def test_decode_random_shapes(case):
     d = gen.decode_inputs(B, Hq, Hkv, max_len=L, seed=B * 31 + L)
     o, lse = run_decode(d)
     check_decode(d, o, lse, str(case))
+
+
+def test_decode_large_v_under_derived_bound():
+    """V ~ 300 N(0, 1) and sharp rows (Q x 4): checked against the large-V
+    bound of tests/tolerance.py (the fp16 rounding of the probabilities moves a
+    nearly cancelling row by up to 2^-11 times its spread, far above 1e-3)."""
+    from tolerance import check_o_large_v, pv_spread_rows
+    d = gen.decode_inputs(6, 16, 4, max_len=900, seed=321, lens=[900, 1, 17, 300, 64, 555],
+                          q_amp=4.0, v_amp=300.0)
+    o, lse = run_decode(d)
+    o_ref, l_ref = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
+                                    d.scale)
+    spread = np.zeros_like(o_ref)
+    sc = att.scale_as_f32(d.scale)
+    for b in range(d.B):
+        n = int(d.seq_lens[b])
+        for h in range(d.Hq):
+            g = att.kv_head_of(h, d.Hq, d.Hkv)
+            kk = att.bf16_to_f64(att.gather_pages(d.k_pool, d.block_table, n, b, g))
+            vv = att.bf16_to_f64(att.gather_pages(d.v_pool, d.block_table, n, b, g))
+            spread[b, h] = pv_spread_rows(att.bf16_to_f64(d.q[b, h:h + 1]), kk, vv, sc)[0]
+    e, r, r_plain = check_o_large_v(host_f64(o), o_ref, spread, "decode large V")
+    check_lse(host_f64(lse), l_ref, "decode large V lse")
+    print(f"decode large V: max err {e:.3g}, err/tol {r:.3f} "
+          f"(err/tol under the plain bound {r_plain:.2f})", flush=True)

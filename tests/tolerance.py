@@ -56,3 +56,80 @@ def check_lse(lse, lse_ref, what=""):
         assert err.max() <= LSE_ABS, f"{what}: LSE err {err[i]:.3g} at flat {i}"
         return float(err.max())
     return 0.0
+
+
+# ---------------------------------------------------------------------------
+# Large V.  The bound above assumes |V| of order one.  The kernels round the
+# probabilities that multiply V to fp16 (unit roundoff u = 2^-11; bf16,
+# u = 2^-8, on the fallback for V beyond the fp16 range) and divide by the sum
+# of the same rounded values.  With p~_j = p_j (1 + e_j) the computed output is,
+# to first order in u,
+#     O~ - O = sum_j pi_j e_j (v_j - O),      pi_j = p_j / l,
+# so |O~ - O| <= sum_j max(u pi_j, 2^-25 / l) |v_j - O|, where 2^-25 (half
+# the fp16 subnormal spacing, probabilities taken against the row max) bounds
+# the error of a probability that falls among the fp16 subnormals.  When a row
+# nearly cancels (|O| << sum_j pi_j |v_j|) this exceeds 1e-3 as soon as |V| is
+# large, whatever the kernel does, so large-V inputs are checked against
+#     |O - O_ref| <= 2 ulp_bf16(|O_ref|) + 1e-3 + (1 + 2^-4) * spread,
+#     spread = sum_j max(u pi_j, 2^-25 / l) |v_j - O_ref|
+# (the factor 1 + 2^-4 covers the second-order terms and the fp32
+# accumulation).  LSE does not depend on V and keeps its bound.
+
+P_UNIT_F16 = 2.0 ** -11
+P_UNIT_BF16 = 2.0 ** -8
+P_SUB_F16 = 2.0 ** -25
+
+
+def pv_spread_rows(q, k, v, scale, n_visible=None, unit=P_UNIT_F16):
+    """spread for query rows q [n, d] against keys k, values v [Sk, d]
+    (float64), row i limited to keys 0..n_visible[i]-1.  Returns [n, d]."""
+    import oracle.attention as att
+    n, d = q.shape[0], v.shape[1]
+    if k.shape[0] == 0:
+        return np.zeros((n, d))
+    s = att.scores(q, k, scale)
+    if n_visible is not None:
+        j = np.arange(k.shape[0])
+        s = np.where(j[None, :] >= np.asarray(n_visible)[:, None], -np.inf, s)
+    p, m, l = att.row_softmax(s)          # p = pi (normalised), l against the row max
+    o = p @ v
+    lsafe = np.where(l > 0, l, 1.0)
+    w = np.maximum(unit * p, np.where(p > 0, P_SUB_F16 / lsafe[:, None], 0.0))
+    spread = np.zeros((n, d))
+    for c in range(d):
+        spread[:, c] = (w * np.abs(v[None, :, c] - o[:, c:c + 1])).sum(axis=1)
+    return spread
+
+
+def pv_spread_prefill(p, unit=P_UNIT_F16):
+    """spread [B, Hq, Sq, d] for a generator prefill problem (bf16 bits)."""
+    import oracle.attention as att
+    qv = att._logical(p.q, p.layout)
+    kv = att._logical(p.k, p.layout)
+    vv = att._logical(p.v, p.layout)
+    sc = att.scale_as_f32(p.scale)
+    nvis = np.array([att.visible_keys(i, p.Sq, p.Sk, p.causal) for i in range(p.Sq)])
+    out = np.zeros((p.B, p.Hq, p.Sq, p.q.shape[-1]))
+    for b in range(p.B):
+        for h in range(p.Hq):
+            g = att.kv_head_of(h, p.Hq, p.Hkv)
+            out[b, h] = pv_spread_rows(att.bf16_to_f64(qv[b, h]), att.bf16_to_f64(kv[b, g]),
+                                       att.bf16_to_f64(vv[b, g]), sc, nvis, unit)
+    return out
+
+
+def check_o_large_v(o, o_ref, spread, what=""):
+    """Assert O parity under the large-V bound; returns (max_err, max err/tol,
+    max err/tol under the plain bound) -- the last is for reporting only."""
+    o = np.asarray(o, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    assert o.shape == o_ref.shape == spread.shape, (o.shape, o_ref.shape, spread.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    err = np.abs(o - o_ref)
+    tol = o_tolerance(o_ref) + (1.0 + 2.0 ** -4) * spread
+    ratio = err / tol
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (
+        f"{what}: O mismatch at {worst}: got {o[worst]!r} ref {o_ref[worst]!r} "
+        f"err {err[worst]:.3g} tol {tol[worst]:.3g}")
+    return float(err.max()), float(ratio.max()), float((err / o_tolerance(o_ref)).max())
