@@ -97,7 +97,12 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   if ((int64_t)(Sk - 1) * a.k_ss * 2 + D * 2 > INT32_MAX) return ATTN_ERR_SHAPE;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
   a.group = Hq / Hkv;
-  const int rows_per_block = hd64 ? attn::prefill_hd_rows_per_block() : attn::kPrefillBM;
+  // d = 128 without ALiBi and a GQA group that is a multiple of 4: the
+  // kernel whose workgroups share each K/V tile among 4 query heads
+  const bool pipe = d == attn::kHeadDim && !alibi_slopes && (Hq / Hkv) % 4 == 0;
+  const int rows_per_block = hd64   ? attn::prefill_hd_rows_per_block()
+                             : pipe ? attn::kPrefillPipeRows
+                                    : attn::kPrefillBM;
   a.n_qt = (Sq + rows_per_block - 1) / rows_per_block;
   if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
   a.c = scale * 1.4426950408889634f;
@@ -109,9 +114,10 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
-  const hipError_t e =
-      hd64 ? attn::launch_prefill_hd(a, d, causal != 0, static_cast<hipStream_t>(stream))
-           : attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = hd64   ? attn::launch_prefill_hd(a, d, causal != 0, st)
+                       : pipe ? attn::launch_prefill_pipe(a, causal != 0, st)
+                              : attn::launch_prefill(a, causal != 0, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

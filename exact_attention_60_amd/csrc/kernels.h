@@ -43,6 +43,13 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 
+// Dense d = 128 forward without ALiBi for GQA groups that are a multiple of
+// 4, pipelined inside each wave: one wave per SIMD, the 4 waves of a
+// workgroup being 4 query heads of one K/V head over the same 64 rows (each
+// loaded K/V tile shared by the four).  n_qt = ceil(Sq / kPrefillPipeRows).
+constexpr int kPrefillPipeRows = 64;
+hipError_t launch_prefill_pipe(const PrefillArgs& a, bool causal, hipStream_t stream);
+
 // ---- FP8 (E4M3) forward ------------------------------------------------------
 constexpr int kFp8RowsPerBlock = 128;   // query rows per workgroup
 

@@ -93,16 +93,32 @@ def test_layouts_agree_bitwise():
     assert torch.equal(l1, l2)
 
 
-def test_gqa_equals_repeated_mha_bitwise():
+def test_gqa_equals_repeated_mha():
+    """GQA/MQA equals MHA over repeated K/V heads (pin P9): both meet the bound
+    against the oracle, and within one kernel the results are bitwise equal.
+    Group sizes that are a multiple of 4 run the kernel whose workgroups share
+    K/V tiles among 4 query heads; groups of 1 and 2 run the other one, so the
+    bitwise check pairs groups of 2 with MHA and groups of 8 with groups of 4
+    over duplicated K/V heads."""
     for Hkv in (1, 2, 4):
         p = gen.prefill_inputs(1, 8, Hkv, 150, 260, layout=gen.BSHD, causal=False, seed=79 + Hkv)
         o1, l1 = run_fwd(p)
+        check_full(p, o1, l1, f"gqa Hkv={Hkv}")
         G = 8 // Hkv
-        kr = dev_bf16(np.repeat(p.k, G, axis=2))
-        vr = dev_bf16(np.repeat(p.v, G, axis=2))
-        o2, l2 = ea.attn_fwd(dev_bf16(p.q), kr, vr, causal=False, scale=p.scale, layout="bshd")
+        q = dev_bf16(p.q)
+        o2, l2 = ea.attn_fwd(q, dev_bf16(np.repeat(p.k, G, axis=2)),
+                             dev_bf16(np.repeat(p.v, G, axis=2)), causal=False, scale=p.scale,
+                             layout="bshd")
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2) and torch.equal(l1, l2), Hkv
+        check_full(p, o2, l2, f"repeated mha Hkv={Hkv}")
+        if G == 2:        # both on the kernel for groups of 1 and 2
+            assert torch.equal(o1, o2) and torch.equal(l1, l2), Hkv
+        if G == 8:        # the same K/V head twice: groups of 4, same kernel as groups of 8
+            o3, l3 = ea.attn_fwd(q, dev_bf16(np.repeat(p.k, 2, axis=2)),
+                                 dev_bf16(np.repeat(p.v, 2, axis=2)), causal=False,
+                                 scale=p.scale, layout="bshd")
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o3) and torch.equal(l1, l3), Hkv
 
 
 def test_deterministic_repeat():
@@ -229,3 +245,54 @@ def test_random_shapes_all_elements(shape):
                            seed=7 * Sq + 13 * Sk + Hq, n_hot=min(3, Sq * Hq))
     o, lse = run_fwd(p)
     check_full(p, o, lse, str(shape))
+
+
+# ---- the GQA kernel (query-head groups that are a multiple of 4: the 4 waves
+# of a workgroup are 4 query heads sharing each K/V tile; 64-row query tiles,
+# 32-key K/V tiles)
+
+GQA4_SHAPES = [
+    # B, Hq, Hkv, Sq, Sk, layout, causal
+    (1, 4, 1, 1, 1, gen.BSHD, False),        # MQA, one row, one key
+    (1, 4, 1, 31, 33, gen.BHSD, True),       # ragged 32-key tiles
+    (2, 8, 2, 64, 64, gen.BSHD, True),       # exactly one row tile
+    (1, 8, 2, 65, 700, gen.BSHD, False),     # one row past a tile, many key tiles
+    (1, 8, 1, 200, 130, gen.BHSD, True),     # Sq > Sk: first rows see no key
+    (1, 16, 2, 129, 129, gen.BSHD, True),    # group of 8: two workgroups per K/V head
+    (2, 12, 3, 100, 37, gen.BHSD, False),    # three K/V heads, short keys
+    (1, 8, 2, 333, 1000, gen.BSHD, True),    # Sq < Sk bottom-right, diagonal masks
+]
+
+
+@pytest.mark.parametrize("shape", GQA4_SHAPES, ids=lambda s: "B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s" % (
+    s[0], s[1], s[2], s[3], s[4], "bshd" if s[5] == 0 else "bhsd", "causal" if s[6] else "full"))
+def test_gqa_group4_kernel_all_elements(shape):
+    B, Hq, Hkv, Sq, Sk, lay, causal = shape
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=lay, causal=causal,
+                           seed=3 * Sq + 5 * Sk + Hq, n_hot=min(6, Sq * Hq))
+    o, lse = run_fwd(p)
+    check_full(p, o, lse, str(shape))
+
+
+def test_gqa_group4_kernel_v_beyond_fp16_range():
+    """The GQA kernel's bf16 fallback: V entries far beyond the fp16 range."""
+    p = gen.prefill_inputs(1, 8, 2, 150, 300, layout=gen.BSHD, causal=True, seed=84)
+    v = (p.v.astype(np.uint32) << 16).view(np.float32).copy()
+    v[:, :, :, 7] = 3.0e5
+    v[0, 120, 1, 11] = -2.0e6
+    p.v = gen.f32_to_bf16_bits(v)
+    o, lse = run_fwd(p)
+    check_full(p, o, lse, "huge V, gqa kernel")
+    assert np.all(host_f64(o)[..., 7] == 299008.0)
+
+
+def test_gqa_group4_kernel_large_v_under_derived_bound():
+    p = gen.prefill_inputs(1, 8, 2, 140, 400, layout=gen.BHSD, causal=True, seed=85, n_hot=24,
+                           v_amp=300.0)
+    o, lse = run_fwd(p)
+    o_ref, l_ref = att.attention(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
+                                 p.causal, p.layout)
+    e, r, r_plain = check_o_large_v(logical_o(o, p.layout), o_ref, pv_spread_prefill(p),
+                                    "large V, gqa kernel")
+    check_lse(host_f64(lse), l_ref, "large V lse, gqa kernel")
+    print(f"large V (gqa kernel): err/tol {r:.3f} (plain bound {r_plain:.2f})", flush=True)
