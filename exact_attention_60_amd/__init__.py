@@ -44,7 +44,8 @@ STATUS = {
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_alibi", "attn_fwd_varlen", "attn_fwd_fp8",
            "attn_decode_workspace_bytes", "attn_decode_paged",
-           "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_bwd_workspace_bytes",
+           "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_decode_paged_noalloc",
+           "attn_bwd_workspace_bytes",
            "attn_bwd", "attn_bwd_alibi", "attn_bwd_varlen", "attn_status_string", "attn_version")
 
 _lib = None
@@ -87,6 +88,9 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
                                                  i, i, i, f, i, vp, sz, vp]
         lib.attn_decode_paged_append.restype = i
+        lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                                  f, vp]
+        lib.attn_decode_paged_noalloc.restype = i
         lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
         lib.attn_bwd_workspace_bytes.restype = sz
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp,
@@ -373,6 +377,52 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     return out, lse
 
 
+# bytes of the device scratch array attn_decode_paged_noalloc uses (per GPU)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *,
+                              scale: float | None = None, out=None, lse=None, stream=None):
+    """attn_decode_paged (RTNE) through the entry point that allocates
+    nothing: the split partials use the library's own device scratch array
+    (NOALLOC_SCRATCH_BYTES per GPU; larger problems raise).  Pass out and lse
+    to allocate nothing here either.  Calls that overlap on one GPU race."""
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_bf16(n, t)
+    for n, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("q must be [B, Hq, d], the caches [num_pages, 16, Hkv, d], "
+                         "block_table [B, max_blocks] and seq_lens [B]")
+    B, Hq, d = q.shape
+    num_pages, page, Hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d or block_table.shape[0] != B or \
+            seq_lens.numel() != B:
+        raise ValueError("inconsistent decode shapes")
+    _check_same_device(q.device, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                       seq_lens=seq_lens)
+    max_blocks = block_table.shape[1]
+    if attn_decode_workspace_bytes(B, Hq, max_blocks) > NOALLOC_SCRATCH_BYTES:
+        raise ValueError("problem too large for the no-allocation decode's scratch array")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out("out", out, torch.bfloat16, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, torch.float32, (B, Hq), q.device)
+    st = library().attn_decode_paged_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page, max_blocks,
+        num_pages, float(scale), _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode_paged_noalloc")
+    return out, lse
+
+
 def attn_decode_paged_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, **kw):
     """Append the current token (K/V rows k_new, v_new: [B, Hkv, 128]) to the
     paged caches at position seq_lens[b] - 1, then decode over every token;
@@ -475,7 +525,7 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     return dq, dk, dv
 
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append",
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append", "attn_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
            "attn_decode_workspace_bytes", "attn_status_string",
            "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

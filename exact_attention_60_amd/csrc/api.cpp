@@ -248,13 +248,16 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int max_blocks_per_seq) {
 
 namespace {
 
-// The three decode entry points share this: argument checks, then the launch.
-// knew / vnew are null unless the call appends the current token.
+// The decode entry points share this: argument checks, then the launch.
+// knew / vnew are null unless the call appends the current token.  noalloc:
+// the workspace is the library's own device scratch array (workspace and
+// workspace_bytes are ignored); the size limit is checked with the other
+// arguments, the array's address looked up after them.
 int decode_call(const void* q, const void* knew, const void* vnew, const void* k_cache,
                 const void* v_cache, void* kc_out, void* vc_out, const int32_t* block_table,
                 const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d,
                 int page_size, int max_blocks_per_seq, int num_pages, float scale, int rounding,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_pages < 1)
     return ATTN_ERR_SHAPE;
@@ -267,11 +270,16 @@ int decode_call(const void* q, const void* knew, const void* vnew, const void* k
       !aligned16(vnew))
     return ATTN_ERR_ALIGN;
   const size_t need = attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  if (noalloc) {
+    if (need > attn::kDecodeNoAllocScratchBytes) return ATTN_ERR_WORKSPACE;
+  } else {
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  }
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
+  if (noalloc && attn::decode_noalloc_scratch(&workspace) != hipSuccess) return ATTN_ERR_DEVICE;
 
   attn::DecodeArgs a;
   a.q = static_cast<const __bf16*>(q);
@@ -337,6 +345,15 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   return attn_decode_paged_rounded(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv,
                                    d, page_size, max_blocks_per_seq, num_pages, scale,
                                    ATTN_ROUND_RTNE, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                              int max_blocks_per_seq, int num_pages, float scale, void* stream) {
+  return decode_call(q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_table,
+                     seq_lens, o, lse, B, Hq, Hkv, d, page_size, max_blocks_per_seq, num_pages,
+                     scale, ATTN_ROUND_RTNE, nullptr, 0, stream, /*noalloc=*/true);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Sq) {

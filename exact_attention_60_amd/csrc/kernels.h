@@ -115,6 +115,12 @@ struct DecodeArgs {
 int decode_max_splits(int max_blocks);
 hipError_t launch_decode(DecodeArgs a, int num_cus, hipStream_t stream);
 
+// Scratch of the decode entry point that allocates nothing: a file-scope
+// device array of this many bytes per GPU; *ptr is its device address on the
+// current device (looked up once per device).
+constexpr size_t kDecodeNoAllocScratchBytes = size_t(64) << 20;
+hipError_t decode_noalloc_scratch(void** ptr);
+
 // ---- backward ----------------------------------------------------------------
 constexpr int kBwdKvRows = 128;   // keys per dK/dV workgroup
 constexpr int kBwdQRows = 128;    // query rows per dQ workgroup

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 9
+#define ATTN_VERSION 10
 
 typedef enum {
   ATTN_OK = 0,
@@ -304,6 +304,30 @@ int attn_decode_paged_append(const void* q, const void* k_new, const void* v_new
                              int Hkv, int d, int page_size, int max_blocks_per_seq,
                              int num_pages, float scale, int rounding, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_noalloc - attn_decode_paged (RTNE) without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The split partials go to a device array the library
+ * owns (64 MiB = 67108864 bytes per GPU, held until the process ends, its
+ * address looked up once per device); the library calls no allocating
+ * routine.
+ *
+ *   arguments: as for attn_decode_paged, less workspace and workspace_bytes
+ *
+ * Limit: attn_decode_workspace_bytes(B, Hq, max_blocks_per_seq) must be at
+ * most 67108864, else ATTN_ERR_WORKSPACE (checked before any HIP call).  A
+ * failed lookup of the array's device address returns ATTN_ERR_DEVICE.
+ * Every call on a GPU uses that GPU's one array, and nothing in it needs to
+ * start cleared (every partial is written before it is read), so the contents
+ * an earlier call left do no harm; calls that overlap on one GPU (different
+ * streams, or threads) race on the array and must not be issued.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                              int max_blocks_per_seq, int num_pages, float scale, void* stream);
 
 /*
  * attn_bwd_workspace_bytes - device workspace that attn_bwd needs: two fp32

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 9
+    assert ea.attn_version() == 10
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -139,10 +139,53 @@ def test_valid_arguments_need_a_gfx950_device():
     assert fwd(d=64) == -7            # head dims 64 and 256 are supported by attn_fwd
     assert fwd(d=256) == -7
     assert dec() == -7
+    assert noalloc() == -7
     for r in (0, 1, 2):
         assert fwd(rounding=r) == -7
         assert dec(rounding=r) == -7
         assert app(rounding=r) == -7
+
+
+def noalloc(**kw):
+    """attn_decode_paged_noalloc with the same arguments as dec(), less the
+    workspace."""
+    a = dict(q=P, k=P, v=P, tab=P, lens=P, o=P, lse=P, B=2, Hq=8, Hkv=2, d=128, page=16,
+             mb=4, npages=8, scale=0.1, stream=None)
+    a.update(kw)
+    return ea.library().attn_decode_paged_noalloc(
+        a["q"], a["k"], a["v"], a["tab"], a["lens"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+        a["d"], a["page"], a["mb"], a["npages"], a["scale"], a["stream"])
+
+
+NOALLOC_LIMIT = 64 << 20
+
+
+def test_noalloc_limit_matches_the_binding():
+    assert ea.NOALLOC_SCRATCH_BYTES == NOALLOC_LIMIT
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tab=None), -1), (dict(q=None), -1), (dict(o=None), -1),
+    (dict(B=0), -2), (dict(Hq=6, Hkv=4), -2),
+    (dict(d=64), -3), (dict(page=32), -3), (dict(scale=float("nan")), -3),
+    (dict(k=P + 8), -4), (dict(lse=P + 4), -4),
+    (dict(B=64, Hq=32, Hkv=8, mb=256), -5),     # 68.7 MB of partials: beyond the 64 MiB array
+])
+def test_noalloc_argument_errors(kw, code):
+    assert noalloc(**kw) == code
+
+
+def test_noalloc_size_limit_edge():
+    """The largest problem of a family that fits the array is accepted (up to
+    the device check), the next one is refused before any HIP call."""
+    B, Hq, mb = 1, 32, 256
+    while ea.attn_decode_workspace_bytes(B + 1, Hq, mb) <= NOALLOC_LIMIT:
+        B += 1
+    assert ea.attn_decode_workspace_bytes(B, Hq, mb) <= NOALLOC_LIMIT
+    assert noalloc(B=B + 1, Hq=Hq, Hkv=8, mb=mb) == -5
+    import torch
+    if not torch.cuda.is_available():
+        assert noalloc(B=B, Hq=Hq, Hkv=8, mb=mb) == -7    # checks pass; no device here
 
 
 def bwd(**kw):
