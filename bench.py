@@ -11,8 +11,9 @@ are already resident in HBM:
   copies of the KV pool (more than 1 GB in all) are rotated so that the
   256 MB last-level cache cannot serve a call from the previous one;
 * the other prefill workloads (causal GQA B=8 S=8192, diffusion-style self
-  attention S=32760 and its cross attention against 512 keys), timed the
-  same way and reported beside the headline (skip with --no-extra);
+  attention S=32760 and its cross attention against 512 keys), timed exactly
+  like the headline (same steps, warm-up and per-call statistics) and
+  reported beside it with their own roofline objects;
 * the causal GQA shape at head dims 64 and 256 (attn_fwd with d = 64, 256);
 * the causal GQA workload with an ALiBi bias (attn_fwd_alibi);
 * FP8 (E4M3) inputs on the MHA and causal GQA shapes (attn_fwd_fp8),
@@ -28,7 +29,9 @@ fp64 CPU oracle is timed on the host cores on a bounded sample of the same
 workload as a reported baseline.  Prints one JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-    python bench.py --counters      # short run for rocprofv3 counter passes
+    python bench.py --counters      # fixed short sequence for rocprofv3 runs
+    python bench.py --summarize D   # profiles/ from the rocprofv3 output under D
+    python bench.py --trace-summary D   # table of every kernel of a traced default run
 """
 from __future__ import annotations
 
@@ -56,19 +59,24 @@ def sha256_of(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profiles(kernel_key, source, launches_per_call=1):
-    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
-    scaled by a copy kernel of known size), or None if absent or taken on a
-    different version of the kernel source."""
-    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
-    if not os.path.exists(path):
+PROFILE_DATA = os.path.join(ROOT, "profiles", "profile_data.json")
+CSRC = os.path.join(ROOT, "exact_attention_60_amd", "csrc")
+# short kernel name -> the source file it is built from
+KERNEL_SOURCES = {"prefill_kernel": "prefill.hip", "prefill_pipe_kernel": "prefill_pipe.hip",
+                  "decode_partial_kernel": "decode.hip", "decode_merge_kernel": "decode.hip"}
+
+
+def profile_entry(workload, kernel):
+    """What the committed rocprofv3 summary holds for `kernel` on `workload`
+    (HBM bytes per launch, counters, average duration), or None if absent or
+    taken on a different version of the kernel's source."""
+    if not os.path.exists(PROFILE_DATA):
         return None
     try:
-        data = json.load(open(path))
-        ent = data[kernel_key]
-        if ent.get("source_sha256") != sha256_of(source):
+        ent = json.load(open(PROFILE_DATA))["entries"][f"{workload}::{kernel}"]
+        if ent["source_sha256"] != sha256_of(os.path.join(CSRC, KERNEL_SOURCES[kernel])):
             return None
-        return float(ent["hbm_bytes_per_launch"])
+        return ent
     except (KeyError, ValueError, TypeError):
         return None
 
@@ -121,6 +129,69 @@ def device_clock_info(torch):
             "bf16_peak_at_clock_TFLOP/s": round(peak, 1) if peak else None}
 
 
+def prefill_kernel_of(p):
+    """The library kernel attn_fwd launches for problem p (d = 128, no
+    ALiBi): the kernel whose workgroups share K/V tiles among 4 query heads
+    for groups that are a multiple of 4, the other one otherwise."""
+    return "prefill_pipe_kernel" if (p.Hq // p.Hkv) % 4 == 0 else "prefill_kernel"
+
+
+def prefill_bytes(p):
+    """Algorithmic HBM bytes of one forward: Q, K, V read once, O written
+    once (bf16), LSE written once (fp32)."""
+    return 2 * 128 * (2 * p.B * p.Sq * p.Hq + 2 * p.B * p.Sk * p.Hkv) + 4 * p.B * p.Hq * p.Sq
+
+
+def prefill_workloads(gen):
+    """The prefill workloads, headline first: MHA B=4 H=32 S=4096 BHSD;
+    causal GQA B=8 Hq=32 Hkv=8 S=8192 BSHD; diffusion-style self attention
+    B=2 H=12 S=32760 BSHD and its cross attention against 512 keys."""
+    yield gen.config2()
+    yield gen.config3()
+    ps = gen.config4_self()
+    yield ps
+    yield gen.config4_cross(self_problem=ps)
+
+
+def time_prefill(p, args, gen, ea, torch, to_dev, dev, log, dev_info):
+    """One prefill workload, timed like the headline: inputs resident, W
+    warm-up calls, K calls between two HIP events on the launch stream, then
+    the same call timed one by one for the median and minimum."""
+    log(f"timing {p.name}")
+    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+    lay = "bshd" if p.layout == gen.BSHD else "bhsd"
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+    def run(_i):
+        ea.attn_fwd(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
+
+    ms = time_calls(run, args.steps, args.warmup, torch)
+    st = per_call_stats(run, max(args.steps, 20), torch)
+    tf = p.flops / (ms * 1e-3) / 1e12
+    kern = prefill_kernel_of(p)
+    prof = profile_entry(p.name, kern)
+    roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": round(prof["hbm_bytes"]) if prof else None,
+            "algorithmic_bytes": prefill_bytes(p),
+            "mfma_util": prof["derived"].get("mfma_util") if prof else None,
+            "kernel": kern,
+            "per_launch": {"flop": p.flops, "ms": round(ms, 4)},
+            "per_call": {**st, "TFLOP/s_at_median": round(
+                p.flops / (st["median_ms"] * 1e-3) / 1e12, 2)},
+            "profiled_avg_ms": round(prof["avg_us"] / 1e3, 4) if prof else None,
+            "frac_of_peak_at_device_clock": (
+                round(tf / dev_info["bf16_peak_at_clock_TFLOP/s"], 4)
+                if dev_info["bf16_peak_at_clock_TFLOP/s"] else None)}
+    res = {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
+           "d": 128, "layout": lay, "causal": p.causal, "ms_per_call": round(ms, 4),
+           "TFLOP/s": round(tf, 2), "roofline": roof,
+           "products": "Q.K^T on bf16 MFMA, P.V on fp16 MFMA (P and V rounded to fp16), fp32 "
+                       "accumulation"}
+    return res, (q, k, v, o, lse, run)
+
+
 def snapshot_outputs(p, o, lse, od, torch):
     """Host copies of 64 random rows of the timed prefill's O and LSE and of
     the timed decode's O, for the sampled parity check of the oracle leg."""
@@ -133,15 +204,16 @@ def snapshot_outputs(p, o, lse, od, torch):
 
 def sampled_parity(p, d, snap):
     """The snapshot against the oracle (part of the oracle leg): worst error
-    over the tolerance, and the worst LSE error."""
+    over the tolerance, and the worst LSE error.  Every element of every
+    workload is checked by the GPU tests; this confirms the timed outputs."""
     import oracle.attention as att
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from tolerance import o_tolerance
     rows = snap["rows"]
     o_ref, l_ref = att.attention_sampled(p.q, p.k, p.v, p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.scale,
-                                         False, p.layout, rows)
+                                         False, p.layout, rows, workers=oracle_threads())
     od_ref, _ = att.decode_paged(d.q, d.k_pool, d.v_pool, d.block_table, d.seq_lens, d.Hkv,
-                                 d.scale)
+                                 d.scale, workers=oracle_threads())
     return {"prefill_sampled_rows": len(rows),
             "prefill_max_err_over_tol": round(float(
                 (np.abs(snap["o"] - o_ref) / o_tolerance(o_ref)).max()), 4),
@@ -150,12 +222,18 @@ def sampled_parity(p, d, snap):
                 (np.abs(snap["od"] - od_ref) / o_tolerance(od_ref)).max()), 4)}
 
 
+def oracle_threads():
+    """Worker threads for the oracle beside the GPU: one per core this process
+    may use, at most 16 (the host share of one GPU on the benchmark boxes)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def cpu_baseline(p, budget_s, torch):
     """Time the oracle (as it is) on whole (b, h) heads of the prefill
     workload until about budget_s seconds of host work are done."""
     import oracle.attention as att
     from threadpoolctl import threadpool_info
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = oracle_threads()
     flops = 0.0
     heads = 0
     t0 = time.perf_counter()
@@ -172,178 +250,272 @@ def cpu_baseline(p, budget_s, torch):
     dt = time.perf_counter() - t0
     blas = sorted({i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"})
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "host_cores": os.cpu_count(), "cores_this_process_may_use":
+                len(os.sched_getaffinity(0)),
             "sample": f"{heads} of {p.B * p.Hq} (b,h) heads of the same workload, all "
                       f"{p.Sq} query rows x {p.Sk} keys, fp64 NumPy, {workers} worker threads "
-                      f"x 1 BLAS thread (BLAS pool size {blas}); {dt:.1f} s",
+                      f"x 1 BLAS thread (BLAS pool size {blas}); {dt:.1f} s; the thread count "
+                      f"is capped at 16, the host share of one GPU on the benchmark boxes",
             "seconds": dt}
 
 
-TRAFFIC_FILE = "hbm_traffic__prefill_mha_b4_h32_s4096__decode_b32_hq32_hkv8.json"
-
-
-def summarize_profiles(ktrace_dir, fetch_dir, write_dir, command):
-    """Turn rocprofv3 output (a --kernel-trace --stats run of bench.py and two
-    --pmc runs of `bench.py --counters`, FETCH_SIZE then WRITE_SIZE) into the
-    short summaries kept under profiles/, one per kernel and workload, and the
-    per-launch HBM traffic that bench.py reports."""
+def trace_summary(trace_dir, out_dir=None):
+    """One table of every library kernel in the kernel trace of a default
+    benchmark run (dispatch count, average / min / max duration), written to
+    library_kernels__bench_default_run.md in out_dir (profiles/ by default)."""
     import csv
-    out_dir = os.path.join(ROOT, "profiles")
-    os.makedirs(out_dir, exist_ok=True)
-    stats = {r["Name"]: r for r in csv.DictReader(open(os.path.join(ktrace_dir,
-                                                                    "run_kernel_stats.csv")))}
-    # the bench launches each workload's calls back to back in a fixed order,
-    # so the n-th dispatch of a kernel belongs to a known workload
-    trace = list(csv.DictReader(open(os.path.join(ktrace_dir, "run_kernel_trace.csv"))))
-    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    by_kernel = {}
-    for r in trace:
-        by_kernel.setdefault(r["Kernel_Name"], []).append(
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    per_wl = {}   # (workload, kernel part) -> durations
-    for kpart, plan in command["plan"].items():
-        names = [n for n in by_kernel if kpart in n]
-        if len(names) != 1 or len(by_kernel[names[0]]) != sum(c for _, c in plan):
-            raise SystemExit(f"summarize: dispatches of {kpart} do not match the bench's plan")
-        durs, i = by_kernel[names[0]], 0
-        for wl, cnt in plan:
-            per_wl[(wl, kpart)] = durs[i:i + cnt]
-            i += cnt
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        if "attn::" in r["Kernel_Name"]:
+            by.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 900 rocprofv3 --kernel-trace "
+           "--stats --output-format csv -d /root/repo/gpurun_out/prof/bench -o run -- python3 -u "
+           "/root/repo/bench.py --no-cpu-baseline")
+    lines = ["# Every library kernel of a default benchmark run", "",
+             "Command (then `python3 bench.py --trace-summary /root/repo/gpurun_out/prof/bench`):",
+             "", "```", cmd, "```", "",
+             "Kernels in order of first launch; each workload's calls include its warm-up and "
+             "its one-by-one timed calls, so the counts differ between kernels.", "",
+             "| kernel | dispatches | average us | min us | max us |", "|---|---|---|---|---|"]
+    for name, ds in by.items():
+        short = name.replace("void ", "").replace("attn::(anonymous namespace)::", "")
+        lines.append(f"| `{short}` | {len(ds)} | {sum(ds) / len(ds):.1f} | {min(ds):.1f} | "
+                     f"{max(ds):.1f} |")
+    with open(os.path.join(out_dir, "library_kernels__bench_default_run.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {len(by)} kernels")
 
-    # ---- HBM traffic per launch
-    fetch = list(csv.DictReader(open(os.path.join(fetch_dir, "run_counter_collection.csv"))))
-    write = list(csv.DictReader(open(os.path.join(write_dir, "run_counter_collection.csv"))))
-    wmap = {r["Dispatch_Id"]: r for r in write}
-    copy_bytes = float(1 << 30)
-    # the reference copy is the largest copyBuffer dispatch (1 GiB read + 1 GiB written)
-    copies = [r for r in fetch if "copyBuffer" in r["Kernel_Name"]]
-    cref = max(copies, key=lambda r: float(r["Counter_Value"]))
-    f_fetch = copy_bytes / (float(cref["Counter_Value"]) * 1024)
-    f_write = copy_bytes / (float(wmap[cref["Dispatch_Id"]]["Counter_Value"]) * 1024)
-    per = {}
-    for r in fetch:
-        name = r["Kernel_Name"]
-        key = next((kk for kk in ("prefill_kernel", "prefill_fp8_kernel", "decode_partial_kernel",
-                                  "decode_merge_kernel",
-                                  "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
-                    if kk in name), None)
-        if key is None:
+
+# ---------------------------------------------------------------------------
+# rocprofv3 runs: a fixed sequence of calls (--counters), and the summaries
+# under profiles/ made from their output (--summarize)
+
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "sq": ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+           "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE"],
+    "sq2": ["SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+            "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "TCC_HIT_sum", "TCC_MISS_sum",
+            "GRBM_GUI_ACTIVE"],
+}
+
+
+def rocprof_commands():
+    """The commands that make the rocprofv3 output --summarize reads (the
+    manifest is the stdout of the first)."""
+    pre = "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
+    run = "-o run -- python3 -u /root/repo/bench.py --counters"
+    cmds = {"ktrace": f"{pre}rocprofv3 --kernel-trace --stats --output-format csv "
+                      f"-d /root/repo/gpurun_out/prof/ktrace {run} > "
+                      f"/root/repo/gpurun_out/prof/manifest.json"}
+    for name, ctrs in COUNTER_PASSES.items():
+        cmds[name] = (f"{pre}rocprofv3 --pmc {' '.join(ctrs)} --output-format csv "
+                      f"-d /root/repo/gpurun_out/prof/{name} {run}")
+    return cmds
+
+
+def counters_run(gen, ea, torch, dev, to_dev):
+    """A fixed, short sequence for rocprofv3: a 1 GiB device copy (the
+    reference that scales FETCH_SIZE and WRITE_SIZE to bytes), then each
+    prefill workload and the decode workload, one warm-up call and five
+    calls each.  Prints the sequence as JSON (the manifest --summarize
+    needs)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    seq = []
+    warm, calls = 1, 5
+    for p in prefill_workloads(gen):
+        print(f"counters: {p.name}", file=sys.stderr, flush=True)
+        q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
+        lay = "bshd" if p.layout == gen.BSHD else "bhsd"
+        o = torch.empty_like(q)
+        lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+        for _ in range(warm + calls):
+            ea.attn_fwd(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
+        torch.cuda.synchronize()
+        seq.append({"workload": p.name, "warmup": warm, "calls": calls,
+                    "kernels": [prefill_kernel_of(p)], "flop": p.flops,
+                    "algorithmic_bytes": prefill_bytes(p)})
+        del q, k, v, o, lse
+    d = gen.config5()
+    print(f"counters: {d.name}", file=sys.stderr, flush=True)
+    qd = to_dev(d.q)
+    kp0, vp0 = to_dev(d.k_pool), to_dev(d.v_pool)
+    pools = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(3)]
+    tab = torch.from_numpy(d.block_table).to(dev)
+    lens = torch.from_numpy(d.seq_lens).to(dev)
+    ws = torch.empty(ea.attn_decode_workspace_bytes(d.B, d.Hq, d.max_blocks), dtype=torch.uint8,
+                     device=dev)
+    for i in range(warm + calls):
+        kp, vp = pools[i % 4]
+        ea.attn_decode_paged(qd, kp, vp, tab, lens, scale=d.scale, workspace=ws)
+    torch.cuda.synchronize()
+    seq.append({"workload": d.name, "warmup": warm, "calls": calls,
+                "kernels": ["decode_partial_kernel", "decode_merge_kernel"], "flop": d.flops,
+                "algorithmic_bytes": d.bytes})
+    print(json.dumps({"counters_run": True, "copy_bytes": n, "sequence": seq}), flush=True)
+
+
+def _dispatches(rows):
+    """Library kernel dispatches of a rocprofv3 CSV in launch order, each with
+    its duration and the counters of its rows (one row per dispatch and
+    counter, already summed over the counter's instances)."""
+    by = {}
+    for r in rows:
+        if "attn::" not in r["Kernel_Name"]:
             continue
-        fb = float(r["Counter_Value"]) * 1024 * f_fetch
-        wb = float(wmap[r["Dispatch_Id"]]["Counter_Value"]) * 1024 * f_write
-        per.setdefault(key, []).append((fb, wb))
-    srcs = {"prefill_kernel": "prefill.hip", "prefill_fp8_kernel": "prefill_fp8.hip",
-            "decode_partial_kernel": "decode.hip",
-            "decode_merge_kernel": "decode.hip", "bwd_prep_kernel": "backward.hip",
-            "bwd_dkdv_kernel": "backward.hip", "bwd_dq_kernel": "backward.hip"}
-    traffic = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
-                        "dispatch), each scaled by the reading of a 1 GiB device copy; prefill "
-                        "and backward on mha_prefill_b4_h32_s4096_bhsd (FP8: its E4M3 copy), decode on "
-                        "paged_decode_b32_hq32_hkv8_len4096_page16",
-               "fetch_scale": f_fetch, "write_scale": f_write,
-               "commands": [command["fetch"], command["write"]]}
-    trows = {}
-    for key, vals in per.items():
-        fb = sum(v[0] for v in vals) / len(vals)
-        wb = sum(v[1] for v in vals) / len(vals)
-        traffic[key] = {"source_sha256": sha256_of(os.path.join(ROOT, "exact_attention_60_amd",
-                                                                 "csrc", srcs[key])),
-                        "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-                        "hbm_bytes_per_launch": fb + wb, "launches": len(vals)}
-        trows[key] = (f"| {key} | {len(vals)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
-                      f"{(fb + wb) / 1e6:.1f} |")
-    with open(os.path.join(out_dir, TRAFFIC_FILE), "w") as f:
-        json.dump(traffic, f, indent=1)
+        d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "ctr": {}})
+        d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "Counter_Name" in r:
+            d["ctr"][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [by[k] for k in sorted(by)]
 
-    def kstats_row(kpart):
-        for name, r in stats.items():
-            if kpart in name:
-                return (f"| `{kpart}` (all workloads of the run) | {r['Calls']} | "
-                        f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
-                        f"{float(r['MaxNs']) / 1e3:.1f} |")
-        return f"| `{kpart}` | - | - | - | - |"
 
-    def wl_row(wl, kpart):
-        d = per_wl[(wl, kpart)]
-        return (f"| `{kpart}` on {wl} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | "
-                f"{max(d):.1f} |")
+def _assign(dispatches, manifest):
+    """(workload, kernel) -> the dispatches of its timed calls, walking the
+    manifest's sequence in launch order (warm-up calls dropped)."""
+    out, i = {}, 0
+    for ent in manifest["sequence"]:
+        for call in range(ent["warmup"] + ent["calls"]):
+            for kern in ent["kernels"]:
+                d = dispatches[i]
+                if f"::{kern}" not in d["name"]:
+                    raise SystemExit(f"summarize: dispatch {i} is {d['name']}, expected {kern} "
+                                     f"of {ent['workload']}")
+                if call >= ent["warmup"]:
+                    out.setdefault((ent["workload"], kern), []).append(d)
+                i += 1
+    if i != len(dispatches):
+        raise SystemExit(f"summarize: {len(dispatches) - i} library dispatches left over")
+    return out
 
-    head = ["Command (from the repository root on the GPU box):", "", "```", command["ktrace"],
-            "```", "", "| kernel / workload | dispatches | average us | min us | max us |",
-            "|---|---|---|---|---|"]
-    thead = ["", "HBM traffic per launch (rocprofv3 --pmc), commands:", "", "```",
-             command["fetch"], command["write"], "```", "",
-             f"Scale factors from a 1 GiB device copy: FETCH_SIZE x {f_fetch:.4f}, "
-             f"WRITE_SIZE x {f_write:.4f}.", "",
-             "| kernel | launches | read MB | written MB | total MB |", "|---|---|---|---|---|"]
-    files = {
-        "prefill_kernel__mha_prefill_b4_h32_s4096_bhsd.md": (
-            "# prefill_kernel on mha_prefill_b4_h32_s4096_bhsd (B=4, H=32, S=4096, BHSD)",
-            [wl_row("mha_prefill_b4_h32_s4096_bhsd", "prefill_kernel<false, false>")] +
-            [wl_row(f"mha_prefill_b4_h32_s4096_bhsd_{m}", "prefill_kernel<false, false>")
-             for m in ROUNDING_MODES] +
-            [kstats_row("prefill_kernel<false, false>")], ["prefill_kernel"]),
-        "decode_partial_and_merge_kernels__paged_decode_b32_hq32_hkv8_len4096.md": (
-            "# decode_partial_kernel + decode_merge_kernel on paged_decode_b32_hq32_hkv8_"
-            "len4096_page16",
-            [wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_partial_kernel"),
-             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16", "decode_merge_kernel"),
-             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_partial_kernel"),
-             wl_row("paged_decode_b32_hq32_hkv8_len4096_page16_append", "decode_merge_kernel")],
-            ["decode_partial_kernel", "decode_merge_kernel"]),
-        "prefill_fp8_kernel__fp8_mha_s4096_and_causal_gqa_s8192.md": (
-            "# prefill_fp8_kernel (attn_fwd_fp8, E4M3 inputs) on fp8_mha_prefill_b4_h32_s4096_bhsd "
-            "and fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
-            [wl_row("fp8_mha_prefill_b4_h32_s4096_bhsd", "prefill_fp8_kernel<false>"),
-             wl_row("fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_fp8_kernel<true>")],
-            ["prefill_fp8_kernel"]),
-        "prefill_kernel__causal_gqa_s8192_and_diffusion_s32760.md": (
-            "# prefill_kernel on the causal GQA and diffusion-style workloads",
-            [wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd", "prefill_kernel<true, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi",
-                    "prefill_kernel<true, true>"),
-             wl_row("diffusion_self_b2_h12_s32760_bshd", "prefill_kernel<false, false>"),
-             wl_row("diffusion_cross_b2_h12_sq32760_sk512_bshd", "prefill_kernel<false, false>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192", "prefill_kernel<true, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd",
-                    "prefill_hd_kernel<64, true>"),
-             wl_row("gqa_causal_prefill_b4_hq32_hkv8_s4096_d256_bshd",
-                    "prefill_hd_kernel<256, true>")],
-            []),
-        "backward_kernels__mha_b4_h32_s4096_bhsd_and_causal_gqa_s8192.md": (
-            "# bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel (attn_bwd) on "
-            "mha_prefill_b4_h32_s4096_bhsd and gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
-            [wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_prep_kernel<128>"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dkdv_kernel<128, false, false, false>"),
-             wl_row("mha_prefill_b4_h32_s4096_bhsd_backward", "bwd_dq_kernel<128, false, false, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward", "bwd_prep_kernel<128>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                    "bwd_dkdv_kernel<128, true, false, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                    "bwd_dq_kernel<128, true, false, false>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward", "bwd_prep_kernel<128>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                    "bwd_dkdv_kernel<128, true, true, false>"),
-             wl_row("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                    "bwd_dq_kernel<128, true, true, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", "bwd_prep_kernel<128>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward",
-                    "bwd_dkdv_kernel<128, true, false, true>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward",
-                    "bwd_dq_kernel<128, true, false, true>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward",
-                    "bwd_prep_kernel<64>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward",
-                    "bwd_dkdv_kernel<64, true, false, false>"),
-             wl_row("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward",
-                    "bwd_dq_kernel<64, true, false, false>")],
-            ["bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]),
-    }
-    for fname, (title, rows, tkeys) in files.items():
-        body = [title, ""] + head + rows
-        if tkeys:
-            body += thead + [trows[k] for k in tkeys if k in trows]
+
+def summarize(prof_dir, out_dir=None):
+    """profile_data.json and one *.md summary per workload, in out_dir
+    (profiles/ by default), from the rocprofv3 output of rocprof_commands()
+    under prof_dir.  GRBM_GUI_ACTIVE is read summed over the XCDs, so one
+    XCD's busy cycles are it divided by their number."""
+    import csv
+    manifest = json.loads([l for l in open(os.path.join(prof_dir, "manifest.json"))
+                           if l.startswith("{")][-1])
+    cmds = rocprof_commands()
+    csvs = {}
+    for name in ["ktrace"] + list(COUNTER_PASSES):
+        f = "run_kernel_trace.csv" if name == "ktrace" else "run_counter_collection.csv"
+        csvs[name] = list(csv.DictReader(open(os.path.join(prof_dir, name, f))))
+    gpu = [r for r in csv.DictReader(open(os.path.join(prof_dir, "sq", "run_agent_info.csv")))
+           if r["Agent_Type"] == "GPU"][0]
+    cus, simds, xccs = int(gpu["Cu_Count"]), int(gpu["Simd_Count"]), int(gpu["Num_Xcc"])
+    # scale factors of FETCH_SIZE / WRITE_SIZE from the 1 GiB copy
+    ref = {}
+    for name in ("fetch", "write"):
+        copy = max(float(r["Counter_Value"]) for r in csvs[name]
+                   if "copyBuffer" in r["Kernel_Name"])
+        ref[name] = manifest["copy_bytes"] / (copy * 1024)
+    trace = _assign(_dispatches(csvs["ktrace"]), manifest)
+    passes = {name: _assign(_dispatches(csvs[name]), manifest)
+              for name in COUNTER_PASSES}
+    entries = {}
+    for ent in manifest["sequence"]:
+        wl = ent["workload"]
+        for kern in ent["kernels"]:
+            durs = [d["dur_us"] for d in trace[(wl, kern)]]
+            ctr = {}
+            for name, ds in passes.items():
+                for c in COUNTER_PASSES[name]:
+                    if c == "GRBM_GUI_ACTIVE" and name != "sq":
+                        continue
+                    ctr[c] = sum(d["ctr"].get(c, 0.0) for d in ds[(wl, kern)]) / len(ds[(wl, kern)])
+            rd = ctr.pop("FETCH_SIZE") * 1024 * ref["fetch"]
+            wr = ctr.pop("WRITE_SIZE") * 1024 * ref["write"]
+            g = ctr["GRBM_GUI_ACTIVE"] / xccs          # busy cycles of one XCD
+            sq_us = [d["dur_us"] for d in passes["sq"][(wl, kern)]]
+            mops = ctr["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + ctr["SQ_INSTS_VALU_MFMA_MOPS_F16"]
+            hits, miss = ctr["TCC_HIT_sum"], ctr["TCC_MISS_sum"]
+            avg = sum(durs) / len(durs)
+            derived = {
+                "mfma_util": round(ctr["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds), 4),
+                "valu_busy": round(ctr["SQ_ACTIVE_INST_VALU"] / (cus * g), 4),
+                "lds_util": round(ctr["SQ_LDS_IDX_ACTIVE"] / (cus * g), 4),
+                "lds_bank_conflict_share": round(ctr["SQ_LDS_BANK_CONFLICT"] /
+                                                 max(ctr["SQ_LDS_IDX_ACTIVE"], 1.0), 4),
+                "l2_hit_rate": round(hits / max(hits + miss, 1.0), 4),
+                "mfma_flop": mops * 512,
+                "clock_mhz": round(g / (sum(sq_us) / len(sq_us)), 1),
+                "hbm_GB/s": round((rd + wr) / (avg * 1e-6) / 1e9, 1),
+            }
+            if kern.startswith("prefill"):
+                derived["mfma_flop_over_algorithmic"] = round(mops * 512 / ent["flop"], 4)
+            entries[f"{wl}::{kern}"] = {
+                "workload": wl, "kernel": kern, "kernel_name": trace[(wl, kern)][0]["name"],
+                "source": KERNEL_SOURCES[kern],
+                "source_sha256": sha256_of(os.path.join(CSRC, KERNEL_SOURCES[kern])),
+                "dispatches": len(durs), "avg_us": avg, "min_us": min(durs), "max_us": max(durs),
+                "read_bytes": rd, "write_bytes": wr, "hbm_bytes": rd + wr,
+                "algorithmic_bytes": ent["algorithmic_bytes"], "flop": ent["flop"],
+                "counters_per_dispatch": ctr, "derived": derived}
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    data = {"about": "rocprofv3 kernel trace and counters of `bench.py --counters` (five timed "
+                     "calls per workload after one warm-up); counters averaged per dispatch; "
+                     "FETCH_SIZE and WRITE_SIZE in bytes, each scaled by its reading of a 1 GiB "
+                     "device copy",
+            "fetch_scale": ref["fetch"], "write_scale": ref["write"], "cus": cus, "simds": simds,
+            "commands": cmds, "entries": entries}
+    with open(os.path.join(out_dir, "profile_data.json"), "w") as f:
+        json.dump(data, f, indent=1)
+    for ent in manifest["sequence"]:
+        wl = ent["workload"]
+        lines = [f"# {' + '.join(ent['kernels'])} on {wl}", "",
+                 "Commands (then `python3 bench.py --summarize /root/repo/gpurun_out/prof`):", "",
+                 "```"] + list(cmds.values()) + ["```", ""]
+        lines += [f"Scale factors from a 1 GiB device copy: FETCH_SIZE x {ref['fetch']:.4f}, "
+                  f"WRITE_SIZE x {ref['write']:.4f}.  {cus} CUs, {simds} SIMDs.", "",
+                  "| kernel | dispatches | avg us | min us | max us | HBM read MB | HBM written "
+                  "MB | algorithmic MB |", "|---|---|---|---|---|---|---|---|"]
+        for kern in ent["kernels"]:
+            e = entries[f"{wl}::{kern}"]
+            lines.append(f"| `{e['kernel_name']}` | {e['dispatches']} | {e['avg_us']:.1f} | "
+                         f"{e['min_us']:.1f} | {e['max_us']:.1f} | {e['read_bytes'] / 1e6:.1f} | "
+                         f"{e['write_bytes'] / 1e6:.1f} | "
+                         f"{ent['algorithmic_bytes'] / 1e6:.1f} (whole call) |")
+        lines += ["", "Derived (per dispatch): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                  "(GRBM_GUI_ACTIVE x SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE "
+                  "x CUs); LDS util = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE x CUs); bank-conflict "
+                  "share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit rate = TCC_HIT / "
+                  "(TCC_HIT + TCC_MISS); MFMA FLOP = (MOPS_BF16 + MOPS_F16) x 512.", "",
+                  "| kernel | MFMA busy | VALU busy | LDS util | bank-conflict share | L2 hit "
+                  "| MFMA FLOP / algorithmic | clock MHz | HBM GB/s |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for kern in ent["kernels"]:
+            dv = entries[f"{wl}::{kern}"]["derived"]
+            lines.append(f"| {kern} | {dv['mfma_util']:.3f} | {dv['valu_busy']:.3f} | "
+                         f"{dv['lds_util']:.3f} | {dv['lds_bank_conflict_share']:.3f} | "
+                         f"{dv['l2_hit_rate']:.3f} | {dv.get('mfma_flop_over_algorithmic', '-')} "
+                         f"| {dv['clock_mhz']} | {dv['hbm_GB/s']} |")
+        lines += ["", "Raw counters (per dispatch):", "",
+                  "| counter | " + " | ".join(ent["kernels"]) + " |",
+                  "|---|" + "---|" * len(ent["kernels"])]
+        names = list(entries[f"{wl}::{ent['kernels'][0]}"]["counters_per_dispatch"])
+        for c in names:
+            lines.append(f"| {c} | " + " | ".join(
+                f"{entries[f'{wl}::{k}']['counters_per_dispatch'][c]:.4g}" for k in ent["kernels"])
+                + " |")
+        fname = f"{'_and_'.join(ent['kernels'])}__{wl}.md"
         with open(os.path.join(out_dir, fname), "w") as f:
-            f.write("\n".join(body) + "\n")
+            f.write("\n".join(lines) + "\n")
+    print(f"wrote {out_dir}/profile_data.json and {len(manifest['sequence'])} summaries")
 
 
 def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
@@ -351,27 +523,6 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     headline: inputs resident, HIP events on the launch stream)."""
     res = []
     steps = max(3, min(args.steps, 10))
-    p4 = None
-    for make in (gen.config3, gen.config4_self, lambda: gen.config4_cross(self_problem=p4)):
-        p = make()
-        if p.Sk == p.Sq == 32760:
-            p4 = p
-        log(f"timing {p.name}")
-        q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
-        lay = "bshd" if p.layout == gen.BSHD else "bhsd"
-        o = torch.empty_like(q)
-        lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
-
-        def run(_i):
-            ea.attn_fwd(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
-
-        ms = time_calls(run, steps, 2, torch)
-        tf = p.flops / (ms * 1e-3) / 1e12
-        res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq,
-                    "Sk": p.Sk, "causal": p.causal, "layout": lay, "ms_per_call": round(ms, 4),
-                    "flop": p.flops, "TFLOP/s": round(tf, 2),
-                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-        del q, k, v, o, lse
     # FP8 (E4M3) inputs on the MHA and causal GQA shapes (attn_fwd_fp8)
     def u8(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
@@ -395,9 +546,6 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
                "frac_of_fp16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         if not p.causal:
             ent["algorithmic_bytes"] = 3 * q.numel() + 2 * o.numel() + 4 * lse.numel()
-            ent["traffic"] = traffic_from_profiles(
-                "prefill_fp8_kernel",
-                os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill_fp8.hip"))
         res.append(ent)
         del q, k, v, o, lse
     # head dim 64 on the causal GQA shape
@@ -507,13 +655,8 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
                "TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}
         if p.name == "mha_prefill_b4_h32_s4096_bhsd":
-            # HBM bytes the three kernels moved per call (counter passes), against the
-            # algorithmic Q, K, V, O, dO, LSE read once and dQ, dK, dV written once
-            src_b = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "backward.hip")
-            parts = [traffic_from_profiles(kk, src_b) for kk in
-                     ("bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")]
+            # algorithmic bytes: Q, K, V, O, dO, LSE read once, dQ, dK, dV written once
             ent["algorithmic_bytes"] = 8 * q.numel() * 2 + 4 * p.B * p.Hq * p.Sq
-            ent["traffic"] = None if None in parts else sum(parts)
         res.append(ent)
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
@@ -635,94 +778,27 @@ def rounding_modes(args, p, ea, torch, q, k, v, o, lse, log):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="host seconds spent timing the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the other prefill workloads (causal GQA, diffusion self/cross)")
+                    help="skip the variants (rounding rules, cache append, FP8, head dims, "
+                         "ALiBi, packed sequences, backward)")
     ap.add_argument("--counters", action="store_true",
-                    help="no timing: one device copy of 1 GiB, then 3 prefill and 3 decode "
-                         "calls, for rocprofv3 counter passes")
-    ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/kernel_stats.md and profiles/traffic.json from rocprofv3 "
-                         "output directories (no GPU needed)")
+                    help="no timing: a fixed short sequence of calls for rocprofv3 runs")
+    ap.add_argument("--summarize", metavar="PROF_DIR",
+                    help="write profiles/ from the rocprofv3 output under PROF_DIR (no GPU)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="write the table of every library kernel from the kernel trace of a "
+                         "default run under TRACE_DIR (no GPU)")
     args = ap.parse_args()
     if args.summarize:
-        st, wu, xs = 30, 5, 12   # bench defaults: steps, warmup; extra workloads 10 + 2
-        cmd = {"plan": {"prefill_fp8_kernel<false>": [("fp8_mha_prefill_b4_h32_s4096_bhsd", xs)],
-                        "prefill_fp8_kernel<true>": [("fp8_gqa_causal_prefill_b8_hq32_hkv8_s8192"
-                                                      "_bshd", xs)],
-                        "prefill_hd_kernel<64, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192"
-                                                         "_d64_bshd", xs),
-                                                        ("gqa_causal_prefill_b8_hq32_hkv8_s8192"
-                                                         "_d64_bshd_backward_fwd", 1)],
-                        "bwd_prep_kernel<64>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd"
-                                                 "_backward", xs)],
-                        "bwd_dkdv_kernel<64, true, false, false>": [(
-                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward", xs)],
-                        "bwd_dq_kernel<64, true, false, false>": [(
-                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_d64_bshd_backward", xs)],
-                        "prefill_hd_kernel<256, true>": [("gqa_causal_prefill_b4_hq32_hkv8_s4096"
-                                                          "_d256_bshd", xs)],
-                        "prefill_kernel<true, true>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                        "_alibi", xs),
-                                                       ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                        "_alibi_backward_fwd", 1)],
-                        "prefill_kernel<false, false>": [("mha_prefill_b4_h32_s4096_bhsd",
-                                                          st + wu + max(st, 20))] +
-                                                 [(f"mha_prefill_b4_h32_s4096_bhsd_{m}", xs)
-                                                  for m in ROUNDING_MODES] +
-                                                 [("diffusion_self_b2_h12_s32760_bshd", xs),
-                                                  ("diffusion_cross_b2_h12_sq32760_sk512_bshd", xs),
-                                                  ("mha_prefill_b4_h32_s4096_bhsd_backward_fwd", 1)],
-                        "prefill_kernel<true, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd",
-                                                         xs),
-                                                        ("varlen_causal_gqa_b16_hq32_hkv8_len8192",
-                                                         xs),
-                                                 ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                  "_backward_fwd", 1),
-                                                 ("varlen_causal_gqa_b16_hq32_hkv8_len8192"
-                                                  "_backward_fwd", 1)],
-                        "bwd_prep_kernel<128>": [("mha_prefill_b4_h32_s4096_bhsd_backward", xs),
-                                            ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_backward",
-                                             xs),
-                                            ("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi"
-                                             "_backward", xs),
-                                            ("varlen_causal_gqa_b16_hq32_hkv8_len8192_backward",
-                                             xs)],
-                        "bwd_dkdv_kernel<128, false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
-                                                           xs)],
-                        "bwd_dq_kernel<128, false, false, false>": [("mha_prefill_b4_h32_s4096_bhsd_backward",
-                                                         xs)],
-                        "bwd_dkdv_kernel<128, true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                          "_backward", xs)],
-                        "bwd_dq_kernel<128, true, false, false>": [("gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd"
-                                                        "_backward", xs)],
-                        "bwd_dkdv_kernel<128, true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
-                                                         "_backward", xs)],
-                        "bwd_dq_kernel<128, true, true, false>": [("varlen_causal_gqa_b16_hq32_hkv8_len8192"
-                                                       "_backward", xs)],
-                        "bwd_dkdv_kernel<128, true, false, true>": [(
-                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
-                        "bwd_dq_kernel<128, true, false, true>": [(
-                            "gqa_causal_prefill_b8_hq32_hkv8_s8192_bshd_alibi_backward", xs)],
-                        "decode_partial_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
-                                                   max(st, 20) + wu + max(st, 40)),
-                                                  ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
-                                                   max(st, 20) + 3)],
-                        "decode_merge_kernel": [("paged_decode_b32_hq32_hkv8_len4096_page16",
-                                                 max(st, 20) + wu + max(st, 40)),
-                                                ("paged_decode_b32_hq32_hkv8_len4096_page16_append",
-                                                 max(st, 20) + 3)]},
-               "ktrace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace "
-                         "-o run -- python3 -u bench.py --no-cpu-baseline",
-               "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch "
-                        "-o run -- python3 -u bench.py --counters",
-               "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write "
-                        "-o run -- python3 -u bench.py --counters"}
-        summarize_profiles(*args.summarize, cmd)
+        summarize(args.summarize)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -742,14 +818,27 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ---- prefill inputs (resident in HBM before timing)
-    p = gen.config2()
-    q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
-    o = torch.empty_like(q)
-    lse = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+    if args.counters:
+        counters_run(gen, ea, torch, dev, to_dev)
+        return
 
-    def prefill(_i):
-        ea.attn_fwd(q, k, v, causal=False, scale=p.scale, layout="bhsd", out=o, lse=lse)
+    def log(msg):
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+    dev_info = device_clock_info(torch)
+    # ---- prefill: the headline workload, then the others, timed alike
+    prefills = []
+    keep = None
+    for p in prefill_workloads(gen):
+        res, bufs = time_prefill(p, args, gen, ea, torch, to_dev, dev, log, dev_info)
+        prefills.append(res)
+        if keep is None:
+            keep = (p, bufs)          # the headline's buffers stay for the variants
+        else:
+            del bufs
+        torch.cuda.empty_cache()
+    p, (q, k, v, o, lse, prefill) = keep
+    head = prefills[0]
 
     # ---- decode inputs: four copies of the pool, rotated
     d = gen.config5()
@@ -767,56 +856,25 @@ def main():
         kp, vp = pools[i % len(pools)]
         ea.attn_decode_paged(qd, kp, vp, tab, lens, scale=d.scale, out=od, lse=lsed, workspace=ws)
 
-    if args.counters:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)          # reference: reads and writes exactly 1 GiB
-        for i in range(3):
-            prefill(i)
-        for i in range(3):
-            decode(i)
-        do = to_dev(gen.output_grad(p, 2))
-        for i in range(3):
-            ea.attn_bwd(q, k, v, o, lse, do, causal=False, scale=p.scale, layout="bhsd")
-        p8 = gen.fp8_mha_prefill()
-        q8, k8, v8 = (torch.from_numpy(x).to(dev) for x in (p8.q, p8.k, p8.v))
-        for i in range(3):
-            ea.attn_fwd_fp8(q8, k8, v8, scale=p8.scale, layout="bhsd", out=o, lse=lse)
-        torch.cuda.synchronize()
-        print(json.dumps({"counters_run": True, "copy_bytes": n}))
-        return
-
-    def log(msg):
-        print(f"bench: {msg}", file=sys.stderr, flush=True)
-
     torch.cuda.synchronize()
-    log("inputs resident; timing prefill")
-    ms_p = time_calls(prefill, args.steps, args.warmup, torch)
-    log(f"prefill {ms_p:.3f} ms/call; timing decode")
+    log("timing decode")
     ms_d = time_calls(decode, max(args.steps, 20), args.warmup, torch)
-    log(f"decode {ms_d * 1e3:.1f} us/call")
-
-    tflops = p.flops / (ms_p * 1e-3) / 1e12
-    gbs = d.bytes / (ms_d * 1e-3) / 1e9
-    # per-call distribution of the same two calls (median and minimum)
-    st_p = per_call_stats(prefill, max(args.steps, 20), torch)
     st_d = per_call_stats(decode, max(args.steps, 40), torch)
-    dev_info = device_clock_info(torch)
+    gbs = d.bytes / (ms_d * 1e-3) / 1e9
+    pp = profile_entry(d.name, "decode_partial_kernel")
+    pm = profile_entry(d.name, "decode_merge_kernel")
+    prefill(0)     # the headline's outputs, for the oracle leg
+    torch.cuda.synchronize()
     snap = snapshot_outputs(p, o, lse, od, torch)
 
-    src_p = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "prefill.hip")
-    src_d = os.path.join(ROOT, "exact_attention_60_amd", "csrc", "decode.hip")
     out = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": head["TFLOP/s"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_p, 4),
+        "ms_per_step": head["ms_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -824,25 +882,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq,
                    "Sk": p.Sk, "d": 128, "layout": "bhsd", "causal": False,
-                   "parallelism": "none (one GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profiles("prefill_kernel", src_p),
-                     "kernel": "prefill_kernel<false, false>",
-                     "per_launch": {"flop": p.flops, "ms": round(ms_p, 4)},
-                     "per_call": {**st_p, "TFLOP/s_at_median": round(
-                         p.flops / (st_p["median_ms"] * 1e-3) / 1e12, 2)},
-                     "device": dev_info,
-                     "frac_of_peak_at_device_clock": (
-                         round(tflops / dev_info["bf16_peak_at_clock_TFLOP/s"], 4)
-                         if dev_info["bf16_peak_at_clock_TFLOP/s"] else None)},
+                   "parallelism": "none (one GPU)",
+                   "products": "Q.K^T on bf16 MFMA, P.V on fp16 MFMA, fp32 accumulation"},
+        "roofline": {**head["roofline"], "device": dev_info},
+        "prefill_workloads": prefills,
         "decode": {"workload": d.name, "value": round(gbs, 1), "unit": "GB/s",
                    "us_per_call": round(ms_d * 1e3, 2), "tokens": d.tokens,
                    "algorithmic_bytes": d.bytes,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": traffic_from_profiles("decode_partial_kernel", src_d),
-                                "kernel": "decode_partial_kernel + decode_merge_kernel"},
+                                "traffic": (round(pp["hbm_bytes"] + pm["hbm_bytes"])
+                                            if pp and pm else None),
+                                "kernel": "decode_partial_kernel + decode_merge_kernel",
+                                "profiled_avg_us": (round(pp["avg_us"] + pm["avg_us"], 2)
+                                                    if pp and pm else None)},
                    "per_call": {"median_us": round(st_d["median_ms"] * 1e3, 2),
                                 "min_us": round(st_d["min_ms"] * 1e3, 2), "reps": st_d["reps"],
                                 "GB/s_at_median": round(d.bytes / (st_d["median_ms"] * 1e-3) / 1e9,
@@ -852,6 +905,8 @@ def main():
         out["decode_append"] = decode_append(args, d, ea, torch, qd, pools, tab, lens, od, lsed,
                                              ws, to_dev, log)
         out["rounding_modes"] = rounding_modes(args, p, ea, torch, q, k, v, o, lse, log)
+        del pools, kp0, vp0
+        torch.cuda.empty_cache()
         out["other_workloads"] = extra_workloads(args, gen, ea, torch, dev, to_dev, log)
         out["backward"] = backward_workloads(args, gen, ea, torch, to_dev, log)
     if not args.no_cpu_baseline:
