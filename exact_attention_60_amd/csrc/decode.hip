@@ -98,29 +98,20 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// The four K fragments of a page (d = 32*ks + 8*grp .. +8 of one token row).
-// The loads are issued as plain instructions that the compiler does not
-// track: its own wait counts ignore the LDS copies issued in between, so it
-// would wait for later pages' loads too.  wait_page<N> is the matching wait
-// (vmcnt(N)); it names the fragments as operands so that no use of them is
-// scheduled before it.
+// The four K fragments of a page (d = 32*ks + 8*grp .. +8 of one token row),
+// as ordinary loads: the compiler tracks them and waits for them before
+// their first use.
 __device__ __forceinline__ void load_k(bf16x8 (&kf)[4], const __bf16* row) {
-  asm volatile(
-      "global_load_dwordx4 %0, %4, off\n\t"
-      "global_load_dwordx4 %1, %4, off offset:64\n\t"
-      "global_load_dwordx4 %2, %4, off offset:128\n\t"
-      "global_load_dwordx4 %3, %4, off offset:192"
-      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3])
-      : "v"(row)
-      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kf[i] = *(const bf16x8*)(row + 32 * i);
 }
+// s_waitcnt vmcnt(N) for the LDS copies of a page: at most N of this wave's
+// memory operations still in flight.  The "memory" clobber keeps every
+// load and copy issued before it on this side of the wait.
 template <int N>
-__device__ __forceinline__ void wait_page(bf16x8 (&kf)[4]) {
+__device__ __forceinline__ void wait_page() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%4)"
-               : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3])
-               : "n"(N)
-               : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 
@@ -219,11 +210,11 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
   auto page_of = [&](int p) { return __builtin_amdgcn_readlane(tab_lane, p - p0); };
   // cache append: page pn (-1 if not in this segment), slot sn of the current
   // token; lanes 0..15 hold d = 8*lane .. 8*lane+7 of its K and V rows.  The
-  // two loads are issued right after the segment's first page, untracked like
-  // the page loads: every later wait_page (vmcnt(8), only the newest page's
-  // eight operations allowed in flight) has completed them, so they cost no
-  // wait of their own.  A table entry outside [0, num_pages) for that page
-  // makes the page contribute nothing and suppresses the cache write.
+  // two loads are issued right after the segment's first page, so the first
+  // wait_page (vmcnt(8), only the newest page's eight operations allowed in
+  // flight) has completed them before any use.  A table entry outside
+  // [0, num_pages) for that page makes the page contribute nothing and
+  // suppresses the cache write.
   const int t_new = len - 1;
   const int pn = (a.knew != nullptr && t_new >= 0 && t_new / kPage >= p0 && t_new / kPage < p1)
                      ? t_new / kPage : -1;
@@ -232,12 +223,8 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
   u32x4 kn = u32x4{}, vn = u32x4{};
   auto load_new_rows = [&]() {
     if (pn >= 0 && lane < 16) {
-      asm volatile(
-          "global_load_dwordx4 %0, %2, off\n\t"
-          "global_load_dwordx4 %1, %3, off"
-          : "=&v"(kn), "=&v"(vn)
-          : "v"(a.knew + new_row + 8 * lane), "v"(a.vnew + new_row + 8 * lane)
-          : "memory");
+      kn = *(const u32x4*)(a.knew + new_row + 8 * lane);
+      vn = *(const u32x4*)(a.vnew + new_row + 8 * lane);
     }
   };
   // tokens of page p that take part: those before the sequence end, none if
@@ -270,20 +257,27 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
                                                0, 0);
   };
 
-  // V^T operands of a page from its LDS slot (ds_read_b64_tr_b16), as
-  // untracked instructions too: the compiler would otherwise wait for every
-  // LDS copy in flight, the later pages' included.  The page's copies have
-  // landed (wait_page) before this runs.
+  // V^T operands of a page from its LDS slot (ds_read_b64_tr_b16), the eight
+  // reads and their wait in one instruction block that the compiler does not
+  // track: it would otherwise wait for every LDS copy in flight, the later
+  // pages' included.  The page's copies have landed (wait_page) before this
+  // runs.
   auto read_v_page = [&](u32x2 (&vf)[8], const char* vs) {
     const uint32_t addr = (uint32_t)(uintptr_t)(const ATTN_LDS char*)vs + tr_lane;
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk)
-      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vf[blk]) : "v"(addr), "n"(512 * blk) : "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(vf[0]), "+v"(vf[1]), "+v"(vf[2]), "+v"(vf[3]), "+v"(vf[4]), "+v"(vf[5]),
-                   "+v"(vf[6]), "+v"(vf[7])
-                 :
-                 : "memory");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:512\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:1536\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:3584\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(vf[4]), "=&v"(vf[5]),
+          "=&v"(vf[6]), "=&v"(vf[7])
+        : "v"(addr)
+        : "memory");
   };
 
   auto compute_page = [&](const bf16x8 (&kf)[4], char* vs, int p) {
@@ -371,11 +365,11 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
       load_new_rows();
       for (;;) {
         issue_page(kb, vb, min(p + 1, plast));
-        wait_page<8>(ka);
+        wait_page<8>();
         compute_page(ka, va, p);
         if (++p >= p1) break;
         issue_page(ka, va, min(p + 1, plast));
-        wait_page<8>(kb);
+        wait_page<8>();
         compute_page(kb, vb, p);
         if (++p >= p1) break;
       }
@@ -386,15 +380,15 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
       issue_page(kb, vb, min(p + 1, plast));
       for (;;) {
         issue_page(kc, vc, min(p + 2, plast));
-        wait_page<16>(ka);
+        wait_page<16>();
         compute_page(ka, va, p);
         if (++p >= p1) break;
         issue_page(ka, va, min(p + 2, plast));
-        wait_page<16>(kb);
+        wait_page<16>();
         compute_page(kb, vb, p);
         if (++p >= p1) break;
         issue_page(kb, vb, min(p + 2, plast));
-        wait_page<16>(kc);
+        wait_page<16>();
         compute_page(kc, vc, p);
         if (++p >= p1) break;
       }
@@ -403,7 +397,6 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, char* va, char*
   }
   // the appended token's rows into the cache (one writer per (b, K/V head))
   if (pn >= 0 && hb == 0 && lane < 16 && (uint32_t)page_of(pn) < (uint32_t)a.num_pages) {
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(kn), "+v"(vn) : : "memory");
     const int64_t at = (int64_t)page_of(pn) * a.page_stride + (int64_t)sn * a.token_stride +
                        (int64_t)g * D + 8 * lane;
     *(u32x4*)(a.kc_out + at) = kn;

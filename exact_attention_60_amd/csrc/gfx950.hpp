@@ -21,6 +21,37 @@
 
 namespace attn {
 
+// Causal launch order.  Workgroups are dealt to the 8 XCDs round robin
+// (XCD = i % 8).  Workgroup i gets head h in [0, NH) and query tile qt so that
+// each XCD takes NH / 8 whole heads (every K/V tile of a head is then read
+// through one L2), and within an XCD the 32 heaviest query tiles of one head
+// come first -- one per CU of the XCD, all streaming the same K/V tiles at
+// the same time -- then those of the XCD's next head, then the next 32 tiles
+// of each head, down to the lightest.  NH must be a multiple of 8 and the
+// grid NH * n_qt workgroups.
+__device__ __forceinline__ void causal_xcd_order(int i, int NH, int n_qt, int& h, int& qt) {
+  constexpr int BAND = 32;
+  const int x = i & 7, j = i >> 3;
+  const int hpx = NH >> 3;               // heads per XCD
+  const int full = n_qt / BAND;          // full bands of 32 tiles
+  const int in_full = full * hpx * BAND;
+  int hl, row;
+  if (j < in_full) {
+    const int band = j / (hpx * BAND);
+    const int r = j - band * hpx * BAND;
+    hl = r / BAND;
+    row = band * BAND + (r - hl * BAND);
+  } else {
+    const int t = j - in_full;
+    const int rows_t = n_qt - full * BAND;
+    hl = t / rows_t;
+    row = full * BAND + (t - hl * rows_t);
+  }
+  h = x * hpx + hl;
+  qt = n_qt - 1 - row;
+}
+
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));

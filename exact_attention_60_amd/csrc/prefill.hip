@@ -53,7 +53,9 @@
 //    diagonal, and the heaviest query tiles are dispatched first.
 //  * blockIdx is remapped so that workgroups sharing K/V land on one XCD
 //    (workgroups are dealt to the 8 XCDs round robin), keeping K/V re-reads in
-//    that XCD's L2.
+//    that XCD's L2; causal launches (head count a multiple of 8) also keep the
+//    query tiles running at once on an XCD within one or two heads
+//    (causal_xcd_order), so the tiles they stream are shared in L2.
 //  * Packed sequences of different lengths (cu_q/cu_k offsets): a workgroup
 //    reads its sequence's offsets first and returns at once if its query tile
 //    lies past the sequence; the heads of one sequence are spread over the
@@ -531,7 +533,9 @@ void prefill_kernel(PrefillArgs a) {
   // ---- which (batch, head, query tile) this workgroup computes
   const int BH = a.B * a.Hq;
   int bh, qt;
-  if (CAUSAL || a.cu_q) {
+  if (CAUSAL && !a.cu_q && (BH & 7) == 0) {
+    causal_xcd_order(blockIdx.x, BH, a.n_qt, bh, qt);
+  } else if (CAUSAL || a.cu_q) {
     const int row = blockIdx.x / BH;     // heaviest query tiles first
     qt = a.n_qt - 1 - row;
     // packed sequences of different lengths: the heads of one sequence are

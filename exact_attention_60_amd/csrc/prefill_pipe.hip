@@ -59,7 +59,9 @@
 //    boundary tiles are masked (a second loop over the masked tiles at the
 //    end), heaviest query tiles are dispatched first.
 //  * blockIdx is remapped so that workgroups sharing K/V land on one XCD
-//    (workgroups are dealt to the 8 XCDs round robin).
+//    (workgroups are dealt to the 8 XCDs round robin); causal launches also
+//    keep the query tiles running at once on an XCD within one or two heads
+//    (causal_xcd_order), so the K/V tiles they stream are shared in L2.
 #include "gfx950.hpp"
 #include "kernels.h"
 
@@ -563,7 +565,9 @@ void prefill_pipe_kernel(PrefillArgs a) {
   const int NHG = a.Hq / NW;               // groups of 4 query heads per batch entry
   const int NBH = a.B * NHG;
   int bhg, qt;
-  if (CAUSAL) {
+  if (CAUSAL && (NBH & 7) == 0) {
+    causal_xcd_order(blockIdx.x, NBH, a.n_qt, bhg, qt);
+  } else if (CAUSAL) {
     const int row = blockIdx.x / NBH;      // heaviest query tiles first
     qt = a.n_qt - 1 - row;
     bhg = xcd_remap(blockIdx.x - row * NBH, NBH);
