@@ -323,8 +323,9 @@ def rocprof_commands():
 def counters_run(gen, ea, torch, dev, to_dev):
     """A fixed, short sequence for rocprofv3: a 1 GiB device copy (the
     reference that scales FETCH_SIZE and WRITE_SIZE to bytes), then each
-    prefill workload and the decode workload, one warm-up call and five
-    calls each.  Prints the sequence as JSON (the manifest --summarize
+    prefill workload and the decode workload, 20 warm-up calls (the engine
+    clock settles under load, as in the timed runs) and 20 calls each (40
+    for the decode).  Prints the sequence as JSON (the manifest --summarize
     needs)."""
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -335,7 +336,7 @@ def counters_run(gen, ea, torch, dev, to_dev):
     torch.cuda.synchronize()
     del src, dst
     seq = []
-    warm, calls = 1, 5
+    warm, calls = 20, 20
     for p in prefill_workloads(gen):
         print(f"counters: {p.name}", file=sys.stderr, flush=True)
         q, k, v = to_dev(p.q), to_dev(p.k), to_dev(p.v)
@@ -358,11 +359,11 @@ def counters_run(gen, ea, torch, dev, to_dev):
     lens = torch.from_numpy(d.seq_lens).to(dev)
     ws = torch.empty(ea.attn_decode_workspace_bytes(d.B, d.Hq, d.max_blocks), dtype=torch.uint8,
                      device=dev)
-    for i in range(warm + calls):
+    for i in range(warm + 2 * calls):
         kp, vp = pools[i % 4]
         ea.attn_decode_paged(qd, kp, vp, tab, lens, scale=d.scale, workspace=ws)
     torch.cuda.synchronize()
-    seq.append({"workload": d.name, "warmup": warm, "calls": calls,
+    seq.append({"workload": d.name, "warmup": warm, "calls": 2 * calls,
                 "kernels": ["decode_partial_kernel", "decode_merge_kernel"], "flop": d.flops,
                 "algorithmic_bytes": d.bytes})
     print(json.dumps({"counters_run": True, "copy_bytes": n, "sequence": seq}), flush=True)
@@ -453,7 +454,9 @@ def summarize(prof_dir, out_dir=None):
                                                  max(ctr["SQ_LDS_IDX_ACTIVE"], 1.0), 4),
                 "l2_hit_rate": round(hits / max(hits + miss, 1.0), 4),
                 "mfma_flop": mops * 512,
-                "clock_mhz": round(g / (sum(sq_us) / len(sq_us)), 1),
+                # busy cycles over duration; meaningless for short dispatches
+                "clock_mhz": (round(g / (sum(sq_us) / len(sq_us)), 1)
+                              if min(sq_us) >= 200 else None),
                 "hbm_GB/s": round((rd + wr) / (avg * 1e-6) / 1e9, 1),
             }
             if kern.startswith("prefill"):
@@ -467,8 +470,9 @@ def summarize(prof_dir, out_dir=None):
                 "algorithmic_bytes": ent["algorithmic_bytes"], "flop": ent["flop"],
                 "counters_per_dispatch": ctr, "derived": derived}
     out_dir = out_dir or os.path.join(ROOT, "profiles")
-    data = {"about": "rocprofv3 kernel trace and counters of `bench.py --counters` (five timed "
-                     "calls per workload after one warm-up); counters averaged per dispatch; "
+    data = {"about": "rocprofv3 kernel trace and counters of `bench.py --counters` (20 timed "
+                     "calls per workload, 40 for the decode, after 20 warm-up calls); counters "
+                     "averaged per dispatch; "
                      "FETCH_SIZE and WRITE_SIZE in bytes, each scaled by its reading of a 1 GiB "
                      "device copy",
             "fetch_scale": ref["fetch"], "write_scale": ref["write"], "cus": cus, "simds": simds,
@@ -503,7 +507,7 @@ def summarize(prof_dir, out_dir=None):
             lines.append(f"| {kern} | {dv['mfma_util']:.3f} | {dv['valu_busy']:.3f} | "
                          f"{dv['lds_util']:.3f} | {dv['lds_bank_conflict_share']:.3f} | "
                          f"{dv['l2_hit_rate']:.3f} | {dv.get('mfma_flop_over_algorithmic', '-')} "
-                         f"| {dv['clock_mhz']} | {dv['hbm_GB/s']} |")
+                         f"| {dv['clock_mhz'] or '-'} | {dv['hbm_GB/s']} |")
         lines += ["", "Raw counters (per dispatch):", "",
                   "| counter | " + " | ".join(ent["kernels"]) + " |",
                   "|---|" + "---|" * len(ent["kernels"])]

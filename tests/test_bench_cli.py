@@ -47,12 +47,13 @@ def _fake_profile(tmp, copy_kib, kernels):
     t = 1000
     spans = []
     for _ in names:
-        spans.append((t, t + 100_000))      # 100 us each
-        t += 200_000
+        spans.append((t, t + 400_000))      # 400 us each
+        t += 500_000
+    cyc = 800_000.0                          # busy cycles of one XCD: 2000 MHz over 400 us
     values = {"FETCH_SIZE": 2.0 * (1 << 20), "WRITE_SIZE": 1.0 * (1 << 20),
-              "GRBM_GUI_ACTIVE": 8 * 200_000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 200_000 * 1024,
-              "SQ_ACTIVE_INST_VALU": 0.25 * 200_000 * 256, "SQ_LDS_IDX_ACTIVE": 0.1 * 200_000 * 256,
-              "SQ_LDS_BANK_CONFLICT": 0.01 * 200_000 * 256, "TCC_HIT_sum": 3.0, "TCC_MISS_sum": 1.0,
+              "GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cyc * 1024,
+              "SQ_ACTIVE_INST_VALU": 0.25 * cyc * 256, "SQ_LDS_IDX_ACTIVE": 0.1 * cyc * 256,
+              "SQ_LDS_BANK_CONFLICT": 0.01 * cyc * 256, "TCC_HIT_sum": 3.0, "TCC_MISS_sum": 1.0,
               "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1e12 / 2 / 512, "SQ_INSTS_VALU_MFMA_MOPS_F16":
                   1e12 / 2 / 512}
     for pas, ctrs in [("ktrace", None)] + list(bench.COUNTER_PASSES.items()):
@@ -96,7 +97,7 @@ def test_summarize_derives_counters_per_dispatch(tmp_path):
     data = json.load(open(out / "profile_data.json"))
     assert abs(data["fetch_scale"] - 0.5) < 1e-12 and abs(data["write_scale"] - 1.0) < 1e-12
     e = data["entries"]["wa::prefill_pipe_kernel"]
-    assert e["dispatches"] == 5 and abs(e["avg_us"] - 100.0) < 1e-9
+    assert e["dispatches"] == 5 and abs(e["avg_us"] - 400.0) < 1e-9
     assert abs(e["read_bytes"] - (1 << 30)) < 1 and abs(e["write_bytes"] - (1 << 30)) < 1
     dv = e["derived"]
     assert abs(dv["mfma_util"] - 0.5) < 1e-4 and abs(dv["valu_busy"] - 0.25) < 1e-4
