@@ -50,6 +50,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+# peak of a product pair run half on fp8 and half on fp16 MFMA
+PEAK_FP8_FP16_MIX = round(1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS), 1)
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (d=128); paged decode HBM GB/s"
 ROUNDING_MODES = ("rtne", "rtna", "rtz")   # rules of the bf16 output, timed on the headline
 
@@ -542,11 +545,15 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
         def run_f(_i):
             ea.attn_fwd_fp8(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
 
-        ms = time_calls(run_f, steps, 2, torch)
+        ms = time_calls(run_f, steps, args.warmup, torch)
         tf = p.flops / (ms * 1e-3) / 1e12
         ent = {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
-               "inputs": "e4m3", "compute": "fp16 MFMA", "causal": p.causal, "layout": lay,
+               "inputs": "e4m3", "compute": "Q.K^T on fp8 MFMA, P.V on fp16 MFMA",
+               "causal": p.causal, "layout": lay,
                "ms_per_call": round(ms, 4), "flop": p.flops, "TFLOP/s": round(tf, 2),
+               # half the FLOP at the fp8 rate, half at the fp16 rate
+               "peak_TFLOP/s": PEAK_FP8_FP16_MIX,
+               "frac_of_peak": round(tf / PEAK_FP8_FP16_MIX, 4),
                "frac_of_fp16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         if not p.causal:
             ent["algorithmic_bytes"] = 3 * q.numel() + 2 * o.numel() + 4 * lse.numel()

@@ -198,9 +198,8 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, f
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   // the descales and the scale fold into two fp32 constants, which must stay
   // normal, positive and finite
-  const double cd = (double)scale * 1.4426950408889634 * (double)descale_q * (double)descale_k *
-                    65536.0;
-  const double od = (double)descale_v * 256.0;
+  const double cd = (double)scale * 1.4426950408889634 * (double)descale_q * (double)descale_k;
+  const double od = (double)descale_v;
   const bool consts_ok = std::isfinite(cd) && std::isfinite(od) && cd >= 1.2e-38 &&
                          od >= 1.2e-38 && cd <= 3.0e38 && od <= 3.0e38;
   if (d != attn::kHeadDim || (layout != ATTN_BSHD && layout != ATTN_BHSD) ||
@@ -223,6 +222,8 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, f
     a.q_sb = (int64_t)Hq * Sq * D; a.q_sh = (int64_t)Sq * D; a.q_ss = D;
     a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
   }
+  // K/V of one (batch, kv head) are addressed with 32-bit byte offsets
+  if ((int64_t)(Sk - 1) * a.k_ss + D > INT32_MAX) return ATTN_ERR_SHAPE;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk;
   a.group = Hq / Hkv;
   a.n_qt = (Sq + attn::kFp8RowsPerBlock - 1) / attn::kFp8RowsPerBlock;

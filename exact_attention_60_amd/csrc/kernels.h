@@ -51,7 +51,7 @@ constexpr int kPrefillPipeRows = 64;
 hipError_t launch_prefill_pipe(const PrefillArgs& a, bool causal, hipStream_t stream);
 
 // ---- FP8 (E4M3) forward ------------------------------------------------------
-constexpr int kFp8RowsPerBlock = 128;   // query rows per workgroup
+constexpr int kFp8RowsPerBlock = 256;   // query rows per workgroup
 
 struct Fp8Args {
   const uint8_t* q;          // E4M3 bytes, d = 128 innermost
@@ -64,8 +64,8 @@ struct Fp8Args {
   int B, Hq, Hkv, Sq, Sk;
   int group;                 // Hq / Hkv
   int n_qt;                  // ceil(Sq / kFp8RowsPerBlock)
-  float c;                   // scale * log2(e) * descale_q * descale_k * 2^16
-  float out_scale;           // descale_v * 2^8
+  float c;                   // scale * log2(e) * descale_q * descale_k
+  float out_scale;           // descale_v
 };
 
 hipError_t launch_prefill_fp8(const Fp8Args& a, bool causal, hipStream_t stream);

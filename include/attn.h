@@ -169,14 +169,16 @@ int attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* 
  * as a variant and say that FP8 handling falls back to FP16 on ROCm
  * ("Engineering the FlashAttention-4 kernel port to ROCm", HIP migration
  * section; "IO-aware tiling strategy in FlashAttention-4", monitoring
- * paragraph): the bytes are widened exactly to fp16 inside the kernel and
- * both products run on fp16 MFMA with fp32 accumulation.
+ * paragraph): Q.K^T runs on the FP8 matrix core (exact products, fp32
+ * accumulation: the scores of the exactly widened values), V is widened
+ * exactly to fp16 inside the kernel and P.V runs on fp16 MFMA with fp32
+ * accumulation.
  *
  *   q, k, v      device E4M3 bytes in `layout` (BSHD [B,S,H,128] or BHSD
- *                [B,H,S,128]), 16-byte aligned, finite values: the E4M3 NaN
- *                encoding is not recognised (it reads as +-480)
- *   descale_*    positive finite fp32; scale*descale_q*descale_k*log2(e)*2^16
- *                and descale_v*2^8 must be normal fp32 values, otherwise
+ *                [B,H,S,128]), 16-byte aligned, finite values (the E4M3 NaN
+ *                encoding s.1111.111 propagates to the rows it touches)
+ *   descale_*    positive finite fp32; scale*descale_q*descale_k*log2(e) and
+ *                descale_v must be normal fp32 values, otherwise
  *                ATTN_ERR_UNSUPPORTED
  *   o, lse       as for attn_fwd (O bf16 rounded to nearest even in q's
  *                layout, LSE fp32 [B,Hq,Sq] of the descaled scores)

@@ -353,6 +353,7 @@ def fwd_fp8(**kw):
     (dict(d=64), -3), (dict(layout=2), -3), (dict(causal=2), -3), (dict(dq=0.0), -3),
     (dict(dk=-1.0), -3), (dict(dv=float("inf")), -3), (dict(dv=float("nan")), -3),
     (dict(dq=1e-30, dk=1e-30), -3), (dict(dq=1e30, dk=1e30), -3), (dict(v=P + 8), -4),
+    (dict(Sk=1 << 24, Hq=2, Hkv=1), -2),    # K/V head beyond 32-bit byte offsets
 ])
 def test_fwd_fp8_argument_errors(kw, code):
     assert fwd_fp8(**kw) == code
