@@ -1,8 +1,9 @@
 """Parity of the FP8 (E4M3) forward (attn_fwd_fp8) with the fp64 oracle on
 the decoded, descaled inputs (GPU), under the forward's tolerance:
 |O - O_ref| <= 2 ulp_bf16(|O_ref|) + 1e-3 and |LSE - LSE_ref| <= 1e-3.  The
-widening of E4M3 to fp16 is exact, so the arithmetic after it is that of the
-bf16 forward (fp32 accumulation, fp16 probabilities for P.V, bf16 output)."""
+products of E4M3 values in Q.K^T are exact in fp32 and the widening of V to
+fp16 is exact, so the arithmetic after them is that of the bf16 forward (fp32
+accumulation, fp16 probabilities for P.V, bf16 output)."""
 import numpy as np
 import pytest
 import torch
@@ -65,8 +66,9 @@ def test_descales_and_peaky_rows():
 
 
 def test_subnormal_inputs():
-    # amp 0.02: most bytes are E4M3 subnormals (|x| < 2^-6), widened to fp16
-    # subnormals; the descales bring the scores back to order one
+    # amp 0.02: most bytes are E4M3 subnormals (|x| < 2^-6): subnormal
+    # operands of the fp8 MFMA, and fp16 subnormals after the widening of V;
+    # the descales bring the scores back to order one
     p = gen.fp8_prefill_inputs(1, 4, 4, 128, 192, layout=gen.BHSD, seed=22,
                                descales=(64.0, 64.0, 32.0), amp=(0.02, 0.02, 0.02))
     frac = np.mean((p.q & 0x78) == 0)
