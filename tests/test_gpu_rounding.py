@@ -162,6 +162,7 @@ CONSISTENCY = [
     (1, 4, 2, 300, 333, gen.BSHD, False),
     (2, 4, 1, 257, 257, gen.BHSD, True),
     (1, 2, 2, 100, 700, gen.BHSD, True),
+    (2, 16, 16, 2100, 200, gen.BSHD, False),   # 288 workgroups, ragged last query tile
 ]
 
 
