@@ -11,7 +11,7 @@ import torch
 import attn_inputs as gen
 import exact_attention_60_amd as ea
 import oracle.fp8 as f8
-from gpu_util import host_f64, logical_o, need_gpu
+from gpu_util import host_f64, logical_o, need_gpu, oracle_workers
 from tolerance import check_lse, check_o
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +52,9 @@ def check_all(p, what):
     (1, 4, 1, 70, 600, gen.BHSD, True),        # MQA, bottom-right alignment
     (1, 2, 2, 1, 1, gen.BSHD, False),          # one row, one key
     (1, 2, 1, 129, 1000, gen.BSHD, False),     # one row past a block, many tiles
+    (1, 4, 4, 600, 333, gen.BHSD, True),       # several 256-row workgroups, ragged tile
+    (2, 6, 3, 513, 700, gen.BSHD, False),      # group 2, a 256-row block plus one row
+    (1, 8, 8, 1000, 1000, gen.BSHD, True),     # 8 heads: the XCD-grouped causal order
 ])
 def test_shapes_all_elements(B, Hq, Hkv, Sq, Sk, layout, causal):
     p = gen.fp8_prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=Sq + Sk)
@@ -120,6 +123,20 @@ def test_mha_full_size_sampled_rows():
     e = check_o(got[idx], o_ref[idx], p.name)
     el = check_lse(gl[idx], l_ref[idx], p.name)
     print(f"{p.name}: sampled err/tol {e[1]:.3f} lse {el:.3g}", flush=True)
+
+
+def test_mha_full_size_every_element():
+    """The benchmark's FP8 MHA workload (B=4, H=32, S=4096, BHSD), every
+    element of O and LSE against the whole oracle."""
+    p = gen.fp8_mha_prefill()
+    print(f"case: {p.name} (every element)", flush=True)
+    o, lse = run(p)
+    o_ref, l_ref = f8.attention_fp8(p.q, p.k, p.v, p.descale_q, p.descale_k, p.descale_v, p.B,
+                                    p.Hq, p.Hkv, p.Sq, p.Sk, p.scale, p.causal, p.layout,
+                                    workers=oracle_workers())
+    e = check_o(logical_o(o, p.layout), o_ref, p.name)
+    el = check_lse(host_f64(lse), l_ref, p.name)
+    print(f"{p.name}: every element err/tol {e[1]:.3f} lse {el:.3g}", flush=True)
 
 
 def test_float8_dtype_accepted_and_deterministic():
