@@ -664,7 +664,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         tf = fl / (ms * 1e-3) / 1e12
         ent = {"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
                "TFLOP/s": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-               "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}
+               "kernels": "bwd_prep_kernel + bwd_dkdv_pair_kernel + bwd_dq_kernel"}
         if p.name == "mha_prefill_b4_h32_s4096_bhsd":
             # algorithmic bytes: Q, K, V, O, dO, LSE read once, dQ, dK, dV written once
             ent["algorithmic_bytes"] = 8 * q.numel() * 2 + 4 * p.B * p.Hq * p.Sq
@@ -692,7 +692,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
     res.append({"workload": p.name + "_alibi_backward", "ms_per_call": round(ms, 4), "flop": fl,
                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
                 "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+                "kernels": "bwd_prep_kernel + bwd_dkdv_pair_kernel + bwd_dq_kernel"})
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     # the causal GQA backward at head dim 64
@@ -714,7 +714,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
     res.append({"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
                 "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+                "kernels": "bwd_prep_kernel + bwd_dkdv_pair_kernel + bwd_dq_kernel"})
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     # packed sequences of mixed lengths (attn_bwd_varlen)
@@ -739,7 +739,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
     res.append({"workload": pv.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
                 "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "kernels": "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"})
+                "kernels": "bwd_prep_kernel + bwd_dkdv_pair_kernel + bwd_dq_kernel"})
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return res

@@ -18,13 +18,16 @@
 //  * bwd_prep_kernel: D and the LSE in log2 units (+inf for rows that see no
 //    key, so that their recomputed probabilities are exactly 0), one pass over
 //    O and dO.
-//  * bwd_dkdv_kernel: one workgroup = 4 waves = 128 keys of one (batch, K/V
-//    head); each wave keeps its 32 keys' K and V fragments and fp32 dK, dV
-//    accumulators in registers and walks every query head of the group and
-//    every 64-row query block that can see its keys.  Q, dO, LSE and D blocks
-//    are copied HBM -> LDS by the buffer unit (buffer_load ... lds), double
-//    buffered one block ahead.  The GQA sum stays inside the workgroup, so
-//    there are no atomics and the result is deterministic.
+//  * bwd_dkdv_pair_kernel: one workgroup = 8 waves = 128 keys of one (batch,
+//    K/V head), two waves per SIMD sharing 32 keys: one keeps their K
+//    fragments and the dV accumulators (S, P, dV += P^T dO), the other their
+//    V fragments and the dK accumulators (dP, then dS = P (dP - D) and
+//    dK += dS^T Q a step later, with P passed through LDS as fp16).  The
+//    workgroup walks every query head of the group and every 64-row query
+//    block that can see its keys; Q, dO, LSE and D blocks are copied HBM ->
+//    LDS by the buffer unit (buffer_load ... lds) into a ring of three, one
+//    block ahead.  The GQA sum stays inside the workgroup, so there are no
+//    atomics and the result is deterministic.
 //  * bwd_dq_kernel: one workgroup = 4 waves = 128 query rows of one (batch,
 //    query head); each wave keeps its rows' Q and dO fragments and fp32 dQ
 //    accumulators in registers, and the 64-key K/V tiles stream through
@@ -39,12 +42,8 @@
 //    with the gfx950 transpose read (ds_read_b64_tr_b16).
 //  * LDS rows are 256 B with an XOR swizzle of their 16-byte chunks so that
 //    both the row reads and the transpose reads spread over the banks.
-//  * The dK/dV kernel runs one wave per SIMD (K, V fragments and two
-//    accumulators take 370+ registers), so it overlaps its own MFMAs and VALU
-//    work: when both 32-row halves of a query block are whole, the S/dP
-//    MFMAs of one half run beside the softmax gradient of the other, and the
-//    dV/dK MFMAs of one beside the next (an interleave requested from the
-//    scheduler).  The dQ kernel fits two waves per SIMD and relies on that.
+//  * Both main kernels run two waves per SIMD, so one wave's exponentials and
+//    operand reads run beside the other's MFMAs.
 //  * blockIdx is remapped so that workgroups reading the same Q/dO (or K/V)
 //    run on one XCD and share its L2; causal dQ blocks are dispatched
 //    heaviest first.  Packed sequences (PACKED variants) spread the heads of
@@ -176,112 +175,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 
-// ---- pieces of the dK/dV loop (lane (c, h) = (lane % 32, lane / 32)) ----
-
-// A operands of S = Q K^T and dP = dO V^T: Q and dO row `row`, head-dim
-// slots 16*ks + 8*h .. +7
-template <int D>
-__device__ __forceinline__ void read_rows(bf16x8 (&qa)[BG<D>::KS], bf16x8 (&oa)[BG<D>::KS],
-                                          const char* qt, const char* dt, int row, int h) {
-#pragma unroll
-  for (int ks = 0; ks < BG<D>::KS; ++ks) {
-    qa[ks] = lds_row<D>(qt, row, 2 * ks + h);
-    oa[ks] = lds_row<D>(dt, row, 2 * ks + h);
-  }
-}
-// S and dP of one 32-row sub-block against the wave's 32 keys
-template <int KS>
-__device__ __forceinline__ void mfma_sdp(f32x16& s, f32x16& p, const bf16x8 (&qa)[KS],
-                                         const bf16x8 (&oa)[KS], const bf16x8 (&kf)[KS],
-                                         const bf16x8 (&vf)[KS]) {
-  s = f32x16{};
-  p = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    s = mfma32(qa[ks], kf[ks], s);
-    p = mfma32(oa[ks], vf[ks], p);
-  }
-}
-// B operands of dV += P^T dO and dK += dS^T Q for a sub-block starting at
-// tile row r32: dO and Q columns, both halves of the 32 rows
-template <int D>
-__device__ __forceinline__ void read_cols(bf16x8 (&oc)[2][BG<D>::NTD], bf16x8 (&qc)[2][BG<D>::NTD],
-                                          const char* qt, const char* dt, int r32, int lane) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int n = 0; n < BG<D>::NTD; ++n) {
-      oc[t][n] = lds_cols<D>(dt, r32 + 16 * t, 32 * n, lane);
-      qc[t][n] = lds_cols<D>(qt, r32 + 16 * t, 32 * n, lane);
-    }
-}
-// log2-LSE and D of the 16 rows a lane's accumulator registers hold
-__device__ __forceinline__ void read_rowvals(f32x4 (&l4)[4], f32x4 (&d4)[4], const float* lb,
-                                             const float* db, int r32, int h) {
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    l4[q4] = *reinterpret_cast<const f32x4*>(lb + r32 + 8 * q4 + 4 * h);
-    d4[q4] = *reinterpret_cast<const f32x4*>(db + r32 + 8 * q4 + 4 * h);
-  }
-}
-// P = exp2(S*c - L) and dS = P (dP - D), rounded to bf16 as the A operands of
-// the dV and dK products.  With MASK, entries whose key is past the end or
-// (causal) past the row's diagonal get P = 0: row0 is the global row of
-// register 0 (4h included), key the lane's key.  With ALIBI the exponent also
-// gets alibi2 * |d0 + 8*q4 + i| (alibi2 = -slope*log2(e), d0 = the distance
-// row + off - key of register 0).
-template <bool MASK, bool ALIBI = false>
-__device__ __forceinline__ void softmax_grad(bf16x8 (&pa)[2], bf16x8 (&da)[2], const f32x16& s,
-                                             const f32x16& p, const f32x4 (&l4)[4],
-                                             const f32x4 (&d4)[4], float c, int row0, int key,
-                                             int Sk, int off, int causal, float alibi2 = 0.f,
-                                             float d0 = 0.f) {
-  float pv[16], dv[16];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q4 + i;
-      float e = s[r] * c - l4[q4][i];
-      if (ALIBI) e = __builtin_fmaf(alibi2, __builtin_fabsf(d0 + (float)(8 * q4 + i)), e);
-      float x = fast_exp2(e);
-      if (MASK) {
-        const int row = row0 + 8 * q4 + i;
-        if (key >= Sk || (causal && key > row + off)) x = 0.f;
-      }
-      pv[r] = x;
-      dv[r] = x * (p[r] - d4[q4][i]);
-    }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    pa[t] = to_bf16x8(pv + 8 * t);
-    da[t] = to_bf16x8(dv + 8 * t);
-  }
-}
-// dV += P^T dO, dK += dS^T Q for one sub-block
-template <int NTD>
-__device__ __forceinline__ void mfma_dvdk(f32x16 (&dv)[NTD], f32x16 (&dk)[NTD],
-                                          const bf16x8 (&pa)[2], const bf16x8 (&da)[2],
-                                          const bf16x8 (&oc)[2][NTD], const bf16x8 (&qc)[2][NTD]) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int n = 0; n < NTD; ++n) {
-      dv[n] = mfma32(pa[t], oc[t][n], dv[n]);
-      dk[n] = mfma32(da[t], qc[t][n], dk[n]);
-    }
-}
-// Scheduling request for the region since the last sched_barrier: N MFMAs
-// each followed by up to 6 VALU instructions.
-template <int N>
-__device__ __forceinline__ void interleave_mfma_valu() {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-  }
-}
-
 // Workgroups are dealt to the 8 XCDs round robin (XCD = i % 8).  Index i of
 // a row of B*Hq workgroups goes to K/V head group (i % 8) + 8 * (i / 8 / G),
 // query head (i / 8) % G of that group: the G query heads of a group share an
@@ -358,25 +251,67 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// ---- dK, dV ----------------------------------------------------------------
-template <int D, bool CAUSAL, bool PACKED, bool ALIBI>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int TILE = BG<D>::TILE, KS = BG<D>::KS, NTD = BG<D>::NTD;
-  __shared__ __attribute__((aligned(1024))) char qbuf[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) char dobuf[2 * TILE];
-  __shared__ __attribute__((aligned(16))) float lbuf[2 * QB];
-  __shared__ __attribute__((aligned(16))) float dbuf[2 * QB];
+// ---- dK, dV with a pair of waves per 32 keys ---------------------------------
+// One workgroup = 8 waves = 128 keys of one (batch, K/V head), two waves per
+// SIMD.  Waves w and w + 4 (one SIMD) share the keys kw0 .. kw0+31 and split
+// the four products of a 64-row query block between them:
+//  * the first (role 0) keeps the keys' K fragments and the dV accumulators:
+//    S = Q K^T, P = exp2(S*c - L) (masked), P to LDS as fp16, dV += P^T dO;
+//  * the second (role 1) keeps the V fragments and the dK accumulators:
+//    dP = dO V^T, and one step later (when P of that block is in LDS)
+//    dS = P (dP - D), dK += dS^T Q.
+// Each wave's VALU work runs beside the other's MFMAs on the shared SIMD, and
+// the register budget of two waves per SIMD holds either half (K or V
+// fragments, one accumulator set).  Q, dO, L and D blocks go through a ring of
+// three LDS buffers (the second role reads block s-1 while block s+1 is
+// copied); P goes through two.  One barrier per step.
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Copy of 8 rows (this wave's share of a 64-row tile, 8 waves) from HBM into
+// LDS, laid out as RowCopy lays out 16.
+template <int D>
+struct RowCopy8 {
+  static constexpr int RPI = BG<D>::RPI, NC = BG<D>::NC, CPW = 8 / RPI;
+  static_assert(CPW >= 1 && CPW * RPI == 8, "8 rows per wave");
+  uint32_t voff[CPW];
+  int row0;
+  __device__ void init(int64_t row_stride, int wave, int lane) {
+    row0 = 8 * wave;
+    const uint32_t ss = (uint32_t)(row_stride * 2);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int row = row0 + RPI * j + lane / NC;
+      voff[j] = (uint32_t)row * ss + (uint32_t)(((lane % NC) ^ swz<NC>(row & 15)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char* tile, uint32_t base) const {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (ATTN_LDS void*)(tile + (row0 + RPI * j) * BG<D>::RB), 16, voff[j] + base, 0, 0, 0);
+  }
+};
+
+template <int D, bool CAUSAL, bool PACKED, bool ALIBI>
+__global__ __launch_bounds__(2 * NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_pair_kernel(BwdArgs a) {
+  constexpr int TILE = BG<D>::TILE, KS = BG<D>::KS, NTD = BG<D>::NTD;
+  constexpr int NB = 3;                         // Q / dO / L / D ring
+  constexpr int PSUB = 2 * 64 * 16;             // one sub-block of P: 64 lanes x 32 B
+  __shared__ __attribute__((aligned(1024))) char qbuf[NB * TILE];
+  __shared__ __attribute__((aligned(1024))) char dobuf[NB * TILE];
+  __shared__ __attribute__((aligned(1024))) char pbuf[2 * NW * 2 * PSUB];   // [step&1][pair][sub-block]
+  __shared__ __attribute__((aligned(16))) float lbuf[NB * QB];
+  __shared__ __attribute__((aligned(16))) float dbuf[NB * QB];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // 8 waves
+  const int role = wave >> 2, w4 = wave & 3;
   const int c = lane & 31, h = lane >> 5;
   const int n_kb = (a.Sk + KV_ROWS - 1) / KV_ROWS;
   int bg, kb;
   if (PACKED) {
-    // packed sequences: rows of B*Hkv workgroups per key block, so the K/V
-    // heads of one sequence land on different XCDs
-    const int BG = a.B * a.Hkv;
-    kb = blockIdx.x / BG;
-    bg = blockIdx.x - kb * BG;
+    const int BG_ = a.B * a.Hkv;
+    kb = blockIdx.x / BG_;
+    bg = blockIdx.x - kb * BG_;
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     bg = L / n_kb;
@@ -387,36 +322,29 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int Sq = sv.Sq, Sk = sv.Sk;
   const int k0 = kb * KV_ROWS;
   if (k0 >= Sk) return;                 // whole workgroup: past this sequence's keys
-  const int kw0 = k0 + 32 * wave;       // this wave's first key
-  const int off = Sk - Sq;              // key j visible from row i iff j <= i + off (causal)
+  const int kw0 = k0 + 32 * w4;         // this pair's first key
+  const int off = Sk - Sq;
 
-  // K and V fragments of the wave's keys: B operand of S = Q K^T and of
-  // dP = dO V^T (lane: key kw0 + c, head-dim slots 16*ks + 8*h .. +7)
-  const __bf16* kp = a.k + sv.kbase + g * a.k_sh;
-  const __bf16* vp = a.v + sv.kbase + g * a.k_sh;
-  bf16x8 kf[KS], vf[KS];
+  // K (role 0) or V (role 1) fragments of the pair's keys: B operand of
+  // S = Q K^T or dP = dO V^T (lane: key kw0 + c, head-dim slots 16*ks + 8*h)
+  bf16x8 kvf[KS];
   {
+    const __bf16* src = (role == 0 ? a.k : a.v) + sv.kbase + g * a.k_sh;
     const int key = kw0 + c;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (key < Sk) {
-        kf[ks] = *reinterpret_cast<const bf16x8*>(kp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
-        vf[ks] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)key * a.k_ss + 16 * ks + 8 * h);
-      } else {
-        kf[ks] = bf16x8{};
-        vf[ks] = bf16x8{};
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      kvf[ks] = key < Sk ? *reinterpret_cast<const bf16x8*>(src + (int64_t)key * a.k_ss + 16 * ks +
+                                                            8 * h)
+                         : bf16x8{};
   }
 
-  // query blocks that can see a key of this workgroup, for each head of the group
   const int qstart = CAUSAL ? max(0, k0 - off) : 0;
   const int qb_first = qstart / QB;
   const int n_qb = (Sq + QB - 1) / QB;
   const int per_head = n_qb - qb_first;
   const int total = a.group * per_head;
 
-  RowCopy<D> cp;
+  RowCopy8<D> cp;
   cp.init(a.q_ss, wave, lane);
   const uint32_t q_bytes = Sq > 0 ? (uint32_t)((int64_t)(Sq - 1) * a.q_ss * 2 + BG<D>::RB) : 0u;
   const uint32_t blk_bytes = (uint32_t)(QB * a.q_ss * 2);
@@ -433,114 +361,161 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
                                                4, (uint32_t)(qb * QB + lane) * 4, 0, 0, 0);
     }
   };
+  // which 32-row sub-blocks of step s's query block see some of the pair's
+  // keys, and whether any of their entries needs the mask
+  auto step_q0 = [&](int s) { return (qb_first + s % per_head) * QB; };
+  auto active = [&](int q0, int qs) {
+    return kw0 < Sk && !(CAUSAL && kw0 > q0 + 32 * qs + 31 + off);
+  };
+  auto masked = [&](int q0, int qs) {
+    const int r0 = q0 + 32 * qs;
+    return (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > Sk);
+  };
+  // this lane's 32 bytes of sub-block qs of P in buffer `pb`: two 16-byte
+  // halves, each contiguous over the 64 lanes (no bank conflicts)
+  auto p_slot = [&](int pb, int qs) { return pbuf + ((pb * NW + w4) * 2 + qs) * PSUB + 16 * lane; };
 
-  f32x16 dk[NTD], dv[NTD];
+  f32x16 acc[NTD];                      // dV (role 0) or dK (role 1)
 #pragma unroll
-  for (int n = 0; n < NTD; ++n) {
-    dk[n] = f32x16{};
-    dv[n] = f32x16{};
-  }
+  for (int n = 0; n < NTD; ++n) acc[n] = f32x16{};
 
   if (total > 0) issue(0, 0);
-  for (int s = 0; s < total; ++s) {
-    const int st = s & 1;
-    wait_all();
-    barrier();
-    if (s + 1 < total) issue(s + 1, st ^ 1);
-    const int q0 = (qb_first + s % per_head) * QB;
-    // ALiBi: -slope * log2(e) of this step's query head, and the distance
-    // row + off - key of register 0 of sub-block 0 (sub-block 1: +32)
-    const float alibi2 = ALIBI ? -a.alibi[g * a.group + s / per_head] * kLog2e : 0.f;
-    const float ad0 = (float)(q0 + 4 * h + off - (kw0 + c));
-    const char* qt = qbuf + st * TILE;
-    const char* dt = dobuf + st * TILE;
-    const float* lb = lbuf + st * QB;
-    const float* db = dbuf + st * QB;
-    // which 32-row sub-blocks of this block see some of the wave's keys, and
-    // whether any entry of them needs the mask (key tail or causal diagonal)
-    bool act[2], msk[2];
+  // The two roles run separate loops (so that neither holds the other's
+  // registers) with the same barriers: total + 1 steps, one barrier each.
+  if (role == 0) {
+    for (int s = 0; s <= total; ++s) {
+      wait_all();
+      barrier();   // block s's copies are visible; P of step s-2 has been read
+      if (s + 1 < total) issue(s + 1, (s + 1) % NB);
+      if (s >= total) continue;
+      const int st = s % NB;
+      const int q0 = step_q0(s);
+      const float alibi2 = ALIBI ? -a.alibi[g * a.group + s / per_head] * kLog2e : 0.f;
+      const float ad0 = (float)(q0 + 4 * h + off - (kw0 + c));
+      const char* qt = qbuf + st * TILE;
+      const char* dt = dobuf + st * TILE;
+      const float* lb = lbuf + st * QB;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int r0 = q0 + 32 * qs;
-      act[qs] = kw0 < Sk && !(CAUSAL && kw0 > r0 + 31 + off);
-      msk[qs] = (CAUSAL && kw0 + 31 > r0 + off) || (kw0 + 32 > Sk);
-    }
-    if (act[0] && act[1] && !msk[0] && !msk[1]) {
-      // Both sub-blocks whole: software-pipelined, so that each block of
-      // MFMAs has independent VALU work beside it (the wave's VALU
-      // instructions issue while its MFMAs execute).  Order: S, dP of
-      // sub-block 0 | S, dP of 1 beside the softmax gradient of 0 | dV, dK of
-      // 0 beside the softmax gradient of 1 | dV, dK of 1.
-      bf16x8 qa[KS], oa[KS], qa1[KS], oa1[KS];
-      read_rows<D>(qa, oa, qt, dt, c, h);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 s0, p0, s1, p1;
-      mfma_sdp(s0, p0, qa, oa, kf, vf);
-      read_rows<D>(qa1, oa1, qt, dt, 32 + c, h);
-      bf16x8 oc0[2][NTD], qc0[2][NTD];
-      read_cols<D>(oc0, qc0, qt, dt, 0, lane);
-      f32x4 l0[4], d0[4], l1[4], d1[4];
-      read_rowvals(l0, d0, lb, db, 0, h);
-      read_rowvals(l1, d1, lb, db, 32, h);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_sdp(s1, p1, qa1, oa1, kf, vf);
-      bf16x8 pa0[2], da0[2];
-      softmax_grad<false, ALIBI>(pa0, da0, s0, p0, l0, d0, a.c, 0, 0, 0, 0, 0, alibi2, ad0);
-      interleave_mfma_valu<2 * KS>();
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 oc1[2][NTD], qc1[2][NTD];
-      read_cols<D>(oc1, qc1, qt, dt, 32, lane);
-      mfma_dvdk(dv, dk, pa0, da0, oc0, qc0);
-      bf16x8 pa1[2], da1[2];
-      softmax_grad<false, ALIBI>(pa1, da1, s1, p1, l1, d1, a.c, 0, 0, 0, 0, 0, alibi2,
-                                 ad0 + 32.f);
-      interleave_mfma_valu<4 * NTD>();
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_dvdk(dv, dk, pa1, da1, oc1, qc1);
-      continue;
-    }
+      for (int qs = 0; qs < 2; ++qs) {
+        if (!active(q0, qs)) continue;
+        bf16x8 qa[KS];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      if (!act[qs]) continue;
-      const int r0 = q0 + 32 * qs;
-      // operand reads are issued in batches ahead of the MFMAs that use them
-      // (sched_barrier keeps the compiler from sinking each read next to its
-      // use, which would expose the LDS latency once per MFMA)
-      bf16x8 qa[KS], oa[KS];
-      read_rows<D>(qa, oa, qt, dt, 32 * qs + c, h);
-      __builtin_amdgcn_sched_barrier(0);
-      // S[q][key] and dP[q][key]: accumulator register r of lane (c, h) holds
-      // row 8*(r/4) + 4h + r%4 of the sub-block against key kw0 + c
-      f32x16 sacc, pacc;
-      mfma_sdp(sacc, pacc, qa, oa, kf, vf);
-      bf16x8 oc[2][NTD], qc[2][NTD];
-      read_cols<D>(oc, qc, qt, dt, 32 * qs, lane);
-      f32x4 l4[4], d4[4];
-      read_rowvals(l4, d4, lb, db, 32 * qs, h);
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 pa[2], da[2];
-      if (msk[qs])
-        softmax_grad<CAUSAL, ALIBI>(pa, da, sacc, pacc, l4, d4, a.c, r0 + 4 * h, kw0 + c, Sk, off,
-                                    1, alibi2, ad0 + 32.f * qs);
-      else
-        softmax_grad<false, ALIBI>(pa, da, sacc, pacc, l4, d4, a.c, 0, 0, 0, 0, 0, alibi2,
-                                   ad0 + 32.f * qs);
-      mfma_dvdk(dv, dk, pa, da, oc, qc);
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_row<D>(qt, 32 * qs + c, 2 * ks + h);
+        f32x4 l4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          l4[q4] = *reinterpret_cast<const f32x4*>(lb + 32 * qs + 8 * q4 + 4 * h);
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sacc = mfma32(qa[ks], kvf[ks], sacc);
+        // P = exp2(S*c - L), masked entries 0 (register r: row
+        // q0 + 32*qs + 8*(r/4) + 4h + r%4, key kw0 + c)
+        const bool msk = masked(q0, qs);
+        const int row0 = q0 + 32 * qs + 4 * h, key = kw0 + c;
+        float pv[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q4 + i;
+            float e = sacc[r] * a.c - l4[q4][i];
+            if (ALIBI)
+              e = __builtin_fmaf(alibi2, __builtin_fabsf(ad0 + 32.f * qs + (float)(8 * q4 + i)), e);
+            float x = fast_exp2(e);
+            if (msk) {
+              const int row = row0 + 8 * q4 + i;
+              if (key >= Sk || (CAUSAL && key > row + off)) x = 0.f;
+            }
+            pv[r] = x;
+          }
+        // P for the partner (fp16: dS = P (dP - D) is rounded to bf16 after,
+        // so the fp16 rounding of P is far below the result's precision)
+        char* ps = p_slot(s & 1, qs);
+        *reinterpret_cast<u32x4*>(ps) = u32x4{pack_f16(pv[0], pv[1]), pack_f16(pv[2], pv[3]),
+                                              pack_f16(pv[4], pv[5]), pack_f16(pv[6], pv[7])};
+        *reinterpret_cast<u32x4*>(ps + 64 * 16) =
+            u32x4{pack_f16(pv[8], pv[9]), pack_f16(pv[10], pv[11]), pack_f16(pv[12], pv[13]),
+                  pack_f16(pv[14], pv[15])};
+        // dV += P^T dO
+        const bf16x8 pa[2] = {to_bf16x8(pv), to_bf16x8(pv + 8)};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int n = 0; n < NTD; ++n)
+            acc[n] = mfma32(pa[t], lds_cols<D>(dt, 32 * qs + 16 * t, 32 * n, lane), acc[n]);
+      }
+    }
+  } else {
+    f32x16 dp[2];                       // dP of the previous step's sub-blocks
+    dp[0] = f32x16{};
+    dp[1] = f32x16{};
+    for (int s = 0; s <= total; ++s) {
+      wait_all();
+      barrier();   // block s's copies and P of step s-1 are visible
+      if (s + 1 < total) issue(s + 1, (s + 1) % NB);
+      if (s >= 1) {
+        // finish step s-1: dS = P (dP - D), dK += dS^T Q
+        const int q0 = step_q0(s - 1);
+        const int stp = (s + NB - 1) % NB;
+        const char* qt = qbuf + stp * TILE;
+        const float* db = dbuf + stp * QB;
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          if (!active(q0, qs)) continue;
+          const char* ps = p_slot((s - 1) & 1, qs);
+          const u32x4 p0 = *reinterpret_cast<const u32x4*>(ps);
+          const u32x4 p1 = *reinterpret_cast<const u32x4*>(ps + 64 * 16);
+          f32x4 d4[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            d4[q4] = *reinterpret_cast<const f32x4*>(db + 32 * qs + 8 * q4 + 4 * h);
+          float dsv[16];
+#pragma unroll
+          for (int r2 = 0; r2 < 8; ++r2) {
+            const uint32_t u = r2 < 4 ? p0[r2] : p1[r2 - 4];
+            const f16x2 hp = __builtin_bit_cast(f16x2, u);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 2 * r2 + e;
+              dsv[r] = (float)hp[e] * (dp[qs][r] - d4[r >> 2][r & 3]);
+            }
+          }
+          const bf16x8 da[2] = {to_bf16x8(dsv), to_bf16x8(dsv + 8)};
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int n = 0; n < NTD; ++n)
+              acc[n] = mfma32(da[t], lds_cols<D>(qt, 32 * qs + 16 * t, 32 * n, lane), acc[n]);
+        }
+      }
+      if (s < total) {
+        // dP = dO V^T of step s
+        const int q0 = step_q0(s);
+        const char* dt = dobuf + (s % NB) * TILE;
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          if (!active(q0, qs)) continue;
+          bf16x8 oa[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) oa[ks] = lds_row<D>(dt, 32 * qs + c, 2 * ks + h);
+          f32x16 pacc = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) pacc = mfma32(oa[ks], kvf[ks], pacc);
+          dp[qs] = pacc;
+        }
+      }
     }
   }
 
   // register r of lane (c, h), d block n: key kw0 + 8*(r/4) + 4h + r%4, dim 32n + c
-  __bf16* dkp = a.dk + sv.kbase + g * a.k_sh;
-  __bf16* dvp = a.dv + sv.kbase + g * a.k_sh;
+  __bf16* dst = (role == 0 ? a.dv : a.dk) + sv.kbase + g * a.k_sh;
+  const float mul = role == 0 ? 1.f : a.scale;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
     if (key < Sk) {
 #pragma unroll
-      for (int n = 0; n < NTD; ++n) {
-        dkp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)(dk[n][r] * a.scale);
-        dvp[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)dv[n][r];
-      }
+      for (int n = 0; n < NTD; ++n) dst[(int64_t)key * a.k_ss + 32 * n + c] = (__bf16)(acc[n][r] * mul);
     }
   }
 }
@@ -701,42 +676,43 @@ hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
   if (n_prep > 0x7fffffff || a.Hq > 65535 || a.B > 65535 || g_kv > 0x7fffffff ||
       g_q > 0x7fffffff || (a.D != 64 && a.D != 128) || (a.D == 64 && (a.cu_q || a.alibi)))
     return hipErrorInvalidValue;
-  const dim3 gp((unsigned)n_prep, a.Hq, prep_b), gk((unsigned)g_kv), gq((unsigned)g_q), bt(NT);
+  const dim3 gp((unsigned)n_prep, a.Hq, prep_b), gk((unsigned)g_kv), gq((unsigned)g_q), bt(NT),
+      bt2(2 * NT);
   const bool packed = a.cu_q != nullptr;
   if (a.D == 64) {
     hipLaunchKernelGGL((bwd_prep_kernel<64>), gp, dim3(256), 0, stream, a);
     if (causal) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, false, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<64, true, false, false>), gk, bt2, 0, stream, a);
       hipLaunchKernelGGL((bwd_dq_kernel<64, true, false, false>), gq, bt, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, false, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<64, false, false, false>), gk, bt2, 0, stream, a);
       hipLaunchKernelGGL((bwd_dq_kernel<64, false, false, false>), gq, bt, 0, stream, a);
     }
   } else if (packed) {
     hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
     if (causal) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, true, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, true, true, false>), gk, bt2, 0, stream, a);
       hipLaunchKernelGGL((bwd_dq_kernel<128, true, true, false>), gq, bt, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, true, false>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, false, true, false>), gk, bt2, 0, stream, a);
       hipLaunchKernelGGL((bwd_dq_kernel<128, false, true, false>), gq, bt, 0, stream, a);
     }
   } else if (a.alibi) {
     hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
     if (causal) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, false, true>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, true, false, true>), gk, bt2, 0, stream, a);
       hipLaunchKernelGGL((bwd_dq_kernel<128, true, false, true>), gq, bt, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, false, true>), gk, bt, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, false, false, true>), gk, bt2, 0, stream, a);
       hipLaunchKernelGGL((bwd_dq_kernel<128, false, false, true>), gq, bt, 0, stream, a);
     }
   } else if (causal) {
     hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, false, false>), gk, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, true, false, false>), gk, bt2, 0, stream, a);
     hipLaunchKernelGGL((bwd_dq_kernel<128, true, false, false>), gq, bt, 0, stream, a);
   } else {
     hipLaunchKernelGGL((bwd_prep_kernel<128>), gp, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, false, false>), gk, bt, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, false, false, false>), gk, bt2, 0, stream, a);
     hipLaunchKernelGGL((bwd_dq_kernel<128, false, false, false>), gq, bt, 0, stream, a);
   }
   return hipGetLastError();
@@ -746,8 +722,8 @@ hipError_t launch_backward(const BwdArgs& a, bool causal, hipStream_t stream) {
 // host pass otherwise left some of them without their launch stubs).
 template __global__ void bwd_prep_kernel<64>(BwdArgs);
 template __global__ void bwd_prep_kernel<128>(BwdArgs);
-#define ATTN_BWD_VARIANT(D, C, P, A)                              \
-  template __global__ void bwd_dkdv_kernel<D, C, P, A>(BwdArgs); \
+#define ATTN_BWD_VARIANT(D, C, P, A)                                   \
+  template __global__ void bwd_dkdv_pair_kernel<D, C, P, A>(BwdArgs); \
   template __global__ void bwd_dq_kernel<D, C, P, A>(BwdArgs);
 ATTN_BWD_VARIANT(64, true, false, false)
 ATTN_BWD_VARIANT(64, false, false, false)
