@@ -251,6 +251,47 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
+// Per-lane LDS offsets of the operand reads of a 64-row tile.  The swizzle
+// only XORs the 16-byte chunk index with a function of (row % 16), so for rows
+// r32 + c (r32 a multiple of 32) and 16-row groups r16 + ... the offsets of
+// other k-steps and d blocks follow from one base by an XOR, plus the row
+// offset as an immediate:
+//   lds_row(tile, r32 + c, 2*ks + h)  = tile + (row ^ (ks << 5)) + r32 * RB
+//   lds_cols(tile, r16, 32*n, lane)   = transposed reads at
+//                                       tile + (col[x] ^ (n << 6)) + r16 * RB
+template <int D>
+struct TileAddr {
+  int row, col[2];
+  __device__ void init(int lane) {
+    const int c = lane & 31, h = lane >> 5, L = lane & 15;
+    row = tile_off<D>(c, h);
+    const int r = 4 * h + (L >> 2);
+    const int cc = 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+    col[0] = elem_off<D>(r, cc);
+    col[1] = elem_off<D>(r + 8, cc);
+  }
+  __device__ __forceinline__ bf16x8 row_op(const char* tile, int r32, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(tile + (row ^ (ks << 5)) + r32 * BG<D>::RB);
+  }
+  __device__ __forceinline__ bf16x8 col_op(const char* tile, int r16, int n) const {
+    const bf16x4 lo = lds_read_tr(tile + (col[0] ^ (n << 6)) + r16 * BG<D>::RB);
+    const bf16x4 hi = lds_read_tr(tile + (col[1] ^ (n << 6)) + r16 * BG<D>::RB);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// Walk over the steps of a K/V workgroup: query head hl of the group (local
+// index) and query block qb, advanced without divisions.
+struct StepPos {
+  int hl, qb;
+  __device__ __forceinline__ void next(int qb_first, int qb_end) {
+    if (++qb == qb_end) {
+      qb = qb_first;
+      ++hl;
+    }
+  }
+};
+
 // ---- dK, dV with a pair of waves per 32 keys ---------------------------------
 // One workgroup = 8 waves = 128 keys of one (batch, K/V head), two waves per
 // SIMD.  Waves w and w + 4 (one SIMD) share the keys kw0 .. kw0+31 and split
@@ -346,11 +387,13 @@ void bwd_dkdv_pair_kernel(BwdArgs a) {
 
   RowCopy8<D> cp;
   cp.init(a.q_ss, wave, lane);
+  TileAddr<D> ta;
+  ta.init(lane);
   const uint32_t q_bytes = Sq > 0 ? (uint32_t)((int64_t)(Sq - 1) * a.q_ss * 2 + BG<D>::RB) : 0u;
   const uint32_t blk_bytes = (uint32_t)(QB * a.q_ss * 2);
-  auto issue = [&](int s, int st) {
-    const int hq = g * a.group + s / per_head;
-    const int qb = qb_first + s % per_head;
+  auto issue = [&](const StepPos& sp, int st) {
+    const int hq = g * a.group + sp.hl;
+    const int qb = sp.qb;
     const int64_t hoff = sv.qbase + hq * a.q_sh;
     cp.issue(rsrc(a.q + hoff, q_bytes), qbuf + st * TILE, (uint32_t)qb * blk_bytes);
     cp.issue(rsrc(a.dout + hoff, q_bytes), dobuf + st * TILE, (uint32_t)qb * blk_bytes);
@@ -363,7 +406,7 @@ void bwd_dkdv_pair_kernel(BwdArgs a) {
   };
   // which 32-row sub-blocks of step s's query block see some of the pair's
   // keys, and whether any of their entries needs the mask
-  auto step_q0 = [&](int s) { return (qb_first + s % per_head) * QB; };
+  const int qb_end = qb_first + per_head;
   auto active = [&](int q0, int qs) {
     return kw0 < Sk && !(CAUSAL && kw0 > q0 + 32 * qs + 31 + off);
   };
@@ -379,18 +422,20 @@ void bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < NTD; ++n) acc[n] = f32x16{};
 
-  if (total > 0) issue(0, 0);
+  // positions of the current step and of the next (the one being copied)
+  StepPos cur{0, qb_first}, nxt = cur;
+  nxt.next(qb_first, qb_end);
+  if (total > 0) issue(cur, 0);
   // The two roles run separate loops (so that neither holds the other's
   // registers) with the same barriers: total + 1 steps, one barrier each.
   if (role == 0) {
-    for (int s = 0; s <= total; ++s) {
+    for (int s = 0, st = 0; s <= total; ++s, st = (st == NB - 1) ? 0 : st + 1) {
       wait_all();
       barrier();   // block s's copies are visible; P of step s-2 has been read
-      if (s + 1 < total) issue(s + 1, (s + 1) % NB);
+      if (s + 1 < total) issue(nxt, st == NB - 1 ? 0 : st + 1);
       if (s >= total) continue;
-      const int st = s % NB;
-      const int q0 = step_q0(s);
-      const float alibi2 = ALIBI ? -a.alibi[g * a.group + s / per_head] * kLog2e : 0.f;
+      const int q0 = cur.qb * QB;
+      const float alibi2 = ALIBI ? -a.alibi[g * a.group + cur.hl] * kLog2e : 0.f;
       const float ad0 = (float)(q0 + 4 * h + off - (kw0 + c));
       const char* qt = qbuf + st * TILE;
       const char* dt = dobuf + st * TILE;
@@ -400,7 +445,7 @@ void bwd_dkdv_pair_kernel(BwdArgs a) {
         if (!active(q0, qs)) continue;
         bf16x8 qa[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[ks] = lds_row<D>(qt, 32 * qs + c, 2 * ks + h);
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = ta.row_op(qt, 32 * qs, ks);
         f32x4 l4[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
@@ -442,21 +487,24 @@ void bwd_dkdv_pair_kernel(BwdArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int n = 0; n < NTD; ++n)
-            acc[n] = mfma32(pa[t], lds_cols<D>(dt, 32 * qs + 16 * t, 32 * n, lane), acc[n]);
+            acc[n] = mfma32(pa[t], ta.col_op(dt, 32 * qs + 16 * t, n), acc[n]);
       }
+      cur = nxt;
+      nxt.next(qb_first, qb_end);
     }
   } else {
     f32x16 dp[2];                       // dP of the previous step's sub-blocks
     dp[0] = f32x16{};
     dp[1] = f32x16{};
-    for (int s = 0; s <= total; ++s) {
+    int prev_q0 = 0;
+    for (int s = 0, st = 0; s <= total; ++s, st = (st == NB - 1) ? 0 : st + 1) {
       wait_all();
       barrier();   // block s's copies and P of step s-1 are visible
-      if (s + 1 < total) issue(s + 1, (s + 1) % NB);
+      if (s + 1 < total) issue(nxt, st == NB - 1 ? 0 : st + 1);
       if (s >= 1) {
         // finish step s-1: dS = P (dP - D), dK += dS^T Q
-        const int q0 = step_q0(s - 1);
-        const int stp = (s + NB - 1) % NB;
+        const int q0 = prev_q0;
+        const int stp = st == 0 ? NB - 1 : st - 1;
         const char* qt = qbuf + stp * TILE;
         const float* db = dbuf + stp * QB;
 #pragma unroll
@@ -485,24 +533,27 @@ void bwd_dkdv_pair_kernel(BwdArgs a) {
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int n = 0; n < NTD; ++n)
-              acc[n] = mfma32(da[t], lds_cols<D>(qt, 32 * qs + 16 * t, 32 * n, lane), acc[n]);
+              acc[n] = mfma32(da[t], ta.col_op(qt, 32 * qs + 16 * t, n), acc[n]);
         }
       }
       if (s < total) {
         // dP = dO V^T of step s
-        const int q0 = step_q0(s);
-        const char* dt = dobuf + (s % NB) * TILE;
+        const int q0 = cur.qb * QB;
+        const char* dt = dobuf + st * TILE;
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
           if (!active(q0, qs)) continue;
           bf16x8 oa[KS];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) oa[ks] = lds_row<D>(dt, 32 * qs + c, 2 * ks + h);
+          for (int ks = 0; ks < KS; ++ks) oa[ks] = ta.row_op(dt, 32 * qs, ks);
           f32x16 pacc = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) pacc = mfma32(oa[ks], kvf[ks], pacc);
           dp[qs] = pacc;
         }
+        prev_q0 = q0;
+        cur = nxt;
+        nxt.next(qb_first, qb_end);
       }
     }
   }
