@@ -633,6 +633,8 @@ void bwd_dq_kernel(BwdArgs a) {
 
   RowCopy<D> cp;
   cp.init(a.k_ss, wave, lane);
+  TileAddr<D> ta;
+  ta.init(lane);
   const __bf16* kp = a.k + sv.kbase + g * a.k_sh;
   const __bf16* vp = a.v + sv.kbase + g * a.k_sh;
   const uint32_t k_bytes = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * a.k_ss * 2 + BG<D>::RB) : 0u;
@@ -669,10 +671,10 @@ void bwd_dq_kernel(BwdArgs a) {
       // MFMAs so that they arrive under them
       bf16x8 ka[KS], va[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_row<D>(kt, 32 * ks2 + c, 2 * ks + h);
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = ta.row_op(kt, 32 * ks2, ks);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) va[ks] = lds_row<D>(vt, 32 * ks2 + c, 2 * ks + h);
+      for (int ks = 0; ks < KS; ++ks) va[ks] = ta.row_op(vt, 32 * ks2, ks);
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sacc = mfma32(ka[ks], qf[ks], sacc);
@@ -700,7 +702,7 @@ void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 da = to_bf16x8(ds + 8 * u);
 #pragma unroll
         for (int n = 0; n < NTD; ++n)
-          dq[n] = mfma32(da, lds_cols<D>(kt, 32 * ks2 + 16 * u, 32 * n, lane), dq[n]);
+          dq[n] = mfma32(da, ta.col_op(kt, 32 * ks2 + 16 * u, n), dq[n]);
       }
     }
   }
