@@ -135,15 +135,23 @@ __device__ __forceinline__ void with_rounding(int mode, F&& f) {
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
-// sum of the two fp16 halves of u added to acc in fp32 (v_dot2c_f32_f16)
+// The row sums below avoid the dot-product instructions (v_dot2*): measured
+// on gfx950, a dot instruction of one wave waits for the matrix core while
+// another wave of the SIMD runs MFMAs (about 70 cycles each instead of 5),
+// whereas ordinary VALU instructions, v_fma_mix_f32 included, issue beside
+// them.
+// sum of the two fp16 halves of u added to acc in fp32: each half widened
+// exactly and added with one rounding (v_fma_mix_f32 with 1.0: lo, then hi)
 __device__ __forceinline__ float sum2_f16(uint32_t u, float acc) {
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u), one, acc, false);
+  float r, t;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(t) : "v"(u), "v"(acc));
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(u), "v"(t));
+  return r;
 }
-// sum of the two bf16 halves of u added to acc in fp32 (v_dot2c_f32_bf16)
+// sum of the two bf16 halves of u added to acc in fp32 (each half widened
+// exactly by a shift or mask)
 __device__ __forceinline__ float sum2_bf16(uint32_t u, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), one, acc, false);
+  return (acc + __uint_as_float(u << 16)) + __uint_as_float(u & 0xffff0000u);
 }
 // two bf16 (packed in u) -> two fp16 (packed); exact for |x| in the fp16
 // normal range, |x| >= 65520 becomes +-inf

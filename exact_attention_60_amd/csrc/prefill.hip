@@ -103,12 +103,34 @@ __device__ __forceinline__ int spread_groups(int i, int G, int n_groups) {
   return (x + 8 * (j / G)) * G + (j - (j / G) * G);
 }
 
-// Asynchronous copy of a wave's 16 rows of one K or V tile from HBM into LDS
-// (buffer_load_dwordx4 ... lds).  Each instruction moves 1 KB: lane i lands
-// at byte 16*i, i.e. row +i/16, physical chunk i%16, so it fetches the
-// logical chunk that the swizzle puts there.
+// One 1 KB asynchronous copy (buffer_load_dwordx4 ... lds): lane i's 16 bytes
+// at byte offset voff of the buffer land at LDS byte lds + 16*i.  Written as
+// an asm statement so that the compiler does not see an LDS write in flight:
+// it would otherwise wait for every outstanding copy before the wave's next
+// LDS read, and a copy could not stay in flight across the wave's operand
+// reads.  The loop orders the copies with explicit waits and barriers.  M0
+// holds the LDS address (one wait state before the copy reads it).
+__device__ __forceinline__ void lds_copy16(const u32x4& rsrc, uint32_t voff, const char* lds) {
+  const uint32_t m =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const ATTN_LDS char*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Buffer descriptor: base address, no stride, nrec bytes, raw dword access.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* p, uint32_t nrec) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nrec, 0x00020000u};
+}
+
+// Asynchronous copy of a wave's 16 rows of one K or V tile from HBM into LDS.
+// Each instruction moves 1 KB: lane i lands at byte 16*i, i.e. row +i/16,
+// physical chunk i%16, so it fetches the logical chunk that the swizzle puts
+// there.  Bytes past the buffer's end (nrec) read as zero.
 struct TileLoader {
-  __amdgpu_buffer_rsrc_t rk, rv;
+  u32x4 rk, rv;
   uint32_t voff[4];       // per-lane byte offset, rows 4*j + lane/16 of the wave's 16
   uint32_t tile_bytes;    // BN * row stride in bytes
   int row0;               // first tile row this wave copies
@@ -118,8 +140,8 @@ struct TileLoader {
     wave &= 3;
     const uint32_t ss = (uint32_t)(k_ss * 2);
     const uint32_t nrec = Sk > 0 ? (uint32_t)((int64_t)(Sk - 1) * ss + 256) : 0u;
-    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)nrec, 0x00020000);
-    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)nrec, 0x00020000);
+    rk = buffer_rsrc(kp, nrec);
+    rv = buffer_rsrc(vp, nrec);
     tile_bytes = ss * BN;
     row0 = ROWS_PER_WAVE_DMA * wave;
 #pragma unroll
@@ -132,16 +154,12 @@ struct TileLoader {
   __device__ __forceinline__ void issue_k(int tile, char* kt) const {
     const uint32_t base = (uint32_t)tile * tile_bytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ATTN_LDS void*)(kt + (row0 + 4 * j) * 256), 16,
-                                               voff[j] + base, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) lds_copy16(rk, voff[j] + base, kt + (row0 + 4 * j) * 256);
   }
   __device__ __forceinline__ void issue_v(int tile, char* vt) const {
     const uint32_t base = (uint32_t)tile * tile_bytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vt + (row0 + 4 * j) * 256), 16,
-                                               voff[j] + base, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) lds_copy16(rv, voff[j] + base, vt + (row0 + 4 * j) * 256);
   }
 };
 
@@ -149,6 +167,16 @@ struct TileLoader {
 // about it: vmcnt(0) (this wave's LDS copies have landed), and
 // vmcnt(0) lgkmcnt(0) (also its LDS writes are done).
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// all but this wave's last n copies have landed (n = 0, 4 or 8: the copies
+// of one tile step; vector memory loads complete in order)
+__device__ __forceinline__ void wait_copies_but(int n) {
+  if (n == 8)
+    __builtin_amdgcn_s_waitcnt(0x0F78);
+  else if (n == 4)
+    __builtin_amdgcn_s_waitcnt(0x0F74);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 __device__ __forceinline__ void wait_copies_and_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
 // lgkmcnt(0) only: this wave's LDS writes are done
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -427,11 +455,13 @@ struct Ctx {
 // The phased tile loop.  Phase 2t: group 0 runs the MFMA phase of tile t
 // (Q.K of t, P.V of t-1), group 1 the softmax of tile t-1; phase 2t+1:
 // group 0 the softmax of t, group 1 the MFMA phase of t.
-//  * Group 1 copies K(t+1) and V(t) (bf16) at the start of phase 2t (a
-//    softmax phase, no LDS reads) and waits for both before the mid barrier,
-//    so from phase 2t+1 on they are visible to every wave.  K(t+1) goes to
-//    the K buffer last read in phase 2t-1; the single V staging buffer was
-//    last read in phase 2t-1.
+//  * Group 1 copies K(t+2) and V(t+1) (bf16) at the start of phase 2t (a
+//    softmax phase, no LDS reads), one tile step ahead, and before the mid
+//    barrier waits for the copies of the step before (K(t+1), V(t)), so from
+//    phase 2t+1 on those are visible to every wave.  K has three buffers:
+//    K(t+2) goes to the one last read in phase 2t-1 (K(t-1)'s); V has two
+//    staging buffers: V(t+1) goes to the one V(t-1) was transposed from in
+//    phase 2t-1.
 //  * In phase 2t+1 each group-1 wave transposes the 16 rows of V(t) it
 //    copied into the V^T buffer last read in phase 2t-1 (V^T(t-2)'s),
 //    converting to fp16, with the instructions spread between the MFMAs of
@@ -453,13 +483,31 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   };
   const bool g0 = x.group == 0;
   Prefetch pf;
-  if (T > 0 && !g0) x.ld.issue_k(0, kbuf);
+  auto kslot = [&](int t) { return kbuf + (t % 3) * TILE_BYTES; };
+  auto vslot = [&](int t) { return vbuf + (t & 1) * TILE_BYTES; };
+  // copies of tile step t: K(t+1) and V(t); returns how many were issued
+  auto issue_step = [&](int t) {
+    int n = 0;
+    if (t + 1 < T) {
+      x.ld.issue_k(t + 1, kslot(t + 1));
+      n += 4;
+    }
+    if (t < T) {
+      x.ld.issue_v(t, vslot(t));
+      n += 4;
+    }
+    return n;
+  };
+  if (T > 0 && !g0) {
+    x.ld.issue_k(0, kslot(0));
+    wait_copies_but(issue_step(0));
+  }
   wait_copies_and_lds();
   barrier();
   bool pre = false;   // this wave holds the first operands of its next MFMA phase
   for (int t = 0; t <= T; ++t) {
-    char* kt = kbuf + (t & 1) * TILE_BYTES;             // K(t)
-    char* knext = kbuf + ((t + 1) & 1) * TILE_BYTES;    // K(t+1)
+    char* kt = kslot(t);                                // K(t)
+    char* knext = kslot(t + 1);                         // K(t+1)
     char* vtprev = vtbuf + ((t + 1) & 1) * TILE_BYTES;  // V^T(t-1)
     char* vtcur = vtbuf + (t & 1) * TILE_BYTES;         // V^T(t), written in phase 2t+1
     // ---- phase 2t
@@ -467,11 +515,10 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
       mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre, NoExtra{}, [] {});
       pre = false;
     } else {
-      if (t + 1 < T) x.ld.issue_k(t + 1, knext);
-      if (t < T) x.ld.issue_v(t, vbuf);
+      const int n_new = issue_step(t + 1);
       if (visible(t - 1)) softmax_phase<CAUSAL, F16, ALIBI>(w, (t - 1) * BN, x.Sk, x.off, x.c,
                                                                    x.alibi);
-      wait_copies();
+      wait_copies_but(n_new);
       pre = visible(t);
       if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
     }
@@ -483,7 +530,7 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
       if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
     } else {
       // V(t) -> V^T(t) between the MFMAs (V(t) landed before the mid barrier)
-      VTranspose tr(w, vbuf, vtcur, x.wave);
+      VTranspose tr(w, vslot(t), vtcur, x.wave);
       const bool tr_now = t < T;
       mfma_phase<F16>(
           w, pf, kt, vtprev, visible(t), visible(t - 1), pre,
@@ -516,8 +563,8 @@ __device__ __forceinline__ bool state_finite(const Wave& w) {
 template <bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kbuf[2 * TILE_BYTES];   // K, double buffered
-  __shared__ __attribute__((aligned(1024))) char vbuf[TILE_BYTES];       // V as copied (bf16)
+  __shared__ __attribute__((aligned(1024))) char kbuf[3 * TILE_BYTES];   // K, three buffers
+  __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];   // V as copied (bf16), two
   __shared__ __attribute__((aligned(1024))) char vtbuf[2 * TILE_BYTES];  // V^T (fp16), double buffered
 
   Ctx x;
