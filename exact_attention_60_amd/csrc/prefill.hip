@@ -164,8 +164,7 @@ struct TileLoader {
 };
 
 // s_waitcnt through the intrinsic, so the compiler's own wait tracking knows
-// about it: vmcnt(0) (this wave's LDS copies have landed), and
-// vmcnt(0) lgkmcnt(0) (also its LDS writes are done).
+// about it: vmcnt(0) (this wave's LDS copies have landed).
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // all but this wave's last n copies have landed (n = 0, 4 or 8: the copies
 // of one tile step; vector memory loads complete in order)
@@ -177,7 +176,6 @@ __device__ __forceinline__ void wait_copies_but(int n) {
   else
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
-__device__ __forceinline__ void wait_copies_and_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
 // lgkmcnt(0) only: this wave's LDS writes are done
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without a hardware memory fence: every cross-wave LDS
@@ -454,14 +452,17 @@ struct Ctx {
 
 // The phased tile loop.  Phase 2t: group 0 runs the MFMA phase of tile t
 // (Q.K of t, P.V of t-1), group 1 the softmax of tile t-1; phase 2t+1:
-// group 0 the softmax of t, group 1 the MFMA phase of t.
-//  * Group 1 copies K(t+2) and V(t+1) (bf16) at the start of phase 2t (a
-//    softmax phase, no LDS reads), one tile step ahead, and before the mid
-//    barrier waits for the copies of the step before (K(t+1), V(t)), so from
-//    phase 2t+1 on those are visible to every wave.  K has three buffers:
-//    K(t+2) goes to the one last read in phase 2t-1 (K(t-1)'s); V has two
-//    staging buffers: V(t+1) goes to the one V(t-1) was transposed from in
-//    phase 2t-1.
+// group 0 the softmax of t, group 1 the MFMA phase of t.  The HBM copies are
+// issued at the start of the softmax phases, split between the groups so
+// that each side carries half of the issue time:
+//  * group 1 copies K(t+2) at the start of phase 2t, one tile step ahead, and
+//    before the mid barrier waits for K(t+1) (issued in phase 2t-2), so from
+//    phase 2t+1 on it is visible to every wave.  K has three buffers: K(t+2)
+//    goes to the one last read in phase 2t-1 (K(t-1)'s);
+//  * group 0 copies V(t+1) at the start of phase 2t+1 and waits for it at
+//    the end of its MFMA phase 2t+2, before the mid barrier of tile t+1.  V
+//    has two staging buffers: V(t+1) goes to the one V(t-1) was transposed
+//    from in phase 2t-1.
 //  * In phase 2t+1 each group-1 wave transposes the 16 rows of V(t) it
 //    copied into the V^T buffer last read in phase 2t-1 (V^T(t-2)'s),
 //    converting to fp16, with the instructions spread between the MFMAs of
@@ -485,24 +486,25 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   Prefetch pf;
   auto kslot = [&](int t) { return kbuf + (t % 3) * TILE_BYTES; };
   auto vslot = [&](int t) { return vbuf + (t & 1) * TILE_BYTES; };
-  // copies of tile step t: K(t+1) and V(t); returns how many were issued
-  auto issue_step = [&](int t) {
-    int n = 0;
-    if (t + 1 < T) {
-      x.ld.issue_k(t + 1, kslot(t + 1));
-      n += 4;
-    }
-    if (t < T) {
-      x.ld.issue_v(t, vslot(t));
-      n += 4;
-    }
-    return n;
+  // copy of K(t) (group 1) or V(t) (group 0); returns how many copies were issued
+  auto issue_kt = [&](int t) {
+    if (t >= T) return 0;
+    x.ld.issue_k(t, kslot(t));
+    return 4;
   };
-  if (T > 0 && !g0) {
-    x.ld.issue_k(0, kslot(0));
-    wait_copies_but(issue_step(0));
+  auto issue_vt = [&](int t) {
+    if (t >= T) return 0;
+    x.ld.issue_v(t, vslot(t));
+    return 4;
+  };
+  if (g0) {
+    issue_vt(0);
+    wait_copies();
+  } else if (T > 0) {
+    issue_kt(0);
+    wait_copies_but(issue_kt(1));
   }
-  wait_copies_and_lds();
+  wait_lds();
   barrier();
   bool pre = false;   // this wave holds the first operands of its next MFMA phase
   for (int t = 0; t <= T; ++t) {
@@ -514,17 +516,19 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
     if (g0) {
       mfma_phase<F16>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre, NoExtra{}, [] {});
       pre = false;
+      wait_copies();                                    // V(t), copied in phase 2t-1
     } else {
-      const int n_new = issue_step(t + 1);
+      const int n_new = issue_kt(t + 2);
       if (visible(t - 1)) softmax_phase<CAUSAL, F16, ALIBI>(w, (t - 1) * BN, x.Sk, x.off, x.c,
                                                                    x.alibi);
       wait_copies_but(n_new);
       pre = visible(t);
       if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
     }
-    barrier();   // K(t+1), V(t) copies have landed (group 1 waited for them)
+    barrier();   // K(t+1) (group 1) and V(t) (group 0) copies have landed
     // ---- phase 2t+1
     if (g0) {
+      issue_vt(t + 1);
       if (visible(t)) softmax_phase<CAUSAL, F16, ALIBI>(w, t * BN, x.Sk, x.off, x.c, x.alibi);
       pre = visible(t + 1);
       if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
