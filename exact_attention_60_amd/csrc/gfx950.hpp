@@ -159,6 +159,29 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
   return pack_f16(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
 
+// One 1 KB asynchronous copy (buffer_load_dwordx4 ... lds): lane i's 16 bytes
+// at byte offset voff of the buffer land at LDS byte lds + 16*i.  Written as
+// an asm statement so that the compiler does not see an LDS write in flight:
+// it would otherwise wait for every outstanding copy before the wave's next
+// LDS read, and a copy could not stay in flight across the wave's operand
+// reads.  The callers order the copies with explicit vmcnt waits and
+// barriers (vector memory loads complete in order).  M0 holds the LDS
+// address (one wait state before the copy reads it).
+__device__ __forceinline__ void lds_copy16(const u32x4& rsrc, uint32_t voff, const char* lds) {
+  const uint32_t m =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const ATTN_LDS char*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Buffer descriptor: base address, no stride, nrec bytes, raw dword access.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* p, uint32_t nrec) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nrec, 0x00020000u};
+}
+
 // p must point into __shared__ memory (8-byte aligned).
 __device__ __forceinline__ bf16x4 lds_read_tr(const void* p) {
   i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p));

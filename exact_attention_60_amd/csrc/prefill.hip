@@ -103,28 +103,6 @@ __device__ __forceinline__ int spread_groups(int i, int G, int n_groups) {
   return (x + 8 * (j / G)) * G + (j - (j / G) * G);
 }
 
-// One 1 KB asynchronous copy (buffer_load_dwordx4 ... lds): lane i's 16 bytes
-// at byte offset voff of the buffer land at LDS byte lds + 16*i.  Written as
-// an asm statement so that the compiler does not see an LDS write in flight:
-// it would otherwise wait for every outstanding copy before the wave's next
-// LDS read, and a copy could not stay in flight across the wave's operand
-// reads.  The loop orders the copies with explicit waits and barriers.  M0
-// holds the LDS address (one wait state before the copy reads it).
-__device__ __forceinline__ void lds_copy16(const u32x4& rsrc, uint32_t voff, const char* lds) {
-  const uint32_t m =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const ATTN_LDS char*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-
-// Buffer descriptor: base address, no stride, nrec bytes, raw dword access.
-__device__ __forceinline__ u32x4 buffer_rsrc(const void* p, uint32_t nrec) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nrec, 0x00020000u};
-}
-
 // Asynchronous copy of a wave's 16 rows of one K or V tile from HBM into LDS.
 // Each instruction moves 1 KB: lane i lands at byte 16*i, i.e. row +i/16,
 // physical chunk i%16, so it fetches the logical chunk that the swizzle puts

@@ -149,16 +149,17 @@ struct Loader {
   // latency.  Their completion is ordered explicitly instead: vmcnt waits
   // and the workgroup barrier before any wave reads a slot.  The instruction
   // has no register results (its data goes to LDS); M0 holds the LDS
-  // address.
+  // address, written one wait state before the copy reads it (the compiler's
+  // hazard tracking does not look inside the asm statement).
   __device__ __forceinline__ void issue_one(int tile, int slot, int which) const {
     const uint32_t base = (uint32_t)tile * tile_bytes;
     const int j = which & 1;
     const uint32_t m0 = (which < 2 ? lds_k : lds_v) + (uint32_t)(slot * TB + 4 * j * 256);
     if (which < 2)
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    : : "s"(m0), "v"(voff[j] + base), "s"(rk) : "memory", "m0");
     else
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    : : "s"(m0), "v"(voff[j] + base), "s"(rv) : "memory", "m0");
   }
   __device__ __forceinline__ void issue(int tile, int slot) const {
