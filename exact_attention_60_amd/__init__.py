@@ -42,7 +42,8 @@ STATUS = {
 }
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_fwd_alibi", "attn_fwd_varlen", "attn_fwd_fp8",
+EXPORTS = ("attn_fwd", "attn_fwd_rounded", "attn_prep_v_bytes", "attn_prep_v", "attn_fwd_prepped",
+           "attn_fwd_alibi", "attn_fwd_varlen", "attn_fwd_fp8",
            "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_rounded", "attn_decode_paged_append", "attn_decode_paged_noalloc",
            "attn_bwd_workspace_bytes",
@@ -70,6 +71,13 @@ def library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd_rounded.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
         lib.attn_fwd_rounded.restype = i
+        lib.attn_prep_v_bytes.argtypes = [i, i, i, i, i]
+        lib.attn_prep_v_bytes.restype = sz
+        lib.attn_prep_v.argtypes = [vp, i, i, i, i, i, i, vp, sz, vp]
+        lib.attn_prep_v.restype = i
+        lib.attn_fwd_prepped.argtypes = [vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, i, i, i,
+                                         vp]
+        lib.attn_fwd_prepped.restype = i
         lib.attn_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
         lib.attn_fwd_alibi.restype = i
         lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
@@ -187,13 +195,29 @@ def _rounding_code(rounding: str) -> int:
         raise ValueError(f"rounding must be one of {sorted(ROUNDING)}, got {rounding!r}") from None
 
 
+# query tiles (256 rows) per K/V head from which attn_fwd prepares V by default
+PREPARE_V_MIN_TILES = 32
+
+
+def attn_prep_v_bytes(B: int, Hq: int, Hkv: int, Sk: int, d: int) -> int:
+    return library().attn_prep_v_bytes(B, Hq, Hkv, Sk, d)
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
              layout: str = "bshd", rounding: str = "rtne", out=None, lse=None, stream=None,
-             alibi_slopes=None):
+             alibi_slopes=None, prepare_v: bool | None = None, vt=None):
     """Fused exact attention forward.  q: [B, Sq, Hq, d] (bshd) or
     [B, Hq, Sq, d] (bhsd); k, v likewise with Hkv heads and Sk keys.  The head
     dim d is 128, 64 or 256 (64 and 256 without ALiBi).
     alibi_slopes: optional fp32 GPU tensor [Hq] (ALiBi bias, attn_fwd_alibi).
+    prepare_v: where the shape uses prepared fp16 V^T tiles
+    (attn_prep_v_bytes > 0, no ALiBi), True runs attn_prep_v into `vt` (a
+    uint8 GPU tensor of at least that many bytes, allocated here if None) and
+    then attn_fwd_prepped; False runs the single-call attn_fwd /
+    attn_fwd_rounded.  None (default) prepares when each K/V head serves at
+    least PREPARE_V_MIN_TILES query tiles of 256 rows (Sq * Hq / Hkv), where
+    the one conversion per head costs less than the per-workgroup ones it
+    replaces (measured: a net loss at 16 tiles, a gain at 128).
     Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -226,6 +250,18 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
         st = library().attn_fwd_alibi(*args[:5], alibi_slopes.data_ptr(), *args[5:], rnd,
                                       _stream_ptr(stream))
         where = "attn_fwd_alibi"
+    elif (prepare_v if prepare_v is not None else
+          (Sq * (Hq // Hkv) + 255) // 256 >= PREPARE_V_MIN_TILES) and \
+            (nvt := library().attn_prep_v_bytes(B, Hq, Hkv, Sk, d)) > 0:
+        vt = _workspace(vt, nvt, q.device)
+        nb = vt.numel() * vt.element_size()
+        st = library().attn_prep_v(v.data_ptr(), B, Hq, Hkv, Sk, d, lay, vt.data_ptr(), nb,
+                                   _stream_ptr(stream))
+        where = "attn_prep_v"
+        if st == 0:
+            st = library().attn_fwd_prepped(*args[:3], vt.data_ptr(), nb, *args[3:], rnd,
+                                            _stream_ptr(stream))
+            where = "attn_fwd_prepped"
     elif rnd == ROUNDING["rtne"]:
         st, where = library().attn_fwd(*args, _stream_ptr(stream)), "attn_fwd"
     else:
@@ -527,5 +563,5 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
 
 __all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append", "attn_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
            "attn_decode_workspace_bytes", "attn_status_string",
-           "attn_version", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
+           "attn_version", "attn_prep_v_bytes", "PREPARE_V_MIN_TILES", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

@@ -66,9 +66,16 @@ const char* attn_status_string(int status) {
   }
 }
 
+// whether the dense d = 128 forward runs the GQA kernel (groups of 4k query
+// heads share each K/V tile; it converts V itself)
+static bool uses_pipe(int Hq, int Hkv, int d, bool alibi) {
+  return d == attn::kHeadDim && !alibi && (Hq / Hkv) % 4 == 0;
+}
+
 static int fwd_call(const void* q, const void* k, const void* v, void* o, float* lse,
                     const float* alibi_slopes, int B, int Hq, int Hkv, int Sq, int Sk, int d,
-                    float scale, int causal, int layout, int rounding, void* stream) {
+                    float scale, int causal, int layout, int rounding, void* stream,
+                    const void* vt = nullptr) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   // head dim 128 (every variant), or 64 and 256 (dense, no ALiBi)
@@ -99,7 +106,7 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   a.group = Hq / Hkv;
   // d = 128 without ALiBi and a GQA group that is a multiple of 4: the
   // kernel whose workgroups share each K/V tile among 4 query heads
-  const bool pipe = d == attn::kHeadDim && !alibi_slopes && (Hq / Hkv) % 4 == 0;
+  const bool pipe = uses_pipe(Hq, Hkv, d, alibi_slopes != nullptr);
   const int rows_per_block = hd64   ? attn::prefill_hd_rows_per_block()
                              : pipe ? attn::kPrefillPipeRows
                                     : attn::kPrefillBM;
@@ -111,6 +118,8 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
   a.alibi = alibi_slopes;
+  a.vt = (!hd64 && !pipe) ? static_cast<const uint8_t*>(vt) : nullptr;
+  a.n_kt = (Sk + attn::kPrefillBN - 1) / attn::kPrefillBN;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
@@ -166,6 +175,59 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   if (ds != ATTN_OK) return ds;
   const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_prep_v_bytes(int B, int Hq, int Hkv, int Sk, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0 || d != attn::kHeadDim ||
+      uses_pipe(Hq, Hkv, d, false))
+    return 0;
+  const int64_t n_kt = (Sk + attn::kPrefillBN - 1) / attn::kPrefillBN;
+  return (size_t)B * Hkv * n_kt * attn::kVtTileBytes;
+}
+
+int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout, void* vt,
+                size_t vt_bytes, void* stream) {
+  if (!v) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (layout != ATTN_BSHD && layout != ATTN_BHSD) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_prep_v_bytes(B, Hq, Hkv, Sk, d);
+  if (need == 0) return ATTN_OK;                     // this shape does not use the tiles
+  if (!vt || vt_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(v) || !aligned16(vt)) return ATTN_ERR_ALIGN;
+  const int64_t D = d;
+  attn::PrepVArgs a;
+  a.v = static_cast<const __bf16*>(v);
+  a.vt = static_cast<uint8_t*>(vt);
+  if (layout == ATTN_BSHD) {
+    a.k_sb = (int64_t)Sk * Hkv * D; a.k_sh = D; a.k_ss = (int64_t)Hkv * D;
+  } else {
+    a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
+  }
+  a.B = B; a.Hkv = Hkv; a.Sk = Sk;
+  a.n_kt = (Sk + attn::kPrefillBN - 1) / attn::kPrefillBN;
+  if ((int64_t)B * Hkv * a.n_kt > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)a.n_kt * attn::kVtTileBytes > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
+  int cus = 0;
+  const int ds = current_device_cus(&cus);
+  if (ds != ATTN_OK) return ds;
+  const hipError_t e = attn::launch_prep_v(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd_prepped(const void* q, const void* k, const void* v, const void* vt,
+                     size_t vt_bytes, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk,
+                     int d, float scale, int causal, int layout, int rounding, void* stream) {
+  const size_t need = attn_prep_v_bytes(B, Hq, Hkv, Sk, d);
+  if (need != 0) {
+    if (!vt) return ATTN_ERR_NULL;
+    if (vt_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(vt)) return ATTN_ERR_ALIGN;
+    if ((int64_t)((Sk + attn::kPrefillBN - 1) / attn::kPrefillBN) * attn::kVtTileBytes >
+        (int64_t)UINT32_MAX)
+      return ATTN_ERR_SHAPE;
+  }
+  return fwd_call(q, k, v, o, lse, nullptr, B, Hq, Hkv, Sq, Sk, d, scale, causal, layout,
+                  rounding, stream, need != 0 ? vt : nullptr);
 }
 
 int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse, int B,

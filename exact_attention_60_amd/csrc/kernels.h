@@ -39,9 +39,29 @@ struct PrefillArgs {
   // ALiBi slopes [Hq] (null: no bias): -slope * |i + Sk - Sq - j| is added to
   // the scaled scores of query head h
   const float* alibi;
+  // V as fp16 V^T tiles written by launch_prep_v (null: the kernel converts
+  // and transposes each V tile itself).  Dense batches without ALiBi only.
+  const uint8_t* vt = nullptr;
+  int n_kt = 0;              // ceil(Sk / kPrefillBN): tiles per (batch, kv head)
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
+
+// V of a dense batch as fp16 V^T tiles for the d = 128 prefill kernel: tile t
+// of (batch b, kv head h) -- keys 64t .. 64t+63 (zeros past Sk), all 128 d --
+// is kVtTileBytes bytes at vt + ((b * Hkv + h) * n_kt + t) * kVtTileBytes,
+// laid out exactly as the kernel's LDS V^T tile (row d of 128 bytes holds the
+// 64 keys in MFMA k-slot order, 16-byte chunks swizzled), so that the kernel
+// copies it into LDS as it is.  Values are rounded to fp16 (nearest even);
+// |v| >= 65520 becomes +-inf, which the kernel meets with its bf16 redo.
+constexpr int kVtTileBytes = kPrefillBN * kHeadDim * 2;
+struct PrepVArgs {
+  const __bf16* v;
+  uint8_t* vt;
+  int64_t k_sb, k_sh, k_ss;  // element strides of batch, head, sequence of v
+  int B, Hkv, Sk, n_kt;
+};
+hipError_t launch_prep_v(const PrepVArgs& a, hipStream_t stream);
 
 // Dense d = 128 forward without ALiBi for GQA groups that are a multiple of
 // 4, pipelined inside each wave: one wave per SIMD, the 4 waves of a

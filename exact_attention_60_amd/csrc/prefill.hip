@@ -109,9 +109,11 @@ __device__ __forceinline__ int spread_groups(int i, int G, int n_groups) {
 // there.  Bytes past the buffer's end (nrec) read as zero.
 struct TileLoader {
   u32x4 rk, rv;
+  u32x4 rvt;              // prepared fp16 V^T tiles of this (batch, kv head)
   uint32_t voff[4];       // per-lane byte offset, rows 4*j + lane/16 of the wave's 16
   uint32_t tile_bytes;    // BN * row stride in bytes
   int row0;               // first tile row this wave copies
+  uint32_t vt_off;        // this wave's quarter of a prepared tile, lane's 16 bytes
 
   __device__ void init(const __bf16* kp, const __bf16* vp, int64_t k_ss, int Sk, int wave,
                        int lane) {
@@ -138,6 +140,18 @@ struct TileLoader {
     const uint32_t base = (uint32_t)tile * tile_bytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) lds_copy16(rv, voff[j] + base, vt + (row0 + 4 * j) * 256);
+  }
+  // prepared tiles: the byte layout in HBM is the LDS one, so each wave
+  // copies its 4 KB quarter of the 16 KB tile as it is
+  __device__ void init_vt(const uint8_t* vtp, int n_kt, int wave, int lane) {
+    rvt = buffer_rsrc(vtp, (uint32_t)n_kt * (uint32_t)kVtTileBytes);
+    vt_off = (uint32_t)(wave & 3) * 4096u + (uint32_t)lane * 16u;
+  }
+  __device__ __forceinline__ void issue_vt(int tile, char* dst) const {
+    const uint32_t base = (uint32_t)tile * (uint32_t)kVtTileBytes + vt_off;
+    char* d = dst + (vt_off & ~1023u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_copy16(rvt, base + 1024u * j, d + 1024 * j);
   }
 };
 
@@ -533,6 +547,81 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   }
 }
 
+// The phased tile loop with prepared fp16 V^T tiles (no transpose): the same
+// phases, and both groups run the plain MFMA phase.
+//  * group 1 copies K(t+2) at the start of phase 2t and waits for K(t+1)
+//    before the mid barrier, as above;
+//  * group 0 copies V^T(t+1) at the start of phase 2t+1 and waits for V^T(t)
+//    (copied in phase 2t-1) at its end, so that V^T(t) is visible from phase
+//    2t+2, where it is first read.  V^T has three buffers: V^T(t+1) goes to
+//    V^T(t-2)'s, last read in phase 2t-1.
+// The three V^T buffers take the place of the V staging buffers and the
+// first V^T buffer of the transposing loop (vtbuf3 = vbuf).
+template <bool CAUSAL>
+__device__ __forceinline__ void tile_loop_pre(Wave& w, const Ctx& x, char* kbuf, char* vtbuf3) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) w.oacc[db] = f32x16{};
+  w.m_use = -INFINITY;
+  w.lsum = 0.f;
+  const int T = x.n_tiles;
+  auto visible = [&](int t) {
+    return t >= 0 && t < T && w.first <= w.last && (!CAUSAL || t * BN <= w.last + x.off);
+  };
+  const bool g0 = x.group == 0;
+  Prefetch pf;
+  auto kslot = [&](int t) { return kbuf + (t % 3) * TILE_BYTES; };
+  auto vtslot = [&](int t) { return vtbuf3 + (t % 3) * TILE_BYTES; };
+  auto issue_kt = [&](int t) {
+    if (t >= T) return 0;
+    x.ld.issue_k(t, kslot(t));
+    return 4;
+  };
+  auto issue_vtt = [&](int t) {
+    if (t >= T) return 0;
+    x.ld.issue_vt(t, vtslot(t));
+    return 4;
+  };
+  if (g0) {
+    issue_vtt(0);
+  } else if (T > 0) {
+    issue_kt(0);
+    wait_copies_but(issue_kt(1));
+  }
+  wait_lds();
+  barrier();
+  bool pre = false;   // this wave holds the first operands of its next MFMA phase
+  for (int t = 0; t <= T; ++t) {
+    char* kt = kslot(t);                                // K(t)
+    char* knext = kslot(t + 1);                         // K(t+1)
+    char* vtprev = vtslot(t + 2);                       // V^T(t-1): slot (t-1) % 3
+    // ---- phase 2t
+    if (g0) {
+      mfma_phase<true>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre, NoExtra{}, [] {});
+      pre = false;
+    } else {
+      const int n_new = issue_kt(t + 2);
+      if (visible(t - 1)) softmax_phase<CAUSAL, true, false>(w, (t - 1) * BN, x.Sk, x.off, x.c,
+                                                                    0.f);
+      wait_copies_but(n_new);
+      pre = visible(t);
+      if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
+    }
+    barrier();   // K(t+1) has landed (group 1 waited for it)
+    // ---- phase 2t+1
+    if (g0) {
+      const int n_new = issue_vtt(t + 1);
+      if (visible(t)) softmax_phase<CAUSAL, true, false>(w, t * BN, x.Sk, x.off, x.c, 0.f);
+      pre = visible(t + 1);
+      if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
+      wait_copies_but(n_new);                           // V^T(t), copied in phase 2t-1
+    } else {
+      mfma_phase<true>(w, pf, kt, vtprev, visible(t), visible(t - 1), pre, NoExtra{}, [] {});
+      pre = false;
+    }
+    barrier();
+  }
+}
+
 __device__ __forceinline__ bool state_finite(const Wave& w) {
   bool ok = __builtin_isfinite(w.lsum);
 #pragma unroll
@@ -542,12 +631,15 @@ __device__ __forceinline__ bool state_finite(const Wave& w) {
   return ok;
 }
 
-template <bool CAUSAL, bool ALIBI>
+template <bool CAUSAL, bool ALIBI, bool PRE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kbuf[3 * TILE_BYTES];   // K, three buffers
-  __shared__ __attribute__((aligned(1024))) char vbuf[2 * TILE_BYTES];   // V as copied (bf16), two
-  __shared__ __attribute__((aligned(1024))) char vtbuf[2 * TILE_BYTES];  // V^T (fp16), double buffered
+  // K (three buffers), V as copied (bf16, two), V^T (fp16, two); with
+  // prepared V^T tiles, their three buffers start at vbuf
+  __shared__ __attribute__((aligned(1024))) char lds[7 * TILE_BYTES];
+  char* const kbuf = lds;
+  char* const vbuf = lds + 3 * TILE_BYTES;
+  char* const vtbuf = lds + 5 * TILE_BYTES;
 
   Ctx x;
   const int tid = threadIdx.x;
@@ -616,6 +708,7 @@ void prefill_kernel(PrefillArgs a) {
   w.first = q0 + 32 * rb;
   w.last = min(w.first + 31, Sq - 1);
   x.ld.init(kp, vp, a.k_ss, Sk, x.wave, lane);
+  if (PRE) x.ld.init_vt(a.vt + (int64_t)(b * a.Hkv + hk) * a.n_kt * kVtTileBytes, a.n_kt, x.wave, lane);
 
   // ---- per-lane LDS offsets
   // K operand (A of S^T): row kb*32 + l32, chunk 2*ks + hi
@@ -656,7 +749,10 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  tile_loop<CAUSAL, true, ALIBI>(w, x, kbuf, vbuf, vtbuf);
+  if (PRE)
+    tile_loop_pre<CAUSAL>(w, x, kbuf, vbuf);
+  else
+    tile_loop<CAUSAL, true, ALIBI>(w, x, kbuf, vbuf, vtbuf);
   // A V value beyond the fp16 range (|v| >= 65520) or a non-finite input
   // shows up as a non-finite accumulator: redo this workgroup with bf16
   // probabilities and bf16 V, which covers the whole bf16 range.
@@ -699,23 +795,81 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// One prepared V^T tile per workgroup of 256 threads: the 64 x 128 bf16 V
+// tile (keys past Sk read as zero) is staged in LDS row by row, then each
+// thread builds 16-byte chunks of V^T rows -- chunk c of row d holds the keys
+// of k-step c/2 for lane half c%2 (see vt_off), as fp16 rounded to nearest
+// even -- and writes them at their swizzled place, 8 threads per 128-byte
+// row.  HBM-bound: 16 KB read and 16 KB written per tile.
+__global__ __launch_bounds__(256) void prep_v_kernel(PrepVArgs a) {
+  constexpr int RS = D + 8;                      // padded LDS row (bf16 elements)
+  __shared__ __attribute__((aligned(16))) __bf16 tile[BN * RS];
+  const int64_t id = blockIdx.x;
+  const int t = (int)(id % a.n_kt);
+  const int64_t bh = id / a.n_kt;
+  const int h = (int)(bh % a.Hkv);
+  const int b = (int)(bh / a.Hkv);
+  const __bf16* vp = a.v + b * a.k_sb + h * a.k_sh;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int r = 16 * pass + (tid >> 4), c = tid & 15;
+    const int key = t * BN + r;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (key < a.Sk) val = *(const u32x4*)(vp + (int64_t)key * a.k_ss + 8 * c);
+    *(u32x4*)(tile + r * RS + 8 * c) = val;
+  }
+  __syncthreads();
+  uint8_t* out = a.vt + id * kVtTileBytes;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int idx = 256 * pass + tid;
+    const int d = idx >> 3, ch = idx & 7;
+    const int k0 = 16 * (ch >> 1) + 4 * (ch & 1);
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (float)tile[(k0 + (j < 4 ? j : j + 4)) * RS + d];
+    const u32x4 y = u32x4{pack_f16(f[0], f[1]), pack_f16(f[2], f[3]), pack_f16(f[4], f[5]),
+                          pack_f16(f[6], f[7])};
+    *(u32x4*)(out + vt_off(d, ch)) = y;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.Hq * a.n_qt;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.alibi) {
+  if (a.vt) {
+    // prepared V^T tiles: dense batches without ALiBi
+    if (a.alibi || a.cu_q || a.n_kt != (a.Sk + BN - 1) / BN) return hipErrorInvalidValue;
     if (causal)
-      hipLaunchKernelGGL((prefill_kernel<true, true>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<true, false, true>), dim3((unsigned)grid), dim3(NT), 0,
+                         stream, a);
     else
-      hipLaunchKernelGGL((prefill_kernel<false, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                         a);
+      hipLaunchKernelGGL((prefill_kernel<false, false, true>), dim3((unsigned)grid), dim3(NT), 0,
+                         stream, a);
+  } else if (a.alibi) {
+    if (causal)
+      hipLaunchKernelGGL((prefill_kernel<true, true, false>), dim3((unsigned)grid), dim3(NT), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<false, true, false>), dim3((unsigned)grid), dim3(NT), 0,
+                         stream, a);
   } else if (causal) {
-    hipLaunchKernelGGL((prefill_kernel<true, false>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<true, false, false>), dim3((unsigned)grid), dim3(NT), 0,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       a);
+    hipLaunchKernelGGL((prefill_kernel<false, false, false>), dim3((unsigned)grid), dim3(NT), 0,
+                       stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_v(const PrepVArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.B * a.Hkv * a.n_kt;
+  if (grid <= 0 || grid > 0x7fffffff || a.n_kt != (a.Sk + BN - 1) / BN) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_v_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

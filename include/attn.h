@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 10
+#define ATTN_VERSION 11
 
 typedef enum {
   ATTN_OK = 0,
@@ -141,6 +141,45 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                      int layout, int rounding, void* stream);
+
+/*
+ * attn_prep_v_bytes / attn_prep_v / attn_fwd_prepped - attn_fwd_rounded in
+ * two steps, with V prepared once as the P.V product reads it.  Where each
+ * operand lives is what sets the speed of the kernels in "MoonMath AI
+ * open-sources a HIP attention kernel for AMD MI300X that beats AITER v3"
+ * (data-placement paragraph); here the fp16 V^T tiles the matrix cores read
+ * are written once per K/V head, instead of being converted and transposed
+ * in LDS by every query-tile workgroup.  The result is bit-identical to
+ * attn_fwd_rounded on the same inputs.
+ *
+ * attn_prep_v_bytes(B, Hq, Hkv, Sk, d): bytes of the prepared tiles, or 0
+ *   where the forward does not use them (d != 128, or Hq / Hkv a multiple of
+ *   4, whose kernel shares each V tile among four query heads itself); also
+ *   0 for invalid sizes.  B * Hkv * ceil(Sk / 64) * 16384 otherwise.
+ * attn_prep_v(v, B, Hq, Hkv, Sk, d, layout, vt, vt_bytes, stream): writes
+ *   the tiles of v (bf16, attn_fwd's k/v layout) into vt (device memory,
+ *   16-byte aligned, at least attn_prep_v_bytes; owned by the caller).  Each
+ *   value is rounded to fp16 (nearest even); |v| >= 65520 becomes +-inf,
+ *   which attn_fwd_prepped detects and answers with the bf16 path, as
+ *   attn_fwd does.  Returns ATTN_OK without work where the size is 0;
+ *   ATTN_ERR_WORKSPACE if vt is NULL or smaller, ATTN_ERR_ALIGN,
+ *   ATTN_ERR_SHAPE (ceil(Sk / 64) * 16384 must stay below 2^32),
+ *   ATTN_ERR_UNSUPPORTED for another layout.
+ * attn_fwd_prepped(q, k, v, vt, vt_bytes, o, lse, ...): attn_fwd_rounded,
+ *   reading V^T from vt, which must hold attn_prep_v's output for this v
+ *   with the same B, Hkv, Sk, layout (not checked; v itself is still read
+ *   by the bf16 path).  vt is not written; the call may be repeated with
+ *   other q on the same prepared tiles.  Where attn_prep_v_bytes is 0, vt
+ *   is ignored.  Otherwise vt NULL returns ATTN_ERR_NULL, too small
+ *   ATTN_ERR_WORKSPACE, misaligned ATTN_ERR_ALIGN.  Other arguments,
+ *   limits and statuses as for attn_fwd_rounded.
+ */
+size_t attn_prep_v_bytes(int B, int Hq, int Hkv, int Sk, int d);
+int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout, void* vt,
+                size_t vt_bytes, void* stream);
+int attn_fwd_prepped(const void* q, const void* k, const void* v, const void* vt,
+                     size_t vt_bytes, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk,
+                     int d, float scale, int causal, int layout, int rounding, void* stream);
 
 /*
  * attn_fwd_alibi - attn_fwd_rounded with an ALiBi linear position bias: for

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 10
+    assert ea.attn_version() == 11
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -74,6 +74,78 @@ def test_fwd_argument_errors(kw, code):
     assert fwd(**kw) == code
     for r in (0, 1, 2):                      # the rounded variant checks the same
         assert fwd(rounding=r, **kw) == code
+
+
+def test_prep_v_bytes():
+    tile = 64 * 128 * 2
+    # B * Hkv * ceil(Sk / 64) tiles of 16 KB where the prefill kernel reads them
+    assert ea.attn_prep_v_bytes(2, 4, 2, 100, 128) == 2 * 2 * 2 * tile
+    assert ea.attn_prep_v_bytes(4, 32, 32, 4096, 128) == 4 * 32 * 64 * tile
+    assert ea.attn_prep_v_bytes(1, 6, 3, 64, 128) == 3 * 1 * tile
+    assert ea.attn_prep_v_bytes(1, 1, 1, 65, 128) == 2 * tile
+    # none where the forward does not use them: groups of 4k heads, other d
+    assert ea.attn_prep_v_bytes(2, 8, 2, 100, 128) == 0
+    assert ea.attn_prep_v_bytes(2, 32, 8, 100, 128) == 0
+    assert ea.attn_prep_v_bytes(2, 4, 4, 100, 64) == 0
+    assert ea.attn_prep_v_bytes(2, 4, 4, 100, 256) == 0
+    # invalid sizes
+    assert ea.attn_prep_v_bytes(0, 4, 4, 100, 128) == 0
+    assert ea.attn_prep_v_bytes(1, 3, 2, 100, 128) == 0
+    assert ea.attn_prep_v_bytes(1, 4, 4, 0, 128) == 0
+
+
+def prep(**kw):
+    a = dict(v=P, B=1, Hq=4, Hkv=2, Sk=8, d=128, layout=0, vt=P, vtb=1 << 40, stream=None)
+    a.update(kw)
+    return ea.library().attn_prep_v(a["v"], a["B"], a["Hq"], a["Hkv"], a["Sk"], a["d"],
+                                    a["layout"], a["vt"], a["vtb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), -1), (dict(B=0), -2), (dict(Hq=3, Hkv=2), -2), (dict(Sk=0), -2),
+    (dict(layout=2), -3), (dict(vt=None), -5), (dict(vtb=16384 * 2 - 1), -5),
+    (dict(v=P + 2), -4), (dict(vt=P + 8), -4),
+    (dict(Sk=(1 << 24) + 1), -2),                  # one head's tiles exceed 32-bit offsets
+])
+def test_prep_v_argument_errors(kw, code):
+    assert prep(**kw) == code
+
+
+def test_prep_v_without_tiles_is_a_no_op():
+    # shapes that do not use the tiles return at once (no device call)
+    assert prep(Hq=8, Hkv=2, vt=None, vtb=0) == 0
+    assert prep(d=64, vt=None, vtb=0) == 0
+
+
+def prepped(rounding=0, vt=P, vtb=1 << 62, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.1,
+             causal=0, layout=0, stream=None)
+    a.update(kw)
+    return ea.library().attn_fwd_prepped(
+        a["q"], a["k"], a["v"], vt, vtb, a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+        a["Sk"], a["d"], a["scale"], a["causal"], a["layout"], rounding, a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(vt=None), -1), (dict(vtb=16384 * 2 - 1), -5), (dict(vt=P + 8), -4),
+    (dict(Sk=(1 << 24) + 1, Hkv=4), -2),
+    # the tiles are ignored where the shape does not use them
+    (dict(vt=None, Hq=8, Hkv=2, scale=0.0), -3), (dict(vt=None, d=64, q=None), -1),
+])
+def test_fwd_prepped_argument_errors(kw, code):
+    assert prepped(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(B=0), -2), (dict(Hq=3, Hkv=2), -2),
+    (dict(d=96), -3), (dict(layout=2), -3), (dict(scale=float("nan")), -3), (dict(o=P + 2), -4),
+    (dict(Sk=(1 << 22) + 1, Hkv=2, Hq=2, layout=0), -2),
+])
+def test_fwd_prepped_checks_like_fwd(kw, code):
+    assert fwd(**kw) == code
+    for r in (0, 1, 2):
+        assert prepped(rounding=r, **kw) == code
+    assert prepped(rounding=3) == -3
 
 
 @pytest.mark.parametrize("r", [-1, 3, 100])

@@ -49,7 +49,7 @@ class StubLib:
         self.calls = []
 
     def __getattr__(self, name):
-        if name.startswith("attn_") and name.endswith("workspace_bytes"):
+        if name.startswith("attn_") and name.endswith("_bytes"):
             return lambda *a: 1 << 20
         def call(*a):
             self.calls.append(name)
@@ -91,10 +91,37 @@ BAD_OUT = [
 ]
 
 
+def good_vt():
+    return FakeT((1 << 20,), U8)
+
+
 def test_good_outputs_reach_the_library(lib):
     q, k, v = fwd_args()
+    ea.attn_fwd(q, k, v, stream=Stream(), vt=good_vt(), prepare_v=True, **good_fwd_out())
+    assert lib.calls == ["attn_prep_v", "attn_fwd_prepped"]
+    lib.calls.clear()
+    # default: 64 rows per head are one query tile, below the threshold
     ea.attn_fwd(q, k, v, stream=Stream(), **good_fwd_out())
     assert lib.calls == ["attn_fwd"]
+    lib.calls.clear()
+    ea.attn_fwd(q, k, v, stream=Stream(), prepare_v=False, **good_fwd_out())
+    assert lib.calls == ["attn_fwd"]
+    lib.calls.clear()
+    ea.attn_fwd(q, k, v, stream=Stream(), prepare_v=False, rounding="rtz", **good_fwd_out())
+    assert lib.calls == ["attn_fwd_rounded"]
+
+
+@pytest.mark.parametrize("bad", [
+    FakeT(((1 << 20) - 1,), U8),                 # too small
+    FakeT((1 << 20,), U8, device="cpu"),         # host memory
+    FakeT((1 << 20,), U8, device="cuda:1"),      # another GPU
+    FakeT((1 << 20,), U8, contiguous=False),
+])
+def test_fwd_rejects_bad_vt(lib, bad):
+    q, k, v = fwd_args()
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, k, v, stream=Stream(), vt=bad, prepare_v=True, **good_fwd_out())
+    assert lib.calls == []
 
 
 @pytest.mark.parametrize("name,bad", BAD_OUT)
