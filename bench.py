@@ -62,10 +62,24 @@ def sha256_of(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+# headers every kernel source includes: a change there changes the kernels too
+SHARED_HEADERS = ("gfx950.hpp", "kernels.h")
+
+
+def kernel_source_sha256(source):
+    """Hash of a kernel's source file and the shared headers it includes."""
+    h = hashlib.sha256()
+    for name in (source,) + SHARED_HEADERS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 PROFILE_DATA = os.path.join(ROOT, "profiles", "profile_data.json")
 CSRC = os.path.join(ROOT, "exact_attention_60_amd", "csrc")
 # short kernel name -> the source file it is built from
 KERNEL_SOURCES = {"prefill_kernel": "prefill.hip", "prefill_pipe_kernel": "prefill_pipe.hip",
+                  "prep_v_kernel": "prefill.hip",
                   "decode_partial_kernel": "decode.hip", "decode_merge_kernel": "decode.hip"}
 
 
@@ -77,7 +91,7 @@ def profile_entry(workload, kernel):
         return None
     try:
         ent = json.load(open(PROFILE_DATA))["entries"][f"{workload}::{kernel}"]
-        if ent["source_sha256"] != sha256_of(os.path.join(CSRC, KERNEL_SOURCES[kernel])):
+        if ent["source_sha256"] != kernel_source_sha256(KERNEL_SOURCES[kernel]):
             return None
         return ent
     except (KeyError, ValueError, TypeError):
@@ -349,8 +363,11 @@ def counters_run(gen, ea, torch, dev, to_dev):
         for _ in range(warm + calls):
             ea.attn_fwd(q, k, v, causal=p.causal, scale=p.scale, layout=lay, out=o, lse=lse)
         torch.cuda.synchronize()
+        kerns = [prefill_kernel_of(p)]
+        if ea.prepares_v(p.B, p.Hq, p.Hkv, p.Sq, p.Sk, 128):
+            kerns = ["prep_v_kernel"] + kerns      # the binding prepares V first
         seq.append({"workload": p.name, "warmup": warm, "calls": calls,
-                    "kernels": [prefill_kernel_of(p)], "flop": p.flops,
+                    "kernels": kerns, "flop": p.flops,
                     "algorithmic_bytes": prefill_bytes(p)})
         del q, k, v, o, lse
     d = gen.config5()
@@ -467,7 +484,7 @@ def summarize(prof_dir, out_dir=None):
             entries[f"{wl}::{kern}"] = {
                 "workload": wl, "kernel": kern, "kernel_name": trace[(wl, kern)][0]["name"],
                 "source": KERNEL_SOURCES[kern],
-                "source_sha256": sha256_of(os.path.join(CSRC, KERNEL_SOURCES[kern])),
+                "source_sha256": kernel_source_sha256(KERNEL_SOURCES[kern]),
                 "dispatches": len(durs), "avg_us": avg, "min_us": min(durs), "max_us": max(durs),
                 "read_bytes": rd, "write_bytes": wr, "hbm_bytes": rd + wr,
                 "algorithmic_bytes": ent["algorithmic_bytes"], "flop": ent["flop"],

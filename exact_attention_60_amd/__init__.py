@@ -203,6 +203,13 @@ def attn_prep_v_bytes(B: int, Hq: int, Hkv: int, Sk: int, d: int) -> int:
     return library().attn_prep_v_bytes(B, Hq, Hkv, Sk, d)
 
 
+def prepares_v(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int) -> bool:
+    """Whether attn_fwd (no ALiBi, prepare_v=None) runs attn_prep_v +
+    attn_fwd_prepped for this shape."""
+    return ((Sq * (Hq // Hkv) + 255) // 256 >= PREPARE_V_MIN_TILES and
+            attn_prep_v_bytes(B, Hq, Hkv, Sk, d) > 0)
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
              layout: str = "bshd", rounding: str = "rtne", out=None, lse=None, stream=None,
              alibi_slopes=None, prepare_v: bool | None = None, vt=None):
@@ -250,8 +257,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
         st = library().attn_fwd_alibi(*args[:5], alibi_slopes.data_ptr(), *args[5:], rnd,
                                       _stream_ptr(stream))
         where = "attn_fwd_alibi"
-    elif (prepare_v if prepare_v is not None else
-          (Sq * (Hq // Hkv) + 255) // 256 >= PREPARE_V_MIN_TILES) and \
+    elif (prepare_v if prepare_v is not None else prepares_v(B, Hq, Hkv, Sq, Sk, d)) and \
             (nvt := library().attn_prep_v_bytes(B, Hq, Hkv, Sk, d)) > 0:
         vt = _workspace(vt, nvt, q.device)
         nb = vt.numel() * vt.element_size()
@@ -563,5 +569,5 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
 
 __all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append", "attn_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
            "attn_decode_workspace_bytes", "attn_status_string",
-           "attn_version", "attn_prep_v_bytes", "PREPARE_V_MIN_TILES", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
+           "attn_version", "attn_prep_v_bytes", "prepares_v", "PREPARE_V_MIN_TILES", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]
