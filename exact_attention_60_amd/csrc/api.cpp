@@ -118,8 +118,9 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
   a.alibi = alibi_slopes;
-  a.vt = (!hd64 && !pipe) ? static_cast<const uint8_t*>(vt) : nullptr;
-  a.n_kt = (Sk + attn::kPrefillBN - 1) / attn::kPrefillBN;
+  const int tk = pipe ? attn::kPrefillPipeBN : attn::kPrefillBN;
+  a.vt = !hd64 ? static_cast<const uint8_t*>(vt) : nullptr;
+  a.n_kt = (Sk + tk - 1) / tk;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
@@ -177,12 +178,16 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// keys per prepared tile: that of the kernel attn_fwd runs for the shape
+static int prep_tile_keys(int Hq, int Hkv) {
+  return uses_pipe(Hq, Hkv, attn::kHeadDim, false) ? attn::kPrefillPipeBN : attn::kPrefillBN;
+}
+
 size_t attn_prep_v_bytes(int B, int Hq, int Hkv, int Sk, int d) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0 || d != attn::kHeadDim ||
-      uses_pipe(Hq, Hkv, d, false))
-    return 0;
-  const int64_t n_kt = (Sk + attn::kPrefillBN - 1) / attn::kPrefillBN;
-  return (size_t)B * Hkv * n_kt * attn::kVtTileBytes;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0 || d != attn::kHeadDim) return 0;
+  const int tk = prep_tile_keys(Hq, Hkv);
+  const int64_t n_kt = (Sk + tk - 1) / tk;
+  return (size_t)B * Hkv * n_kt * tk * attn::kHeadDim * 2;
 }
 
 int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout, void* vt,
@@ -204,9 +209,12 @@ int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout
     a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
   }
   a.B = B; a.Hkv = Hkv; a.Sk = Sk;
-  a.n_kt = (Sk + attn::kPrefillBN - 1) / attn::kPrefillBN;
+  a.tk = prep_tile_keys(Hq, Hkv);
+  a.n_kt = (Sk + a.tk - 1) / a.tk;
   if ((int64_t)B * Hkv * a.n_kt > INT32_MAX) return ATTN_ERR_SHAPE;
-  if ((int64_t)a.n_kt * attn::kVtTileBytes > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
+  // one head's tiles are addressed with 32-bit offsets (the same bytes at
+  // either tile size)
+  if ((int64_t)a.n_kt * a.tk * attn::kHeadDim * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
@@ -222,8 +230,8 @@ int attn_fwd_prepped(const void* q, const void* k, const void* v, const void* vt
     if (!vt) return ATTN_ERR_NULL;
     if (vt_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(vt)) return ATTN_ERR_ALIGN;
-    if ((int64_t)((Sk + attn::kPrefillBN - 1) / attn::kPrefillBN) * attn::kVtTileBytes >
-        (int64_t)UINT32_MAX)
+    const int tk = prep_tile_keys(Hq, Hkv);
+    if ((int64_t)((Sk + tk - 1) / tk) * tk * attn::kHeadDim * 2 > (int64_t)UINT32_MAX)
       return ATTN_ERR_SHAPE;
   }
   return fwd_call(q, k, v, o, lse, nullptr, B, Hq, Hkv, Sq, Sk, d, scale, causal, layout,

@@ -167,13 +167,16 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
 // reads.  The callers order the copies with explicit vmcnt waits and
 // barriers (vector memory loads complete in order).  M0 holds the LDS
 // address (one wait state before the copy reads it).
-__device__ __forceinline__ void lds_copy16(const u32x4& rsrc, uint32_t voff, const char* lds) {
-  const uint32_t m =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const ATTN_LDS char*)lds);
+__device__ __forceinline__ void lds_copy16_at(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(m), "v"(voff), "s"(rsrc)
                : "memory", "m0");
+}
+// the same with the LDS destination as a pointer into __shared__ memory
+__device__ __forceinline__ void lds_copy16(const u32x4& rsrc, uint32_t voff, const char* lds) {
+  lds_copy16_at(rsrc, voff, (uint32_t)(uintptr_t)(const ATTN_LDS char*)lds);
 }
 
 // Buffer descriptor: base address, no stride, nrec bytes, raw dword access.

@@ -40,9 +40,11 @@ struct PrefillArgs {
   // the scaled scores of query head h
   const float* alibi;
   // V as fp16 V^T tiles written by launch_prep_v (null: the kernel converts
-  // and transposes each V tile itself).  Dense batches without ALiBi only.
+  // and transposes each V tile itself).  Dense batches without ALiBi only;
+  // tiles of the kernel's own key count (kPrefillBN, or kPrefillPipeBN for
+  // the GQA kernel).
   const uint8_t* vt = nullptr;
-  int n_kt = 0;              // ceil(Sk / kPrefillBN): tiles per (batch, kv head)
+  int n_kt = 0;              // tiles per (batch, kv head)
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
@@ -54,12 +56,17 @@ hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream)
 // 64 keys in MFMA k-slot order, 16-byte chunks swizzled), so that the kernel
 // copies it into LDS as it is.  Values are rounded to fp16 (nearest even);
 // |v| >= 65520 becomes +-inf, which the kernel meets with its bf16 redo.
+// The GQA kernel's tiles (launch_prefill_pipe) hold kPrefillPipeBN keys:
+// row d of 64 bytes, 16-byte chunk (2kk + hi) ^ ((d >> 2) & 3).
 constexpr int kVtTileBytes = kPrefillBN * kHeadDim * 2;
+constexpr int kPrefillPipeBN = 32;
+constexpr int kVtPipeTileBytes = kPrefillPipeBN * kHeadDim * 2;
 struct PrepVArgs {
   const __bf16* v;
   uint8_t* vt;
   int64_t k_sb, k_sh, k_ss;  // element strides of batch, head, sequence of v
   int B, Hkv, Sk, n_kt;
+  int tk;                    // keys per tile: kPrefillBN or kPrefillPipeBN
 };
 hipError_t launch_prep_v(const PrepVArgs& a, hipStream_t stream);
 

@@ -795,15 +795,20 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// One prepared V^T tile per workgroup of 256 threads: the 64 x 128 bf16 V
-// tile (keys past Sk read as zero) is staged in LDS row by row, then each
-// thread builds 16-byte chunks of V^T rows -- chunk c of row d holds the keys
-// of k-step c/2 for lane half c%2 (see vt_off), as fp16 rounded to nearest
-// even -- and writes them at their swizzled place, 8 threads per 128-byte
-// row.  HBM-bound: 16 KB read and 16 KB written per tile.
+// One prepared V^T tile of TK keys per workgroup of 256 threads: the TK x 128
+// bf16 V tile (keys past Sk read as zero) is staged in LDS row by row, then
+// each thread builds 16-byte chunks of V^T rows -- chunk c of row d holds the
+// keys 16(c/2) + {4(c%2) .. +3, 8 + 4(c%2) .. +3}, the k-slots of k-step c/2
+// for lane half c%2, as fp16 rounded to nearest even -- and writes them at
+// their swizzled place: for TK = 64 the layout of this file's kernel (vt_off,
+// 128-byte rows), for TK = 32 that of the GQA kernel (64-byte rows, chunk
+// c ^ ((d >> 2) & 3)).  HBM-bound: TK * 256 bytes read and written per tile.
+template <int TK>
 __global__ __launch_bounds__(256) void prep_v_kernel(PrepVArgs a) {
   constexpr int RS = D + 8;                      // padded LDS row (bf16 elements)
-  __shared__ __attribute__((aligned(16))) __bf16 tile[BN * RS];
+  constexpr int CH = TK / 8;                     // 16-byte chunks per V^T row
+  constexpr int PASSES = TK / 16;                // 256 threads x 16 bytes per pass
+  __shared__ __attribute__((aligned(16))) __bf16 tile[TK * RS];
   const int64_t id = blockIdx.x;
   const int t = (int)(id % a.n_kt);
   const int64_t bh = id / a.n_kt;
@@ -812,26 +817,27 @@ __global__ __launch_bounds__(256) void prep_v_kernel(PrepVArgs a) {
   const __bf16* vp = a.v + b * a.k_sb + h * a.k_sh;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = 0; pass < PASSES; ++pass) {
     const int r = 16 * pass + (tid >> 4), c = tid & 15;
-    const int key = t * BN + r;
+    const int key = t * TK + r;
     u32x4 val = u32x4{0u, 0u, 0u, 0u};
     if (key < a.Sk) val = *(const u32x4*)(vp + (int64_t)key * a.k_ss + 8 * c);
     *(u32x4*)(tile + r * RS + 8 * c) = val;
   }
   __syncthreads();
-  uint8_t* out = a.vt + id * kVtTileBytes;
+  uint8_t* out = a.vt + id * (TK * D * 2);
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = 0; pass < PASSES; ++pass) {
     const int idx = 256 * pass + tid;
-    const int d = idx >> 3, ch = idx & 7;
+    const int d = idx / CH, ch = idx % CH;
     const int k0 = 16 * (ch >> 1) + 4 * (ch & 1);
     float f[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) f[j] = (float)tile[(k0 + (j < 4 ? j : j + 4)) * RS + d];
     const u32x4 y = u32x4{pack_f16(f[0], f[1]), pack_f16(f[2], f[3]), pack_f16(f[4], f[5]),
                           pack_f16(f[6], f[7])};
-    *(u32x4*)(out + vt_off(d, ch)) = y;
+    const int off = TK == 64 ? vt_off(d, ch) : d * 64 + ((ch ^ ((d >> 2) & 3)) << 4);
+    *(u32x4*)(out + off) = y;
   }
 }
 
@@ -868,8 +874,14 @@ hipError_t launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream)
 
 hipError_t launch_prep_v(const PrepVArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.Hkv * a.n_kt;
-  if (grid <= 0 || grid > 0x7fffffff || a.n_kt != (a.Sk + BN - 1) / BN) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prep_v_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  if (grid <= 0 || grid > 0x7fffffff || (a.tk != BN && a.tk != kPrefillPipeBN) ||
+      a.n_kt != (a.Sk + a.tk - 1) / a.tk)
+    return hipErrorInvalidValue;
+  if (a.tk == BN)
+    hipLaunchKernelGGL((prep_v_kernel<BN>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prep_v_kernel<kPrefillPipeBN>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       a);
   return hipGetLastError();
 }
 

@@ -69,14 +69,15 @@ namespace attn {
 namespace {
 
 constexpr int D = kHeadDim;       // 128
-constexpr int BN = 32;            // keys per K/V tile
+constexpr int BN = kPrefillPipeBN;   // keys per K/V tile (32)
 constexpr int NW = 4;             // waves per workgroup, one per SIMD
 constexpr int NT = NW * 64;       // 256 threads
 constexpr int TB = BN * 256;      // bytes of one bf16 K or V tile (8 KB)
-constexpr int VTB = D * BN * 2;   // bytes of one V^T tile (8 KB)
+constexpr int VTB = kVtPipeTileBytes;   // bytes of one V^T tile (8 KB)
 constexpr int NBUF = 4;           // K/V copy ring: tiles t+1 .. t+3 resident or in flight
 constexpr int AHEAD = NBUF - 1;   // copies run this many tiles ahead
 constexpr int COPIES = 4;         // copy instructions per wave per tile
+constexpr int NVT = 5;            // V^T ring with prepared tiles: t-1 .. t+3
 
 // 4-bit swizzle of a row index: a bijection on 0..15 that sends rows r and
 // r+4k to different 4-chunk groups.
@@ -123,6 +124,17 @@ struct Loader {
   uint32_t tile_bytes;
   int row0;
   uint32_t lds_k, lds_v;   // LDS byte addresses of this wave's first K and V row of ring slot 0
+  // prepared fp16 V^T tiles (8 KB, in the LDS layout): each wave copies its
+  // contiguous 2 KB quarter as two 1 KB instructions
+  u32x4 rvt;
+  uint32_t vt_off;         // this wave's quarter, lane's 16 bytes
+  uint32_t lds_vt;         // LDS byte address of this wave's quarter of V^T ring slot 0
+
+  __device__ void init_vt(const uint8_t* vtp, int n_kt, int wave, int lane, uint32_t vt_lds) {
+    rvt = buffer_rsrc(vtp, (uint32_t)n_kt * (uint32_t)VTB);
+    vt_off = (uint32_t)wave * 2048u + (uint32_t)lane * 16u;
+    lds_vt = vt_lds + (uint32_t)wave * 2048u;
+  }
 
   __device__ void init(const __bf16* kp, const __bf16* vp, int64_t k_ss, int Sk, int wave,
                        int lane, uint32_t kbuf_lds, uint32_t vbuf_lds) {
@@ -151,9 +163,17 @@ struct Loader {
   // has no register results (its data goes to LDS); M0 holds the LDS
   // address, written one wait state before the copy reads it (the compiler's
   // hazard tracking does not look inside the asm statement).
-  __device__ __forceinline__ void issue_one(int tile, int slot, int which) const {
+  // With prepared tiles (PRE), which = 2, 3 copy this wave's quarter of the
+  // V^T tile into V^T ring slot vslot instead of V rows.
+  template <bool PRE = false>
+  __device__ __forceinline__ void issue_one(int tile, int slot, int which, int vslot = 0) const {
     const uint32_t base = (uint32_t)tile * tile_bytes;
     const int j = which & 1;
+    if (PRE && which >= 2) {
+      lds_copy16_at(rvt, (uint32_t)tile * (uint32_t)VTB + vt_off + 1024u * j,
+                    lds_vt + (uint32_t)(vslot * VTB) + 1024u * j);
+      return;
+    }
     const uint32_t m0 = (which < 2 ? lds_k : lds_v) + (uint32_t)(slot * TB + 4 * j * 256);
     if (which < 2)
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -162,9 +182,10 @@ struct Loader {
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    : : "s"(m0), "v"(voff[j] + base), "s"(rv) : "memory", "m0");
   }
-  __device__ __forceinline__ void issue(int tile, int slot) const {
+  template <bool PRE = false>
+  __device__ __forceinline__ void issue(int tile, int slot, int vslot = 0) const {
 #pragma unroll
-    for (int which = 0; which < 4; ++which) issue_one(tile, slot, which);
+    for (int which = 0; which < 4; ++which) issue_one<PRE>(tile, slot, which, vslot);
   }
 };
 
@@ -355,7 +376,9 @@ __device__ __forceinline__ void rescale_tile(Wave& w, const Ctx& x, int t, const
 // only) sets scores past Sk or past a row's diagonal to -inf as they leave
 // the AGPRs.  After the slots, the lazy-rescale check; its rare slow path
 // recomputes S(t).
-template <bool CAUSAL, bool F16, bool MASK>
+// With prepared V^T tiles (PRE) the copies bring V^T(t+3) into a ring of 5
+// (V^T(t-1) .. V^T(t+3)) and there is no conversion.
+template <bool CAUSAL, bool F16, bool MASK, bool PRE = false>
 __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kbuf, char* vbuf,
                                           char* vtbuf) {
   int lim[2] = {0, 0};   // last visible key of this lane's row, relative to its half
@@ -369,10 +392,12 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
   }
   const float c = x.c;
   const int cslot = (t + AHEAD) % NBUF;                // copies of tile t+3 (past the keys: zeros)
+  const int vcslot = (t + AHEAD) % NVT;                // PRE: V^T(t+3)
   const char* knext = kbuf + ((t + 1) % NBUF) * TB;
   const char* vraw = vbuf + ((t + 1) % NBUF) * TB;
-  const char* vt_prev = vtbuf + ((t + 2) % 3) * VTB;   // V^T(t-1)
-  char* vt_next = vtbuf + ((t + 1) % 3) * VTB;         // V^T(t+1)
+  const char* vt_prev = PRE ? vtbuf + ((t + NVT - 1) % NVT) * VTB   // V^T(t-1)
+                            : vtbuf + ((t + 2) % 3) * VTB;
+  char* vt_next = vtbuf + ((t + 1) % 3) * VTB;         // V^T(t+1), converted here
   auto pack = [&](float a, float b) -> uint32_t { return F16 ? pack_f16(a, b) : pack_bf16(a, b); };
   auto sum2 = [&](uint32_t u, float acc) -> float {
     return F16 ? sum2_f16(u, acc) : sum2_bf16(u, acc);
@@ -412,7 +437,7 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
       if (rb == 0 && f + 2 < 8)
         vf[f + 2] = *(const bf16x8*)(vt_prev + ((f + 2) & 3) * 32 * 64 + w.vtoff[(f + 2) >> 2]);
     }
-    if ((j & 3) == 1) x.ld.issue_one(t + AHEAD, cslot, j >> 2);
+    if ((j & 3) == 1) x.ld.issue_one<PRE>(t + AHEAD, cslot, j >> 2, vcslot);
     if (j >= 12) kf[j - 12] = *(const bf16x8*)(knext + w.koff[j - 12]);
     {
       const float nm = -w.m[j >> 3];
@@ -445,7 +470,7 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
       const int q = (j - 3) >> 1;
       acc[2 + (q & 1)] = sum2(u[8 + q], acc[2 + (q & 1)]);
     }
-    {
+    if (!PRE) {
       // conversion of this wave's d block of V(t+1): k-step 0 in slots 0-6,
       // k-step 1 in slots 7-13
       const int h = j < 7 ? 0 : 1, js = j < 7 ? j : j - 7;
@@ -491,7 +516,7 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
   barrier();
 }
 
-template <bool CAUSAL, bool F16>
+template <bool CAUSAL, bool F16, bool PRE = false>
 __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, char* vbuf,
                                           char* vtbuf) {
 #pragma unroll
@@ -505,15 +530,16 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   }
   const int T = x.T;
   if (T <= 0) return;
-  // prologue: V^T(-1) (ring slot 2) zeroed, copies of tiles 0 .. AHEAD-1,
-  // V^T(0), S(0)
-  *(u32x4*)(vtbuf + 2 * VTB + 32 * threadIdx.x) = u32x4{};
-  *(u32x4*)(vtbuf + 2 * VTB + 32 * threadIdx.x + 16) = u32x4{};
+  // prologue: V^T(-1) (ring slot 2, or 4 with prepared tiles) zeroed, copies
+  // of tiles 0 .. AHEAD-1, V^T(0), S(0)
+  char* vt_m1 = vtbuf + (PRE ? NVT - 1 : 2) * VTB;
+  *(u32x4*)(vt_m1 + 32 * threadIdx.x) = u32x4{};
+  *(u32x4*)(vt_m1 + 32 * threadIdx.x + 16) = u32x4{};
 #pragma unroll
-  for (int i = 0; i < AHEAD; ++i) x.ld.issue(i, i);
+  for (int i = 0; i < AHEAD; ++i) x.ld.issue<PRE>(i, i, i);
   wait_vm_lds<2 * COPIES>();
   barrier();   // tile 0 and the zeros visible
-  transpose_v<F16>(w, vbuf, vtbuf);
+  if (!PRE) transpose_v<F16>(w, vbuf, vtbuf);
   qk_mfmas(w, w.s, kbuf);
   wait_vm_lds<COPIES>();
   barrier();   // tile 1 and V^T(0) visible
@@ -529,10 +555,10 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   }
   tm = __builtin_amdgcn_readfirstlane(tm);
   int t = 0;
-  for (; t < tm; ++t) iteration<CAUSAL, F16, false>(w, x, t, kbuf, vbuf, vtbuf);
-  for (; t < T; ++t) iteration<CAUSAL, F16, true>(w, x, t, kbuf, vbuf, vtbuf);
+  for (; t < tm; ++t) iteration<CAUSAL, F16, false, PRE>(w, x, t, kbuf, vbuf, vtbuf);
+  for (; t < T; ++t) iteration<CAUSAL, F16, true, PRE>(w, x, t, kbuf, vbuf, vtbuf);
   // drain: P(T-1).V(T-1)
-  pv_mfmas<F16>(w, vtbuf + ((T - 1) % 3) * VTB);
+  pv_mfmas<F16>(w, vtbuf + ((T - 1) % (PRE ? NVT : 3)) * VTB);
 }
 
 __device__ __forceinline__ bool state_finite(const Wave& w) {
@@ -546,12 +572,16 @@ __device__ __forceinline__ bool state_finite(const Wave& w) {
   return ok;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PRE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_pipe_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kbuf[NBUF * TB];
-  __shared__ __attribute__((aligned(1024))) char vbuf[NBUF * TB];
-  __shared__ __attribute__((aligned(1024))) char vtbuf[3 * VTB];
+  // K ring, V ring (bf16), V^T ring of 3; with prepared V^T tiles their
+  // ring of 5 starts at vbuf
+  __shared__ __attribute__((aligned(1024))) char lds[2 * NBUF * TB + 3 * VTB];
+  static_assert(NVT * VTB <= NBUF * TB + 3 * VTB, "LDS plan");
+  char* const kbuf = lds;
+  char* const vbuf = lds + NBUF * TB;
+  char* const vtbuf = vbuf + NBUF * TB;
 
   Wave w;
   const int tid = threadIdx.x;
@@ -600,6 +630,9 @@ void prefill_pipe_kernel(PrefillArgs a) {
   x.ld.init(kp, vp, a.k_ss, Sk, w.wave, lane,
             __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS char*)kbuf),
             __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS char*)vbuf));
+  if (PRE)
+    x.ld.init_vt(a.vt + (int64_t)(b * a.Hkv + hk) * a.n_kt * VTB, a.n_kt, w.wave, lane,
+                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS char*)vbuf));
 
   // ---- per-lane LDS offsets
 #pragma unroll
@@ -636,7 +669,10 @@ void prefill_pipe_kernel(PrefillArgs a) {
     }
   }
 
-  tile_loop<CAUSAL, true>(w, x, kbuf, vbuf, vtbuf);
+  if (PRE)
+    tile_loop<CAUSAL, true, true>(w, x, kbuf, vbuf, vbuf);
+  else
+    tile_loop<CAUSAL, true>(w, x, kbuf, vbuf, vtbuf);
   // A V value beyond the fp16 range (|v| >= 65520) or a non-finite input
   // shows up as a non-finite accumulator: redo this workgroup with bf16
   // probabilities and bf16 V, which covers the whole bf16 range.
@@ -701,10 +737,18 @@ hipError_t launch_prefill_pipe(const PrefillArgs& a, bool causal, hipStream_t st
   if (a.cu_q || a.alibi || a.group % NW) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)a.B * (a.Hq / NW) * a.n_qt;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (causal)
-    hipLaunchKernelGGL((prefill_pipe_kernel<true>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_pipe_kernel<false>), dim3((unsigned)grid), dim3(NT), 0, stream, a);
+  if (a.vt && a.n_kt != (a.Sk + BN - 1) / BN) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), blk(NT);
+  if (a.vt) {
+    if (causal)
+      hipLaunchKernelGGL((prefill_pipe_kernel<true, true>), g, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_pipe_kernel<false, true>), g, blk, 0, stream, a);
+  } else if (causal) {
+    hipLaunchKernelGGL((prefill_pipe_kernel<true, false>), g, blk, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_pipe_kernel<false, false>), g, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -83,9 +83,11 @@ def test_prep_v_bytes():
     assert ea.attn_prep_v_bytes(4, 32, 32, 4096, 128) == 4 * 32 * 64 * tile
     assert ea.attn_prep_v_bytes(1, 6, 3, 64, 128) == 3 * 1 * tile
     assert ea.attn_prep_v_bytes(1, 1, 1, 65, 128) == 2 * tile
-    # none where the forward does not use them: groups of 4k heads, other d
-    assert ea.attn_prep_v_bytes(2, 8, 2, 100, 128) == 0
-    assert ea.attn_prep_v_bytes(2, 32, 8, 100, 128) == 0
+    # groups of 4k query heads: the GQA kernel's tiles of 32 keys (8 KB)
+    assert ea.attn_prep_v_bytes(2, 8, 2, 100, 128) == 2 * 2 * 4 * 8192
+    assert ea.attn_prep_v_bytes(8, 32, 8, 8192, 128) == 8 * 8 * 256 * 8192
+    assert ea.attn_prep_v_bytes(1, 4, 1, 32, 128) == 8192
+    # none for other head dims
     assert ea.attn_prep_v_bytes(2, 4, 4, 100, 64) == 0
     assert ea.attn_prep_v_bytes(2, 4, 4, 100, 256) == 0
     # invalid sizes
@@ -113,8 +115,11 @@ def test_prep_v_argument_errors(kw, code):
 
 def test_prep_v_without_tiles_is_a_no_op():
     # shapes that do not use the tiles return at once (no device call)
-    assert prep(Hq=8, Hkv=2, vt=None, vtb=0) == 0
     assert prep(d=64, vt=None, vtb=0) == 0
+    assert prep(d=256, vt=None, vtb=0) == 0
+    # groups of 4k heads use them (32-key tiles)
+    assert prep(Hq=8, Hkv=2, vt=None, vtb=0) == -5
+    assert prep(Hq=8, Hkv=2, vtb=8192 - 1) == -5
 
 
 def prepped(rounding=0, vt=P, vtb=1 << 62, **kw):
@@ -130,7 +135,8 @@ def prepped(rounding=0, vt=P, vtb=1 << 62, **kw):
     (dict(vt=None), -1), (dict(vtb=16384 * 2 - 1), -5), (dict(vt=P + 8), -4),
     (dict(Sk=(1 << 24) + 1, Hkv=4), -2),
     # the tiles are ignored where the shape does not use them
-    (dict(vt=None, Hq=8, Hkv=2, scale=0.0), -3), (dict(vt=None, d=64, q=None), -1),
+    (dict(vt=None, d=64, scale=0.0), -3), (dict(vt=None, d=64, q=None), -1),
+    (dict(vt=None, Hq=8, Hkv=2), -1), (dict(Hq=8, Hkv=2, vtb=8191), -5),
 ])
 def test_fwd_prepped_argument_errors(kw, code):
     assert prepped(**kw) == code

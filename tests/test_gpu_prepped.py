@@ -2,8 +2,9 @@
 against the single-call forward (attn_fwd / attn_fwd_rounded) on the same
 inputs: both round V and P to fp16 and run the same products in the same
 order, so O and LSE must agree bit for bit (GPU).  Parity of either with the
-fp64 oracle is covered by the other forward tests, which run through the
-binding's default (prepared) path."""
+fp64 oracle is covered by the other forward tests: through the binding's
+default, the full-size workloads run the prepared path and the smaller
+shapes the single call."""
 
 import numpy as np
 import pytest
@@ -39,8 +40,8 @@ def both(p, rounding="rtne", q2=None):
 
 
 SHAPES = [
-    # B, Hq, Hkv, Sq, Sk, layout, causal: groups of 1, 2, 3 (the GQA kernel
-    # takes groups of 4k and does not use the tiles)
+    # B, Hq, Hkv, Sq, Sk, layout, causal: groups of 1, 2, 3 (prefill kernel,
+    # 64-key tiles) and of 4k (GQA kernel, 32-key tiles)
     (1, 2, 2, 1, 1, gen.BSHD, False),
     (1, 2, 1, 17, 15, gen.BSHD, False),
     (2, 4, 2, 63, 65, gen.BHSD, False),
@@ -53,6 +54,13 @@ SHAPES = [
     (3, 2, 2, 1, 333, gen.BHSD, True),
     (2, 8, 8, 1024, 1024, gen.BHSD, False),   # 64 workgroups of 16 tiles
     (1, 16, 16, 600, 2000, gen.BSHD, True),   # 48 workgroups, ragged tails
+    (1, 4, 1, 1, 1, gen.BSHD, False),
+    (1, 4, 1, 33, 31, gen.BSHD, False),
+    (2, 8, 2, 100, 97, gen.BHSD, True),
+    (1, 8, 1, 300, 700, gen.BSHD, True),
+    (1, 16, 2, 257, 129, gen.BHSD, False),
+    (2, 32, 8, 500, 1000, gen.BSHD, True),    # cfg3's group shape, ragged
+    (1, 4, 1, 400, 150, gen.BSHD, True),      # Sq > Sk: first rows see no key
 ]
 
 
@@ -99,6 +107,35 @@ def test_prepared_tiles_serve_several_queries():
     torch.cuda.synchronize()
     assert np.array_equal(bits_of(o_ref), bits_of(o))
     assert np.array_equal(l_ref.cpu().numpy().view(np.uint32), lse.cpu().numpy().view(np.uint32))
+
+
+def test_prepared_gqa_tile_layout():
+    # groups of 4k query heads: 32-key tiles, row d of 64 bytes holds keys
+    # 32t + 16kk + {4hi..4hi+3, 8+4hi..8+4hi+3} at chunk (2kk + hi) ^ ((d >> 2) & 3)
+    B, Hq, Hkv, Sk = 2, 8, 2, 50
+    p = gen.prefill_inputs(B, Hq, Hkv, 1, Sk, layout=gen.BHSD, causal=False, seed=4)
+    v = dev_bf16(p.v)
+    nvt = ea.attn_prep_v_bytes(B, Hq, Hkv, Sk, 128)
+    assert nvt == B * Hkv * 2 * 8192
+    vt = torch.full((nvt,), 0x55, dtype=torch.uint8, device=v.device)
+    st = ea.library().attn_prep_v(v.data_ptr(), B, Hq, Hkv, Sk, 128, ea.ATTN_BHSD, vt.data_ptr(),
+                                  nvt, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    got = vt.cpu().numpy().view(np.float16).reshape(B, Hkv, 2, 128, 32)
+    vf = (p.v.astype(np.uint32) << 16).view(np.float32)          # [B, Hkv, Sk, d]
+    want = np.zeros((B, Hkv, 2, 128, 32), dtype=np.float16)
+    for t in range(2):
+        for d in range(128):
+            for c in range(4):
+                kk, hi = c >> 1, c & 1
+                keys = [32 * t + 16 * kk + 4 * hi + j for j in range(4)] + \
+                       [32 * t + 16 * kk + 8 + 4 * hi + j for j in range(4)]
+                pc = c ^ ((d >> 2) & 3)
+                for j, key in enumerate(keys):
+                    if key < Sk:
+                        want[:, :, t, d, 8 * pc + j] = vf[:, :, key, d].astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
 def test_prepared_tile_layout():
