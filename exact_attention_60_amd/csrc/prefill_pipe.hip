@@ -557,8 +557,12 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   int t = 0;
   for (; t < tm; ++t) iteration<CAUSAL, F16, false, PRE>(w, x, t, kbuf, vbuf, vtbuf);
   for (; t < T; ++t) iteration<CAUSAL, F16, true, PRE>(w, x, t, kbuf, vbuf, vtbuf);
-  // drain: P(T-1).V(T-1)
+  // drain: P(T-1).V(T-1); then the copies of the tiles past the loop (issued
+  // by its last iterations) are waited for, so that nothing lands in the
+  // rings after this point (the epilogue stages O there, a bf16 redo starts
+  // its own copies)
   pv_mfmas<F16>(w, vtbuf + ((T - 1) % (PRE ? NVT : 3)) * VTB);
+  wait_vm_lds<0>();
 }
 
 __device__ __forceinline__ bool state_finite(const Wave& w) {
