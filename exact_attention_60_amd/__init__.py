@@ -197,6 +197,7 @@ def _rounding_code(rounding: str) -> int:
 
 # query tiles (256 rows) per K/V head from which attn_fwd prepares V by default
 PREPARE_V_MIN_TILES = 32
+PREPARE_V_MIN_BLOCKS_D256 = 16
 
 
 def attn_prep_v_bytes(B: int, Hq: int, Hkv: int, Sk: int, d: int) -> int:
@@ -205,9 +206,14 @@ def attn_prep_v_bytes(B: int, Hq: int, Hkv: int, Sk: int, d: int) -> int:
 
 def prepares_v(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int) -> bool:
     """Whether attn_fwd (no ALiBi, prepare_v=None) runs attn_prep_v +
-    attn_fwd_prepped for this shape."""
-    return ((Sq * (Hq // Hkv) + 255) // 256 >= PREPARE_V_MIN_TILES and
-            attn_prep_v_bytes(B, Hq, Hkv, Sk, d) > 0)
+    attn_fwd_prepped for this shape: at d = 128 when each K/V head serves at
+    least PREPARE_V_MIN_TILES query tiles of 256 rows, at d = 256 at least
+    PREPARE_V_MIN_BLOCKS_D256 query blocks of 128 rows (Sq * Hq / Hkv rows per
+    K/V head)."""
+    rows = Sq * (Hq // Hkv)
+    many = ((rows + 127) // 128 >= PREPARE_V_MIN_BLOCKS_D256 if d == 256
+            else (rows + 255) // 256 >= PREPARE_V_MIN_TILES)
+    return many and attn_prep_v_bytes(B, Hq, Hkv, Sk, d) > 0
 
 
 def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
@@ -221,10 +227,11 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
     (attn_prep_v_bytes > 0, no ALiBi), True runs attn_prep_v into `vt` (a
     uint8 GPU tensor of at least that many bytes, allocated here if None) and
     then attn_fwd_prepped; False runs the single-call attn_fwd /
-    attn_fwd_rounded.  None (default) prepares when each K/V head serves at
-    least PREPARE_V_MIN_TILES query tiles of 256 rows (Sq * Hq / Hkv), where
-    the one conversion per head costs less than the per-workgroup ones it
-    replaces (measured: a net loss at 16 tiles, a gain at 128).
+    attn_fwd_rounded.  None (default) follows prepares_v: the one conversion
+    per head costs less than the per-workgroup ones it replaces once each K/V
+    head serves enough query rows (measured at d = 128: a net loss at 16 tiles
+    of 256 rows, a gain at 128; at d = 256: a loss at 8 blocks of 128 rows, a
+    gain at 32).
     Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -569,5 +576,6 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
 
 __all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append", "attn_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
            "attn_decode_workspace_bytes", "attn_status_string",
-           "attn_version", "attn_prep_v_bytes", "prepares_v", "PREPARE_V_MIN_TILES", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
+           "attn_version", "attn_prep_v_bytes", "prepares_v", "PREPARE_V_MIN_TILES",
+           "PREPARE_V_MIN_BLOCKS_D256", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["api.cpp", "prefill.hip", "prefill_pipe.hip", "prefill_hd.hip", "prefill_fp8.hip", "decode.hip", "decode_noalloc.hip", "backward.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "prefill_pipe.hip", "prefill_hd.hip", "prefill_d256.hip", "prefill_fp8.hip", "decode.hip", "decode_noalloc.hip", "backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

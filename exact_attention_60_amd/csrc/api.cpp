@@ -107,7 +107,7 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   // d = 128 without ALiBi and a GQA group that is a multiple of 4: the
   // kernel whose workgroups share each K/V tile among 4 query heads
   const bool pipe = uses_pipe(Hq, Hkv, d, alibi_slopes != nullptr);
-  const int rows_per_block = hd64   ? attn::prefill_hd_rows_per_block()
+  const int rows_per_block = hd64   ? attn::kPrefillHdRows
                              : pipe ? attn::kPrefillPipeRows
                                     : attn::kPrefillBM;
   a.n_qt = (Sq + rows_per_block - 1) / rows_per_block;
@@ -118,14 +118,15 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
   a.alibi = alibi_slopes;
-  const int tk = pipe ? attn::kPrefillPipeBN : attn::kPrefillBN;
-  a.vt = !hd64 ? static_cast<const uint8_t*>(vt) : nullptr;
+  const int tk = d == 256 ? attn::kPrefillD256BN : pipe ? attn::kPrefillPipeBN : attn::kPrefillBN;
+  a.vt = d != 64 ? static_cast<const uint8_t*>(vt) : nullptr;
   a.n_kt = (Sk + tk - 1) / tk;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = hd64   ? attn::launch_prefill_hd(a, d, causal != 0, st)
+  const hipError_t e = d == 64    ? attn::launch_prefill_hd(a, causal != 0, st)
+                       : d == 256 ? attn::launch_prefill_d256(a, causal != 0, st)
                        : pipe ? attn::launch_prefill_pipe(a, causal != 0, st)
                               : attn::launch_prefill(a, causal != 0, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
@@ -179,15 +180,18 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 }
 
 // keys per prepared tile: that of the kernel attn_fwd runs for the shape
-static int prep_tile_keys(int Hq, int Hkv) {
+// keys per prepared tile: the tile size of the kernel that reads them
+static int prep_tile_keys(int Hq, int Hkv, int d) {
+  if (d == 256) return attn::kPrefillD256BN;
   return uses_pipe(Hq, Hkv, attn::kHeadDim, false) ? attn::kPrefillPipeBN : attn::kPrefillBN;
 }
 
 size_t attn_prep_v_bytes(int B, int Hq, int Hkv, int Sk, int d) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0 || d != attn::kHeadDim) return 0;
-  const int tk = prep_tile_keys(Hq, Hkv);
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0) return 0;
+  if (d != attn::kHeadDim && d != 256) return 0;
+  const int tk = prep_tile_keys(Hq, Hkv, d);
   const int64_t n_kt = (Sk + tk - 1) / tk;
-  return (size_t)B * Hkv * n_kt * tk * attn::kHeadDim * 2;
+  return (size_t)B * Hkv * n_kt * tk * d * 2;
 }
 
 int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout, void* vt,
@@ -209,16 +213,16 @@ int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout
     a.k_sb = (int64_t)Hkv * Sk * D; a.k_sh = (int64_t)Sk * D; a.k_ss = D;
   }
   a.B = B; a.Hkv = Hkv; a.Sk = Sk;
-  a.tk = prep_tile_keys(Hq, Hkv);
+  a.tk = prep_tile_keys(Hq, Hkv, d);
   a.n_kt = (Sk + a.tk - 1) / a.tk;
   if ((int64_t)B * Hkv * a.n_kt > INT32_MAX) return ATTN_ERR_SHAPE;
-  // one head's tiles are addressed with 32-bit offsets (the same bytes at
-  // either tile size)
-  if ((int64_t)a.n_kt * a.tk * attn::kHeadDim * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
+  // one head's tiles are addressed with 32-bit offsets
+  if ((int64_t)a.n_kt * a.tk * D * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
-  const hipError_t e = attn::launch_prep_v(a, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = d == 256 ? attn::launch_prep_v_d256(a, st) : attn::launch_prep_v(a, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -230,9 +234,8 @@ int attn_fwd_prepped(const void* q, const void* k, const void* v, const void* vt
     if (!vt) return ATTN_ERR_NULL;
     if (vt_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(vt)) return ATTN_ERR_ALIGN;
-    const int tk = prep_tile_keys(Hq, Hkv);
-    if ((int64_t)((Sk + tk - 1) / tk) * tk * attn::kHeadDim * 2 > (int64_t)UINT32_MAX)
-      return ATTN_ERR_SHAPE;
+    const int tk = prep_tile_keys(Hq, Hkv, d);
+    if ((int64_t)((Sk + tk - 1) / tk) * tk * d * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_SHAPE;
   }
   return fwd_call(q, k, v, o, lse, nullptr, B, Hq, Hkv, Sq, Sk, d, scale, causal, layout,
                   rounding, stream, need != 0 ? vt : nullptr);

@@ -1,4 +1,4 @@
-// Exact attention forward for head dims 64 and 256 on gfx950: O = softmax(scale Q K^T) V
+// Exact attention forward for head dim 64 on gfx950: O = softmax(scale Q K^T) V
 // with the same online softmax as the d = 128 kernel ("IO-aware tiling
 // strategy in FlashAttention-4", body: Q in row tiles, K/V in column tiles
 // brought on chip, a running row max m and denominator l merged block by
@@ -11,8 +11,7 @@
 //  * one workgroup = 4 waves = 128 query rows of one (batch, query head); a
 //    wave owns 32 rows, with its Q fragments and the fp32 O^T accumulator in
 //    registers (about 110 VGPRs, so several workgroups share a CU).
-//  * K and V tiles of 64 keys (d = 64, 128-byte rows) or 32 keys (d = 256,
-//    512-byte rows) are copied HBM -> LDS by
+//  * K and V tiles of 64 keys (128-byte rows) are copied HBM -> LDS by
 //    buffer_load ... lds, double buffered one tile ahead; rows are XOR-swizzled
 //    in 16-byte chunks; keys past Sk fall outside the buffer range and read 0.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row in each lane
@@ -38,6 +37,7 @@ namespace {
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int QR = NW * 32;    // query rows per workgroup
+static_assert(QR == kPrefillHdRows, "rows per workgroup");
 
 template <int D>
 struct Geom {
@@ -331,19 +331,12 @@ void prefill_hd_kernel(PrefillArgs a) {
 
 }  // namespace
 
-int prefill_hd_rows_per_block() { return QR; }
-
-hipError_t launch_prefill_hd(const PrefillArgs& a, int d, bool causal, hipStream_t stream) {
+hipError_t launch_prefill_hd(const PrefillArgs& a, bool causal, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.Hq * a.n_qt;
-  if (grid <= 0 || grid > 0x7fffffff || (d != 64 && d != 256)) return hipErrorInvalidValue;
+  if (grid <= 0 || grid > 0x7fffffff || a.cu_q || a.alibi || a.vt) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), bt(NT);
-  if (d == 64) {
-    if (causal) hipLaunchKernelGGL((prefill_hd_kernel<64, true>), g, bt, 0, stream, a);
-    else hipLaunchKernelGGL((prefill_hd_kernel<64, false>), g, bt, 0, stream, a);
-  } else {
-    if (causal) hipLaunchKernelGGL((prefill_hd_kernel<256, true>), g, bt, 0, stream, a);
-    else hipLaunchKernelGGL((prefill_hd_kernel<256, false>), g, bt, 0, stream, a);
-  }
+  if (causal) hipLaunchKernelGGL((prefill_hd_kernel<64, true>), g, bt, 0, stream, a);
+  else hipLaunchKernelGGL((prefill_hd_kernel<64, false>), g, bt, 0, stream, a);
   return hipGetLastError();
 }
 

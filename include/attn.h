@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 11
+#define ATTN_VERSION 12
 
 typedef enum {
   ATTN_OK = 0,
@@ -153,10 +153,10 @@ int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float
  * attn_fwd_rounded on the same inputs.
  *
  * attn_prep_v_bytes(B, Hq, Hkv, Sk, d): bytes of the prepared tiles, or 0
- *   where the forward does not use them (d != 128) and for invalid sizes:
- *   B * Hkv * ceil(Sk / 64) * 16384, or B * Hkv * ceil(Sk / 32) * 8192 when
- *   Hq / Hkv is a multiple of 4 (the kernel for those groups works on
- *   32-key tiles).
+ *   where the forward does not use them (d = 64) and for invalid sizes.
+ *   d = 128: B * Hkv * ceil(Sk / 64) * 16384, or B * Hkv * ceil(Sk / 32) *
+ *   8192 when Hq / Hkv is a multiple of 4 (the kernel for those groups works
+ *   on 32-key tiles); d = 256: B * Hkv * ceil(Sk / 32) * 16384.
  * attn_prep_v(v, B, Hq, Hkv, Sk, d, layout, vt, vt_bytes, stream): writes
  *   the tiles of v (bf16, attn_fwd's k/v layout) into vt (device memory,
  *   16-byte aligned, at least attn_prep_v_bytes; owned by the caller).  Each
@@ -164,7 +164,7 @@ int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float
  *   which attn_fwd_prepped detects and answers with the bf16 path, as
  *   attn_fwd does.  Returns ATTN_OK without work where the size is 0;
  *   ATTN_ERR_WORKSPACE if vt is NULL or smaller, ATTN_ERR_ALIGN,
- *   ATTN_ERR_SHAPE (one head's tiles, about Sk * 256 bytes, must stay
+ *   ATTN_ERR_SHAPE (one head's tiles, about Sk * 2 * d bytes, must stay
  *   below 2^32 bytes),
  *   ATTN_ERR_UNSUPPORTED for another layout.
  * attn_fwd_prepped(q, k, v, vt, vt_bytes, o, lse, ...): attn_fwd_rounded,

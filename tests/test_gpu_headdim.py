@@ -117,3 +117,42 @@ def test_d256_v_beyond_fp16_range_takes_the_bf16_path():
     o, lse = run(p)
     assert torch.isfinite(o.float()).all()
     check(p, o, lse, "d256 large V")
+
+
+def test_d256_rounding_rules_and_determinism():
+    p = gen.prefill_inputs(1, 4, 2, 200, 300, layout=gen.BHSD, causal=True, seed=15, d=256)
+    outs = {m: run(p, m) for m in ("rtne", "rtna", "rtz")}
+    o_ref = check(p, outs["rtne"][0], outs["rtne"][1], "d256 rtne")
+    for m in ("rtna", "rtz"):
+        check_o(logical_o(outs[m][0], p.layout), o_ref, f"d256 {m}")
+    a = host_f64(outs["rtz"][0])
+    b = host_f64(outs["rtne"][0])
+    assert np.all(np.abs(a) <= np.abs(b))
+    o2, l2 = run(p)
+    assert torch.equal(o2.view(torch.int16), outs["rtne"][0].view(torch.int16))
+    assert torch.equal(l2, outs["rtne"][1])
+
+
+def test_d256_many_tiles_all_elements():
+    # several 128-row query blocks and 32-key tiles, ragged on both sides,
+    # non-causal and causal (the binding's default: single call at this size)
+    for causal in (False, True):
+        p = gen.prefill_inputs(1, 4, 1, 700, 1100, layout=gen.BSHD, causal=causal, seed=31,
+                               n_hot=3, d=256)
+        o, lse = run(p)
+        check(p, o, lse, f"d256 Sq700 Sk1100 causal{causal}")
+
+
+def test_d256_causal_gqa_full_size_sampled_group():
+    # the timed head-dim-256 shape (B=4, Hq=32, Hkv=8, S=4096, causal; the
+    # binding prepares V here), one K/V head's group against the oracle
+    p = gen.prefill_inputs(4, 32, 8, 4096, 4096, layout=gen.BSHD, causal=True, seed=8, d=256)
+    assert ea.prepares_v(p.B, p.Hq, p.Hkv, p.Sq, p.Sk, 256)
+    o, lse = run(p)
+    b, g, G = 2, 3, 4
+    sub = [np.ascontiguousarray(x[b:b + 1, :, h0:h1])
+           for x, h0, h1 in ((p.q, g * G, g * G + G), (p.k, g, g + 1), (p.v, g, g + 1))]
+    o_ref, l_ref = att.attention(*sub, 1, G, 1, p.Sq, p.Sk, p.scale, True, gen.BSHD)
+    e = check_o(logical_o(o[b:b + 1, :, g * G:g * G + G], gen.BSHD), o_ref, "d256 full size")
+    check_lse(host_f64(lse[b:b + 1, g * G:g * G + G]), l_ref, "d256 full size lse")
+    print(f"d256 causal gqa full size b{b} g{g}: err/tol {e[1]:.3f}", flush=True)

@@ -24,15 +24,16 @@ def _gpu():
 
 def both(p, rounding="rtne", q2=None):
     q, k, v = dev_bf16(p.q), dev_bf16(p.k), dev_bf16(p.v)
+    d = p.q.shape[-1]
     lay = "bshd" if p.layout == gen.BSHD else "bhsd"
     kw = dict(causal=p.causal, scale=p.scale, layout=lay, rounding=rounding)
     o1, l1 = ea.attn_fwd(q, k, v, prepare_v=False, **kw)
-    nvt = ea.attn_prep_v_bytes(p.B, p.Hq, p.Hkv, p.Sk, 128)
+    nvt = ea.attn_prep_v_bytes(p.B, p.Hq, p.Hkv, p.Sk, d)
     assert nvt > 0
     vt = torch.full((nvt,), 0x7f, dtype=torch.uint8, device=q.device)
     o2, l2 = ea.attn_fwd(q, k, v, vt=vt, prepare_v=True, **kw)
     torch.cuda.synchronize()
-    print(f"case: B{p.B} Hq{p.Hq} Hkv{p.Hkv} Sq{p.Sq} Sk{p.Sk} {lay} causal={p.causal} "
+    print(f"case: B{p.B} Hq{p.Hq} Hkv{p.Hkv} Sq{p.Sq} Sk{p.Sk} d{d} {lay} causal={p.causal} "
           f"{rounding}", flush=True)
     assert np.array_equal(bits_of(o1), bits_of(o2))
     assert np.array_equal(l1.cpu().numpy().view(np.uint32), l2.cpu().numpy().view(np.uint32))
@@ -72,6 +73,30 @@ def test_prepped_equals_single_call(shape):
     both(p)
 
 
+SHAPES_D256 = [
+    # head dim 256: 32-key tiles, 128 query rows per workgroup
+    (1, 2, 2, 1, 1, gen.BSHD, False),
+    (1, 2, 1, 17, 15, gen.BSHD, False),
+    (2, 4, 2, 63, 65, gen.BHSD, False),
+    (1, 3, 3, 129, 127, gen.BSHD, True),
+    (1, 4, 4, 257, 257, gen.BHSD, True),
+    (1, 2, 1, 400, 150, gen.BSHD, True),      # Sq > Sk: first rows see no key
+    (1, 2, 2, 100, 700, gen.BHSD, True),
+    (1, 8, 2, 600, 1000, gen.BSHD, True),     # several query blocks, ragged tails
+    (1, 4, 4, 300, 77, gen.BSHD, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_D256, ids=lambda s: "d256_B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s"
+                         % (s[0], s[1], s[2], s[3], s[4], "bshd" if s[5] == 0 else "bhsd",
+                            "causal" if s[6] else "full"))
+def test_prepped_equals_single_call_d256(shape):
+    B, Hq, Hkv, Sq, Sk, layout, causal = shape
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=13 + Sq + Sk,
+                           d=256)
+    both(p)
+
+
 @pytest.mark.parametrize("rounding", ["rtne", "rtna", "rtz"])
 def test_prepped_rounding_rules(rounding):
     p = gen.prefill_inputs(1, 4, 2, 300, 500, layout=gen.BSHD, causal=True, seed=5)
@@ -85,6 +110,17 @@ def test_prepped_v_beyond_fp16_range_takes_the_bf16_path():
     v = (p.v.astype(np.uint32) << 16).view(np.float32).copy()
     v[:, :, :, 5] = 3.0e5
     v[0, 700, 1, 9] = -2.0e6
+    p.v = gen.f32_to_bf16_bits(v)
+    both(p)
+
+
+def test_prepped_d256_rounding_and_large_v():
+    p = gen.prefill_inputs(1, 4, 2, 300, 500, layout=gen.BSHD, causal=True, seed=7, d=256)
+    for rounding in ("rtna", "rtz"):
+        both(p, rounding)
+    v = (p.v.astype(np.uint32) << 16).view(np.float32).copy()
+    v[:, :, :, 200] = 3.0e5
+    v[0, 333, 1, 9] = -2.0e6
     p.v = gen.f32_to_bf16_bits(v)
     both(p)
 
@@ -160,6 +196,35 @@ def test_prepared_tile_layout():
                 keys = [64 * t + 16 * kk + 4 * hi + j for j in range(4)] + \
                        [64 * t + 16 * kk + 8 + 4 * hi + j for j in range(4)]
                 pc = c ^ ((d >> 1) & 7)
+                for j, key in enumerate(keys):
+                    if key < Sk:
+                        want[:, :, t, d, 8 * pc + j] = vf[:, key, :, d].astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_prepared_d256_tile_layout():
+    # head dim 256: 32-key tiles of 16 KB, row d of 64 bytes holds keys
+    # 32t + 16kk + {4hi..4hi+3, 8+4hi..8+4hi+3} at chunk (2kk + hi) ^ ((d >> 2) & 3)
+    B, Hq, Hkv, Sk = 2, 2, 2, 40
+    p = gen.prefill_inputs(B, Hq, Hkv, 1, Sk, layout=gen.BSHD, causal=False, seed=6, d=256)
+    v = dev_bf16(p.v)
+    nvt = ea.attn_prep_v_bytes(B, Hq, Hkv, Sk, 256)
+    assert nvt == B * Hkv * 2 * 16384
+    vt = torch.full((nvt,), 0x55, dtype=torch.uint8, device=v.device)
+    st = ea.library().attn_prep_v(v.data_ptr(), B, Hq, Hkv, Sk, 256, ea.ATTN_BSHD, vt.data_ptr(),
+                                  nvt, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    got = vt.cpu().numpy().view(np.float16).reshape(B, Hkv, 2, 256, 32)
+    vf = (p.v.astype(np.uint32) << 16).view(np.float32)          # [B, Sk, Hkv, d]
+    want = np.zeros((B, Hkv, 2, 256, 32), dtype=np.float16)
+    for t in range(2):
+        for d in range(256):
+            for c in range(4):
+                kk, hi = c >> 1, c & 1
+                keys = [32 * t + 16 * kk + 4 * hi + j for j in range(4)] + \
+                       [32 * t + 16 * kk + 8 + 4 * hi + j for j in range(4)]
+                pc = c ^ ((d >> 2) & 3)
                 for j, key in enumerate(keys):
                     if key < Sk:
                         want[:, :, t, d, 8 * pc + j] = vf[:, key, :, d].astype(np.float16)
