@@ -30,9 +30,12 @@
 //    beyond the fp16 range or a non-finite input leaves a non-finite
 //    accumulator and the workgroup redoes its tiles with bf16 P and V.
 //  * With V prepared once per K/V head (prep_v_d256_kernel: fp16 V^T tiles
-//    in HBM, laid out as the LDS tile) the copies bring V^T(t+3) into a ring
-//    of 5 (V^T(t-1) .. V^T(t+3)) and there is no conversion; the results are
-//    bit-identical to the converting path.
+//    in HBM, laid out as the LDS tile) the copies bring V^T(t+2) into a ring
+//    of 4 (V^T(t-1) .. V^T(t+2)) and there is no conversion; the results are
+//    bit-identical to the converting path.  With both rings of 4 slots the
+//    loop runs four iterations per pass, each with its ring slots fixed at
+//    compile time, so that every LDS operand address is a per-lane register
+//    plus an instruction offset.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row in each lane
 //    column, so the probabilities are directly the B operand of the P.V
 //    MFMAs and the row sum is in-lane plus one v_permlane32_swap.
@@ -43,7 +46,7 @@
 //  * Causal: tiles past the workgroup's last diagonal are never loaded, only
 //    boundary tiles are masked, heaviest query blocks are dispatched first.
 //  * LDS: K 4 x 16 KB + V 3 x 16 KB + V^T 3 x 16 KB = 160 KB (prepared: K 4
-//    + V^T 5 = 144 KB of the same array), one workgroup per CU.
+//    + V^T 4 = 128 KB of the same array), one workgroup per CU.
 #include "gfx950.hpp"
 #include "kernels.h"
 
@@ -61,7 +64,7 @@ constexpr int VTB = D * BN * 2; // one fp16 V^T tile (16 KB)
 constexpr int NK = 4;           // K ring: K(t) .. K(t+3)
 constexpr int NV = 3;           // V ring: V(t+1) .. V(t+3)
 constexpr int NVT = 3;          // V^T ring: V^T(t-1) .. V^T(t+1)
-constexpr int NVP = 5;          // prepared V^T ring: V^T(t-1) .. V^T(t+3)
+constexpr int NVP = 4;          // prepared V^T ring: V^T(t-1) .. V^T(t+2)
 constexpr int AHEAD = 3;        // copies run this many tiles ahead
 constexpr int COPIES = 8;       // copy instructions per wave per tile (4 K, 4 V)
 constexpr int KS = D / 16;      // k-steps of S^T = K Q^T
@@ -146,27 +149,32 @@ struct Loader {
     vt_lane = (uint32_t)wave * 4096u + (uint32_t)lane * 16u;
     lds_vt = vt_lds + (uint32_t)wave * 4096u;
   }
-  // copy instruction `which` of tile `tile`: 0..3 K rows into K ring slot
-  // kslot, 4..7 V rows into V ring slot vslot (PRE: a quarter of the V^T tile
-  // into prepared ring slot vslot)
+  // copy instruction `which`: 0..3 rows of K tile `tile` into K ring slot
+  // kslot, 4..7 rows of V tile `vtile` into V ring slot vslot (PRE: a quarter
+  // of V^T tile `vtile` into prepared ring slot vslot)
   template <bool PRE>
-  __device__ __forceinline__ void issue_one(int tile, int kslot, int vslot, int which) const {
+  __device__ __forceinline__ void issue_one(int tile, int kslot, int vtile, int vslot,
+                                            int which) const {
     const int j = which & 3;
     if (which < 4) {
       lds_copy16_at(rk, voff[j] + (uint32_t)tile * tile_bytes,
                     lds_k + (uint32_t)(kslot * TB + j * 1024));
     } else if (PRE) {
-      lds_copy16_at(rvt, (uint32_t)tile * (uint32_t)VTB + vt_lane + 1024u * j,
+      lds_copy16_at(rvt, (uint32_t)vtile * (uint32_t)VTB + vt_lane + 1024u * j,
                     lds_vt + (uint32_t)(vslot * VTB + j * 1024));
     } else {
-      lds_copy16_at(rv, voff[j] + (uint32_t)tile * tile_bytes,
+      lds_copy16_at(rv, voff[j] + (uint32_t)vtile * tile_bytes,
                     lds_v + (uint32_t)(vslot * TB + j * 1024));
     }
   }
-  template <bool PRE>
-  __device__ __forceinline__ void issue(int tile, int kslot, int vslot) const {
+  __device__ __forceinline__ void issue_k(int tile, int kslot) const {
 #pragma unroll
-    for (int which = 0; which < 8; ++which) issue_one<PRE>(tile, kslot, vslot, which);
+    for (int which = 0; which < 4; ++which) issue_one<false>(tile, kslot, 0, 0, which);
+  }
+  template <bool PRE>
+  __device__ __forceinline__ void issue_v(int vtile, int vslot) const {
+#pragma unroll
+    for (int which = 4; which < 8; ++which) issue_one<PRE>(0, 0, vtile, vslot, which);
   }
 };
 
@@ -179,6 +187,8 @@ struct Wave {
   float l;             // this lane's part of the row sum
   int koff[KS];        // K operand offsets per k-step
   int vtoff[2];        // V^T operand offsets per key step (d block 0)
+  const char* kl[KS];  // K ring slot 0 + koff
+  const char* vtl[2];  // prepared V^T ring slot 0 + vtoff
   int cvoff[4][2];     // transposed reads of the bf16 V tile [conversion unit][half]
   int first;           // first query row of the wave
   int l32, hi, wave;
@@ -330,25 +340,32 @@ __device__ __forceinline__ float rescale_tile(Wave& w, const Ctx& x, int t, cons
 //  group 1, slot j = 0..15: MFMA j of O^T += V^T(t-1) P(t-1)^T (d block j%8,
 //    key step j/8); score j of S(t) moved out of the accumulator, masked
 //    (MASK), scaled and shifted; the exponential of score j-1; V^T fragments
-//    read four slots ahead; copy instruction (j-1)/2 of tile t+3 in odd
-//    slots; conversion units 0 and 1; K fragments of group 2 in slots 12-15.
+//    read four slots ahead; copy instruction (j-1)/2 in odd slots (K(t+3),
+//    then V(t+3)); conversion units 0 and 1; K fragments of group 2 in
+//    slots 12-15.
 //  group 2, slot j = 0..15: MFMA j of S(t+1) = K(t+1) Q^T (overwriting the
 //    score registers, all read by then); the last exponential; the
 //    probabilities packed and summed as they become ready; conversion units
 //    2 and 3; K fragments read four slots ahead.
 // With prepared tiles (PRE), vbuf is the prepared ring: the copies bring
-// V^T(t+3) into its slot (t+3) % 5 and the conversion units are left out.
-template <bool CAUSAL, bool F16, bool MASK, bool PRE>
+// V^T(t+2) into its slot (t+2) % 4, the conversion units are left out, and
+// S = t % 4 fixes every ring slot at compile time.
+template <bool CAUSAL, bool F16, bool MASK, bool PRE, int S>
 __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kbuf, char* vbuf,
                                           char* vtbuf) {
+  static_assert(!PRE || (S >= 0 && S < NK && NK == NVP), "ring phase of the prepared loop");
   const int lim = MASK ? visible_lim<CAUSAL>(w, x, t * BN) : 0;
   const float c = x.c;
-  const int ck = (t + AHEAD) % NK, cv = PRE ? (t + AHEAD) % NVP : (t + AHEAD) % NV;
-  const char* knext = kbuf + ((t + 1) % NK) * TB;
+  const int kn = PRE ? (S + 1) % NK : (t + 1) % NK;         // K(t+1)
+  const int kcur = PRE ? S : t % NK;                        // K(t), for the slow path
+  const int ck = PRE ? (S + AHEAD) % NK : (t + AHEAD) % NK; // K(t+3) copies
+  const int vtile = PRE ? t + 2 : t + AHEAD;                // V tile copied here
+  const int cv = PRE ? (S + 2) % NVP : (t + AHEAD) % NV;
+  const int vp = PRE ? (S + NVP - 1) % NVP : 0;             // prepared V^T(t-1)
   const char* vraw = vbuf + ((t + 1) % NV) * TB;
-  const char* vt_prev = PRE ? vbuf + ((t + NVP - 1) % NVP) * VTB
-                            : vtbuf + ((t + NVT - 1) % NVT) * VTB;
+  const char* vt_prev = vtbuf + ((t + NVT - 1) % NVT) * VTB;
   char* vt_next = vtbuf + ((t + 1) % NVT) * VTB;
+  auto kfrag = [&](int ks) { return *(const bf16x8*)(w.kl[ks] + kn * TB); };
   auto pack = [&](float a, float b) -> uint32_t { return F16 ? pack_f16(a, b) : pack_bf16(a, b); };
   auto sum2 = [&](uint32_t u, float acc) -> float {
     return F16 ? sum2_f16(u, acc) : sum2_bf16(u, acc);
@@ -362,6 +379,7 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
     return __builtin_fmaf(sv, c, nm);
   };
   auto vt_frag = [&](int f) {
+    if (PRE) return *(const bf16x8*)(w.vtl[f >> 3] + vp * VTB + (f & 7) * 32 * 64);
     return *(const bf16x8*)(vt_prev + (f & 7) * 32 * 64 + w.vtoff[f >> 3]);
   };
   float xs[16];
@@ -399,8 +417,8 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
         w.o[n] = mfma32(vf[j & 3], __builtin_bit_cast(bf16x8, w.pf[kk]), w.o[n]);
       if (j + 4 < 16) vf[j & 3] = vt_frag(j + 4);
     }
-    if (j & 1) x.ld.issue_one<PRE>(t + AHEAD, ck, cv, j >> 1);
-    if (j >= 12) kf[j - 12] = *(const bf16x8*)(knext + w.koff[j - 12]);
+    if (j & 1) x.ld.issue_one<PRE>(t + AHEAD, ck, vtile, cv, j >> 1);
+    if (j >= 12) kf[j - 12] = kfrag(j - 12);
     xs[j] = score(j, nm);
     if (j >= 1) xs[j - 1] = fast_exp2(xs[j - 1]);
     if (j >= 4 && j < 8) conv_step(j - 4, 0);
@@ -412,7 +430,7 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     w.s = mfma32(kf[j & 3], w.qf[j], j == 0 ? f32x16{} : w.s);
-    if (j + 4 < 16) kf[j & 3] = *(const bf16x8*)(knext + w.koff[j + 4]);
+    if (j + 4 < 16) kf[j & 3] = kfrag(j + 4);
     if (j == 0) xs[15] = fast_exp2(xs[15]);
     if (j >= 1 && j <= 8) u[j - 1] = pack(xs[2 * (j - 1)], xs[2 * (j - 1) + 1]);
     if (j >= 2 && j <= 9) acc[j & 1] = sum2(u[j - 2], acc[j & 1]);
@@ -427,12 +445,42 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
   // otherwise (rare) the slow path
   float tsum = acc[0] + acc[1];
   if (wave_any(!(w.m != -INFINITY && tsum <= 4096.f)))
-    tsum = rescale_tile<CAUSAL, F16>(w, x, t, kbuf + (t % NK) * TB);
+    tsum = rescale_tile<CAUSAL, F16>(w, x, t, kbuf + kcur * TB);
   w.l += tsum;
   // tile t+2's copies have landed (t+3's may still be in flight), this wave's
   // V^T writes are done; the barrier publishes both
   wait_vm_lds<COPIES>();
   barrier();
+}
+
+// Iterations t .. tend-1.  The prepared loop enters its four-iteration pass
+// at the phase t % 4 and then runs whole passes.
+template <bool CAUSAL, bool F16, bool MASK, bool PRE>
+__device__ __forceinline__ void iterations(Wave& w, const Ctx& x, int& t, int tend, char* kbuf,
+                                           char* vbuf, char* vtbuf) {
+  if constexpr (PRE) {
+    while (t < tend) {
+      switch (t & 3) {
+        case 0:
+          iteration<CAUSAL, F16, MASK, PRE, 0>(w, x, t, kbuf, vbuf, vtbuf);
+          if (++t >= tend) break;
+          [[fallthrough]];
+        case 1:
+          iteration<CAUSAL, F16, MASK, PRE, 1>(w, x, t, kbuf, vbuf, vtbuf);
+          if (++t >= tend) break;
+          [[fallthrough]];
+        case 2:
+          iteration<CAUSAL, F16, MASK, PRE, 2>(w, x, t, kbuf, vbuf, vtbuf);
+          if (++t >= tend) break;
+          [[fallthrough]];
+        default:
+          iteration<CAUSAL, F16, MASK, PRE, 3>(w, x, t, kbuf, vbuf, vtbuf);
+          ++t;
+      }
+    }
+  } else {
+    for (; t < tend; ++t) iteration<CAUSAL, F16, MASK, PRE, -1>(w, x, t, kbuf, vbuf, vtbuf);
+  }
 }
 
 template <bool CAUSAL, bool F16, bool PRE = false>
@@ -446,18 +494,33 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   w.pf[0] = w.pf[1] = u32x4{};
   const int T = x.T;
   if (T <= 0) return;
-  // prologue: V^T(-1) (ring slot NVT-1, prepared: NVP-1) zeroed, copies of
-  // tiles 0 .. AHEAD-1, V^T(0), S(0)
+  // prologue: V^T(-1) (ring slot NVT-1, prepared: NVP-1) zeroed; copies of
+  // K(0..2) and V(0..2) (prepared: V^T(0..1)); V^T(0); S(0)
   char* vt_m1 = PRE ? vbuf + (NVP - 1) * VTB : vtbuf + (NVT - 1) * VTB;
 #pragma unroll
   for (int i = 0; i < 4; ++i) *(u32x4*)(vt_m1 + 64 * threadIdx.x + 16 * i) = u32x4{};
+  if (PRE) {
+    x.ld.issue_k(0, 0);
+    x.ld.issue_v<true>(0, 0);
+    x.ld.issue_k(1, 1);
+    x.ld.issue_v<true>(1, 1);
+    x.ld.issue_k(2, 2);
+    wait_vm_lds<3 * COPIES / 2>();
+  } else {
 #pragma unroll
-  for (int i = 0; i < AHEAD; ++i) x.ld.issue<PRE>(i, i % NK, i % (PRE ? NVP : NV));
-  wait_vm_lds<(AHEAD - 1) * COPIES>();
+    for (int i = 0; i < AHEAD; ++i) {
+      x.ld.issue_k(i, i % NK);
+      x.ld.issue_v<false>(i, i % NV);
+    }
+    wait_vm_lds<(AHEAD - 1) * COPIES>();
+  }
   barrier();   // tile 0 and the zeros visible
   if (!PRE) transpose_v<F16>(w, vbuf, vtbuf);
   w.s = qk_mfmas(w, kbuf);
-  wait_vm_lds<(AHEAD - 2) * COPIES>();
+  if (PRE)
+    wait_vm_lds<COPIES / 2>();
+  else
+    wait_vm_lds<(AHEAD - 2) * COPIES>();
   barrier();   // tile 1 and V^T(0) visible
   // tiles before the first one that needs a mask for some row of the
   // workgroup (a key past Sk, or past the diagonal of the first row)
@@ -472,8 +535,8 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   }
   tm = __builtin_amdgcn_readfirstlane(tm);
   int t = 0;
-  for (; t < tm; ++t) iteration<CAUSAL, F16, false, PRE>(w, x, t, kbuf, vbuf, vtbuf);
-  for (; t < T; ++t) iteration<CAUSAL, F16, true, PRE>(w, x, t, kbuf, vbuf, vtbuf);
+  iterations<CAUSAL, F16, false, PRE>(w, x, t, tm, kbuf, vbuf, vtbuf);
+  iterations<CAUSAL, F16, true, PRE>(w, x, t, T, kbuf, vbuf, vtbuf);
   // drain: P(T-1).V(T-1); then every copy of the ring has landed, so that
   // nothing writes the LDS after the loop (a redo starts its own copies)
   pv_mfmas<F16>(w, PRE ? vbuf + ((T - 1) % NVP) * VTB : vtbuf + ((T - 1) % NVT) * VTB);
@@ -557,9 +620,15 @@ void prefill_d256_kernel(PrefillArgs a) {
 
   // ---- per-lane LDS offsets
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) w.koff[ks] = kv_off(w.l32, 2 * ks + w.hi);
+  for (int ks = 0; ks < KS; ++ks) {
+    w.koff[ks] = kv_off(w.l32, 2 * ks + w.hi);
+    w.kl[ks] = kbuf + w.koff[ks];
+  }
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) w.vtoff[kk] = vt_off(w.l32, 2 * kk + w.hi);
+  for (int kk = 0; kk < 2; ++kk) {
+    w.vtoff[kk] = vt_off(w.l32, 2 * kk + w.hi);
+    w.vtl[kk] = vbuf + w.vtoff[kk];
+  }
   // transposed reads of the bf16 V tile for conversion unit q (d block
   // 2*wave + q/2, key step q%2): lane (beta = lane/16, j = lane%16)
   // addresses row 16*(q%2) + 8*h + 4*hi + j/4, columns
