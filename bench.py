@@ -546,7 +546,7 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     """Time attn_fwd on the other prefill workloads (same method as the
     headline: inputs resident, HIP events on the launch stream)."""
     res = []
-    steps = max(3, min(args.steps, 10))
+    steps = max(3, min(args.steps, 20))
     # FP8 (E4M3) inputs on the MHA and causal GQA shapes (attn_fwd_fp8)
     def u8(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
@@ -586,7 +586,7 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     def run_h(_i):
         ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd", out=o, lse=lse)
 
-    ms = time_calls(run_h, steps, 2, torch)
+    ms = time_calls(run_h, steps, args.warmup, torch)
     tf = p.flops / (ms * 1e-3) / 1e12
     res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
                 "d": 64, "causal": True, "layout": "bshd", "ms_per_call": round(ms, 4),
@@ -604,7 +604,7 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     def run_h2(_i):
         ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd", out=o, lse=lse)
 
-    ms = time_calls(run_h2, steps, 2, torch)
+    ms = time_calls(run_h2, steps, args.warmup, torch)
     tf = p.flops / (ms * 1e-3) / 1e12
     res.append({"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq, "Sk": p.Sk,
                 "d": 256, "causal": True, "layout": "bshd", "ms_per_call": round(ms, 4),
@@ -623,7 +623,7 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
         ea.attn_fwd(q, k, v, causal=True, scale=p.scale, layout="bshd", out=o, lse=lse,
                     alibi_slopes=sl)
 
-    ms = time_calls(run_a, steps, 2, torch)
+    ms = time_calls(run_a, steps, args.warmup, torch)
     tf = p.flops / (ms * 1e-3) / 1e12
     res.append({"workload": p.name + "_alibi", "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "Sq": p.Sq,
                 "Sk": p.Sk, "causal": True, "layout": "bshd", "ms_per_call": round(ms, 4),
@@ -642,7 +642,7 @@ def extra_workloads(args, gen, ea, torch, dev, to_dev, log):
     def run_v(_i):
         ea.attn_fwd_varlen(q, k, v, cq, ck, pv.max_q, causal=True, scale=pv.scale, out=o, lse=lse)
 
-    ms = time_calls(run_v, steps, 2, torch)
+    ms = time_calls(run_v, steps, args.warmup, torch)
     tf = pv.flops / (ms * 1e-3) / 1e12
     res.append({"workload": pv.name, "B": pv.B, "Hq": pv.Hq, "Hkv": pv.Hkv,
                 "total_tokens": int(pv.cu_q[-1]), "max_seqlen": pv.max_q, "causal": True,
@@ -660,7 +660,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
     workloads.  FLOP = 10*B*Hq*Sq*Sk*d (the five products S, dP, dV, dQ, dK),
     halved when causal."""
     res = []
-    steps = max(3, min(args.steps, 10))
+    steps = max(3, min(args.steps, 20))
     for make, seed in ((gen.config2, 2), (gen.config3, 3)):
         p = make()
         log(f"timing the backward of {p.name}")
@@ -676,7 +676,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
             ea.attn_bwd(q, k, v, o, lse, do, causal=p.causal, scale=p.scale, layout=lay, dq=dq,
                         dk=dk, dv=dv, workspace=ws)
 
-        ms = time_calls(run, steps, 2, torch)
+        ms = time_calls(run, steps, args.warmup, torch)
         fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 128 / (2 if p.causal else 1)
         tf = fl / (ms * 1e-3) / 1e12
         ent = {"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
@@ -704,7 +704,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         ea.attn_bwd(q, k, v, o, lse, do, causal=True, scale=p.scale, layout="bshd", dq=dq, dk=dk,
                     dv=dv, workspace=ws, alibi_slopes=sl)
 
-    ms = time_calls(run_a, steps, 2, torch)
+    ms = time_calls(run_a, steps, args.warmup, torch)
     fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 128 / 2
     res.append({"workload": p.name + "_alibi_backward", "ms_per_call": round(ms, 4), "flop": fl,
                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
@@ -726,7 +726,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         ea.attn_bwd(q, k, v, o, lse, do, causal=True, scale=p.scale, layout="bshd", dq=dq, dk=dk,
                     dv=dv, workspace=ws)
 
-    ms = time_calls(run_d, steps, 2, torch)
+    ms = time_calls(run_d, steps, args.warmup, torch)
     fl = 10.0 * p.B * p.Hq * p.Sq * p.Sk * 64 / 2
     res.append({"workload": p.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
@@ -751,7 +751,7 @@ def backward_workloads(args, gen, ea, torch, to_dev, log):
         ea.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, pv.max_q, pv.max_q, causal=True,
                            scale=pv.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    ms = time_calls(run_v, steps, 2, torch)
+    ms = time_calls(run_v, steps, args.warmup, torch)
     fl = 2.5 * pv.flops
     res.append({"workload": pv.name + "_backward", "ms_per_call": round(ms, 4), "flop": fl,
                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
@@ -789,7 +789,7 @@ def rounding_modes(args, p, ea, torch, q, k, v, o, lse, log):
     """The headline prefill under each rounding rule of the bf16 output (every
     shape is measured under RTNE, RTNA and RTZ on the pages)."""
     res = {}
-    steps = max(3, min(args.steps, 10))
+    steps = max(3, min(args.steps, 20))
     for mode in ROUNDING_MODES:
         log(f"timing {p.name} with rounding {mode}")
 
@@ -797,7 +797,7 @@ def rounding_modes(args, p, ea, torch, q, k, v, o, lse, log):
             ea.attn_fwd(q, k, v, causal=False, scale=p.scale, layout="bhsd", rounding=mode,
                         out=o, lse=lse)
 
-        ms = time_calls(run, steps, 2, torch)
+        ms = time_calls(run, steps, args.warmup, torch)
         res[mode] = {"ms_per_call": round(ms, 4),
                      "TFLOP/s": round(p.flops / (ms * 1e-3) / 1e12, 2)}
     return {"workload": p.name, **res}
