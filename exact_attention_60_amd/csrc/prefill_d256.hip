@@ -442,9 +442,11 @@ __device__ __forceinline__ void iteration(Wave& w, const Ctx& x, int t, char* kb
   w.pf[1] = u32x4{u[4], u[5], u[6], u[7]};
   // lazy-rescale check: each lane's tile sum at most 2^12 (so is every
   // probability, far below the fp16 limit) against a finite running max;
-  // otherwise (rare) the slow path
+  // otherwise (rare) the slow path.  The bf16 redo always takes it: with 8
+  // significant bits the dominant probability of a short, peaky row must be
+  // exactly 1, not a rounded power of two off a stale max.
   float tsum = acc[0] + acc[1];
-  if (wave_any(!(w.m != -INFINITY && tsum <= 4096.f)))
+  if (!F16 || wave_any(!(w.m != -INFINITY && tsum <= 4096.f)))
     tsum = rescale_tile<CAUSAL, F16>(w, x, t, kbuf + kcur * TB);
   w.l += tsum;
   // tile t+2's copies have landed (t+3's may still be in flight), this wave's

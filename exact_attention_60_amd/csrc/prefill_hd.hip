@@ -80,21 +80,6 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A operand of O^T += V^T P^T: column col0 + c of the V rows
-// rbase + 4h + {0..3} and rbase + 8 + 4h + {0..3} (k-slot order of a 32x32
-// accumulator's registers 0..7 in a lane half), by two transpose reads: in
-// each 16-lane group lane j gets element j%4 of the 4-element row addressed by
-// lane 4e + j/4.
-template <int D>
-__device__ __forceinline__ bf16x8 v_cols(const char* tile, int rbase, int col0, int lane) {
-  const int L = lane & 15;
-  const int row = rbase + 4 * (lane >> 5) + (L >> 2);
-  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-  const bf16x4 lo = lds_read_tr(tile + hd_elem<D>(row, col));
-  const bf16x4 hi = lds_read_tr(tile + hd_elem<D>(row + 8, col));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 template <int D>
 struct Copier {
   __amdgpu_buffer_rsrc_t rk, rv;
@@ -138,14 +123,38 @@ struct HdState {
   float l;                      // this lane's part of the row sum
 };
 
-// The tile loop; F16 selects fp16 (else bf16) for P and V.
+// The tile loop; F16 selects fp16 (else bf16) for P and V.  Operand
+// addresses are per-lane offsets computed once (the second 32-key half of a
+// tile, and the rows 16 and 8 further on, keep the same swizzle, so they are
+// instruction offsets).  Lazy rescale as in the d = 128 kernels: the
+// probabilities are taken against the running max as it stands while a
+// lane's sum over the 32 keys stays <= 2^12 (every value then far below the
+// fp16 limit, and O = sum p v / sum p does not depend on the max); a row's
+// first keys, or a larger sum, take the row max, rescale and recompute.  The
+// bf16 redo always takes the row max: with 8 significant bits the dominant
+// probability of a short, peaky row must be exactly 1, not a rounded power
+// of two off a stale max.
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char* kbuf,
                                         char* vbuf, int n_kt, int n_keys, int Sk, int Sq, int off,
                                         int qw0, int wave_last, float c, int lane) {
-  constexpr int TILE = Geom<D>::TILE;
+  constexpr int TILE = Geom<D>::TILE, RB = Geom<D>::RB;
   const int cl = lane & 31, h = lane >> 5;
   const int q = qw0 + cl;
+  // K operand of k-step ks: key row cl of the half, d = 16ks + 8h .. +7
+  int koff[Geom<D>::KS];
+#pragma unroll
+  for (int ks = 0; ks < Geom<D>::KS; ++ks) koff[ks] = hd_off<D>(cl, 2 * ks + h);
+  // V^T operand of d block n (two transposed reads, rows r and r + 8): in
+  // each 16-lane group lane L addresses row 4h + L/4 and the 4 columns from
+  // 32n + 16 ((lane >> 4) & 1) + 4 (L % 4)
+  int voffs[Geom<D>::NTD];
+  {
+    const int L = lane & 15;
+#pragma unroll
+    for (int n = 0; n < Geom<D>::NTD; ++n)
+      voffs[n] = hd_elem<D>(4 * h + (L >> 2), 32 * n + 16 * ((lane >> 4) & 1) + 4 * (L & 3));
+  }
 #pragma unroll
   for (int n = 0; n < Geom<D>::NTD; ++n) w.oacc[n] = f32x16{};
   w.m = -INFINITY;
@@ -181,13 +190,13 @@ __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char
       const bool mask = (CAUSAL && kr0 + 31 > qw0 + off) || (kr0 + 32 > Sk);
       // S^T[key][q]: register r of lane (cl, h) holds key kr0 + 8*(r/4) + 4h + r%4
       // K rows read four k-steps at a time ahead of their MFMAs
+      const char* kh = kt + 32 * ks2 * RB;
       f32x16 s = f32x16{};
 #pragma unroll
       for (int k0 = 0; k0 < Geom<D>::KS; k0 += 4) {
         bf16x8 ka[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ka[i] = *reinterpret_cast<const bf16x8*>(kt + hd_off<D>(32 * ks2 + cl, 2 * (k0 + i) + h));
+        for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kh + koff[k0 + i]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s = mfma32(ka[i], w.qf[k0 + i], s);
@@ -199,38 +208,47 @@ __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char
           if (key >= Sk || (CAUSAL && key > q + off)) s[r] = -INFINITY;
         }
       }
-      // online softmax of row q over these 32 keys (16 per lane half)
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(w.m, mx * c);
-      const float alpha = (m_new == w.m) ? 1.f : fast_exp2(w.m - m_new);
-      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      // probabilities of row q over these 32 keys (16 per lane half) against
+      // msub, packed as the B operand of P.V; returns the lane's sum of the
+      // rounded values
       uint32_t pk[8];
-      float tsum = 0.f;
+      auto probs = [&](float msub) {
+        float t0 = 0.f, t1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[2 * i], c, -msub));
-        const float p1 = fast_exp2(__builtin_fmaf(s[2 * i + 1], c, -msub));
-        pk[i] = F16 ? pack_f16(p0, p1) : pack_bf16(p0, p1);
-        tsum = F16 ? sum2_f16(pk[i], tsum) : sum2_bf16(pk[i], tsum);
-      }
-      w.l = w.l * alpha + tsum;
-      w.m = m_new;
-      // the running max of most rows stops moving after the first tiles:
-      // rescale only when some row of the wave changed it
-      if (wave_any(alpha != 1.f)) {
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[2 * i], c, -msub));
+          const float p1 = fast_exp2(__builtin_fmaf(s[2 * i + 1], c, -msub));
+          pk[i] = F16 ? pack_f16(p0, p1) : pack_bf16(p0, p1);
+          if (i & 1) t1 = F16 ? sum2_f16(pk[i], t1) : sum2_bf16(pk[i], t1);
+          else t0 = F16 ? sum2_f16(pk[i], t0) : sum2_bf16(pk[i], t0);
+        }
+        return t0 + t1;
+      };
+      float tsum = F16 ? probs(w.m == -INFINITY ? 0.f : w.m) : 0.f;
+      if (!F16 || wave_any(!(w.m != -INFINITY && tsum <= 4096.f))) {
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = max_halves(mx);
+        const float m_new = fmaxf(w.m, mx * c);
+        const float alpha = (m_new == w.m) ? 1.f : fast_exp2(w.m - m_new);
+        w.l *= alpha;
 #pragma unroll
         for (int n = 0; n < Geom<D>::NTD; ++n) w.oacc[n] *= alpha;
+        w.m = m_new;
+        tsum = probs(m_new == -INFINITY ? 0.f : m_new);
       }
+      w.l += tsum;
       // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const u32x4 pb = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
+        const char* vr = vt + (32 * ks2 + 16 * u) * RB;
 #pragma unroll
         for (int n = 0; n < Geom<D>::NTD; ++n) {
-          const bf16x8 va = v_cols<D>(vt, 32 * ks2 + 16 * u, 32 * n, lane);
+          const bf16x4 lo = lds_read_tr(vr + voffs[n]);
+          const bf16x4 hi = lds_read_tr(vr + voffs[n] + 8 * RB);
+          const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           if constexpr (F16)
             w.oacc[n] = mfma32(__builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, pb),
                                w.oacc[n]);
