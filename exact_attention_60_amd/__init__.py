@@ -198,6 +198,7 @@ def _rounding_code(rounding: str) -> int:
 # query tiles (256 rows) per K/V head from which attn_fwd prepares V by default
 PREPARE_V_MIN_TILES = 32
 PREPARE_V_MIN_BLOCKS_D256 = 16
+PREPARE_V_MIN_BLOCKS_D64 = 32
 
 
 def attn_prep_v_bytes(B: int, Hq: int, Hkv: int, Sk: int, d: int) -> int:
@@ -207,12 +208,16 @@ def attn_prep_v_bytes(B: int, Hq: int, Hkv: int, Sk: int, d: int) -> int:
 def prepares_v(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int) -> bool:
     """Whether attn_fwd (no ALiBi, prepare_v=None) runs attn_prep_v +
     attn_fwd_prepped for this shape: at d = 128 when each K/V head serves at
-    least PREPARE_V_MIN_TILES query tiles of 256 rows, at d = 256 at least
-    PREPARE_V_MIN_BLOCKS_D256 query blocks of 128 rows (Sq * Hq / Hkv rows per
-    K/V head)."""
+    least PREPARE_V_MIN_TILES query tiles of 256 rows, at d = 256 and d = 64
+    at least PREPARE_V_MIN_BLOCKS_D256 / PREPARE_V_MIN_BLOCKS_D64 query blocks
+    of 128 rows (Sq * Hq / Hkv rows per K/V head)."""
     rows = Sq * (Hq // Hkv)
-    many = ((rows + 127) // 128 >= PREPARE_V_MIN_BLOCKS_D256 if d == 256
-            else (rows + 255) // 256 >= PREPARE_V_MIN_TILES)
+    if d == 256:
+        many = (rows + 127) // 128 >= PREPARE_V_MIN_BLOCKS_D256
+    elif d == 64:
+        many = (rows + 127) // 128 >= PREPARE_V_MIN_BLOCKS_D64
+    else:
+        many = (rows + 255) // 256 >= PREPARE_V_MIN_TILES
     return many and attn_prep_v_bytes(B, Hq, Hkv, Sk, d) > 0
 
 
@@ -231,7 +236,8 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: float | None = None,
     per head costs less than the per-workgroup ones it replaces once each K/V
     head serves enough query rows (measured at d = 128: a net loss at 16 tiles
     of 256 rows, a gain at 128; at d = 256: a loss at 8 blocks of 128 rows, a
-    gain at 32).
+    gain at 32; at d = 64: a loss at 8, even at 64 on a short causal shape, a
+    gain of 4-6 % at 32 and 256).
     Returns (o bf16 in q's layout, lse fp32 [B, Hq, Sq])."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -577,5 +583,5 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
 __all__ = ["attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_paged", "attn_decode_paged_append", "attn_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
            "attn_decode_workspace_bytes", "attn_status_string",
            "attn_version", "attn_prep_v_bytes", "prepares_v", "PREPARE_V_MIN_TILES",
-           "PREPARE_V_MIN_BLOCKS_D256", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
+           "PREPARE_V_MIN_BLOCKS_D256", "PREPARE_V_MIN_BLOCKS_D64", "library", "AttnError", "ATTN_BSHD", "ATTN_BHSD", "ROUNDING", "EXPORTS",
            "LIB_PATH"]

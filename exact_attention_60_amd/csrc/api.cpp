@@ -118,8 +118,9 @@ static int fwd_call(const void* q, const void* k, const void* v, void* o, float*
   a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
   a.alibi = alibi_slopes;
-  const int tk = d == 256 ? attn::kPrefillD256BN : pipe ? attn::kPrefillPipeBN : attn::kPrefillBN;
-  a.vt = d != 64 ? static_cast<const uint8_t*>(vt) : nullptr;
+  const int tk = d == 256 ? attn::kPrefillD256BN : d == 64 ? 64
+                 : pipe ? attn::kPrefillPipeBN : attn::kPrefillBN;
+  a.vt = static_cast<const uint8_t*>(vt);
   a.n_kt = (Sk + tk - 1) / tk;
   int cus = 0;
   const int ds = current_device_cus(&cus);
@@ -183,12 +184,13 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 // keys per prepared tile: the tile size of the kernel that reads them
 static int prep_tile_keys(int Hq, int Hkv, int d) {
   if (d == 256) return attn::kPrefillD256BN;
+  if (d == 64) return 64;
   return uses_pipe(Hq, Hkv, attn::kHeadDim, false) ? attn::kPrefillPipeBN : attn::kPrefillBN;
 }
 
 size_t attn_prep_v_bytes(int B, int Hq, int Hkv, int Sk, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0) return 0;
-  if (d != attn::kHeadDim && d != 256) return 0;
+  if (d != attn::kHeadDim && d != 256 && d != 64) return 0;
   const int tk = prep_tile_keys(Hq, Hkv, d);
   const int64_t n_kt = (Sk + tk - 1) / tk;
   return (size_t)B * Hkv * n_kt * tk * d * 2;
@@ -222,7 +224,9 @@ int attn_prep_v(const void* v, int B, int Hq, int Hkv, int Sk, int d, int layout
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = d == 256 ? attn::launch_prep_v_d256(a, st) : attn::launch_prep_v(a, st);
+  const hipError_t e = d == 256 ? attn::launch_prep_v_d256(a, st)
+                       : d == 64  ? attn::launch_prep_v_d64(a, st)
+                                  : attn::launch_prep_v(a, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

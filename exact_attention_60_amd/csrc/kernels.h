@@ -98,15 +98,19 @@ struct Fp8Args {
 hipError_t launch_prefill_fp8(const Fp8Args& a, bool causal, hipStream_t stream);
 
 // head dims 64 and 256 (dense layouts, no ALiBi): query rows per workgroup
-// (n_qt = ceil(Sq / kPrefillHdRows)) and the launches.  d = 64 takes no
-// prepared tiles (vt null); d = 256 takes them optionally: fp16 V^T tiles of
-// kPrefillD256BN keys written by launch_prep_v_d256 (tk = kPrefillD256BN),
-// row d of 64 bytes holding the tile's keys in the same chunk order and
-// swizzle as the GQA kernel's tiles, kVtD256TileBytes per tile.
+// (n_qt = ceil(Sq / kPrefillHdRows)) and the launches, each optionally on
+// prepared tiles.  d = 64: fp16 V tiles of 64 keys (8 KB: the kernel's LDS
+// image, rows of 128 bytes, 16-byte chunk c of row r at ((c ^ s(r)) << 4)
+// with s(r) = ((r & 3) << 1) | ((r >> 2) & 1)) written by launch_prep_v_d64
+// (tk = 64).  d = 256: fp16 V^T tiles of kPrefillD256BN keys written by
+// launch_prep_v_d256 (tk = kPrefillD256BN), row d of 64 bytes holding the
+// tile's keys in the same chunk order and swizzle as the GQA kernel's tiles,
+// kVtD256TileBytes per tile.
 constexpr int kPrefillHdRows = 128;
 constexpr int kPrefillD256BN = 32;
 constexpr int kVtD256TileBytes = kPrefillD256BN * 256 * 2;
 hipError_t launch_prefill_hd(const PrefillArgs& a, bool causal, hipStream_t stream);   // d = 64
+hipError_t launch_prep_v_d64(const PrepVArgs& a, hipStream_t stream);
 hipError_t launch_prefill_d256(const PrefillArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_prep_v_d256(const PrepVArgs& a, hipStream_t stream);
 

@@ -102,15 +102,31 @@ struct Copier {
       voff[j] = (uint32_t)row * sb + (uint32_t)c * 16;
     }
   }
-  __device__ __forceinline__ void issue(int t, char* kt, char* vt) const {
+  // prepared fp16 V tiles (the LDS image of a converted tile): this wave's
+  // rows are a contiguous IPW KB of the tile
+  __amdgpu_buffer_rsrc_t rvt;
+  uint32_t vt_lane;
+  __device__ void init_vt(const uint8_t* vtp, int n_kt, int wave, int lane) {
+    rvt = __builtin_amdgcn_make_buffer_rsrc((void*)vtp, (short)0,
+                                            (int)((uint32_t)n_kt * (uint32_t)Geom<D>::TILE),
+                                            0x00020000);
+    vt_lane = (uint32_t)(wave * Geom<D>::IPW * 1024 + lane * 16);
+  }
+  // pre: V from the prepared tiles
+  __device__ __forceinline__ void issue(int t, char* kt, char* vt, bool pre) const {
     const uint32_t base = (uint32_t)t * tile_bytes;
 #pragma unroll
     for (int j = 0; j < Geom<D>::IPW; ++j) {
       const int r = row0 + j * Geom<D>::RPI;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ATTN_LDS void*)(kt + r * Geom<D>::RB), 16,
                                                voff[j] + base, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vt + r * Geom<D>::RB), 16,
-                                               voff[j] + base, 0, 0, 0);
+      if (pre)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rvt, (ATTN_LDS void*)(vt + r * Geom<D>::RB), 16,
+            (uint32_t)t * (uint32_t)Geom<D>::TILE + vt_lane + 1024u * j, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(vt + r * Geom<D>::RB), 16,
+                                                 voff[j] + base, 0, 0, 0);
     }
   }
 };
@@ -134,10 +150,15 @@ struct HdState {
 // bf16 redo always takes the row max: with 8 significant bits the dominant
 // probability of a short, peaky row must be exactly 1, not a rounded power
 // of two off a stale max.
-template <int D, bool CAUSAL, bool F16>
+// With prepared tiles (PRE) the V copies bring fp16 rows and there is no
+// conversion.  KPRE is the calling kernel's variant: each kernel instantiates
+// its own copies of the loop (the host pass of the compiler rejects one
+// specialization taking the buffer-descriptor struct from two kernels).
+template <int D, bool CAUSAL, bool F16, bool PRE, bool KPRE>
 __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char* kbuf,
                                         char* vbuf, int n_kt, int n_keys, int Sk, int Sq, int off,
                                         int qw0, int wave_last, float c, int lane) {
+  constexpr bool pre = PRE;
   constexpr int TILE = Geom<D>::TILE, RB = Geom<D>::RB;
   const int cl = lane & 31, h = lane >> 5;
   const int q = qw0 + cl;
@@ -159,13 +180,13 @@ __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char
   for (int n = 0; n < Geom<D>::NTD; ++n) w.oacc[n] = f32x16{};
   w.m = -INFINITY;
   w.l = 0.f;
-  if (n_kt > 0) cp.issue(0, kbuf, vbuf);
+  if (n_kt > 0) cp.issue(0, kbuf, vbuf, pre);
   for (int t = 0; t < n_kt; ++t) {
     const int st = t & 1;
     char* kt = kbuf + st * TILE;
     char* vt = vbuf + st * TILE;
     wait_all();    // this wave's copies of tile t have landed
-    if constexpr (F16) {
+    if constexpr (F16 && !PRE) {
       // bf16 -> fp16 in place for the V rows this wave copied (each lane the
       // 16 bytes its copy instructions wrote), before the barrier publishes
       // the tile; no other wave touches these rows meanwhile
@@ -181,7 +202,7 @@ __device__ __forceinline__ void hd_loop(HdState<D>& w, const Copier<D>& cp, char
       wait_all();
     }
     barrier();   // tile t is complete for every wave; tile t-1 is no longer read
-    if (t + 1 < n_kt) cp.issue(t + 1, kbuf + (st ^ 1) * TILE, vbuf + (st ^ 1) * TILE);
+    if (t + 1 < n_kt) cp.issue(t + 1, kbuf + (st ^ 1) * TILE, vbuf + (st ^ 1) * TILE, pre);
 #pragma unroll
     for (int ks2 = 0; ks2 < Geom<D>::KB / 32; ++ks2) {
       const int kr0 = t * Geom<D>::KB + 32 * ks2;
@@ -274,7 +295,7 @@ __device__ __forceinline__ bool hd_finite(const HdState<D>& w) {
 // VGPRs), three with it (the mask paths need more registers; four would
 // spill).  At d = 256 the Q fragments and O^T alone take 192 registers, and
 // the budget of two waves per SIMD spills: one.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PRE>
 __global__ __launch_bounds__(NT)
 __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : (CAUSAL ? 3 : 4), D > 64 ? 1 : 4)))
 void prefill_hd_kernel(PrefillArgs a) {
@@ -318,12 +339,13 @@ void prefill_hd_kernel(PrefillArgs a) {
   }
   Copier<D> cp;
   cp.init(kp, vp, a.k_ss, Sk, wave, lane);
+  if (PRE) cp.init_vt(a.vt + (int64_t)(b * a.Hkv + hk) * a.n_kt * Geom<D>::TILE, a.n_kt, wave, lane);
 
-  hd_loop<D, CAUSAL, true>(w, cp, kbuf, vbuf, n_kt, n_keys, Sk, Sq, off, qw0, wave_last, a.c,
-                           lane);
+  hd_loop<D, CAUSAL, true, PRE, PRE>(w, cp, kbuf, vbuf, n_kt, n_keys, Sk, Sq, off, qw0,
+                                     wave_last, a.c, lane);
   if (__syncthreads_or(!hd_finite(w)))
-    hd_loop<D, CAUSAL, false>(w, cp, kbuf, vbuf, n_kt, n_keys, Sk, Sq, off, qw0, wave_last, a.c,
-                              lane);
+    hd_loop<D, CAUSAL, false, false, PRE>(w, cp, kbuf, vbuf, n_kt, n_keys, Sk, Sq, off, qw0,
+                                          wave_last, a.c, lane);
 
   // epilogue: O = O^T / l in q's layout (register r of lane (cl, h), d block
   // n: d = 32n + 8*(r/4) + 4h + r%4), LSE = (m + log2 l) ln 2
@@ -347,14 +369,57 @@ void prefill_hd_kernel(PrefillArgs a) {
   }
 }
 
+// V of one (batch, K/V head) as the fp16 tiles of the prepared path: tile t
+// (keys 64t .. 64t+63, zeros past Sk) goes to vt + ((b * Hkv + h) * n_kt + t)
+// * TILE as exactly the LDS image the converting path builds (rows of 128
+// bytes, hd_off's chunk swizzle, each value rounded to fp16, nearest even).
+// HBM-bound: 8 KB read and 8 KB written per tile.
+__global__ __launch_bounds__(256) void prep_v_d64_kernel(PrepVArgs a) {
+  constexpr int D = 64, NC = Geom<D>::NC, TILE = Geom<D>::TILE;
+  const int64_t id = blockIdx.x;
+  const int t = (int)(id % a.n_kt);
+  const int64_t bh = id / a.n_kt;
+  const int h = (int)(bh % a.Hkv);
+  const int b = (int)(bh / a.Hkv);
+  const __bf16* vp = a.v + b * a.k_sb + h * a.k_sh;
+  uint8_t* out = a.vt + id * TILE;
+#pragma unroll
+  for (int pass = 0; pass < TILE / (256 * 16); ++pass) {
+    const int idx = 256 * pass + threadIdx.x;
+    const int row = idx / NC, c = idx % NC;
+    const int key = t * Geom<D>::KB + row;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (key < a.Sk) x = *(const u32x4*)(vp + (int64_t)key * a.k_ss + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+    *(u32x4*)(out + hd_off<D>(row, c)) = x;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_hd(const PrefillArgs& a, bool causal, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * a.Hq * a.n_qt;
-  if (grid <= 0 || grid > 0x7fffffff || a.cu_q || a.alibi || a.vt) return hipErrorInvalidValue;
+  if (grid <= 0 || grid > 0x7fffffff || a.cu_q || a.alibi) return hipErrorInvalidValue;
+  if (a.vt && a.n_kt != (a.Sk + Geom<64>::KB - 1) / Geom<64>::KB) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), bt(NT);
-  if (causal) hipLaunchKernelGGL((prefill_hd_kernel<64, true>), g, bt, 0, stream, a);
-  else hipLaunchKernelGGL((prefill_hd_kernel<64, false>), g, bt, 0, stream, a);
+  if (a.vt) {
+    if (causal) hipLaunchKernelGGL((prefill_hd_kernel<64, true, true>), g, bt, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_hd_kernel<64, false, true>), g, bt, 0, stream, a);
+  } else if (causal) {
+    hipLaunchKernelGGL((prefill_hd_kernel<64, true, false>), g, bt, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_hd_kernel<64, false, false>), g, bt, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_v_d64(const PrepVArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.B * a.Hkv * a.n_kt;
+  if (grid <= 0 || grid > 0x7fffffff || a.tk != Geom<64>::KB ||
+      a.n_kt != (a.Sk + Geom<64>::KB - 1) / Geom<64>::KB)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_v_d64_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

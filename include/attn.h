@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define ATTN_VERSION 12
+#define ATTN_VERSION 13
 
 typedef enum {
   ATTN_OK = 0,
@@ -153,10 +153,12 @@ int attn_fwd_rounded(const void* q, const void* k, const void* v, void* o, float
  * attn_fwd_rounded on the same inputs.
  *
  * attn_prep_v_bytes(B, Hq, Hkv, Sk, d): bytes of the prepared tiles, or 0
- *   where the forward does not use them (d = 64) and for invalid sizes.
- *   d = 128: B * Hkv * ceil(Sk / 64) * 16384, or B * Hkv * ceil(Sk / 32) *
- *   8192 when Hq / Hkv is a multiple of 4 (the kernel for those groups works
- *   on 32-key tiles); d = 256: B * Hkv * ceil(Sk / 32) * 16384.
+ *   for an unsupported head dim and for invalid sizes.  d = 128:
+ *   B * Hkv * ceil(Sk / 64) * 16384, or B * Hkv * ceil(Sk / 32) * 8192 when
+ *   Hq / Hkv is a multiple of 4 (the kernel for those groups works on 32-key
+ *   tiles); d = 256: B * Hkv * ceil(Sk / 32) * 16384; d = 64:
+ *   B * Hkv * ceil(Sk / 64) * 8192 (fp16 V rows; that kernel reads V^T by
+ *   transposing LDS reads).
  * attn_prep_v(v, B, Hq, Hkv, Sk, d, layout, vt, vt_bytes, stream): writes
  *   the tiles of v (bf16, attn_fwd's k/v layout) into vt (device memory,
  *   16-byte aligned, at least attn_prep_v_bytes; owned by the caller).  Each

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ea.attn_version() == 12
+    assert ea.attn_version() == 13
     for code in ea.STATUS:
         assert ea.attn_status_string(code)
     assert ea.attn_status_string(12345) == "unknown status"
@@ -91,8 +91,10 @@ def test_prep_v_bytes():
     assert ea.attn_prep_v_bytes(2, 4, 4, 100, 256) == 2 * 4 * 4 * 16384
     assert ea.attn_prep_v_bytes(4, 32, 8, 4096, 256) == 4 * 8 * 128 * 16384
     assert ea.attn_prep_v_bytes(1, 3, 1, 32, 256) == 16384
+    # head dim 64: tiles of 64 keys (8 KB)
+    assert ea.attn_prep_v_bytes(2, 4, 4, 100, 64) == 2 * 4 * 2 * 8192
+    assert ea.attn_prep_v_bytes(8, 32, 8, 8192, 64) == 8 * 8 * 128 * 8192
     # none for other head dims
-    assert ea.attn_prep_v_bytes(2, 4, 4, 100, 64) == 0
     assert ea.attn_prep_v_bytes(2, 4, 4, 100, 96) == 0
     # invalid sizes
     assert ea.attn_prep_v_bytes(0, 4, 4, 100, 128) == 0
@@ -113,6 +115,7 @@ def prep(**kw):
     (dict(v=P + 2), -4), (dict(vt=P + 8), -4),
     (dict(Sk=(1 << 24) + 1), -2),                  # one head's tiles exceed 32-bit offsets
     (dict(d=256, Sk=(1 << 23) + 1), -2),
+    (dict(d=64, vt=None), -5), (dict(d=64, vtb=2 * 8192 - 1), -5),
     (dict(d=256, vt=None), -5), (dict(d=256, vtb=2 * 16384 - 1), -5), (dict(d=256, vt=P + 8), -4),
 ])
 def test_prep_v_argument_errors(kw, code):
@@ -121,7 +124,6 @@ def test_prep_v_argument_errors(kw, code):
 
 def test_prep_v_without_tiles_is_a_no_op():
     # shapes that do not use the tiles return at once (no device call)
-    assert prep(d=64, vt=None, vtb=0) == 0
     assert prep(d=96, vt=None, vtb=0) == 0
     # groups of 4k heads use them (32-key tiles)
     assert prep(Hq=8, Hkv=2, vt=None, vtb=0) == -5
@@ -141,7 +143,8 @@ def prepped(rounding=0, vt=P, vtb=1 << 62, **kw):
     (dict(vt=None), -1), (dict(vtb=16384 * 2 - 1), -5), (dict(vt=P + 8), -4),
     (dict(Sk=(1 << 24) + 1, Hkv=4), -2),
     # the tiles are ignored where the shape does not use them
-    (dict(vt=None, d=64, scale=0.0), -3), (dict(vt=None, d=64, q=None), -1),
+    (dict(vt=None, d=96), -3),
+    (dict(vt=None, d=64), -1), (dict(d=64, vtb=2 * 8192 - 1), -5),
     (dict(vt=None, Hq=8, Hkv=2), -1), (dict(Hq=8, Hkv=2, vtb=8191), -5),
     (dict(vt=None, d=256), -1), (dict(d=256, vtb=2 * 16384 - 1), -5),
     (dict(d=256, Sk=(1 << 23) + 1, Hkv=4), -2),

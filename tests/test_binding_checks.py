@@ -262,11 +262,14 @@ def test_bwd_varlen_rejects_bad_outputs(lib):
 
 def test_prepares_v_rule_per_head_dim():
     # d = 128: at least 32 query tiles of 256 rows per K/V head; d = 256: at
-    # least 16 query blocks of 128 rows; d = 64 never (no prepared tiles)
+    # least 16 query blocks of 128 rows
     assert not ea.prepares_v(4, 32, 32, 4096, 4096, 128)      # 16 tiles
     assert ea.prepares_v(8, 32, 8, 8192, 8192, 128)           # 128 tiles
     assert ea.prepares_v(4, 32, 8, 4096, 4096, 256)           # 128 blocks
     assert ea.prepares_v(2, 16, 16, 4096, 4096, 256)          # 32 blocks
     assert ea.prepares_v(1, 4, 4, 2048, 2048, 256)            # 16 blocks
     assert not ea.prepares_v(4, 8, 8, 1024, 1024, 256)        # 8 blocks
-    assert not ea.prepares_v(8, 32, 8, 8192, 8192, 64)
+    # d = 64: at least 32 query blocks of 128 rows
+    assert ea.prepares_v(8, 32, 8, 8192, 8192, 64)            # 256 blocks
+    assert ea.prepares_v(4, 32, 32, 4096, 4096, 64)           # 32 blocks
+    assert not ea.prepares_v(4, 8, 8, 1024, 1024, 64)         # 8 blocks

@@ -97,6 +97,38 @@ def test_prepped_equals_single_call_d256(shape):
     both(p)
 
 
+SHAPES_D64 = [
+    # head dim 64: 64-key tiles, 128 query rows per workgroup
+    (1, 2, 2, 1, 1, gen.BSHD, False),
+    (2, 4, 2, 63, 65, gen.BHSD, False),
+    (1, 3, 3, 129, 127, gen.BSHD, True),
+    (1, 2, 1, 400, 150, gen.BSHD, True),      # Sq > Sk: first rows see no key
+    (1, 8, 2, 600, 1000, gen.BSHD, True),
+    (1, 4, 4, 300, 77, gen.BHSD, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_D64, ids=lambda s: "d64_B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s"
+                         % (s[0], s[1], s[2], s[3], s[4], "bshd" if s[5] == 0 else "bhsd",
+                            "causal" if s[6] else "full"))
+def test_prepped_equals_single_call_d64(shape):
+    B, Hq, Hkv, Sq, Sk, layout, causal = shape
+    p = gen.prefill_inputs(B, Hq, Hkv, Sq, Sk, layout=layout, causal=causal, seed=17 + Sq + Sk,
+                           d=64)
+    both(p)
+
+
+def test_prepped_d64_rounding_and_large_v():
+    p = gen.prefill_inputs(1, 4, 2, 300, 500, layout=gen.BSHD, causal=True, seed=9, d=64)
+    for rounding in ("rtna", "rtz"):
+        both(p, rounding)
+    v = (p.v.astype(np.uint32) << 16).view(np.float32).copy()
+    v[:, :, :, 40] = 3.0e5
+    v[0, 333, 1, 9] = -2.0e6
+    p.v = gen.f32_to_bf16_bits(v)
+    both(p)
+
+
 @pytest.mark.parametrize("rounding", ["rtne", "rtna", "rtz"])
 def test_prepped_rounding_rules(rounding):
     p = gen.prefill_inputs(1, 4, 2, 300, 500, layout=gen.BSHD, causal=True, seed=5)
@@ -228,4 +260,33 @@ def test_prepared_d256_tile_layout():
                 for j, key in enumerate(keys):
                     if key < Sk:
                         want[:, :, t, d, 8 * pc + j] = vf[:, key, :, d].astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_prepared_d64_tile_layout():
+    # head dim 64: tile t is the fp16 rows of keys 64t .. 64t+63 (128 bytes
+    # each), 16-byte chunk c of row r at (c ^ s(r)) with
+    # s(r) = ((r & 3) << 1) | ((r >> 2) & 1); keys past Sk are 0
+    B, Hq, Hkv, Sk = 2, 2, 2, 100
+    p = gen.prefill_inputs(B, Hq, Hkv, 1, Sk, layout=gen.BHSD, causal=False, seed=8, d=64)
+    v = dev_bf16(p.v)
+    nvt = ea.attn_prep_v_bytes(B, Hq, Hkv, Sk, 64)
+    assert nvt == B * Hkv * 2 * 8192
+    vt = torch.full((nvt,), 0x55, dtype=torch.uint8, device=v.device)
+    st = ea.library().attn_prep_v(v.data_ptr(), B, Hq, Hkv, Sk, 64, ea.ATTN_BHSD, vt.data_ptr(),
+                                  nvt, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    got = vt.cpu().numpy().view(np.float16).reshape(B, Hkv, 2, 64, 64)
+    vf = (p.v.astype(np.uint32) << 16).view(np.float32)          # [B, Hkv, Sk, d]
+    want = np.zeros((B, Hkv, 2, 64, 64), dtype=np.float16)
+    for t in range(2):
+        for r in range(64):
+            key = 64 * t + r
+            if key >= Sk:
+                continue
+            sw = ((r & 3) << 1) | ((r >> 2) & 1)
+            for c in range(8):
+                pc = c ^ sw
+                want[:, :, t, r, 8 * pc:8 * pc + 8] = vf[:, :, key, 8 * c:8 * c + 8].astype(np.float16)
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
