@@ -61,7 +61,10 @@
 //    lies past the sequence; the heads of one sequence are spread over the
 //    XCDs (spread_groups) so the longest sequences do not share one XCD.
 //  * ALiBi (ALIBI variants): the linear bias is added to the raw scores at
-//    the start of each softmax phase, before the mask and the row max.
+//    the start of each softmax phase, before the mask and the row max.  The
+//    key tiles are taken from the one holding the workgroup's diagonal down
+//    to key 0, then upward (causal: the last tile down to the first), so the
+//    row max is found on the first tiles and the lazy rescale rarely runs.
 #include "gfx950.hpp"
 #include "kernels.h"
 
@@ -438,6 +441,7 @@ __device__ __forceinline__ void softmax_phase(Wave& w, int kbase, int Sk, int of
 struct Ctx {
   TileLoader ld;
   int n_tiles, Sk, off, wave, lane, group;
+  int pivot;     // non-causal ALiBi: the key tile taken first (see tile_loop)
   float c;
   float alibi;   // -slope / scale of this head (ALiBi variants)
 };
@@ -471,8 +475,16 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   w.m_use = -INFINITY;
   w.lsum = 0.f;
   const int T = x.n_tiles;
+  // Step t of the loop works on key tile key_tile(t).  With an ALiBi bias
+  // the tiles go from the pivot (the tile of the diagonal, where the bias of
+  // the workgroup's rows is largest) down to key 0, then up from the pivot:
+  // the first tile sets the row max and later tiles rarely raise it (the
+  // lazy rescale stays on its fast path); in key order the max of a row
+  // would grow with nearly every tile up to its diagonal.
+  const int pivot = CAUSAL ? T - 1 : x.pivot;
+  auto key_tile = [&](int t) { return !ALIBI ? t : t <= pivot ? pivot - t : t; };
   auto visible = [&](int t) {
-    return t >= 0 && t < T && w.first <= w.last && (!CAUSAL || t * BN <= w.last + x.off);
+    return t >= 0 && t < T && w.first <= w.last && (!CAUSAL || key_tile(t) * BN <= w.last + x.off);
   };
   const bool g0 = x.group == 0;
   Prefetch pf;
@@ -481,12 +493,12 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
   // copy of K(t) (group 1) or V(t) (group 0); returns how many copies were issued
   auto issue_kt = [&](int t) {
     if (t >= T) return 0;
-    x.ld.issue_k(t, kslot(t));
+    x.ld.issue_k(key_tile(t), kslot(t));
     return 4;
   };
   auto issue_vt = [&](int t) {
     if (t >= T) return 0;
-    x.ld.issue_v(t, vslot(t));
+    x.ld.issue_v(key_tile(t), vslot(t));
     return 4;
   };
   if (g0) {
@@ -511,8 +523,8 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
       wait_copies();                                    // V(t), copied in phase 2t-1
     } else {
       const int n_new = issue_kt(t + 2);
-      if (visible(t - 1)) softmax_phase<CAUSAL, F16, ALIBI>(w, (t - 1) * BN, x.Sk, x.off, x.c,
-                                                                   x.alibi);
+      if (visible(t - 1)) softmax_phase<CAUSAL, F16, ALIBI>(w, key_tile(t - 1) * BN, x.Sk, x.off,
+                                                                   x.c, x.alibi);
       wait_copies_but(n_new);
       pre = visible(t);
       if (pre) prefetch_k(pf, w, kt);                   // K(t) is visible since phase 2t-1
@@ -521,7 +533,8 @@ __device__ __forceinline__ void tile_loop(Wave& w, const Ctx& x, char* kbuf, cha
     // ---- phase 2t+1
     if (g0) {
       issue_vt(t + 1);
-      if (visible(t)) softmax_phase<CAUSAL, F16, ALIBI>(w, t * BN, x.Sk, x.off, x.c, x.alibi);
+      if (visible(t))
+        softmax_phase<CAUSAL, F16, ALIBI>(w, key_tile(t) * BN, x.Sk, x.off, x.c, x.alibi);
       pre = visible(t + 1);
       if (pre) prefetch_k(pf, w, knext);                // K(t+1) is visible since the mid barrier
     } else {
@@ -703,6 +716,10 @@ void prefill_kernel(PrefillArgs a) {
   int n_keys = Sk;
   if (CAUSAL) n_keys = min(Sk, max(0, last_row + x.off + 1));
   x.n_tiles = (n_keys + BN - 1) / BN;
+  // non-causal: the tile holding the diagonal key (i + off) of the
+  // workgroup's middle row (the causal loop takes its last tile)
+  const int mid_key = min(q0 + BM / 2, Sq - 1) + x.off;
+  x.pivot = min(max(mid_key, 0) / BN, max(x.n_tiles - 1, 0));
   // 32-row blocks interleaved between the groups: SIMD s holds blocks 2s, 2s+1
   const int rb = 2 * (x.wave & 3) + x.group;
   w.first = q0 + 32 * rb;
