@@ -164,7 +164,11 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.Sq = max_seqlen_q;
   a.Sk = 0;
   a.group = Hq / Hkv;
-  a.n_qt = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  // groups of 4k query heads run the GQA kernel (64-row query tiles of four
+  // heads), others the 8-wave kernel (256-row tiles of one head)
+  const bool pipe = uses_pipe(Hq, Hkv, d, false);
+  const int rows = pipe ? attn::kPrefillPipeRows : attn::kPrefillBM;
+  a.n_qt = (max_seqlen_q + rows - 1) / rows;
   if ((int64_t)B * Hq * a.n_qt > INT32_MAX) return ATTN_ERR_SHAPE;
   a.c = scale * 1.4426950408889634f;
   a.rounding = rounding;
@@ -176,7 +180,9 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   int cus = 0;
   const int ds = current_device_cus(&cus);
   if (ds != ATTN_OK) return ds;
-  const hipError_t e = attn::launch_prefill(a, causal != 0, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = pipe ? attn::launch_prefill_pipe(a, causal != 0, st)
+                            : attn::launch_prefill(a, causal != 0, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

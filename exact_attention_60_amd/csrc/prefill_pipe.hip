@@ -62,6 +62,11 @@
 //    (workgroups are dealt to the 8 XCDs round robin); causal launches also
 //    keep the query tiles running at once on an XCD within one or two heads
 //    (causal_xcd_order), so the K/V tiles they stream are shared in L2.
+//  * Packed sequences of different lengths (cu_q/cu_k offsets, V converted
+//    in the kernel): a workgroup reads its sequence's offsets first and
+//    returns at once if its query tile lies past the sequence; head groups
+//    are dealt to the XCDs interleaved (every XCD gets a share of each
+//    sequence) and each XCD runs the causal order above over its groups.
 #include "gfx950.hpp"
 #include "kernels.h"
 
@@ -600,7 +605,20 @@ void prefill_pipe_kernel(PrefillArgs a) {
   const int NHG = a.Hq / NW;               // groups of 4 query heads per batch entry
   const int NBH = a.B * NHG;
   int bhg, qt;
-  if (CAUSAL && (NBH & 7) == 0) {
+  if (a.cu_q && (NBH & 7) == 0) {
+    // packed sequences: the causal order below over head groups dealt to the
+    // XCDs interleaved (XCD x takes groups x, x + 8, ...: every XCD gets a
+    // share of each sequence, so none is left with the longest ones), each
+    // XCD running 32 query tiles of one group at a time (its K/V in L2)
+    int h;
+    causal_xcd_order(blockIdx.x, NBH, a.n_qt, h, qt);
+    const int hpx = NBH >> 3;
+    bhg = (h % hpx) * 8 + h / hpx;
+  } else if (a.cu_q) {
+    const int row = blockIdx.x / NBH;      // heaviest query tiles first
+    qt = a.n_qt - 1 - row;
+    bhg = blockIdx.x - row * NBH;
+  } else if (CAUSAL && (NBH & 7) == 0) {
     causal_xcd_order(blockIdx.x, NBH, a.n_qt, bhg, qt);
   } else if (CAUSAL) {
     const int row = blockIdx.x / NBH;      // heaviest query tiles first
@@ -614,11 +632,28 @@ void prefill_pipe_kernel(PrefillArgs a) {
   const int b = bhg / NHG;
   const int hq = (bhg - b * NHG) * NW + w.wave;   // this wave's query head
   const int hk = hq / a.group;
-  const int Sq = a.Sq, Sk = a.Sk;
+  // this sequence's rows: the whole [B, ...] batch entry, or (packed
+  // sequences) rows cu_q[b] .. cu_q[b+1]-1 of q and cu_k[b] .. cu_k[b+1]-1 of
+  // k/v, offsets clamped to the packed sizes
+  int Sq = a.Sq, Sk = a.Sk;
+  int64_t qbase = b * a.q_sb, kbase = b * a.k_sb;
+  int64_t lse_base = (int64_t)(b * a.Hq + hq) * a.Sq;
+  if (a.cu_q) {
+    const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
+    const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
+    const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
+    const int k_hi = min(max(a.cu_k[b + 1], k_lo), a.total_k);
+    Sq = min(q_hi - q_lo, a.Sq);         // a.Sq is the longest query length here
+    Sk = k_hi - k_lo;
+    qbase = (int64_t)q_lo * a.q_ss;
+    kbase = (int64_t)k_lo * a.k_ss;
+    lse_base = (int64_t)hq * a.total_q + q_lo;
+  }
   const int q0 = qt * 64;
-  const __bf16* __restrict__ qp = a.q + b * a.q_sb + hq * a.q_sh;
-  const __bf16* kp = a.k + b * a.k_sb + hk * a.k_sh;
-  const __bf16* vp = a.v + b * a.k_sb + hk * a.k_sh;
+  if (q0 >= Sq) return;                  // whole workgroup: past this sequence's rows
+  const __bf16* __restrict__ qp = a.q + qbase + hq * a.q_sh;
+  const __bf16* kp = a.k + kbase + hk * a.k_sh;
+  const __bf16* vp = a.v + kbase + hk * a.k_sh;
 
   Ctx x;
   x.off = Sk - Sq;
@@ -714,7 +749,7 @@ void prefill_pipe_kernel(PrefillArgs a) {
         }
   });
   wait_vm_lds<0>();
-  __bf16* ob = a.o + b * a.q_sb + hq * a.q_sh;
+  __bf16* ob = a.o + qbase + hq * a.q_sh;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int rr = 4 * k + (lane >> 4), cc = lane & 15;
@@ -728,7 +763,7 @@ void prefill_pipe_kernel(PrefillArgs a) {
       const int row = w.first[rb] + w.l32;
       if (row < Sq) {
         const float l = w.l[rb];
-        a.lse[(int64_t)(b * a.Hq + hq) * Sq + row] =
+        a.lse[lse_base + row] =
             (l > 0.f) ? (w.m[rb] + __log2f(l)) * kLn2 : -INFINITY;
       }
     }
@@ -738,7 +773,7 @@ void prefill_pipe_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_pipe(const PrefillArgs& a, bool causal, hipStream_t stream) {
-  if (a.cu_q || a.alibi || a.group % NW) return hipErrorInvalidValue;
+  if ((a.cu_q && a.vt) || a.alibi || a.group % NW) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)a.B * (a.Hq / NW) * a.n_qt;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
   if (a.vt && a.n_kt != (a.Sk + BN - 1) / BN) return hipErrorInvalidValue;

@@ -41,6 +41,11 @@ def check(p, o, lse, what):
     ([12, 3, 0, 400], [30, 3, 8, 700], False, 4, 4),          # cross lengths, keys-only sequence
     ([513, 64], [0, 64], False, 2, 1),                        # a sequence with no keys at all
     ([1000, 37, 600], [1000, 37, 600], True, 4, 1),           # MQA, several query tiles
+    # groups of 4k query heads: the GQA kernel (64-row tiles of four heads)
+    ([5, 0, 17, 1, 65], [7, 3, 17, 1, 20], True, 8, 2),        # empty, tiny, Sq > Sk rows
+    ([12, 3, 0, 400], [30, 3, 8, 700], False, 8, 2),          # cross lengths, keys-only sequence
+    ([513, 64, 1], [0, 64, 1], False, 4, 1),                  # a sequence with no keys at all
+    ([700, 129, 63], [700, 129, 63], True, 16, 2),            # groups of 8, ragged tails
 ])
 def test_varlen_all_elements(lq, lk, causal, Hq, Hkv):
     p = gen.varlen_inputs(lq, lk, Hq, Hkv, causal=causal, seed=sum(lq) + sum(lk))
@@ -71,6 +76,23 @@ def test_varlen_equals_dense_per_sequence():
         torch.cuda.synchronize()
         assert torch.equal(od[0].view(torch.int16), o[q0:q1].view(torch.int16))
         assert torch.equal(ld[0], lse[:, q0:q1])
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2)], ids=["group2", "group4"])
+def test_varlen_equals_dense_per_sequence_groups(Hq, Hkv):
+    """Groups of 2 run the 8-wave kernel and groups of 4 the GQA kernel, in
+    both calls: each sequence bitwise equals its dense call (V converted in
+    the kernel, as the packed call does)."""
+    p = gen.varlen_inputs([200, 77, 300, 1], [260, 77, 300, 40], Hq, Hkv, causal=True, seed=9)
+    o, lse = run(p)
+    for b in range(p.B):
+        q0, q1, k0, k1 = (int(x) for x in (p.cu_q[b], p.cu_q[b + 1], p.cu_k[b], p.cu_k[b + 1]))
+        od, ld = ea.attn_fwd(dev_bf16(p.q[q0:q1][None]), dev_bf16(p.k[k0:k1][None]),
+                             dev_bf16(p.v[k0:k1][None]), causal=True, scale=p.scale, layout="bshd",
+                             prepare_v=False)
+        torch.cuda.synchronize()
+        assert torch.equal(od[0].view(torch.int16), o[q0:q1].view(torch.int16)), b
+        assert torch.equal(ld[0], lse[:, q0:q1]), b
 
 
 def test_packed_prompt_batch_sampled():
