@@ -254,11 +254,16 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, f
  *   B, Hq, Hkv, total_q, total_k, max_seqlen_q >= 1, Hq % Hkv == 0, d == 128
  *   rounding  one of ATTN_ROUND_* for O
  *
+ * Each sequence's O and LSE equal, bit for bit, those of attn_fwd_rounded on
+ * that sequence alone (the same kernel runs both: groups of 4k query heads
+ * the GQA kernel, other groups the 256-row kernel).
+ *
  * The offsets live on the device and are not read by the host; out-of-order
  * or out-of-range values are clamped to [0, total] (memory-safe, results for
  * such sequences unspecified).  Size limits (ATTN_ERR_SHAPE):
- * (total_k - 1) * Hkv * 256 + 256 < 2^31 and B * Hq * ceil(max_seqlen_q / 256)
- * < 2^31.  Other statuses as for attn_fwd_rounded.
+ * (total_k - 1) * Hkv * 256 + 256 < 2^31 and B * Hq * ceil(max_seqlen_q / R)
+ * < 2^31, R = 64 when Hq / Hkv is a multiple of 4, else 256.  Other statuses
+ * as for attn_fwd_rounded.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
