@@ -8,7 +8,8 @@ import attn_inputs as gen
 import exact_attention_60_amd as ea
 import oracle.attention as att
 from gpu_util import dev_bf16, host_f64, logical_o, need_gpu
-from tolerance import check_lse, check_o
+from tolerance import (P_UNIT_BF16, check_lse, check_lse_bf16_fallback, check_o,
+                       check_o_large_v, pv_spread_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +77,31 @@ def test_zero_slopes_match_plain_attention(causal):
     # l sums fp16-rounded probabilities taken against each order's running
     # max: up to 2^-11 relative in l, i.e. about 5e-4 in LSE, per kernel
     assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_alibi_v_beyond_fp16_range(causal):
+    """V entries far beyond the fp16 range take the bf16 redo of the tile loop,
+    which runs the key tiles in the same order from the diagonal outward;
+    a constant V column still gives that constant."""
+    p = gen.prefill_inputs(1, 4, 2, 300, 1500, layout=gen.BSHD, causal=causal, seed=84)
+    v = (p.v.astype(np.uint32) << 16).view(np.float32).copy()
+    v[:, :, :, 5] = 3.0e5
+    v[0, 700, 1, 9] = -2.0e6
+    p.v = gen.f32_to_bf16_bits(v)
+    sl = slopes(4)
+    o, lse = run(p, sl)
+    o_ref, l_ref = att.attention(p.q, p.k, p.v, 1, 4, 2, 300, 1500, p.scale, causal, p.layout,
+                                 alibi_slopes=sl)
+    # every tile holds V beyond fp16, so the whole problem runs with bf16
+    # probabilities: the large-V bound with the bf16 unit, probabilities of
+    # the biased scores (ALiBi makes the rows peaky, where 8 bits of P exceed
+    # the plain 2-ulp bound)
+    spread = pv_spread_prefill(p, unit=P_UNIT_BF16, alibi_slopes=sl)
+    check_o_large_v(logical_o(o, p.layout), o_ref, spread, "alibi huge V")
+    check_lse_bf16_fallback(host_f64(lse), l_ref, "alibi huge V lse")
+    # 3e5 rounds to the bf16 value 299008 (spacing 2048 there)
+    assert np.all(host_f64(o)[..., 5] == 299008.0)
 
 
 def test_alibi_causal_gqa_full_size_sampled_group():

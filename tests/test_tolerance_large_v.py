@@ -89,3 +89,32 @@ def test_spread_closed_form_for_two_keys():
     spread = pv_spread_rows(q, k, v, 1.0)
     assert np.allclose(spread, P_UNIT_F16 * (0.75 * 100 + 0.25 * 300))
     assert np.all(o_tolerance(o_ref) < spread)
+
+
+def test_lse_bound_on_the_bf16_fallback():
+    """Emulated bf16 probabilities (exact row max, so the largest one is 1)
+    on peaky rows: l sums the rounded values; the LSE error stays within
+    1e-3 + 2^-8 and on some rows exceeds the fp16-path bound of 1e-3."""
+    import attn_inputs as gen
+    from tolerance import LSE_ABS, P_UNIT_BF16
+    r = np.random.default_rng(7)
+    worst = 0.0
+    for _ in range(200):
+        n = int(r.integers(2, 64))
+        s = r.standard_normal(n) * float(r.choice([0.5, 2.0, 6.0]))   # flat to peaky rows
+        m = s.max()
+        p = np.exp(s - m).astype(np.float32)
+        pb = (gen.f32_to_bf16_bits(p).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        lse_emul = m + np.log(pb.sum())
+        lse_exact = m + np.log(np.exp(s - m).sum())
+        err = abs(lse_emul - lse_exact)
+        assert err <= LSE_ABS + P_UNIT_BF16
+        worst = max(worst, err)
+    # a row whose probabilities all sit just below a bf16 rounding midpoint,
+    # (1 + 0.99 * 2^-8) * 2^-j: every one rounds down by almost 2^-8 of itself
+    p = np.concatenate([[1.0], (1.0 + 0.99 * 2.0 ** -8) * 2.0 ** -np.arange(1, 11)])
+    s = np.log(p)
+    pb = (gen.f32_to_bf16_bits(p.astype(np.float32)).astype(np.uint32) << 16).view(np.float32)
+    err = abs(np.log(pb.astype(np.float64).sum()) - np.log(np.exp(s).sum()))
+    assert LSE_ABS < err <= LSE_ABS + P_UNIT_BF16
+    assert worst <= LSE_ABS + P_UNIT_BF16

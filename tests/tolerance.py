@@ -73,21 +73,29 @@ def check_lse(lse, lse_ref, what=""):
 #     |O - O_ref| <= 2 ulp_bf16(|O_ref|) + 1e-3 + (1 + 2^-4) * spread,
 #     spread = sum_j max(u pi_j, 2^-25 / l) |v_j - O_ref|
 # (the factor 1 + 2^-4 covers the second-order terms and the fp32
-# accumulation).  LSE does not depend on V and keeps its bound.
+# accumulation).  LSE does not depend on V; it keeps its bound where the
+# probabilities are fp16 (l moves by at most 2^-11 relative).  On the bf16
+# fallback l sums bf16-rounded probabilities: l~/l - 1 = sum_j pi_j e_j with
+# |e_j| <= 2^-8, so LSE is checked against 1e-3 + 2^-8 there
+# (check_lse_bf16_fallback).
 
 P_UNIT_F16 = 2.0 ** -11
 P_UNIT_BF16 = 2.0 ** -8
 P_SUB_F16 = 2.0 ** -25
 
 
-def pv_spread_rows(q, k, v, scale, n_visible=None, unit=P_UNIT_F16):
+def pv_spread_rows(q, k, v, scale, n_visible=None, unit=P_UNIT_F16, bias=None):
     """spread for query rows q [n, d] against keys k, values v [Sk, d]
-    (float64), row i limited to keys 0..n_visible[i]-1.  Returns [n, d]."""
+    (float64), row i limited to keys 0..n_visible[i]-1; bias [n, Sk] (an
+    ALiBi bias) is added to the scaled scores, so pi are the probabilities of
+    the biased scores.  Returns [n, d]."""
     import oracle.attention as att
     n, d = q.shape[0], v.shape[1]
     if k.shape[0] == 0:
         return np.zeros((n, d))
     s = att.scores(q, k, scale)
+    if bias is not None:
+        s = s + bias
     if n_visible is not None:
         j = np.arange(k.shape[0])
         s = np.where(j[None, :] >= np.asarray(n_visible)[:, None], -np.inf, s)
@@ -101,8 +109,9 @@ def pv_spread_rows(q, k, v, scale, n_visible=None, unit=P_UNIT_F16):
     return spread
 
 
-def pv_spread_prefill(p, unit=P_UNIT_F16):
-    """spread [B, Hq, Sq, d] for a generator prefill problem (bf16 bits)."""
+def pv_spread_prefill(p, unit=P_UNIT_F16, alibi_slopes=None):
+    """spread [B, Hq, Sq, d] for a generator prefill problem (bf16 bits),
+    with the ALiBi bias of query head h when alibi_slopes [Hq] is given."""
     import oracle.attention as att
     qv = att._logical(p.q, p.layout)
     kv = att._logical(p.k, p.layout)
@@ -113,9 +122,28 @@ def pv_spread_prefill(p, unit=P_UNIT_F16):
     for b in range(p.B):
         for h in range(p.Hq):
             g = att.kv_head_of(h, p.Hq, p.Hkv)
+            bias = None
+            if alibi_slopes is not None:
+                bias = att.alibi_bias(np.arange(p.Sq), p.Sq, p.Sk, alibi_slopes[h])
             out[b, h] = pv_spread_rows(att.bf16_to_f64(qv[b, h]), att.bf16_to_f64(kv[b, g]),
-                                       att.bf16_to_f64(vv[b, g]), sc, nvis, unit)
+                                       att.bf16_to_f64(vv[b, g]), sc, nvis, unit, bias)
     return out
+
+
+def check_lse_bf16_fallback(lse, lse_ref, what=""):
+    """LSE of a problem that ran with bf16 probabilities (V beyond the fp16
+    range): |LSE - LSE_ref| <= 1e-3 + 2^-8, -inf rows exact."""
+    lse = np.asarray(lse, dtype=np.float64)
+    lse_ref = np.asarray(lse_ref, dtype=np.float64)
+    assert lse.shape == lse_ref.shape
+    ninf = lse_ref == -np.inf
+    assert np.all(lse[ninf] == -np.inf), f"{what}: empty rows must give LSE=-inf"
+    err = np.abs(lse[~ninf] - lse_ref[~ninf])
+    if err.size:
+        i = int(np.argmax(err))
+        assert err.max() <= LSE_ABS + P_UNIT_BF16, f"{what}: LSE err {err[i]:.3g} at flat {i}"
+        return float(err.max())
+    return 0.0
 
 
 def check_o_large_v(o, o_ref, spread, what=""):
