@@ -34,11 +34,10 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def randn(shape, seed, scale=1.0):
+def randn(shape, seed):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
-    return x.mul_(scale) if scale != 1.0 else x
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
 
 
 def _shape(layout, B, H, S, d):
