@@ -332,11 +332,22 @@ def fwd_varlen(**kw):
     (dict(q=None), -1), (dict(cq=None), -1), (dict(ck=None), -1), (dict(lse=None), -1),
     (dict(B=0), -2), (dict(tq=0), -2), (dict(tk=0), -2), (dict(maxq=0), -2),
     (dict(Hq=3, Hkv=2), -2), (dict(tk=(1 << 21) + 2, Hkv=4), -2),
+    # groups of 4k query heads launch 64-row query tiles: B * Hq * ceil(maxq / 64) >= 2^31
+    (dict(B=1024, Hq=8, Hkv=2, maxq=1 << 25), -2),
     (dict(d=64), -3), (dict(causal=2), -3), (dict(scale=0.0), -3), (dict(rounding=3), -3),
     (dict(q=P + 8), -4), (dict(o=P + 2), -4), (dict(cq=P + 2), -4), (dict(ck=P + 1), -4),
 ])
 def test_fwd_varlen_argument_errors(kw, code):
     assert fwd_varlen(**kw) == code
+
+
+def test_fwd_varlen_launch_limit_follows_the_group_size():
+    """The same sizes with groups of 2 (256-row query tiles) stay within the
+    launch limit and fail only for want of a device."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; valid arguments would launch")
+    assert fwd_varlen(B=1024, Hq=8, Hkv=4, maxq=1 << 25) == -7
 
 
 def test_fwd_varlen_valid_arguments_need_a_gfx950_device():
