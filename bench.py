@@ -241,7 +241,7 @@ def sampled_parity(p, d, snap):
 
 def oracle_threads():
     """Worker threads for the oracle beside the GPU: one per core this process
-    may use, at most 16 (the host share of one GPU on the benchmark boxes)."""
+    may use, at most 16 (one GPU's share of the host cores of an 8-GPU node)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -272,7 +272,7 @@ def cpu_baseline(p, budget_s, torch):
             "sample": f"{heads} of {p.B * p.Hq} (b,h) heads of the same workload, all "
                       f"{p.Sq} query rows x {p.Sk} keys, fp64 NumPy, {workers} worker threads "
                       f"x 1 BLAS thread (BLAS pool size {blas}); {dt:.1f} s; the thread count "
-                      f"is capped at 16, the host share of one GPU on the benchmark boxes",
+                      f"is capped at 16, one GPU's share of the host cores of an 8-GPU node",
             "seconds": dt}
 
 

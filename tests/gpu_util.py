@@ -48,7 +48,7 @@ def logical_o(o: torch.Tensor, layout: int) -> np.ndarray:
 
 def oracle_workers():
     """Host threads for the oracle beside a GPU test: one per core this
-    process may use, at most 16 (a one-GPU machine's share of its host)."""
+    process may use, at most 16 (one GPU's share of the host cores of an 8-GPU node)."""
     import os
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
